@@ -1,0 +1,208 @@
+/*
+ * plp.h -- C ABI of the fused LM-head + GRPO-family policy loss for AMD
+ * MI355X (gfx950).
+ *
+ * One hot path: hidden states h[N,H] and the LM-head weight W[V,H] (optional
+ * bias b[V]) give the target-token log-probabilities and per-token entropies
+ * through a streaming online log-sum-exp over vocabulary tiles (the
+ * [N,V] logits are never stored), then the GMPO or GSPO-token objective with
+ * an optional K3 KL penalty and an optional batch-global high-entropy token
+ * mask, then grad_h, grad_W and grad_b.
+ *
+ * Definitions the entry points implement:
+ *   - GMPO: Liger-Kernel PR #1320 "Add GMPO to fused linear GRPO loss",
+ *     Summary and "The implementation" bullets (one-sided, advantage-dependent
+ *     clipping of each token's log-ratio in log space [-eps_low, +eps_high];
+ *     exp of the masked mean per completion; per-sample reduction; K3 KL;
+ *     clipping metric; outer chunking; input/weight/bias gradients).
+ *   - Streaming entropy and the high-entropy mask: Liger-Kernel PR #1558
+ *     "support top_entropy_quantile", Details bullets (second accumulator
+ *     sum exp(z-m)*z; H = log_z - sum_exp_z/sum_exp; threshold
+ *     quantile(active entropies, 1-q) over the whole batch; the mask
+ *     multiplies the policy term before the KL penalty; q validated to [0,1],
+ *     q = 1 is the feature off).
+ *   - GSPO-token: Tinker "GSPO" page, the sequence-ratio, per-token-ratio and
+ *     objective equations, "Input tensors", "Output diagnostics" and
+ *     "Choosing clipping thresholds".
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE memory owned by the caller. The library
+ *     allocates nothing, never frees or retains a pointer after it returns,
+ *     and uses only the caller's workspace (size from the matching
+ *     *_workspace_size query; the workspace must be 256-byte aligned).
+ *   - Calls only enqueue work on `stream`; outputs are valid once the stream
+ *     has reached that point. Loss and metrics stay in device memory: no
+ *     call synchronises with the host.
+ *   - Every argument check happens on the host before any launch. On error
+ *     nothing is enqueued, a negative PLP_E_* code is returned and
+ *     plp_last_error() (thread-local) describes it.
+ *   - Results are deterministic: the same inputs, sizes and build give
+ *     bitwise-equal outputs (no floating-point atomics).
+ *   - Calls from different host threads are safe when they use distinct
+ *     workspaces; calls that share a workspace on overlapping streams race.
+ *
+ * Layouts: row-major. hidden [N,H] with the B sequences stored one after the
+ * other, T rows each (row n = i*T + t); weight [V,H] (nn.Linear layout);
+ * per-token arrays [N]; advantages [B].
+ */
+#ifndef PLP_H
+#define PLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PLP_API __attribute__((visibility("default")))
+#define PLP_ABI_VERSION 1
+
+/* Return codes. */
+#define PLP_OK 0
+#define PLP_E_INVALID (-1)      /* bad shape, NULL where required, value out of range */
+#define PLP_E_UNSUPPORTED (-2)  /* a combination the method excludes */
+#define PLP_E_WORKSPACE (-3)    /* workspace NULL, misaligned or too small */
+#define PLP_E_HIP (-4)          /* a HIP launch or runtime call failed */
+
+typedef enum { PLP_DTYPE_F32 = 0, PLP_DTYPE_BF16 = 1 } plp_dtype;
+
+/* GMPO: Liger PR #1320. GSPO_TOKEN: Tinker GSPO page (GSPO-token variant). */
+typedef enum { PLP_LOSS_GMPO = 0, PLP_LOSS_GSPO_TOKEN = 1 } plp_loss_type;
+
+/* Importance-sampling level. GMPO rejects SEQUENCE (PR #1320: it clips at
+ * token level before the sequence aggregation); GSPO_TOKEN is inherently a
+ * sequence-level ratio and takes SEQUENCE. */
+typedef enum { PLP_IS_TOKEN = 0, PLP_IS_SEQUENCE = 1 } plp_is_level;
+
+/* SEQ_MEAN: masked mean over each sequence's completion tokens, then the mean
+ * over the B sequences (the per-sample reduction PR #1320 reuses).
+ * TOKEN_SUM: plain sum over completion tokens (the Tinker page's loss:sum). */
+typedef enum { PLP_REDUCE_SEQ_MEAN = 0, PLP_REDUCE_TOKEN_SUM = 1 } plp_reduction;
+
+/* Metrics layout (fp32, PLP_NUM_METRICS entries). */
+enum {
+  PLP_M_CLIP_FRACTION = 0,        /* clipped completion tokens / completion tokens (GSPO: a
+                                     sequence's verdict counts for each of its tokens) */
+  PLP_M_SEQ_LOG_RATIO_MEAN = 1,   /* mean over sequences of mean_{ratio tokens} (lp - old) */
+  PLP_M_CLIPPED_SEQ_FRACTION = 2, /* GSPO: share of sequences whose ratio left the clip range
+                                     (either side); GMPO: 0 */
+  PLP_M_MEAN_KL = 3,              /* mean over sequences of the masked-mean K3 KL (0 without ref) */
+  PLP_M_ENTROPY_THRESHOLD = 4,    /* batch-global entropy threshold; NaN when q = 1 or no
+                                     completion token */
+  PLP_M_ENTROPY_KEPT_FRACTION = 5,/* completion tokens kept by the entropy mask / completion tokens */
+  PLP_M_ACTIVE_TOKENS = 6,        /* number of completion tokens */
+  PLP_M_CLIPPED_TOKENS = 7,       /* number of clipped completion tokens */
+  PLP_NUM_METRICS = 8
+};
+
+/* Inputs of the fused call. Versioned by struct_size (set it to
+ * sizeof(plp_args)); fields are only ever appended. */
+typedef struct plp_args {
+  uint32_t struct_size;
+  int32_t dtype;                /* plp_dtype of hidden, weight, bias and the gradients */
+  int64_t B, T;                 /* sequences, tokens per sequence; N = B*T rows */
+  int32_t H, V;                 /* hidden size, vocabulary size */
+  const void* hidden;           /* [N,H] dtype */
+  const void* weight;           /* [V,H] dtype */
+  const void* bias;             /* [V] dtype, or NULL */
+  const int64_t* targets;       /* [N] token ids in [0,V) */
+  const float* old_logp;        /* [N] sampler log-probs, or NULL = on-policy (log-ratio 0) */
+  const float* ref_logp;        /* [N] KL reference log-probs; required iff beta != 0 */
+  const uint8_t* completion_mask; /* [N] nonzero = token enters the loss */
+  const uint8_t* ratio_mask;    /* [N] nonzero = token enters the sequence ratio and clip;
+                                   NULL = completion_mask (Tinker: sequence_ratio_mask) */
+  const float* advantages;      /* [B] per-sequence advantage */
+  int32_t loss_type;            /* plp_loss_type */
+  int32_t is_level;             /* plp_is_level */
+  int32_t reduction;            /* plp_reduction */
+  int32_t pad0;
+  double epsilon_low;           /* GMPO: log-space lower bound -eps_low; GSPO: ratio 1-eps_low */
+  double epsilon_high;          /* GMPO: log-space upper bound +eps_high; GSPO: ratio 1+eps_high */
+  double beta;                  /* K3 KL weight (>= 0) */
+  double temperature;           /* logits are divided by it (> 0) */
+  double top_entropy_quantile;  /* q in [0,1]; 1 = no entropy mask */
+  int64_t chunk_sequences;      /* outer chunk in whole sequences; 0 = all B at once */
+} plp_args;
+
+/* Outputs of the fused call. Every pointer except loss and metrics may be
+ * NULL to skip that output. Gradients have the input dtype. */
+typedef struct plp_outputs {
+  uint32_t struct_size;
+  uint32_t pad0;
+  float* loss;                  /* [1] */
+  float* metrics;               /* [PLP_NUM_METRICS] */
+  void* grad_hidden;            /* [N,H] */
+  void* grad_weight;            /* [V,H] */
+  void* grad_bias;              /* [V]; requires bias != NULL */
+  float* logp_out;              /* [N] target log-probs */
+  float* entropy_out;           /* [N] entropies */
+  uint8_t* entropy_mask_out;    /* [N] 1 = kept by the entropy mask (all completion tokens when q=1) */
+  float* dlogp_out;             /* [N] dL/dlogp */
+} plp_outputs;
+
+/* Version of this ABI (PLP_ABI_VERSION). */
+PLP_API int plp_abi_version(void);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+PLP_API const char* plp_last_error(void);
+
+/* Workspace bytes needed by plp_fused_lmhead_policy_loss_fwd_bwd for these
+ * arguments (only sizes, dtype, bias/NULL-ness, q and chunk_sequences are
+ * read; pointers may be NULL). Host-only arithmetic: needs no GPU. */
+PLP_API int plp_workspace_size(const plp_args* args, size_t* bytes);
+
+/* The whole path: forward statistics, entropy mask (q < 1), loss, metrics and
+ * the gradients asked for in `out` (Liger PR #1320 fused linear GMPO; PR
+ * #1558 entropy masking; Tinker GSPO-token). Outer chunks of
+ * chunk_sequences whole sequences bound the per-chunk workspace; the entropy
+ * threshold and the batch mean are global, so results do not depend on the
+ * chunk size beyond rounding. Errors: PLP_E_INVALID (shapes, NULLs, q outside
+ * [0,1], beta != 0 without ref_logp, temperature <= 0, negative eps or beta,
+ * chunk_sequences < 0), PLP_E_UNSUPPORTED (GMPO with SEQUENCE importance
+ * sampling; GSPO_TOKEN with TOKEN), PLP_E_WORKSPACE, PLP_E_HIP. */
+PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* args, const plp_outputs* out,
+                                                 void* workspace, size_t workspace_bytes,
+                                                 hipStream_t stream);
+
+/* Streaming entropy and target log-prob over vocabulary tiles without
+ * storing logits (PR #1558 "_selective_entropy_forward": running (m, sum
+ * exp(z-m), sum exp(z-m) z), rescaled when the max moves;
+ * H = log_z - sum_exp_z/sum_exp). hidden [N,H], weight [V,H], bias [V] or
+ * NULL, all of `dtype`. targets [N] or NULL (then logp_out must be NULL).
+ * entropy_out [N] fp32 (required), logp_out [N] fp32 or NULL. */
+PLP_API int plp_selective_entropy_workspace_size(int64_t N, int32_t H, int32_t V, int32_t dtype,
+                                                 size_t* bytes);
+PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const void* bias,
+                                  int64_t N, int32_t H, int32_t V, int32_t dtype, float temperature,
+                                  const int64_t* targets, float* entropy_out, float* logp_out,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Batch-global high-entropy mask (PR #1558, Details bullet 2):
+ * thr = quantile(entropy[active], 1 - q) with torch.quantile's linear
+ * interpolation evaluated in fp32; mask_out[n] = active[n] && entropy[n] >= thr.
+ * No active entry: all-zero mask and thr = NaN. q = 1: mask = active, thr = NaN.
+ * entropy [N] fp32, active [N] u8, mask_out [N] u8, threshold_out [1] fp32
+ * (may be NULL). q outside [0,1] -> PLP_E_INVALID. */
+PLP_API int plp_entropy_quantile_mask_workspace_size(int64_t N, size_t* bytes);
+PLP_API int plp_entropy_quantile_mask(const float* entropy, const uint8_t* active, int64_t N, double q,
+                                      uint8_t* mask_out, float* threshold_out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/* The loss stage alone, from given per-token log-probs (the GMPO / GSPO-token
+ * / K3 KL objective of the pages without the LM head). args: as for the fused
+ * call; hidden, weight, bias and targets are ignored, H and V may be 0.
+ * logp [N] fp32. entropy [N] fp32 is required iff top_entropy_quantile < 1.
+ * out: loss and metrics required; dlogp_out and entropy_mask_out optional;
+ * the gradient, logp_out and entropy_out pointers are ignored. */
+PLP_API int plp_policy_loss_workspace_size(const plp_args* args, size_t* bytes);
+PLP_API int plp_policy_loss_from_logprobs(const plp_args* args, const float* logp, const float* entropy,
+                                          const plp_outputs* out, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PLP_H */

@@ -1,0 +1,147 @@
+// Shared types and launcher declarations of the plp HIP library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace plp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Per (vocabulary split, row) result of the forward sweep: the reference m
+// all exponentials are taken against, sum exp(z-m), sum exp(z-m) z, the
+// target logit when the target falls in the split, and a flag asking the
+// merge to recompute the row exactly (a logit far above the reference).
+struct alignas(8) RowStats {
+  float m;
+  float zy;
+  double s;
+  double sz;
+  int flag;
+  int pad;
+};
+
+// Per compacted token, what the weight-gradient sweep needs.
+struct alignas(16) TokData {
+  float lse;   // log-sum-exp of the token's logits
+  float gs;    // dL/dlogp / temperature
+  int y;       // target id
+  int pad;
+};
+
+// Loss and metric accumulators carried across outer chunks (fp64 sums,
+// integer counts) so the batch-level values are chunk independent.
+struct LossAcc {
+  double loss;
+  double slr;          // sum over sequences of the mean ratio-token log-ratio
+  double mkl;          // sum over sequences of the masked-mean KL
+  unsigned long long n_active, n_clip, n_kept, n_clipseq;
+  float thr;
+  int pad;
+};
+
+// Per-sequence partial sums of the loss stage.
+struct SeqPart {
+  double sum_c;        // GMPO: sum over ratio tokens of the clipped log-ratio
+  double sum_lr;       // sum over ratio tokens of the log-ratio
+  double sum_kl;       // sum over completion tokens of the K3 KL
+  int cnt_m, cnt_r, cnt_k, cnt_clip;
+};
+
+// Per-sequence coefficients of dL/dlogp.
+struct SeqCoef {
+  double pol;          // policy-term coefficient applied to eligible tokens
+  double wbeta;        // w_i * beta
+  float adv;
+  int pad;
+};
+
+struct LossParams {
+  int64_t B_total;     // batch size dividing the per-sample reduction
+  int64_t T;
+  int loss_type;       // 0 GMPO, 1 GSPO_TOKEN
+  int reduction;       // 0 seq mean, 1 token sum
+  float eh32, el32;    // fp32(eps_high), fp32(eps_low)
+  float lo32, hi32;    // GSPO ratio bounds fp32(1-eps_low), fp32(1+eps_high)
+  double beta;
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (each enqueues on `st`; return hipError_t of the launch)
+// ---------------------------------------------------------------------------
+
+// Blocked transposed copy used as the second MFMA operand of the
+// probability-weighted sums: rows [0, rows_pad) of X (or X[idx[k]] when idx
+// is given; rows beyond `rows` are zero) into Xt[rows_pad/32][4][H][8], and,
+// when Xc is not NULL, a compact natural-layout copy Xc[rows_pad][H].
+hipError_t launch_blocked_copy_bf16(const __bf16* X, const int* idx, const int* count_dev,
+                                    int64_t rows, int64_t rows_pad, int H, __bf16* Xt, __bf16* Xc,
+                                    hipStream_t st);
+
+// Forward sweep on MFMA (bf16, H a multiple of 128, H <= 896).
+hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* W, const __bf16* Wt, const __bf16* b,
+                           const int64_t* y, int64_t N, int H, int V, float inv_tau, int Sv,
+                           bool with_o, RowStats* stats, float* O, hipStream_t st);
+
+// Weight-gradient sweep on MFMA over compacted tokens.
+hipError_t launch_bwd_mfma(const __bf16* W, const __bf16* b, const __bf16* hc, const __bf16* ht,
+                           const TokData* tok, const int* count_dev, int64_t n_cap, int H, int V,
+                           float inv_tau, int acc_mode, float* gW_acc, float* gb_acc, __bf16* gW_out,
+                           __bf16* gb_out, hipStream_t st);
+
+// Generic (VALU) forward and weight-gradient sweeps for any H and fp32 or bf16.
+hipError_t launch_fwd_generic(int dtype, const void* h, const void* W, const void* b, const int64_t* y,
+                              int64_t N, int H, int V, float inv_tau, bool with_o, RowStats* stats,
+                              float* O, hipStream_t st);
+hipError_t launch_bwd_generic(int dtype, const void* W, const void* b, const void* hc,
+                              const TokData* tok, const int* count_dev, int H, int V, float inv_tau,
+                              int acc_mode, float* gW_acc, float* gb_acc, void* gW_out, void* gb_out,
+                              hipStream_t st);
+
+// Merge vocabulary splits: lp, H, lse per row and (when vout != NULL)
+// v = sum_v p W_v - W_y as fp32 [N,H]. Rows flagged by the sweep are
+// recomputed here from h, W, b with an exact online max.
+hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int Sv, int64_t N, int H, int V,
+                          const void* h, const void* W, const void* b, float inv_tau, const int64_t* y,
+                          float* lp, float* ent, float* lse, float* vout, hipStream_t st);
+
+// Loss stage.
+hipError_t launch_loss_zero(LossAcc* acc, hipStream_t st);
+hipError_t launch_loss_seq_partial(const LossParams& p, int64_t Bc, const float* lp, const float* old,
+                                   const float* ref, const uint8_t* comp, const uint8_t* ratio,
+                                   const uint8_t* emask, const float* adv, int St, SeqPart* part,
+                                   hipStream_t st);
+hipError_t launch_loss_seq_final(const LossParams& p, int64_t Bc, int St, const SeqPart* part, const float* adv,
+                                 SeqCoef* coef, LossAcc* acc, hipStream_t st);
+hipError_t launch_loss_token_grad(const LossParams& p, int64_t Bc, const float* lp, const float* old,
+                                  const float* ref, const uint8_t* comp, const uint8_t* ratio,
+                                  const uint8_t* emask, const SeqCoef* coef, float* g, hipStream_t st);
+hipError_t launch_loss_finalize(const LossAcc* acc, int64_t B_total, float* loss, float* metrics,
+                                hipStream_t st);
+
+// grad_h = g / tau * v, cast to dtype.
+hipError_t launch_grad_h(int dtype, const float* g, const float* v, int64_t N, int H, float inv_tau,
+                         void* gh, hipStream_t st);
+
+// Token compaction for the weight-gradient sweep: idx of tokens with g != 0
+// in order, their count (device), and the per-token data.
+size_t compact_scratch_bytes(int64_t N);
+hipError_t launch_compact(const float* g, const float* lse, const int64_t* y, int64_t N, float inv_tau,
+                          int* idx, TokData* tok, int* count_dev, void* scratch, hipStream_t st);
+hipError_t launch_gather_rows(int dtype, const void* X, const int* idx, const int* count_dev, int64_t cap,
+                              int H, void* Xc, hipStream_t st);
+
+// Entropy quantile mask.
+size_t select_scratch_bytes();
+hipError_t launch_entropy_select(const float* ent, const uint8_t* active, int64_t N, float p32,
+                                 float* thr_dev, void* scratch, hipStream_t st);
+hipError_t launch_entropy_mask(const float* ent, const uint8_t* active, int64_t N, const float* thr_dev,
+                               uint8_t* mask, hipStream_t st);
+hipError_t launch_store_thr(const float* thr_dev, LossAcc* acc, float* thr_out, hipStream_t st);
+hipError_t launch_copy_mask(const uint8_t* src, int64_t N, uint8_t* dst, hipStream_t st);
+hipError_t launch_set_nan(float* dst, hipStream_t st);
+
+}  // namespace plp

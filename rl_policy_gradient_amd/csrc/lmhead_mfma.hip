@@ -1,0 +1,501 @@
+// MFMA (bf16, gfx950) sweeps of the LM head.
+//
+// Both the forward sweep and the weight-gradient sweep have the shape of an
+// attention block with a very wide head (head dim = hidden size H):
+//   resident rows  Q [64, H]        (forward: 64 token rows of h;
+//                                     weight grad: 64 vocabulary rows of W)
+//   streamed tiles KV[32, H]        (forward: 32 vocabulary rows of W;
+//                                     weight grad: 32 compacted token rows of h)
+//   S^T = KV Q^T                    logits of the tile, contraction over H
+//   P   = epilogue(S)               forward: exp(z - m) with the running max m
+//                                   weight grad: g (onehot - softmax) / tau
+//   Acc += P KV                     forward: sum_v e^{z-m} W_v (for grad_h)
+//                                   weight grad: sum_t dz h_t  (grad_W)
+//
+// H is split across the 4 waves of a workgroup: wave w owns columns
+// [w*H/4, (w+1)*H/4) of Q, of every KV tile and of Acc, so a wave only ever
+// touches its own slice of the streamed tile. The partial S^T of each wave
+// (its slice of the contraction) is reduce-scattered through LDS: wave w ends
+// up with the complete logits of resident-row block w, runs the epilogue on
+// them, and the bf16 P fragments are all-gathered through LDS for the P KV
+// product. The P KV product contracts over tile rows, so its KV operand comes
+// from a blocked transposed copy KVt[tile][g][H][8] (see
+// launch_blocked_copy_bf16) in which the 8 tile rows a lane needs for one
+// column are contiguous.
+//
+// MFMA: v_mfma_f32_16x16x32_bf16. Lane l holds A[l%16][8(l/16)+j],
+// B[8(l/16)+j][l%16] (j = 0..7) and D[4(l/16)+i][l%16] (i = 0..3).
+// The rows of a 32-row tile that lane-group g = l/16 holds after the S^T
+// product are kv(g,j) = 4g+j (j<4) and 16+4g+(j-4) (j>=4); the same order is
+// used as the contraction index of the P KV product, for both operands.
+#include "common.h"
+
+#include <math.h>
+
+namespace plp {
+
+namespace {
+
+constexpr int BQ = 64;   // resident rows per workgroup
+constexpr int BK = 32;   // streamed rows per tile
+constexpr int NW = 4;    // waves per workgroup
+// The forward sweep fixes each row's exponent reference m at the max of the
+// row's first tile and never rescales the accumulator (a rescale of the
+// register-resident accumulator does not fit the register file). A later
+// logit above m + kRefSlack would make e^{z-m} exceed e^64; the row is then
+// flagged and the merge kernel recomputes it exactly. e^64 ~ 6e27 keeps every
+// running sum far inside fp32 and bf16 range.
+constexpr float kRefSlack = 64.0f;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int kv_of(int g, int j) { return j < 4 ? 4 * g + j : 12 + 4 * g + j; }
+
+__device__ __forceinline__ bf16x8 ld16(const __bf16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// Blocked transposed copy: Xt[tile][g][d][j] = X[src(32*tile + kv(g,j))][d]
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void blocked_copy_kernel(const __bf16* __restrict__ X,
+                                                           const int* __restrict__ idx,
+                                                           const int* __restrict__ count_dev,
+                                                           int64_t rows_host, int H,
+                                                           __bf16* __restrict__ Xt,
+                                                           __bf16* __restrict__ Xc) {
+  extern __shared__ uint4 smem_u4[];
+  unsigned short* tile = reinterpret_cast<unsigned short*>(smem_u4);  // [32][H]
+  const int64_t rows = count_dev ? (int64_t)(*count_dev) : rows_host;
+  const int64_t t0 = (int64_t)blockIdx.x * BK;
+  if (t0 >= rows) return;  // tile entirely past the last row (block-uniform)
+  const int cpr = H / 8;   // 16-byte chunks per row
+  for (int c = threadIdx.x; c < BK * cpr; c += blockDim.x) {
+    const int r = c / cpr, cc = c - r * cpr;
+    const int64_t k = t0 + r;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (k < rows) {
+      const int64_t src = idx ? (int64_t)idx[k] : k;
+      v = *reinterpret_cast<const uint4*>(X + src * H + cc * 8);
+    }
+    *reinterpret_cast<uint4*>(tile + r * H + cc * 8) = v;
+    if (Xc) *reinterpret_cast<uint4*>(Xc + k * H + cc * 8) = v;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 4 * H; e += blockDim.x) {
+    const int g = e / H, d = e - g * H;
+    unsigned short u[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) u[j] = tile[kv_of(g, j) * H + d];
+    uint4 v;
+    v.x = u[0] | ((unsigned)u[1] << 16);
+    v.y = u[2] | ((unsigned)u[3] << 16);
+    v.z = u[4] | ((unsigned)u[5] << 16);
+    v.w = u[6] | ((unsigned)u[7] << 16);
+    *reinterpret_cast<uint4*>(Xt + (((int64_t)blockIdx.x * 4 + g) * H + d) * 8) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward sweep: per token row, running (m, sum e^{z-m}, sum e^{z-m} z), the
+// target logit, and (WITH_O) the accumulator O = sum_v e^{z-m} W_v.
+// Grid: (row blocks) x Sv vocabulary splits, block id = rb * Sv + split.
+// ---------------------------------------------------------------------------
+template <int KB, bool WITH_O>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
+                     const __bf16* __restrict__ Wt, const __bf16* __restrict__ bias,
+                     const int64_t* __restrict__ y, int64_t N, int V, float inv_tau, int Sv,
+                     int tiles_per_split, RowStats* __restrict__ stats, float* __restrict__ O) {
+  constexpr int H = 128 * KB;
+  constexpr int DS = 32 * KB;  // columns per wave
+  constexpr int DB = 2 * KB;   // 16-wide column blocks per wave
+  __shared__ f32x4 s_part[NW][2][4][64];
+  __shared__ bf16x8 s_p[4][64];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int rb = blockIdx.x / Sv, sv = blockIdx.x - rb * Sv;
+  const int64_t q0 = (int64_t)rb * BQ;
+  const int d0 = w * DS;
+  const int n_tiles = (V + BK - 1) / BK;
+  const int t_begin = sv * tiles_per_split;
+  const int t_end = min(n_tiles, t_begin + tiles_per_split);
+
+  // Resident h fragments (B operand of S^T): rows q0+16nb+c16, cols d0+32kb+8g.
+  bf16x8 qf[4][KB];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t row = min(q0 + 16 * nb + c16, N - 1);
+    const __bf16* src = h + row * H + d0 + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) qf[nb][kb] = ld16(src + 32 * kb);
+  }
+
+  f32x4 o[4][WITH_O ? DB : 1];
+  if constexpr (WITH_O) {
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[qb][db] = zero4();
+  }
+
+  const int64_t my_row = q0 + 16 * w + c16;  // row whose epilogue this lane runs
+  const int64_t yv = (y != nullptr && my_row < N) ? y[my_row] : -1;
+  float m_ref = -INFINITY;
+  double s_run = 0.0, sz_run = 0.0;
+  float zy = 0.f;
+  bool have_y = false, flag = false;
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int v0 = t * BK;
+    // ---- S^T partial over this wave's columns --------------------------------
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero4();
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int v = min(v0 + 16 * mb + c16, V - 1);  // rows past V are masked in the epilogue
+      const __bf16* src = W + (int64_t)v * H + d0 + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = ld16(src + 32 * kb);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a, qf[nb][kb], acc[mb][nb]);
+      }
+    }
+    // keep the accumulator-operand loads below the logit MFMAs: both operand
+    // sets live at once would not fit the register file
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 bt[WITH_O ? DB : 1];
+    if constexpr (WITH_O) {
+      const __bf16* src = Wt + (((int64_t)t * 4 + g) * H + d0 + c16) * 8;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) bt[db] = ld16(src + 16 * 8 * db);
+    }
+    // ---- reduce-scatter: wave w collects row block w -------------------------
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) s_part[w][mb][nb][lane] = acc[mb][nb];
+    __syncthreads();
+    f32x4 sf[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x4 r = s_part[0][mb][w][lane];
+#pragma unroll
+      for (int src = 1; src < NW; ++src) r += s_part[src][mb][w][lane];
+      sf[mb] = r;
+    }
+    // ---- epilogue on row my_row, tile rows kv(g, j) -------------------------
+    float z[8];
+    bool ok[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int v = v0 + kv_of(g, j);
+      ok[j] = v < V;
+      const float sv_ = j < 4 ? sf[0][j] : sf[1][j - 4];
+      const float bv = bias ? (float)bias[min(v, V - 1)] : 0.f;
+      z[j] = ok[j] ? (sv_ + bv) * inv_tau : -INFINITY;
+    }
+    float mx = z[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    if (t == t_begin) m_ref = mx;
+    flag |= mx > m_ref + kRefSlack;
+    float p[8], sp = 0.f, szp = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = ok[j] ? __expf(fminf(z[j] - m_ref, kRefSlack)) : 0.f;
+      sp += p[j];
+      szp += ok[j] ? p[j] * z[j] : 0.f;
+    }
+    sp += shfl_xor_f(sp, 16);
+    sp += shfl_xor_f(sp, 32);
+    szp += shfl_xor_f(szp, 16);
+    szp += shfl_xor_f(szp, 32);
+    s_run += (double)sp;
+    sz_run += (double)szp;
+    {
+      const int64_t rel = yv - v0;
+      if (rel >= 0 && rel < BK) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (kv_of(g, j) == (int)rel) {
+            zy = z[j];
+            have_y = true;
+          }
+      }
+    }
+    if constexpr (WITH_O) {
+      bf16x8 pa;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pa[j] = (__bf16)p[j];
+      s_p[w][lane] = pa;
+    }
+    __syncthreads();
+    if constexpr (WITH_O) {
+      bf16x8 pf[4];
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) pf[qb] = s_p[qb][lane];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], bt[db], o[qb][db]);
+    }
+  }
+
+  // ---- results ---------------------------------------------------------------
+  float zyv = have_y ? zy : 0.f;
+  zyv += shfl_xor_f(zyv, 16);
+  zyv += shfl_xor_f(zyv, 32);
+  if (g == 0 && my_row < N) {
+    RowStats rs;
+    rs.m = m_ref;
+    rs.zy = zyv;
+    rs.s = s_run;
+    rs.sz = sz_run;
+    rs.flag = flag ? 1 : 0;
+    rs.pad = 0;
+    stats[(int64_t)sv * N + my_row] = rs;
+  }
+  if constexpr (WITH_O) {
+    float* Ob = O + (int64_t)sv * N * H;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = q0 + 16 * qb + 4 * g + i;
+        if (row < N) {
+          float* dst = Ob + row * H + d0 + c16;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) dst[16 * db] = o[qb][db][i];
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight-gradient sweep: per vocabulary row v, over compacted tokens t,
+//   dz[t,v] = gs_t ([v = y_t] - exp(z[t,v] - lse_t)),  gs_t = g_t / tau
+//   grad_W[v] += sum_t dz[t,v] h_t,   grad_b[v] += sum_t dz[t,v]
+// acc_mode: 0 write the output dtype; 1 store fp32 accumulator; 2 add into it;
+// 3 add the fp32 accumulator and write the output dtype.
+// ---------------------------------------------------------------------------
+template <int KB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bias,
+                     const __bf16* __restrict__ hc, const __bf16* __restrict__ ht,
+                     const TokData* __restrict__ tok, const int* __restrict__ count_dev, int V,
+                     float inv_tau, int acc_mode, float* __restrict__ gW_acc,
+                     float* __restrict__ gb_acc, __bf16* __restrict__ gW_out,
+                     __bf16* __restrict__ gb_out) {
+  constexpr int H = 128 * KB;
+  constexpr int DS = 32 * KB;
+  constexpr int DB = 2 * KB;
+  __shared__ f32x4 s_part[NW][2][4][64];
+  __shared__ bf16x8 s_p[4][64];
+  __shared__ TokData s_tok[BK];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int q0 = blockIdx.x * BQ;
+  const int d0 = w * DS;
+  const int n_tok = *count_dev;
+  const int n_tiles = (n_tok + BK - 1) / BK;
+
+  bf16x8 qf[4][KB];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int v = min(q0 + 16 * nb + c16, V - 1);
+    const __bf16* src = W + (int64_t)v * H + d0 + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) qf[nb][kb] = ld16(src + 32 * kb);
+  }
+  f32x4 o[4][DB];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[qb][db] = zero4();
+
+  const int my_v = q0 + 16 * w + c16;
+  const float bv = bias ? (float)bias[min(my_v, V - 1)] : 0.f;
+  double gb_run = 0.0;
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int t0 = t * BK;
+    if (w == 0 && lane < BK) s_tok[lane] = tok[t0 + lane];
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero4();
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const __bf16* src = hc + (int64_t)(t0 + 16 * mb + c16) * H + d0 + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = ld16(src + 32 * kb);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a, qf[nb][kb], acc[mb][nb]);
+      }
+    }
+    bf16x8 bt[DB];
+    {
+      const __bf16* src = ht + (((int64_t)t * 4 + g) * H + d0 + c16) * 8;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) bt[db] = ld16(src + 16 * 8 * db);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) s_part[w][mb][nb][lane] = acc[mb][nb];
+    __syncthreads();
+    f32x4 sf[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x4 r = s_part[0][mb][w][lane];
+#pragma unroll
+      for (int src = 1; src < NW; ++src) r += s_part[src][mb][w][lane];
+      sf[mb] = r;
+    }
+    bf16x8 pa;
+    float gsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kv = kv_of(g, j);
+      const TokData td = s_tok[kv];
+      const float sv_ = j < 4 ? sf[0][j] : sf[1][j - 4];
+      const float z = (sv_ + bv) * inv_tau;
+      const float pr = __expf(z - td.lse);
+      float dz = td.gs * ((td.y == my_v ? 1.f : 0.f) - pr);
+      dz = (t0 + kv < n_tok && my_v < V) ? dz : 0.f;
+      gsum += dz;
+      pa[j] = (__bf16)dz;
+    }
+    gb_run += (double)gsum;
+    s_p[w][lane] = pa;
+    __syncthreads();
+    bf16x8 pf[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) pf[qb] = s_p[qb][lane];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], bt[db], o[qb][db]);
+  }
+
+  // grad_b: the four lane groups of a row hold disjoint token subsets
+  double gbv = gb_run;
+  gbv += __shfl_xor(gbv, 16, 64);
+  gbv += __shfl_xor(gbv, 32, 64);
+  const bool from_acc = acc_mode == 2 || acc_mode == 3;
+  const bool to_acc = acc_mode == 1 || acc_mode == 2;
+  if (g == 0 && my_v < V && (to_acc ? gb_acc != nullptr : gb_out != nullptr)) {
+    double val = gbv;
+    if (from_acc) val += (double)gb_acc[my_v];
+    if (to_acc) gb_acc[my_v] = (float)val;
+    else gb_out[my_v] = (__bf16)(float)val;
+  }
+  if (to_acc ? gW_acc == nullptr : gW_out == nullptr) return;
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = q0 + 16 * qb + 4 * g + i;
+      if (v < V) {
+        const int64_t base = (int64_t)v * H + d0 + c16;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          float val = o[qb][db][i];
+          const int64_t k = base + 16 * db;
+          if (from_acc) val += gW_acc[k];
+          if (to_acc) gW_acc[k] = val;
+          else gW_out[k] = (__bf16)val;
+        }
+      }
+    }
+}
+
+template <int KB>
+hipError_t fwd_dispatch(const __bf16* h, const __bf16* W, const __bf16* Wt, const __bf16* b,
+                        const int64_t* y, int64_t N, int V, float inv_tau, int Sv, int tps, bool with_o,
+                        RowStats* stats, float* O, hipStream_t st) {
+  const int64_t nrb = (N + BQ - 1) / BQ;
+  dim3 grid((unsigned)(nrb * Sv)), block(256);
+  if (with_o)
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true>), grid, block, 0, st, h, W, Wt, b, y, N, V, inv_tau, Sv,
+                       tps, stats, O);
+  else
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false>), grid, block, 0, st, h, W, Wt, b, y, N, V, inv_tau, Sv,
+                       tps, stats, O);
+  return hipGetLastError();
+}
+
+template <int KB>
+hipError_t bwd_dispatch(const __bf16* W, const __bf16* b, const __bf16* hc, const __bf16* ht,
+                        const TokData* tok, const int* count_dev, int V, float inv_tau, int acc_mode,
+                        float* gW_acc, float* gb_acc, __bf16* gW_out, __bf16* gb_out, hipStream_t st) {
+  dim3 grid((unsigned)((V + BQ - 1) / BQ)), block(256);
+  hipLaunchKernelGGL((bwd_mfma_kernel<KB>), grid, block, 0, st, W, b, hc, ht, tok, count_dev, V, inv_tau,
+                     acc_mode, gW_acc, gb_acc, gW_out, gb_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_blocked_copy_bf16(const __bf16* X, const int* idx, const int* count_dev, int64_t rows,
+                                    int64_t rows_pad, int H, __bf16* Xt, __bf16* Xc, hipStream_t st) {
+  const int64_t tiles = rows_pad / BK;
+  if (tiles <= 0) return hipSuccess;
+  const size_t lds = (size_t)BK * H * sizeof(__bf16);
+  hipLaunchKernelGGL(blocked_copy_kernel, dim3((unsigned)tiles), dim3(256), lds, st, X, idx, count_dev, rows, H,
+                     Xt, Xc);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* W, const __bf16* Wt, const __bf16* b,
+                           const int64_t* y, int64_t N, int H, int V, float inv_tau, int Sv, bool with_o,
+                           RowStats* stats, float* O, hipStream_t st) {
+  const int n_tiles = (V + BK - 1) / BK;
+  const int tps = (n_tiles + Sv - 1) / Sv;
+  switch (H / 128) {
+    case 1: return fwd_dispatch<1>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 2: return fwd_dispatch<2>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 3: return fwd_dispatch<3>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 4: return fwd_dispatch<4>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 5: return fwd_dispatch<5>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 6: return fwd_dispatch<6>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 7: return fwd_dispatch<7>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_mfma(const __bf16* W, const __bf16* b, const __bf16* hc, const __bf16* ht,
+                           const TokData* tok, const int* count_dev, int64_t n_cap, int H, int V,
+                           float inv_tau, int acc_mode, float* gW_acc, float* gb_acc, __bf16* gW_out,
+                           __bf16* gb_out, hipStream_t st) {
+  (void)n_cap;
+  switch (H / 128) {
+    case 1: return bwd_dispatch<1>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 2: return bwd_dispatch<2>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 3: return bwd_dispatch<3>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 4: return bwd_dispatch<4>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 5: return bwd_dispatch<5>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 6: return bwd_dispatch<6>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 7: return bwd_dispatch<7>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace plp

@@ -1,0 +1,666 @@
+// Everything after the logits: split merge, the GMPO / GSPO-token / K3 KL
+// loss stage, grad_h, token compaction for the weight-gradient sweep, and the
+// batch-global entropy quantile mask. All reductions run in a fixed order, so
+// results are bitwise reproducible.
+#include "common.h"
+#include "generic_row.h"
+
+#include <math.h>
+
+namespace plp {
+
+namespace {
+
+constexpr int NT = 256;
+
+template <typename T>
+__device__ __forceinline__ float ldf(const T* p, int64_t i) {
+  return (float)p[i];
+}
+
+// ---------------------------------------------------------------------------
+// Merge of vocabulary splits (per row): lse = M + log sum_j e^{m_j-M} s_j,
+// lp = z_y - lse, H = lse - (sum_j e^{m_j-M} sz_j) / (sum_j e^{m_j-M} s_j)
+// (PR #1558: H = log_z - sum_exp_z / sum_exp), and v = O/s - W_y.
+// A row any split flagged is recomputed exactly (row_exact).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict__ stats, const float* __restrict__ O,
+                                                     int Sv, int tps_tiles, int64_t N, int H, int V,
+                                                     const T* __restrict__ h, const T* __restrict__ W,
+                                                     const T* __restrict__ b, float inv_tau,
+                                                     const int64_t* __restrict__ y, float* __restrict__ lp,
+                                                     float* __restrict__ ent, float* __restrict__ lse_out,
+                                                     float* __restrict__ vout) {
+  extern __shared__ float sm[];
+  const int64_t row = blockIdx.x;
+  __shared__ double s_c[64];  // per-split weights e^{m_j - M}, up to 64 splits
+  __shared__ double s_res[3];
+  __shared__ int s_flag;
+  const int64_t yv = y ? y[row] : -1;
+  // targets outside [0, V) are invalid input; clamp the index so they cannot
+  // address memory outside W or the split table
+  const int64_t yc = yv < 0 ? 0 : (yv >= V ? V - 1 : yv);
+  if (threadIdx.x == 0) {
+    int f = 0;
+    for (int j = 0; j < Sv; ++j) f |= stats[(int64_t)j * N + row].flag;
+    s_flag = f;
+  }
+  __syncthreads();
+  if (s_flag) {
+    const RowResult r = row_exact<T>(h + row * H, W, b, yv, H, V, inv_tau, vout != nullptr, sm);
+    const double l = (double)r.m + log(r.s);
+    if (threadIdx.x == 0) {
+      if (lp) lp[row] = (float)((double)r.zy - l);
+      ent[row] = (float)(l - r.sz / r.s);
+      if (lse_out) lse_out[row] = (float)l;
+    }
+    if (vout) {
+      const float* os = sm + H;
+      const double inv_s = 1.0 / r.s;
+      for (int d = threadIdx.x; d < H; d += NT)
+        vout[row * H + d] = (float)((double)os[d] * inv_s - (double)ldf<T>(W, yc * H + d));
+    }
+    return;
+  }
+  if (threadIdx.x == 0) {
+    float M = -INFINITY;
+    for (int j = 0; j < Sv; ++j) M = fmaxf(M, stats[(int64_t)j * N + row].m);
+    double S = 0.0, SZ = 0.0;
+    for (int j = 0; j < Sv; ++j) {
+      const RowStats rs = stats[(int64_t)j * N + row];
+      const double c = rs.s > 0.0 ? exp((double)rs.m - (double)M) : 0.0;
+      s_c[j] = c;
+      S += c * rs.s;
+      SZ += c * rs.sz;
+    }
+    const double l = (double)M + log(S);
+    if (lp) {
+      const int jy = min(Sv - 1, (int)((yc / 32) / tps_tiles));
+      lp[row] = (float)((double)stats[(int64_t)jy * N + row].zy - l);
+    }
+    ent[row] = (float)(l - SZ / S);
+    if (lse_out) lse_out[row] = (float)l;
+    s_res[0] = 1.0 / S;
+  }
+  __syncthreads();
+  if (vout) {
+    const double inv_s = s_res[0];
+    for (int d = threadIdx.x; d < H; d += NT) {
+      double o = 0.0;
+      for (int j = 0; j < Sv; ++j)
+        if (s_c[j] != 0.0) o += s_c[j] * (double)O[((int64_t)j * N + row) * H + d];
+      vout[row * H + d] = (float)(o * inv_s - (double)ldf<T>(W, yc * H + d));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Loss stage
+// ---------------------------------------------------------------------------
+struct TokEval {
+  bool M, R, E;
+  bool clipped;   // GMPO token predicate (ratio tokens only)
+  double c;       // GMPO clipped log-ratio value
+  double lr;      // log-ratio value
+  double kl, dkl;
+};
+
+// Per-token quantities (Liger PR #1320 GMPO clip in log space, advantage
+// dependent and one sided; K3 KL). lr32 = fp32(lp - old) is the predicate
+// operand, compared with fp32 bounds; ties are not clipped.
+__device__ __forceinline__ TokEval eval_tok(const LossParams& p, int64_t t, const float* lp, const float* old,
+                                            const float* ref, const uint8_t* comp, const uint8_t* ratio,
+                                            const uint8_t* emask, float A) {
+  TokEval e;
+  const float lp32 = lp[t];
+  const float old32 = old ? old[t] : lp32;
+  const float lr32 = __fsub_rn(lp32, old32);
+  e.M = comp[t] != 0;
+  e.R = ratio ? ratio[t] != 0 : e.M;
+  e.E = emask ? emask[t] != 0 : true;
+  e.lr = (double)lr32;
+  const bool hi = A > 0.f && lr32 > p.eh32;
+  const bool lo = A < 0.f && lr32 < -p.el32;
+  e.clipped = e.R && (hi || lo);
+  e.c = hi ? (double)p.eh32 : (lo ? -(double)p.el32 : (double)lr32);
+  if (ref) {
+    const double x = (double)ref[t] - (double)lp32;
+    const double ex = exp(x);
+    e.kl = ex - x - 1.0;
+    e.dkl = 1.0 - ex;
+  } else {
+    e.kl = 0.0;
+    e.dkl = 0.0;
+  }
+  return e;
+}
+
+template <typename V_>
+__device__ V_ block_sum(V_ v, V_* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int s = NT / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  const V_ r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(NT) void zero_acc_kernel(LossAcc* acc) {
+  if (threadIdx.x == 0) {
+    acc->loss = 0.0;
+    acc->slr = 0.0;
+    acc->mkl = 0.0;
+    acc->n_active = acc->n_clip = acc->n_kept = acc->n_clipseq = 0ull;
+    acc->thr = __int_as_float(0x7fc00000);
+    acc->pad = 0;
+  }
+}
+
+// grid (Bc, St): partial sums of sequence i over token segment s.
+__global__ __launch_bounds__(NT) void seq_partial_kernel(LossParams p, const float* __restrict__ lp,
+                                                         const float* __restrict__ old, const float* __restrict__ ref,
+                                                         const uint8_t* __restrict__ comp,
+                                                         const uint8_t* __restrict__ ratio,
+                                                         const uint8_t* __restrict__ emask,
+                                                         const float* __restrict__ adv, int St,
+                                                         SeqPart* __restrict__ part) {
+  __shared__ double redd[NT];
+  __shared__ int redi[NT];
+  const int i = blockIdx.x, s = blockIdx.y;
+  const int64_t T = p.T;
+  const int64_t L = (T + St - 1) / St;
+  const int64_t a = (int64_t)s * L, b = min(T, a + L);
+  const float A = adv[i];
+  double sc = 0.0, slr = 0.0, skl = 0.0;
+  int cm = 0, cr = 0, ck = 0, cc = 0;
+  for (int64_t k = a + threadIdx.x; k < b; k += NT) {
+    const int64_t t = (int64_t)i * T + k;
+    const TokEval e = eval_tok(p, t, lp, old, ref, comp, ratio, emask, A);
+    if (e.R) {
+      sc += e.c;
+      slr += e.lr;
+      cr += 1;
+    }
+    if (e.M) {
+      skl += e.kl;
+      cm += 1;
+      ck += e.E ? 1 : 0;
+      cc += e.clipped ? 1 : 0;
+    }
+  }
+  SeqPart out;
+  out.sum_c = block_sum(sc, redd);
+  out.sum_lr = block_sum(slr, redd);
+  out.sum_kl = block_sum(skl, redd);
+  out.cnt_m = block_sum(cm, redi);
+  out.cnt_r = block_sum(cr, redi);
+  out.cnt_k = block_sum(ck, redi);
+  out.cnt_clip = block_sum(cc, redi);
+  if (threadIdx.x == 0) part[(int64_t)i * St + s] = out;
+}
+
+// One block: per-sequence scalars (GMPO r_i, GSPO s_i), gradient
+// coefficients, loss and metric contributions of the chunk.
+__global__ __launch_bounds__(NT) void seq_final_kernel(LossParams p, int64_t Bc, int St,
+                                                       const SeqPart* __restrict__ part,
+                                                       const float* __restrict__ adv, SeqCoef* __restrict__ coef,
+                                                       LossAcc* __restrict__ acc) {
+  __shared__ double redd[NT];
+  __shared__ unsigned long long redu[NT];
+  double loss = 0.0, slr = 0.0, mkl = 0.0;
+  unsigned long long na = 0, nc = 0, nk = 0, ncs = 0;
+  for (int64_t i = threadIdx.x; i < Bc; i += NT) {
+    double sum_c = 0.0, sum_lr = 0.0, sum_kl = 0.0;
+    long long cm = 0, cr = 0, ck = 0, cc = 0;
+    for (int s = 0; s < St; ++s) {
+      const SeqPart q = part[i * St + s];
+      sum_c += q.sum_c;
+      sum_lr += q.sum_lr;
+      sum_kl += q.sum_kl;
+      cm += q.cnt_m;
+      cr += q.cnt_r;
+      ck += q.cnt_k;
+      cc += q.cnt_clip;
+    }
+    const double n = (double)(cm > 0 ? cm : 1);
+    const double nt = (double)(cr > 0 ? cr : 1);
+    const double K = (double)ck;
+    const float A32 = adv[i];
+    const double A = (double)A32;
+    const double w = p.reduction == 0 ? 1.0 / ((double)p.B_total * n) : 1.0;
+    const double seq_lr = sum_lr / nt;
+    double policy_seq, pol;
+    long long clip_tok;
+    int clip_any = 0;
+    if (p.loss_type == 0) {
+      // GMPO: r = exp(masked mean of the clipped log-ratios) (PR #1320)
+      const double r = A32 != 0.f ? exp(sum_c / nt) : 1.0;
+      policy_seq = A32 != 0.f ? -A * r : 0.0;
+      pol = A32 != 0.f ? -A * r * K * w / nt : 0.0;
+      clip_tok = cc;
+    } else {
+      // GSPO-token: s = exp(mean log-ratio), clip(s, 1-eps_l, 1+eps_h) (Tinker GSPO)
+      const double sr = exp(seq_lr);
+      const double lo = (double)p.lo32, hi = (double)p.hi32;
+      const bool clipped = (A32 > 0.f && sr > hi) || (A32 < 0.f && sr < lo);
+      const double scl = fmin(fmax(sr, lo), hi);
+      policy_seq = -fmin(sr * A, scl * A);
+      pol = clipped ? 0.0 : -A * sr * w;
+      clip_tok = clipped ? cm : 0;
+      clip_any = (sr < lo || sr > hi) ? 1 : 0;
+    }
+    loss += w * (policy_seq * K + p.beta * sum_kl);
+    slr += seq_lr;
+    mkl += sum_kl / n;
+    na += (unsigned long long)cm;
+    nc += (unsigned long long)clip_tok;
+    nk += (unsigned long long)ck;
+    ncs += (unsigned long long)clip_any;
+    SeqCoef sc;
+    sc.pol = pol;
+    sc.wbeta = w * p.beta;
+    sc.adv = A32;
+    sc.pad = 0;
+    coef[i] = sc;
+  }
+  loss = block_sum(loss, redd);
+  slr = block_sum(slr, redd);
+  mkl = block_sum(mkl, redd);
+  na = block_sum(na, redu);
+  nc = block_sum(nc, redu);
+  nk = block_sum(nk, redu);
+  ncs = block_sum(ncs, redu);
+  if (threadIdx.x == 0) {
+    acc->loss += loss;
+    acc->slr += slr;
+    acc->mkl += mkl;
+    acc->n_active += na;
+    acc->n_clip += nc;
+    acc->n_kept += nk;
+    acc->n_clipseq += ncs;
+  }
+}
+
+// g_t = dL/dlp_t. GMPO: pol on unclipped ratio tokens; GSPO-token: pol on
+// kept completion tokens; plus w beta (1 - e^{ref - lp}) on completion tokens.
+__global__ __launch_bounds__(NT) void token_grad_kernel(LossParams p, int64_t Nc, const float* __restrict__ lp,
+                                                        const float* __restrict__ old, const float* __restrict__ ref,
+                                                        const uint8_t* __restrict__ comp,
+                                                        const uint8_t* __restrict__ ratio,
+                                                        const uint8_t* __restrict__ emask,
+                                                        const SeqCoef* __restrict__ coef, float* __restrict__ g) {
+  for (int64_t t = (int64_t)blockIdx.x * NT + threadIdx.x; t < Nc; t += (int64_t)gridDim.x * NT) {
+    const int64_t i = t / p.T;
+    const SeqCoef c = coef[i];
+    const TokEval e = eval_tok(p, t, lp, old, ref, comp, ratio, emask, c.adv);
+    double gv = 0.0;
+    if (p.loss_type == 0) {
+      if (e.R && !e.clipped) gv = c.pol;
+    } else {
+      if (e.M && e.E) gv = c.pol;
+    }
+    if (e.M) gv += c.wbeta * e.dkl;
+    g[t] = (float)gv;
+  }
+}
+
+__global__ void finalize_kernel(const LossAcc* __restrict__ acc, int64_t B_total, float* __restrict__ loss,
+                                float* __restrict__ metrics) {
+  if (threadIdx.x != 0) return;
+  const LossAcc a = *acc;
+  loss[0] = (float)a.loss;
+  const float den = (float)(a.n_active > 0 ? a.n_active : 1ull);
+  metrics[0] = (float)a.n_clip / den;
+  metrics[1] = (float)(a.slr / (double)B_total);
+  metrics[2] = (float)((double)a.n_clipseq / (double)B_total);
+  metrics[3] = (float)(a.mkl / (double)B_total);
+  metrics[4] = a.thr;
+  metrics[5] = a.n_active > 0 ? (float)a.n_kept / den : 0.f;
+  metrics[6] = (float)a.n_active;
+  metrics[7] = (float)a.n_clip;
+}
+
+// ---------------------------------------------------------------------------
+// grad_h = (g / tau) v
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(NT) void grad_h_kernel(const float* __restrict__ g, const float* __restrict__ v,
+                                                    int64_t N, int H, float inv_tau, T* __restrict__ gh) {
+  const int64_t total = N * H;
+  for (int64_t k = ((int64_t)blockIdx.x * NT + threadIdx.x) * 4; k < total; k += (int64_t)gridDim.x * NT * 4) {
+    if (k + 3 < total && (H % 4) == 0) {
+      const float s = g[k / H] * inv_tau;
+      const float4 x = *reinterpret_cast<const float4*>(v + k);
+      gh[k] = (T)(s * x.x);
+      gh[k + 1] = (T)(s * x.y);
+      gh[k + 2] = (T)(s * x.z);
+      gh[k + 3] = (T)(s * x.w);
+    } else {
+      for (int64_t e = k; e < min(total, k + 4); ++e) gh[e] = (T)(g[e / H] * inv_tau * v[e]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Token compaction: tokens with g != 0, in order.
+// ---------------------------------------------------------------------------
+constexpr int CB = 1024;  // tokens per compaction block
+
+__global__ __launch_bounds__(NT) void compact_count_kernel(const float* __restrict__ g, int64_t N,
+                                                           int* __restrict__ cnt) {
+  __shared__ int red[NT];
+  const int64_t base = (int64_t)blockIdx.x * CB;
+  int c = 0;
+  for (int k = threadIdx.x; k < CB; k += NT) {
+    const int64_t t = base + k;
+    c += (t < N && g[t] != 0.f) ? 1 : 0;
+  }
+  c = block_sum(c, red);
+  if (threadIdx.x == 0) cnt[blockIdx.x] = c;
+}
+
+__global__ __launch_bounds__(NT) void compact_scan_kernel(const int* __restrict__ cnt, int nb, int* __restrict__ off,
+                                                          int* __restrict__ total) {
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      off[b] = run;
+      run += cnt[b];
+    }
+    *total = run;
+  }
+}
+
+__global__ __launch_bounds__(NT) void compact_scatter_kernel(const float* __restrict__ g, const float* __restrict__ lse,
+                                                             const int64_t* __restrict__ y, int64_t N, float inv_tau,
+                                                             const int* __restrict__ off, int* __restrict__ idx,
+                                                             TokData* __restrict__ tok) {
+  // Each thread owns CB/NT = 4 consecutive tokens; an exclusive scan of the
+  // per-thread counts (fixed order) gives every kept token its slot.
+  __shared__ int sc[NT];
+  constexpr int PER = CB / NT;
+  const int64_t base = (int64_t)blockIdx.x * CB + (int64_t)threadIdx.x * PER;
+  int c = 0;
+  bool f[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int64_t t = base + k;
+    f[k] = t < N && g[t] != 0.f;
+    c += f[k] ? 1 : 0;
+  }
+  sc[threadIdx.x] = c;
+  __syncthreads();
+  for (int s = 1; s < NT; s <<= 1) {  // Hillis-Steele inclusive scan
+    const int v = threadIdx.x >= s ? sc[threadIdx.x - s] : 0;
+    __syncthreads();
+    sc[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int pos = off[blockIdx.x] + sc[threadIdx.x] - c;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (f[k]) {
+      const int64_t t = base + k;
+      idx[pos] = (int)t;
+      TokData td;
+      td.lse = lse[t];
+      td.gs = g[t] * inv_tau;
+      td.y = (int)y[t];
+      td.pad = 0;
+      tok[pos] = td;
+      ++pos;
+    }
+  }
+}
+
+// Natural-layout gather of compacted rows (generic path); rows past the count
+// are zero.
+template <typename T>
+__global__ __launch_bounds__(NT) void gather_rows_kernel(const T* __restrict__ X, const int* __restrict__ idx,
+                                                         const int* __restrict__ count_dev, int64_t cap, int H,
+                                                         T* __restrict__ Xc) {
+  const int n = *count_dev;
+  for (int64_t k = blockIdx.x; k < cap; k += gridDim.x) {
+    if (k >= ((int64_t)n + 31) / 32 * 32) return;
+    for (int d = threadIdx.x; d < H; d += NT) Xc[k * H + d] = k < n ? X[(int64_t)idx[k] * H + d] : (T)0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Batch-global quantile of the active entropies (torch.quantile linear
+// interpolation in fp32), by MSB-first radix select on order-preserving
+// integer keys: one block, four 8-bit digit passes for each of the two order
+// statistics floor(rank) and ceil(rank).
+// ---------------------------------------------------------------------------
+constexpr int SEL_NT = 1024;
+
+__device__ __forceinline__ unsigned f2key(float f) {
+  const unsigned u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__global__ __launch_bounds__(SEL_NT) void select_kernel(const float* __restrict__ ent, const uint8_t* __restrict__ active,
+                                                        int64_t N, float p32, float* __restrict__ thr_out) {
+  __shared__ unsigned hist[2][256];
+  __shared__ unsigned long long red[SEL_NT];
+  __shared__ unsigned pre[2];
+  __shared__ unsigned long long kk[2];
+  unsigned long long c = 0;
+  for (int64_t t = threadIdx.x; t < N; t += SEL_NT) c += active[t] != 0 ? 1ull : 0ull;
+  red[threadIdx.x] = c;
+  __syncthreads();
+  for (int s = SEL_NT / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  const unsigned long long n = red[0];
+  if (n == 0) {
+    if (threadIdx.x == 0) *thr_out = __int_as_float(0x7fc00000);
+    return;
+  }
+  const float rank = __fmul_rn(p32, (float)(n - 1));
+  const float rlo = floorf(rank);
+  const float w = __fsub_rn(rank, rlo);
+  if (threadIdx.x == 0) {
+    kk[0] = (unsigned long long)rlo;
+    kk[1] = (unsigned long long)ceilf(rank);
+    pre[0] = pre[1] = 0u;
+  }
+  __syncthreads();
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const unsigned hmask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
+    for (int k = threadIdx.x; k < 512; k += SEL_NT) (&hist[0][0])[k] = 0u;
+    __syncthreads();
+    const unsigned p0 = pre[0], p1 = pre[1];
+    for (int64_t t = threadIdx.x; t < N; t += SEL_NT) {
+      if (active[t] == 0) continue;
+      const unsigned key = f2key(ent[t]);
+      const unsigned d = (key >> shift) & 255u;
+      if ((key & hmask) == p0) atomicAdd(&hist[0][d], 1u);
+      if ((key & hmask) == p1) atomicAdd(&hist[1][d], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 2) {
+      const int which = threadIdx.x;
+      unsigned long long cum = 0, k = kk[which];
+      int b = 0;
+      for (; b < 255; ++b) {
+        if (k < cum + hist[which][b]) break;
+        cum += hist[which][b];
+      }
+      kk[which] = k - cum;
+      pre[which] |= ((unsigned)b) << shift;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float a = key2f(pre[0]);
+    const float b = key2f(pre[1]);
+    const float d = __fsub_rn(b, a);
+    *thr_out = w < 0.5f ? __fmaf_rn(w, d, a) : __fmaf_rn(__fsub_rn(w, 1.0f), d, b);
+  }
+}
+
+__global__ __launch_bounds__(NT) void mask_kernel(const float* __restrict__ ent, const uint8_t* __restrict__ active,
+                                                  int64_t N, const float* __restrict__ thr_dev,
+                                                  uint8_t* __restrict__ mask) {
+  const float thr = *thr_dev;
+  for (int64_t t = (int64_t)blockIdx.x * NT + threadIdx.x; t < N; t += (int64_t)gridDim.x * NT)
+    mask[t] = (active[t] != 0 && ent[t] >= thr) ? 1 : 0;
+}
+
+__global__ void store_thr_kernel(const float* __restrict__ thr_dev, LossAcc* __restrict__ acc,
+                                 float* __restrict__ thr_out) {
+  if (threadIdx.x == 0) {
+    if (acc) acc->thr = *thr_dev;
+    if (thr_out) *thr_out = *thr_dev;
+  }
+}
+
+__global__ __launch_bounds__(NT) void copy_mask_kernel(const uint8_t* __restrict__ src, int64_t N,
+                                                       uint8_t* __restrict__ dst) {
+  for (int64_t t = (int64_t)blockIdx.x * NT + threadIdx.x; t < N; t += (int64_t)gridDim.x * NT)
+    dst[t] = src[t] != 0 ? 1 : 0;
+}
+
+__global__ void set_nan_kernel(float* dst) {
+  if (threadIdx.x == 0) *dst = __int_as_float(0x7fc00000);
+}
+
+inline unsigned grid_for(int64_t n, int per_block) {
+  int64_t b = (n + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  if (b > 65535 * 16) b = 65535 * 16;
+  return (unsigned)b;
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int Sv, int64_t N, int H, int V,
+                          const void* h, const void* W, const void* b, float inv_tau, const int64_t* y, float* lp,
+                          float* ent, float* lse, float* vout, hipStream_t st) {
+  if (N <= 0) return hipSuccess;
+  const int n_tiles = (V + 31) / 32;
+  const int tps = (n_tiles + Sv - 1) / Sv;
+  const size_t lds = row_exact_smem_bytes(H);
+  if (dtype == 0)
+    hipLaunchKernelGGL((combine_kernel<float>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, tps, N, H, V,
+                       (const float*)h, (const float*)W, (const float*)b, inv_tau, y, lp, ent, lse, vout);
+  else
+    hipLaunchKernelGGL((combine_kernel<__bf16>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, tps, N, H, V,
+                       (const __bf16*)h, (const __bf16*)W, (const __bf16*)b, inv_tau, y, lp, ent, lse, vout);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_zero(LossAcc* acc, hipStream_t st) {
+  hipLaunchKernelGGL(zero_acc_kernel, dim3(1), dim3(64), 0, st, acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_seq_partial(const LossParams& p, int64_t Bc, const float* lp, const float* old,
+                                   const float* ref, const uint8_t* comp, const uint8_t* ratio,
+                                   const uint8_t* emask, const float* adv, int St, SeqPart* part,
+                                   hipStream_t st) {
+  hipLaunchKernelGGL(seq_partial_kernel, dim3((unsigned)Bc, (unsigned)St), dim3(NT), 0, st, p, lp, old, ref, comp,
+                     ratio, emask, adv, St, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_seq_final(const LossParams& p, int64_t Bc, int St, const SeqPart* part, const float* adv,
+                                 SeqCoef* coef, LossAcc* acc, hipStream_t st) {
+  hipLaunchKernelGGL(seq_final_kernel, dim3(1), dim3(NT), 0, st, p, Bc, St, part, adv, coef, acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_token_grad(const LossParams& p, int64_t Bc, const float* lp, const float* old,
+                                  const float* ref, const uint8_t* comp, const uint8_t* ratio,
+                                  const uint8_t* emask, const SeqCoef* coef, float* g, hipStream_t st) {
+  const int64_t Nc = Bc * p.T;
+  hipLaunchKernelGGL(token_grad_kernel, dim3(grid_for(Nc, NT)), dim3(NT), 0, st, p, Nc, lp, old, ref, comp, ratio,
+                     emask, coef, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_finalize(const LossAcc* acc, int64_t B_total, float* loss, float* metrics, hipStream_t st) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(64), 0, st, acc, B_total, loss, metrics);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_h(int dtype, const float* g, const float* v, int64_t N, int H, float inv_tau, void* gh,
+                         hipStream_t st) {
+  const unsigned grid = grid_for(N * H, NT * 4 * 4);
+  if (dtype == 0)
+    hipLaunchKernelGGL((grad_h_kernel<float>), dim3(grid), dim3(NT), 0, st, g, v, N, H, inv_tau, (float*)gh);
+  else
+    hipLaunchKernelGGL((grad_h_kernel<__bf16>), dim3(grid), dim3(NT), 0, st, g, v, N, H, inv_tau, (__bf16*)gh);
+  return hipGetLastError();
+}
+
+size_t compact_scratch_bytes(int64_t N) {
+  const int64_t nb = (N + CB - 1) / CB;
+  return (size_t)(2 * nb) * sizeof(int);
+}
+
+hipError_t launch_compact(const float* g, const float* lse, const int64_t* y, int64_t N, float inv_tau, int* idx,
+                          TokData* tok, int* count_dev, void* scratch, hipStream_t st) {
+  const int64_t nb = (N + CB - 1) / CB;
+  int* cnt = (int*)scratch;
+  int* off = cnt + nb;
+  hipLaunchKernelGGL(compact_count_kernel, dim3((unsigned)nb), dim3(NT), 0, st, g, N, cnt);
+  hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(64), 0, st, cnt, (int)nb, off, count_dev);
+  hipLaunchKernelGGL(compact_scatter_kernel, dim3((unsigned)nb), dim3(NT), 0, st, g, lse, y, N, inv_tau, off, idx,
+                     tok);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(int dtype, const void* X, const int* idx, const int* count_dev, int64_t cap, int H,
+                              void* Xc, hipStream_t st) {
+  const unsigned grid = grid_for(cap, 1);
+  if (dtype == 0)
+    hipLaunchKernelGGL((gather_rows_kernel<float>), dim3(grid), dim3(NT), 0, st, (const float*)X, idx, count_dev,
+                       cap, H, (float*)Xc);
+  else
+    hipLaunchKernelGGL((gather_rows_kernel<__bf16>), dim3(grid), dim3(NT), 0, st, (const __bf16*)X, idx, count_dev,
+                       cap, H, (__bf16*)Xc);
+  return hipGetLastError();
+}
+
+size_t select_scratch_bytes() { return 256; }
+
+hipError_t launch_entropy_select(const float* ent, const uint8_t* active, int64_t N, float p32, float* thr_dev,
+                                 void* scratch, hipStream_t st) {
+  (void)scratch;
+  hipLaunchKernelGGL(select_kernel, dim3(1), dim3(SEL_NT), 0, st, ent, active, N, p32, thr_dev);
+  return hipGetLastError();
+}
+
+hipError_t launch_entropy_mask(const float* ent, const uint8_t* active, int64_t N, const float* thr_dev,
+                               uint8_t* mask, hipStream_t st) {
+  hipLaunchKernelGGL(mask_kernel, dim3(grid_for(N, NT)), dim3(NT), 0, st, ent, active, N, thr_dev, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_thr(const float* thr_dev, LossAcc* acc, float* thr_out, hipStream_t st) {
+  hipLaunchKernelGGL(store_thr_kernel, dim3(1), dim3(64), 0, st, thr_dev, acc, thr_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_mask(const uint8_t* src, int64_t N, uint8_t* dst, hipStream_t st) {
+  hipLaunchKernelGGL(copy_mask_kernel, dim3(grid_for(N, NT)), dim3(NT), 0, st, src, N, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_nan(float* dst, hipStream_t st) {
+  hipLaunchKernelGGL(set_nan_kernel, dim3(1), dim3(64), 0, st, dst);
+  return hipGetLastError();
+}
+
+}  // namespace plp

@@ -1,0 +1,490 @@
+// Host side of the plp C ABI: argument checks, workspace planning and the
+// order of the device passes. No allocation, no host synchronisation.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/plp.h"
+#include "common.h"
+
+using namespace plp;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PLP_OK;
+}
+
+constexpr size_t kAlign = 256;
+constexpr int kBQ = 64, kBK = 32;
+constexpr int kMaxSplits = 64;
+constexpr int64_t kMaxRows = (int64_t)1 << 31;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Sequential carving of the caller's workspace.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t count) {
+    if (count == 0) return nullptr;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+bool mfma_eligible(int dtype, int H) { return dtype == PLP_DTYPE_BF16 && H % 128 == 0 && H >= 128 && H <= 896; }
+bool generic_eligible(int H) { return H >= 1 && H <= 4096; }
+size_t esize(int dtype) { return dtype == PLP_DTYPE_F32 ? 4 : 2; }
+
+// Vocabulary splits of the forward sweep: enough workgroups to fill the
+// 256 compute units when there are few row blocks; every split gets at least
+// one tile. Powers of two keep the row blocks of one split on one XCD.
+int choose_splits(int64_t rows, int V, bool mfma) {
+  if (!mfma) return 1;
+  const int64_t nrb = (rows + kBQ - 1) / kBQ;
+  const int n_tiles = (V + kBK - 1) / kBK;
+  int sv = 1;
+  while ((int64_t)sv * nrb < 256 && sv < kMaxSplits && sv * 2 <= n_tiles) sv *= 2;
+  const int tps = (n_tiles + sv - 1) / sv;
+  return (n_tiles + tps - 1) / tps;
+}
+
+struct Plan {
+  bool mfma = false;
+  bool need_o = false, need_gw = false, need_gb = false;
+  int64_t B = 0, T = 0, N = 0, Bc = 0, Nc = 0, nchunks = 0, cap = 0;
+  int Sv = 1, St = 1;
+  bool entropy = false;        // q < 1
+  bool prepass = false;        // q < 1 with several chunks: stats-only pass first
+};
+
+struct Bufs {
+  __bf16* Wt = nullptr;
+  RowStats* stats = nullptr;
+  float* O = nullptr;
+  float* v = nullptr;
+  float *lp = nullptr, *ent = nullptr, *lse = nullptr;
+  uint8_t* emask = nullptr;
+  SeqPart* part = nullptr;
+  SeqCoef* coef = nullptr;
+  float* g = nullptr;
+  LossAcc* acc = nullptr;
+  float* thr = nullptr;
+  int* idx = nullptr;
+  TokData* tok = nullptr;
+  int* count = nullptr;
+  void* cscratch = nullptr;
+  void* hc = nullptr;
+  __bf16* ht = nullptr;
+  float* gW_acc = nullptr;
+  float* gb_acc = nullptr;
+};
+
+Plan make_plan(const plp_args* a, bool need_o, bool need_gw, bool need_gb) {
+  Plan p;
+  p.mfma = mfma_eligible(a->dtype, a->H);
+  p.need_o = need_o;
+  p.need_gw = need_gw || need_gb;
+  p.need_gb = need_gb;
+  p.B = a->B;
+  p.T = a->T;
+  p.N = a->B * a->T;
+  p.Bc = (a->chunk_sequences > 0 && a->chunk_sequences < a->B) ? a->chunk_sequences : a->B;
+  p.Nc = p.Bc * p.T;
+  p.nchunks = (p.B + p.Bc - 1) / p.Bc;
+  p.cap = round_up(p.Nc, kBK);
+  p.Sv = choose_splits(p.Nc, a->V, p.mfma);
+  p.St = (int)std::min<int64_t>(64, (p.T + 2047) / 2048);
+  if (p.St < 1) p.St = 1;
+  p.entropy = a->top_entropy_quantile < 1.0;
+  p.prepass = p.entropy && p.nchunks > 1;
+  return p;
+}
+
+size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
+  Carver c(ws);
+  const int H = a->H, V = a->V;
+  if (p.mfma && p.need_o) b.Wt = c.take<__bf16>((size_t)round_up(V, kBK) * H);
+  b.stats = c.take<RowStats>((size_t)p.Sv * p.Nc);
+  if (p.need_o) {
+    b.O = c.take<float>((size_t)p.Sv * p.Nc * H);
+    b.v = p.Sv == 1 ? b.O : c.take<float>((size_t)p.Nc * H);
+  }
+  b.lp = c.take<float>(p.N);
+  b.ent = c.take<float>(p.N);
+  b.lse = c.take<float>(p.N);
+  if (p.entropy) b.emask = c.take<uint8_t>(p.N);
+  b.part = c.take<SeqPart>((size_t)p.Bc * p.St);
+  b.coef = c.take<SeqCoef>(p.Bc);
+  b.g = c.take<float>(p.Nc);
+  b.acc = c.take<LossAcc>(1);
+  b.thr = c.take<float>(1);
+  if (p.need_gw) {
+    b.idx = c.take<int>(p.cap);
+    b.tok = c.take<TokData>(p.cap);
+    b.count = c.take<int>(1);
+    b.cscratch = c.take<char>(compact_scratch_bytes(p.Nc));
+    b.hc = c.take<char>((size_t)p.cap * H * esize(a->dtype));
+    if (p.mfma) b.ht = c.take<__bf16>((size_t)p.cap * H);
+    if (p.nchunks > 1) {
+      b.gW_acc = c.take<float>((size_t)V * H);
+      if (p.need_gb) b.gb_acc = c.take<float>(V);
+    }
+  }
+  return c.off + kAlign;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(PLP_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need > have) return fail(PLP_E_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", have, need);
+  if (need > 0 && ws == nullptr) return fail(PLP_E_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)ws) % kAlign != 0) return fail(PLP_E_WORKSPACE, "workspace must be 256-byte aligned");
+  return PLP_OK;
+}
+
+// Checks shared by the fused call and the loss-only call. `pointers`: also
+// check the required pointers (the workspace queries read sizes only).
+int check_loss_args(const plp_args* a, bool pointers = true) {
+  if (!a) return fail(PLP_E_INVALID, "args is NULL");
+  if (a->struct_size < sizeof(plp_args)) return fail(PLP_E_INVALID, "args->struct_size %u < %zu", a->struct_size,
+                                                     sizeof(plp_args));
+  if (a->B < 1 || a->T < 1) return fail(PLP_E_INVALID, "B and T must be >= 1 (B=%lld T=%lld)", (long long)a->B,
+                                        (long long)a->T);
+  if (a->B > kMaxRows / a->T) return fail(PLP_E_INVALID, "B*T must be < 2^31");
+  if (a->loss_type != PLP_LOSS_GMPO && a->loss_type != PLP_LOSS_GSPO_TOKEN)
+    return fail(PLP_E_INVALID, "unknown loss_type %d", a->loss_type);
+  if (a->is_level != PLP_IS_TOKEN && a->is_level != PLP_IS_SEQUENCE)
+    return fail(PLP_E_INVALID, "unknown is_level %d", a->is_level);
+  if (a->loss_type == PLP_LOSS_GMPO && a->is_level == PLP_IS_SEQUENCE)
+    return fail(PLP_E_UNSUPPORTED, "GMPO clips at token level before the sequence aggregation; "
+                                   "sequence-level importance sampling is rejected");
+  if (a->loss_type == PLP_LOSS_GSPO_TOKEN && a->is_level == PLP_IS_TOKEN)
+    return fail(PLP_E_UNSUPPORTED, "GSPO_TOKEN uses the sequence-level ratio; set is_level = PLP_IS_SEQUENCE");
+  if (a->reduction != PLP_REDUCE_SEQ_MEAN && a->reduction != PLP_REDUCE_TOKEN_SUM)
+    return fail(PLP_E_INVALID, "unknown reduction %d", a->reduction);
+  if (!(a->epsilon_low >= 0.0) || !isfinite(a->epsilon_low) || !(a->epsilon_high >= 0.0) ||
+      !isfinite(a->epsilon_high))
+    return fail(PLP_E_INVALID, "epsilon_low and epsilon_high must be finite and >= 0");
+  if (!(a->beta >= 0.0) || !isfinite(a->beta)) return fail(PLP_E_INVALID, "beta must be finite and >= 0");
+  if (pointers && a->beta != 0.0 && a->ref_logp == nullptr) return fail(PLP_E_INVALID, "beta != 0 needs ref_logp");
+  if (!(a->temperature > 0.0) || !isfinite(a->temperature)) return fail(PLP_E_INVALID, "temperature must be > 0");
+  if (!(a->top_entropy_quantile >= 0.0 && a->top_entropy_quantile <= 1.0))
+    return fail(PLP_E_INVALID, "top_entropy_quantile must lie in [0, 1] (got %g)", a->top_entropy_quantile);
+  if (a->chunk_sequences < 0) return fail(PLP_E_INVALID, "chunk_sequences must be >= 0");
+  if (pointers && (!a->completion_mask || !a->advantages))
+    return fail(PLP_E_INVALID, "completion_mask and advantages are required");
+  return PLP_OK;
+}
+
+int check_fused_args(const plp_args* a) {
+  int rc = check_loss_args(a);
+  if (rc) return rc;
+  if (a->dtype != PLP_DTYPE_F32 && a->dtype != PLP_DTYPE_BF16) return fail(PLP_E_INVALID, "unknown dtype %d", a->dtype);
+  if (a->H < 1 || a->V < 1) return fail(PLP_E_INVALID, "H and V must be >= 1");
+  if (!a->hidden || !a->weight || !a->targets) return fail(PLP_E_INVALID, "hidden, weight and targets are required");
+  if (!mfma_eligible(a->dtype, a->H) && !generic_eligible(a->H))
+    return fail(PLP_E_UNSUPPORTED, "H=%d is not supported (bf16 MFMA path: H multiple of 128 up to 896; "
+                                   "generic path: H <= 4096)", a->H);
+  return PLP_OK;
+}
+
+LossParams loss_params(const plp_args* a) {
+  LossParams p;
+  p.B_total = a->B;
+  p.T = a->T;
+  p.loss_type = a->loss_type;
+  p.reduction = a->reduction;
+  p.eh32 = (float)a->epsilon_high;
+  p.el32 = (float)a->epsilon_low;
+  p.lo32 = (float)(1.0 - a->epsilon_low);
+  p.hi32 = (float)(1.0 + a->epsilon_high);
+  p.beta = a->beta;
+  return p;
+}
+
+// Forward sweep + merge for rows [r0, r0 + n).
+int forward_rows(const plp_args* a, const Plan& p, Bufs& b, int64_t r0, int64_t n, bool with_o, hipStream_t st) {
+  const size_t es = esize(a->dtype);
+  const char* h = (const char*)a->hidden + (size_t)r0 * a->H * es;
+  const int64_t* y = a->targets + r0;
+  const float inv_tau = (float)(1.0 / a->temperature);
+  if (p.mfma) {
+    HIP_TRY(launch_fwd_mfma((const __bf16*)h, (const __bf16*)a->weight, b.Wt, (const __bf16*)a->bias, y, n, a->H,
+                            a->V, inv_tau, p.Sv, with_o, b.stats, with_o ? b.O : nullptr, st));
+  } else {
+    HIP_TRY(launch_fwd_generic(a->dtype, h, a->weight, a->bias, y, n, a->H, a->V, inv_tau, with_o, b.stats,
+                               with_o ? b.O : nullptr, st));
+  }
+  HIP_TRY(launch_combine(a->dtype, b.stats, with_o ? b.O : nullptr, p.Sv, n, a->H, a->V, h, a->weight, a->bias,
+                         inv_tau, y, b.lp + r0, b.ent + r0, b.lse + r0, with_o ? b.v : nullptr, st));
+  return PLP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+PLP_API int plp_abi_version(void) { return PLP_ABI_VERSION; }
+
+PLP_API const char* plp_last_error(void) { return g_last_error.c_str(); }
+
+PLP_API int plp_workspace_size(const plp_args* a, size_t* bytes) {
+  if (!bytes) return fail(PLP_E_INVALID, "bytes is NULL");
+  int rc = check_loss_args(a, false);
+  if (rc) return rc;
+  if (a->H < 1 || a->V < 1) return fail(PLP_E_INVALID, "H and V must be >= 1");
+  if (a->dtype != PLP_DTYPE_F32 && a->dtype != PLP_DTYPE_BF16) return fail(PLP_E_INVALID, "unknown dtype %d", a->dtype);
+  // Sized for every gradient output, the largest request.
+  Plan p = make_plan(a, true, true, a->bias != nullptr);
+  Bufs b;
+  *bytes = carve(a, p, nullptr, b);
+  return ok();
+}
+
+PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_outputs* out, void* ws,
+                                                 size_t ws_bytes, hipStream_t st) {
+  int rc = check_fused_args(a);
+  if (rc) return rc;
+  if (!out || out->struct_size < sizeof(plp_outputs)) return fail(PLP_E_INVALID, "outputs NULL or struct_size too small");
+  if (!out->loss || !out->metrics) return fail(PLP_E_INVALID, "loss and metrics outputs are required");
+  if (out->grad_bias && !a->bias) return fail(PLP_E_INVALID, "grad_bias requested without bias");
+  size_t need_full = 0;
+  {
+    Plan pf = make_plan(a, true, true, a->bias != nullptr);
+    Bufs bf;
+    need_full = carve(a, pf, nullptr, bf);
+  }
+  rc = check_ws(ws, ws_bytes, need_full);
+  if (rc) return rc;
+
+  const Plan p = make_plan(a, out->grad_hidden != nullptr, out->grad_weight != nullptr, out->grad_bias != nullptr);
+  Bufs b;
+  carve(a, p, ws, b);
+  const int H = a->H, V = a->V;
+  const size_t es = esize(a->dtype);
+  const float inv_tau = (float)(1.0 / a->temperature);
+  const LossParams lpar = loss_params(a);
+
+  HIP_TRY(launch_loss_zero(b.acc, st));
+  if (b.Wt)
+    HIP_TRY(launch_blocked_copy_bf16((const __bf16*)a->weight, nullptr, nullptr, V, round_up(V, kBK), H, b.Wt,
+                                     nullptr, st));
+
+  bool first_chunk_done = false;
+  if (p.entropy) {
+    if (p.nchunks == 1) {
+      rc = forward_rows(a, p, b, 0, p.N, p.need_o, st);
+      if (rc) return rc;
+      first_chunk_done = true;
+    } else {
+      for (int64_t c = 0; c < p.nchunks; ++c) {
+        const int64_t r0 = c * p.Nc, n = std::min(p.Nc, p.N - r0);
+        rc = forward_rows(a, p, b, r0, n, false, st);
+        if (rc) return rc;
+      }
+    }
+    HIP_TRY(launch_entropy_select(b.ent, a->completion_mask, p.N, (float)(1.0 - a->top_entropy_quantile), b.thr,
+                                  nullptr, st));
+    HIP_TRY(launch_entropy_mask(b.ent, a->completion_mask, p.N, b.thr, b.emask, st));
+    HIP_TRY(launch_store_thr(b.thr, b.acc, nullptr, st));
+  }
+
+  for (int64_t c = 0; c < p.nchunks; ++c) {
+    const int64_t s0 = c * p.Bc, bc = std::min(p.Bc, p.B - s0);
+    const int64_t r0 = s0 * p.T, n = bc * p.T;
+    if (!(c == 0 && first_chunk_done)) {
+      rc = forward_rows(a, p, b, r0, n, p.need_o, st);
+      if (rc) return rc;
+    }
+    const float* old = a->old_logp ? a->old_logp + r0 : nullptr;
+    const float* ref = a->ref_logp ? a->ref_logp + r0 : nullptr;
+    const uint8_t* comp = a->completion_mask + r0;
+    const uint8_t* ratio = a->ratio_mask ? a->ratio_mask + r0 : nullptr;
+    const uint8_t* em = b.emask ? b.emask + r0 : nullptr;
+    const float* adv = a->advantages + s0;
+    HIP_TRY(launch_loss_seq_partial(lpar, bc, b.lp + r0, old, ref, comp, ratio, em, adv, p.St, b.part, st));
+    HIP_TRY(launch_loss_seq_final(lpar, bc, p.St, b.part, adv, b.coef, b.acc, st));
+    float* g = out->dlogp_out ? out->dlogp_out + r0 : b.g;
+    HIP_TRY(launch_loss_token_grad(lpar, bc, b.lp + r0, old, ref, comp, ratio, em, b.coef, g, st));
+    if (p.need_o)
+      HIP_TRY(launch_grad_h(a->dtype, g, b.v, n, H, inv_tau, (char*)out->grad_hidden + (size_t)r0 * H * es, st));
+    if (p.need_gw) {
+      HIP_TRY(launch_compact(g, b.lse + r0, a->targets + r0, n, inv_tau, b.idx, b.tok, b.count, b.cscratch, st));
+      const char* hsrc = (const char*)a->hidden + (size_t)r0 * H * es;
+      if (p.mfma)
+        HIP_TRY(launch_blocked_copy_bf16((const __bf16*)hsrc, b.idx, b.count, n, p.cap, H, b.ht, (__bf16*)b.hc, st));
+      else
+        HIP_TRY(launch_gather_rows(a->dtype, hsrc, b.idx, b.count, p.cap, H, b.hc, st));
+      const int mode = p.nchunks == 1 ? 0 : (c == 0 ? 1 : (c == p.nchunks - 1 ? 3 : 2));
+      if (p.mfma)
+        HIP_TRY(launch_bwd_mfma((const __bf16*)a->weight, (const __bf16*)a->bias, (const __bf16*)b.hc, b.ht, b.tok,
+                                b.count, p.cap, H, V, inv_tau, mode, b.gW_acc, b.gb_acc, (__bf16*)out->grad_weight,
+                                (__bf16*)out->grad_bias, st));
+      else
+        HIP_TRY(launch_bwd_generic(a->dtype, a->weight, a->bias, b.hc, b.tok, b.count, H, V, inv_tau, mode, b.gW_acc,
+                                   b.gb_acc, out->grad_weight, out->grad_bias, st));
+    }
+  }
+  HIP_TRY(launch_loss_finalize(b.acc, p.B, out->loss, out->metrics, st));
+  if (out->logp_out) HIP_TRY(hipMemcpyAsync(out->logp_out, b.lp, p.N * sizeof(float), hipMemcpyDeviceToDevice, st));
+  if (out->entropy_out)
+    HIP_TRY(hipMemcpyAsync(out->entropy_out, b.ent, p.N * sizeof(float), hipMemcpyDeviceToDevice, st));
+  if (out->entropy_mask_out)
+    HIP_TRY(launch_copy_mask(p.entropy ? b.emask : a->completion_mask, p.N, out->entropy_mask_out, st));
+  return ok();
+}
+
+PLP_API int plp_selective_entropy_workspace_size(int64_t N, int32_t H, int32_t V, int32_t dtype, size_t* bytes) {
+  if (!bytes) return fail(PLP_E_INVALID, "bytes is NULL");
+  if (N < 1 || N >= kMaxRows || H < 1 || V < 1) return fail(PLP_E_INVALID, "bad sizes N=%lld H=%d V=%d", (long long)N, H, V);
+  if (dtype != PLP_DTYPE_F32 && dtype != PLP_DTYPE_BF16) return fail(PLP_E_INVALID, "unknown dtype %d", dtype);
+  const int sv = choose_splits(N, V, mfma_eligible(dtype, H));
+  *bytes = align_up((size_t)sv * N * sizeof(RowStats)) + align_up((size_t)N * sizeof(float)) + kAlign;
+  return ok();
+}
+
+PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const void* bias, int64_t N, int32_t H,
+                                  int32_t V, int32_t dtype, float temperature, const int64_t* targets,
+                                  float* entropy_out, float* logp_out, void* ws, size_t ws_bytes, hipStream_t st) {
+  size_t need = 0;
+  int rc = plp_selective_entropy_workspace_size(N, H, V, dtype, &need);
+  if (rc) return rc;
+  if (!hidden || !weight || !entropy_out) return fail(PLP_E_INVALID, "hidden, weight and entropy_out are required");
+  if (logp_out && !targets) return fail(PLP_E_INVALID, "logp_out needs targets");
+  if (!(temperature > 0.f) || !isfinite(temperature)) return fail(PLP_E_INVALID, "temperature must be > 0");
+  if (!mfma_eligible(dtype, H) && !generic_eligible(H)) return fail(PLP_E_UNSUPPORTED, "H=%d is not supported", H);
+  rc = check_ws(ws, ws_bytes, need);
+  if (rc) return rc;
+  const bool mfma = mfma_eligible(dtype, H);
+  const int sv = choose_splits(N, V, mfma);
+  Carver c(ws);
+  RowStats* stats = c.take<RowStats>((size_t)sv * N);
+  float* scratch_lp = c.take<float>(N);
+  const int64_t* y = targets;  // may be NULL: no target logit is gathered
+  const float inv_tau = 1.0f / temperature;
+  if (mfma)
+    HIP_TRY(launch_fwd_mfma((const __bf16*)hidden, (const __bf16*)weight, nullptr, (const __bf16*)bias, y, N, H, V,
+                            inv_tau, sv, false, stats, nullptr, st));
+  else
+    HIP_TRY(launch_fwd_generic(dtype, hidden, weight, bias, y, N, H, V, inv_tau, false, stats, nullptr, st));
+  HIP_TRY(launch_combine(dtype, stats, nullptr, sv, N, H, V, hidden, weight, bias, inv_tau, y,
+                         logp_out ? logp_out : (y ? scratch_lp : nullptr), entropy_out, nullptr, nullptr, st));
+  return ok();
+}
+
+PLP_API int plp_entropy_quantile_mask_workspace_size(int64_t N, size_t* bytes) {
+  if (!bytes) return fail(PLP_E_INVALID, "bytes is NULL");
+  if (N < 0 || N >= kMaxRows) return fail(PLP_E_INVALID, "bad N=%lld", (long long)N);
+  *bytes = kAlign * 2;
+  return ok();
+}
+
+PLP_API int plp_entropy_quantile_mask(const float* entropy, const uint8_t* active, int64_t N, double q,
+                                      uint8_t* mask_out, float* threshold_out, void* ws, size_t ws_bytes,
+                                      hipStream_t st) {
+  size_t need = 0;
+  int rc = plp_entropy_quantile_mask_workspace_size(N, &need);
+  if (rc) return rc;
+  if (!(q >= 0.0 && q <= 1.0)) return fail(PLP_E_INVALID, "q must lie in [0, 1] (got %g)", q);
+  if (N > 0 && (!entropy || !active || !mask_out)) return fail(PLP_E_INVALID, "entropy, active and mask_out are required");
+  rc = check_ws(ws, ws_bytes, need);
+  if (rc) return rc;
+  float* thr = (float*)ws;
+  if (q == 1.0) {
+    if (N > 0) HIP_TRY(launch_copy_mask(active, N, mask_out, st));
+    if (threshold_out) HIP_TRY(launch_set_nan(threshold_out, st));
+    return ok();
+  }
+  HIP_TRY(launch_entropy_select(entropy, active, N, (float)(1.0 - q), thr, nullptr, st));
+  if (N > 0) HIP_TRY(launch_entropy_mask(entropy, active, N, thr, mask_out, st));
+  if (threshold_out) HIP_TRY(launch_store_thr(thr, nullptr, threshold_out, st));
+  return ok();
+}
+
+PLP_API int plp_policy_loss_workspace_size(const plp_args* a, size_t* bytes) {
+  if (!bytes) return fail(PLP_E_INVALID, "bytes is NULL");
+  int rc = check_loss_args(a, false);
+  if (rc) return rc;
+  const int64_t N = a->B * a->T;
+  const int St = (int)std::max<int64_t>(1, std::min<int64_t>(64, (a->T + 2047) / 2048));
+  Carver c(nullptr);
+  c.take<uint8_t>(N);
+  c.take<SeqPart>((size_t)a->B * St);
+  c.take<SeqCoef>(a->B);
+  c.take<float>(N);
+  c.take<LossAcc>(1);
+  c.take<float>(1);
+  *bytes = c.off + kAlign;
+  return ok();
+}
+
+PLP_API int plp_policy_loss_from_logprobs(const plp_args* a, const float* logp, const float* entropy,
+                                          const plp_outputs* out, void* ws, size_t ws_bytes, hipStream_t st) {
+  size_t need = 0;
+  int rc = check_loss_args(a);
+  if (rc) return rc;
+  rc = plp_policy_loss_workspace_size(a, &need);
+  if (rc) return rc;
+  if (!logp) return fail(PLP_E_INVALID, "logp is required");
+  if (!out || out->struct_size < sizeof(plp_outputs) || !out->loss || !out->metrics)
+    return fail(PLP_E_INVALID, "outputs with loss and metrics are required");
+  const bool q_on = a->top_entropy_quantile < 1.0;
+  if (q_on && !entropy) return fail(PLP_E_INVALID, "entropy is required when top_entropy_quantile < 1");
+  rc = check_ws(ws, ws_bytes, need);
+  if (rc) return rc;
+  const int64_t N = a->B * a->T;
+  const int St = (int)std::max<int64_t>(1, std::min<int64_t>(64, (a->T + 2047) / 2048));
+  Carver c(ws);
+  uint8_t* emask = c.take<uint8_t>(N);
+  SeqPart* part = c.take<SeqPart>((size_t)a->B * St);
+  SeqCoef* coef = c.take<SeqCoef>(a->B);
+  float* gbuf = c.take<float>(N);
+  LossAcc* acc = c.take<LossAcc>(1);
+  float* thr = c.take<float>(1);
+  const LossParams lpar = loss_params(a);
+  HIP_TRY(launch_loss_zero(acc, st));
+  if (q_on) {
+    HIP_TRY(launch_entropy_select(entropy, a->completion_mask, N, (float)(1.0 - a->top_entropy_quantile), thr, nullptr, st));
+    HIP_TRY(launch_entropy_mask(entropy, a->completion_mask, N, thr, emask, st));
+    HIP_TRY(launch_store_thr(thr, acc, nullptr, st));
+  }
+  const uint8_t* em = q_on ? emask : nullptr;
+  HIP_TRY(launch_loss_seq_partial(lpar, a->B, logp, a->old_logp, a->ref_logp, a->completion_mask, a->ratio_mask, em,
+                                  a->advantages, St, part, st));
+  HIP_TRY(launch_loss_seq_final(lpar, a->B, St, part, a->advantages, coef, acc, st));
+  float* g = out->dlogp_out ? out->dlogp_out : gbuf;
+  HIP_TRY(launch_loss_token_grad(lpar, a->B, logp, a->old_logp, a->ref_logp, a->completion_mask, a->ratio_mask, em,
+                                 coef, g, st));
+  HIP_TRY(launch_loss_finalize(acc, a->B, out->loss, out->metrics, st));
+  if (out->entropy_mask_out) HIP_TRY(launch_copy_mask(q_on ? emask : a->completion_mask, N, out->entropy_mask_out, st));
+  return ok();
+}
+
+}  // extern "C"

@@ -206,10 +206,12 @@ def ref_noise(spec: Spec) -> Optional[np.ndarray]:
 
 
 def compose_logp(current_logp: np.ndarray, noise: Optional[np.ndarray]) -> Optional[np.ndarray]:
-    """fp32(current + noise): the recipe for old/ref log-probs."""
+    """fp32(fp32(current) + noise): the recipe for old/ref log-probs (the
+    current-policy log-prob is taken at fp32, as a sampler would report it)."""
     if noise is None:
         return None
-    return (np.asarray(current_logp, dtype=np.float64) + noise).astype(np.float32)
+    cur = np.asarray(current_logp, dtype=np.float32).astype(np.float64)
+    return (cur + noise).astype(np.float32)
 
 
 def small(name="small", **kw) -> Spec:

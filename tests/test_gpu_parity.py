@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, element by element.
+
+Bars (fp32 | bf16): loss rel 1e-5 | abs 1e-4; gradients rel-L2 1e-4 | 1e-2
+with cosine >= 0.9999 for bf16; log-prob and entropy abs 1e-5 | 2e-5; clip
+metric, counts and entropy mask bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_helpers import (clip_margin, cosine, dev_tensor, grad_tol, make_case, rel_l2, require_gpu,
+                               run_gpu, run_oracle)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    import rl_policy_gradient_amd  # noqa: F401  (fails loudly when the library is missing)
+    yield
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _check_fused(spec, d, gpu, ref, lp_tol=None):
+    lp_tol = lp_tol or (1e-5 if spec.dtype == "f32" else 2e-5)
+    np.testing.assert_allclose(gpu["logp"], ref["logp"], rtol=0, atol=lp_tol)
+    np.testing.assert_allclose(gpu["entropy"], ref["entropy"], rtol=0, atol=lp_tol)
+    margin = clip_margin(spec, d, ref["logp"])
+    assert margin > 10 * lp_tol, f"a clip predicate sits {margin:.2e} from its bound: pick another seed"
+    if spec.dtype == "f32":
+        assert abs(gpu["loss"][0] - ref["loss"]) <= 1e-5 * max(1.0, abs(ref["loss"])), (gpu["loss"][0], ref["loss"])
+    else:
+        assert abs(gpu["loss"][0] - ref["loss"]) <= 1e-4, (gpu["loss"][0], ref["loss"])
+    m, mo = gpu["metrics"], ref["metrics"]
+    assert m[6] == mo[6] and m[7] == mo[7], (m, mo)                      # counts exact
+    assert np.float32(m[0]).view(np.uint32) == np.float32(mo[0]).view(np.uint32)  # clip fraction bit-exact
+    np.testing.assert_allclose(m[[1, 2, 3, 5]], mo[[1, 2, 3, 5]], rtol=1e-4, atol=1e-6)
+    if np.isnan(mo[4]):
+        assert np.isnan(m[4])
+    else:
+        assert abs(m[4] - mo[4]) <= lp_tol
+    if ref["entropy_mask"] is not None:
+        np.testing.assert_array_equal(gpu["entropy_mask"].astype(bool), ref["entropy_mask"])
+    g_scale = max(1e-30, np.abs(ref["g"]).max())
+    np.testing.assert_allclose(gpu["dlogp"], ref["g"], rtol=0, atol=1e-4 * g_scale + 1e-12)
+    tol_l2, tol_cos = grad_tol(spec)
+    for k_gpu, k_ref in (("grad_hidden", "grad_h"), ("grad_weight", "grad_W"), ("grad_bias", "grad_b")):
+        if k_gpu not in gpu:
+            continue
+        a, b = gpu[k_gpu], ref[k_ref]
+        r, c = rel_l2(a, b), cosine(a, b)
+        assert r <= tol_l2 and c >= tol_cos, (k_gpu, r, c)
+
+
+# ---------------------------------------------------------------------------
+# The fused path on small shapes that span several tiles with ragged tails
+# ---------------------------------------------------------------------------
+
+SMALL = {
+    # bf16 MFMA path: N = 200 (64-row tiles + 8), V = 1000 (32-wide tiles + 8)
+    "mfma_gmpo": synth.small("mfma_gmpo", B=2, T=100, H=256, V=1000, eps_low=0.2, eps_high=0.3),
+    "mfma_gmpo_kl_bias_tau": synth.small("mfma_gmpo_kl", cfg_id=101, B=3, T=70, H=128, V=777, bias=True,
+                                         beta=0.04, ref_noise_std=0.05, temperature=0.8, eps_low=0.2,
+                                         eps_high=0.3),
+    "mfma_gspo_q": synth.small("mfma_gspo_q", cfg_id=102, B=2, T=96, H=256, V=1500, loss_type=synth.GSPO_TOKEN,
+                               eps_low=3e-3, eps_high=4e-3, old_noise_std=1e-2, top_entropy_quantile=0.5),
+    "mfma_gmpo_q_chunked": synth.small("mfma_gmpo_q_ch", cfg_id=103, B=5, T=40, H=384, V=900, bias=True,
+                                       top_entropy_quantile=0.5, chunk_sequences=2, beta=0.04,
+                                       ref_noise_std=0.05),
+    "mfma_gmpo_h896": synth.small("mfma_h896", cfg_id=104, B=1, T=130, H=896, V=2053, w_std=0.02),
+    "mfma_zero_adv_token_sum": synth.small("mfma_tsum", cfg_id=105, B=4, T=33, H=128, V=600,
+                                           zero_adv_fraction=0.5, reduction="token_sum"),
+    # generic (vector ALU) path: fp32, and bf16 with H not a multiple of 128
+    "generic_f32_cfg1": synth.CONFIGS[1],
+    "generic_bf16_h96": synth.small("generic_h96", cfg_id=106, B=2, T=50, H=96, V=700, bias=True),
+    "generic_f32_gspo_chunked": synth.small("generic_gspo", cfg_id=107, dtype="f32", B=3, T=30, H=48, V=300,
+                                            loss_type=synth.GSPO_TOKEN, eps_low=0.01, eps_high=0.01,
+                                            old_noise_std=0.01, chunk_sequences=2, top_entropy_quantile=0.3),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fused_small(name):
+    spec = SMALL[name]
+    _say(f"fused {name} B={spec.B} T={spec.T} H={spec.H} V={spec.V} {spec.dtype}")
+    d = make_case(spec)
+    ref = run_oracle(spec, d)
+    gpu = run_gpu(spec, d)
+    _check_fused(spec, d, gpu, ref)
+
+
+def test_fused_deterministic():
+    spec = SMALL["mfma_gmpo_q_chunked"]
+    _say("determinism")
+    d = make_case(spec)
+    a = run_gpu(spec, d)
+    b = run_gpu(spec, d)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_fused_chunk_invariance():
+    """Outer chunk sizes 1, 2 and B agree (batch-global threshold and mean)."""
+    base = SMALL["mfma_gmpo_q_chunked"]
+    d = make_case(base)
+    outs = []
+    for cs in (1, 2, 0):
+        _say(f"chunk {cs}")
+        outs.append(run_gpu(base.replace(chunk_sequences=cs), d))
+    for o in outs[1:]:
+        assert abs(o["loss"][0] - outs[0]["loss"][0]) < 1e-6
+        np.testing.assert_array_equal(o["entropy_mask"], outs[0]["entropy_mask"])
+        assert rel_l2(o["grad_weight"], outs[0]["grad_weight"]) < 1e-2
+        assert rel_l2(o["grad_hidden"], outs[0]["grad_hidden"]) < 1e-2
+
+
+def test_fused_flagged_rows_recomputed():
+    """Logits far above the first vocabulary tile's max (bias -100 on the first
+    tile, +60 further on) make the MFMA sweep flag the rows; the merge
+    recomputes them exactly."""
+    spec = synth.small("flagged", cfg_id=108, B=2, T=40, H=128, V=1000, bias=True)
+    _say("flagged rows")
+    d = synth.make(spec)
+    b = d["b"].copy()
+    b[:32] = -100.0
+    b[700:710] = 60.0
+    d["b_raw"] = synth.round_bf16_bits(b)
+    d["b"] = synth.bf16_bits_to_f32(d["b_raw"])
+    d["fwd"] = oracle.forward_rows(d["h"], d["W"], d["b"], spec.temperature, d["targets"])
+    d["old"] = synth.compose_logp(d["fwd"]["logp"], d["old_noise"])
+    d["ref"] = None
+    ref = run_oracle(spec, d)
+    gpu = run_gpu(spec, d)
+    _check_fused(spec, d, gpu, ref, lp_tol=1e-4)
+
+
+def test_fused_outputs_optional():
+    """Skipping gradients leaves loss, metrics and diagnostics unchanged."""
+    spec = SMALL["mfma_gmpo"]
+    d = make_case(spec)
+    _say("optional outputs")
+    full = run_gpu(spec, d)
+    part = run_gpu(spec, d, grad_hidden=False, grad_weight=False)
+    for k in ("loss", "metrics", "logp", "entropy", "dlogp"):
+        np.testing.assert_array_equal(full[k], part[k], err_msg=k)
+    assert "grad_hidden" not in part and "grad_weight" not in part
+
+
+# ---------------------------------------------------------------------------
+# selective_entropy
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", [
+    dict(N=200, H=256, V=1000, dtype="bf16", bias=False, tau=1.0),
+    dict(N=131, H=896, V=4099, dtype="bf16", bias=True, tau=1.3),
+    dict(N=37, H=64, V=517, dtype="f32", bias=True, tau=0.7),
+    dict(N=70, H=96, V=300, dtype="bf16", bias=False, tau=1.0),
+])
+def test_selective_entropy(case):
+    import rl_policy_gradient_amd as plp
+    spec = synth.small("se", cfg_id=110, B=1, T=case["N"], H=case["H"], V=case["V"], dtype=case["dtype"],
+                       bias=case["bias"], w_std=0.05)
+    _say(f"selective_entropy {case}")
+    d = synth.make(spec)
+    ref = oracle.forward_rows(d["h"], d["W"], d["b"], case["tau"], d["targets"])
+    dt = "bf16" if spec.dtype == "bf16" else None
+    ent, lp = plp.selective_entropy(dev_tensor(d["h_raw"], dt), dev_tensor(d["W_raw"], dt),
+                                    dev_tensor(d["b_raw"], dt) if d["b_raw"] is not None else None,
+                                    dev_tensor(d["targets"]), temperature=case["tau"])
+    ent2, none = plp.selective_entropy(dev_tensor(d["h_raw"], dt), dev_tensor(d["W_raw"], dt),
+                                       dev_tensor(d["b_raw"], dt) if d["b_raw"] is not None else None, None,
+                                       temperature=case["tau"])
+    torch.cuda.synchronize()
+    tol = 1e-5 if spec.dtype == "f32" else 2e-5
+    np.testing.assert_allclose(ent.cpu().numpy(), ref["entropy"], rtol=0, atol=tol)
+    np.testing.assert_allclose(lp.cpu().numpy(), ref["logp"], rtol=0, atol=tol)
+    assert none is None
+    np.testing.assert_array_equal(ent.cpu().numpy(), ent2.cpu().numpy())
+
+
