@@ -102,7 +102,7 @@ hipError_t launch_bwd_generic(int dtype, const void* W, const void* b, const voi
                               hipStream_t st);
 
 // Merge vocabulary splits: lp, H, lse per row and (when vout != NULL)
-// v = sum_v p W_v - W_y as fp32 [N,H]. Rows flagged by the sweep are
+// v = W_y - sum_v p W_v as fp32 [N,H] (grad_h = g / tau * v). Rows flagged by the sweep are
 // recomputed here from h, W, b with an exact online max.
 hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int Sv, int64_t N, int H, int V,
                           const void* h, const void* W, const void* b, float inv_tau, const int64_t* y,

@@ -21,7 +21,8 @@ __device__ __forceinline__ float ldf(const T* p, int64_t i) {
 // ---------------------------------------------------------------------------
 // Merge of vocabulary splits (per row): lse = M + log sum_j e^{m_j-M} s_j,
 // lp = z_y - lse, H = lse - (sum_j e^{m_j-M} sz_j) / (sum_j e^{m_j-M} s_j)
-// (PR #1558: H = log_z - sum_exp_z / sum_exp), and v = O/s - W_y.
+// (PR #1558: H = log_z - sum_exp_z / sum_exp), and v = W_y - O/s, so that
+// grad_h = (g / tau) v since d lp / d z_v = [v = y] - p_v.
 // A row any split flagged is recomputed exactly (row_exact).
 // ---------------------------------------------------------------------------
 template <typename T>
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
       const float* os = sm + H;
       const double inv_s = 1.0 / r.s;
       for (int d = threadIdx.x; d < H; d += NT)
-        vout[row * H + d] = (float)((double)os[d] * inv_s - (double)ldf<T>(W, yc * H + d));
+        vout[row * H + d] = (float)((double)ldf<T>(W, yc * H + d) - (double)os[d] * inv_s);
     }
     return;
   }
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
       double o = 0.0;
       for (int j = 0; j < Sv; ++j)
         if (s_c[j] != 0.0) o += s_c[j] * (double)O[((int64_t)j * N + row) * H + d];
-      vout[row * H + d] = (float)(o * inv_s - (double)ldf<T>(W, yc * H + d));
+      vout[row * H + d] = (float)((double)ldf<T>(W, yc * H + d) - o * inv_s);
     }
   }
 }
