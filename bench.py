@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Throughput of the fused LM-head + GMPO / GSPO-token forward+backward on one
+MI355X, with the roofline of the dominant kernel and the CPU oracle beside it.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|4|5]
+
+One step = one call of plp_fused_lmhead_policy_loss_fwd_bwd on one batch of
+synthetic inputs already resident in HBM: forward statistics, loss, metrics,
+grad_hidden, grad_weight (and grad_bias). Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "tokens/s fused LM-head+GMPO fwd+bwd, H=896 V=151936; % bf16 MFMA peak"
+
+
+def _workload(cfg: int, device):
+    """Inputs of workload `cfg` on the GPU. cfg 2 uses the seeded generators
+    shared with the parity tests; the larger ones draw the same distributions
+    with a seeded torch generator on the device (host generation of 7.5 GB of
+    hidden states would dominate the run)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from rl_policy_gradient_amd import selective_entropy
+
+    spec = synth.CONFIGS[cfg]
+    B, T, H, V, N = spec.B, spec.T, spec.H, spec.V, spec.N
+    if cfg in (1, 2):
+        d = synth.make(spec)
+        dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+
+        def up(x, bf):
+            if x is None:
+                return None
+            if bf:
+                return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+            return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+        bf = spec.dtype == "bf16"
+        h, W = up(d["h_raw"], bf), up(d["W_raw"], bf)
+        b = up(d["b_raw"], bf)
+        y = up(d["targets"], False)
+        comp = up(d["completion_mask"], False)
+        adv = up(d["advantages"], False)
+        old_noise = torch.from_numpy(d["old_noise"]).to(device)
+        ref_noise = None if d["ref_noise"] is None else torch.from_numpy(d["ref_noise"]).to(device)
+    else:
+        g = torch.Generator(device=device)
+        g.manual_seed(1000 + cfg)
+        h = torch.randn(N, H, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+        W = (torch.randn(V, H, generator=g, device=device) * spec.w_std).to(torch.bfloat16)
+        b = (torch.randn(V, generator=g, device=device) * spec.b_std).to(torch.bfloat16) if spec.bias else None
+        y = torch.randint(0, V, (N,), generator=g, device=device, dtype=torch.int64)
+        P = torch.randint(spec.prompt_lo, spec.prompt_hi + 1, (B,), generator=g, device=device)
+        comp = (torch.arange(T, device=device)[None, :] >= P[:, None]).to(torch.uint8).reshape(-1).contiguous()
+        adv = torch.randn(B, generator=g, device=device)
+        if spec.zero_adv_fraction > 0:
+            k = int(round(spec.zero_adv_fraction * B))
+            adv[torch.randperm(B, generator=g, device=device)[:k]] = 0
+        old_noise = torch.randn(N, generator=g, device=device, dtype=torch.float64) * spec.old_noise_std
+        ref_noise = (torch.randn(N, generator=g, device=device, dtype=torch.float64) * spec.ref_noise_std
+                     if spec.ref_noise_std is not None else None)
+    # old / ref = current log-prob + noise; the current log-prob comes from the
+    # GPU's own forward (outside the timed region)
+    _, lp = selective_entropy(h, W, b, y, temperature=spec.temperature)
+    old = (lp.double() + old_noise).float().contiguous()
+    ref = (lp.double() + ref_noise).float().contiguous() if ref_noise is not None else None
+    torch.cuda.synchronize()
+    return spec, dict(hidden=h, weight=W, bias=b, targets=y, completion_mask=comp, advantages=adv,
+                      old_logp=old, ref_logp=ref)
+
+
+def _kernel_src_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("lmhead_mfma.hip", "loss_stage.hip", "plp_api.cpp"):
+        with open(os.path.join(ROOT, "rl_policy_gradient_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain-copy calibration), read from the committed
+    summary; None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_src_hash") != _kernel_src_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def _cpu_baseline(spec) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the workload: one
+    sequence of up to 512 tokens at the workload's H and V (the whole workload
+    for config 2), forward + loss + backward, on all host cores."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    sample = spec.replace(B=1, T=min(spec.T, 512), chunk_sequences=0)
+    d = synth.make(sample)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    fwd = oracle.forward_rows(d["h"], d["W"], d["b"], sample.temperature, d["targets"])
+    old = synth.compose_logp(fwd["logp"], d["old_noise"])
+    ref = synth.compose_logp(fwd["logp"], d["ref_noise"])
+    out = oracle.run(oracle.LossConfig.from_spec(sample), d["h"], d["W"], d["b"], d["targets"], old, ref,
+                     d["completion_mask"], None, d["advantages"], fwd=fwd)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out["loss"])
+    return {"value": round(sample.N / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"B=1 T={sample.T} H={sample.H} V={sample.V} ({sample.N} tokens of {spec.name}); "
+                      f"fp64 forward+loss+backward in {dt:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "the data-parallel sharding is described in DESIGN.md", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import rl_policy_gradient_amd as plp
+    from rl_policy_gradient_amd import _abi
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec, inp = _workload(args.config, dev)
+    N, H, V = spec.N, spec.H, spec.V
+    kw = dict(B=spec.B, T=spec.T, loss_type=spec.loss_type, epsilon_low=spec.eps_low, epsilon_high=spec.eps_high,
+              beta=spec.beta, temperature=spec.temperature, top_entropy_quantile=spec.top_entropy_quantile,
+              chunk_sequences=spec.chunk_sequences, diagnostics=False)
+    ws = torch.empty(plp.workspace_size(spec.B, spec.T, H, V, bias=spec.bias,
+                                        top_entropy_quantile=spec.top_entropy_quantile,
+                                        chunk_sequences=spec.chunk_sequences, loss_type=spec.loss_type),
+                     dtype=torch.uint8, device=dev)
+    call_args = (inp["hidden"], inp["weight"], inp["targets"], inp["completion_mask"], inp["advantages"])
+    call_kw = dict(bias=inp["bias"], old_logp=inp["old_logp"], ref_logp=inp["ref_logp"], workspace=ws, **kw)
+    out = plp.fused_lmhead_policy_loss_fwd_bwd(*call_args, **call_kw)
+    out["dlogp"] = torch.empty(N, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        plp.fused_lmhead_policy_loss_fwd_bwd(*call_args, out=out, **call_kw)
+    torch.cuda.synchronize()
+
+    L = _abi.lib()
+    n_chunks = 1 if spec.chunk_sequences == 0 else -(-spec.B // spec.chunk_sequences)
+    _abi.check(L.plp_profile_start(4 * args.steps * n_chunks + 8))
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        plp.fused_lmhead_policy_loss_fwd_bwd(*call_args, out=out, **call_kw)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (ctypes.c_double * 2)()
+    cnt = (ctypes.c_int32 * 2)()
+    _abi.check(L.plp_profile_stop(ms, cnt))
+    elapsed = t1 - t0
+    ms_step = 1e3 * elapsed / args.steps
+    tokens_s = N * args.steps / elapsed
+    flops_tok = 6.0 * H * V
+    tflops = tokens_s * flops_tok / 1e12
+
+    # roofline of the dominant sweep
+    n_active = int((out["dlogp"] != 0).sum().item())
+    per_launch = {
+        "fwd_sweep": (4.0 * H * V * N / n_chunks, ms[0] / max(1, cnt[0])),
+        "wgrad_sweep": (2.0 * H * V * n_active / n_chunks, ms[1] / max(1, cnt[1])),
+    }
+    dom = "fwd_sweep" if ms[0] >= ms[1] else "wgrad_sweep"
+    flops, avg_ms = per_launch[dom]
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    workload = f"cfg{args.config}_{spec.name}"
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": _traffic_from_profiles(dom, workload),
+                "kernel": dom, "avg_launch_ms": round(avg_ms, 4),
+                "launches": int(cnt[0] if dom == "fwd_sweep" else cnt[1]),
+                "other_sweep_ms_per_step": round((ms[1] if dom == "fwd_sweep" else ms[0]) / args.steps, 4)}
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "tflops_6nhv": round(tflops, 2),
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": workload, "B": spec.B, "T": spec.T, "H": H, "V": V,
+                   "loss_type": spec.loss_type, "bias": spec.bias, "beta": spec.beta,
+                   "top_entropy_quantile": spec.top_entropy_quantile, "chunk_sequences": spec.chunk_sequences,
+                   "global_batch_tokens": N, "active_tokens_with_grad": n_active,
+                   "event_ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4)},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = _cpu_baseline(spec)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

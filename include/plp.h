@@ -201,6 +201,19 @@ PLP_API int plp_policy_loss_from_logprobs(const plp_args* args, const float* log
                                           const plp_outputs* out, void* workspace, size_t workspace_bytes,
                                           hipStream_t stream);
 
+/* ---- Measurement helpers (not part of the method) -------------------------
+ * Per-kernel timing of the two LM-head sweeps with HIP events recorded on the
+ * stream of each call, for benchmarks and roofline reports.
+ * plp_profile_start(max_records): pre-creates 2*max_records events and turns
+ * recording on (PLP_E_INVALID if max_records < 1; PLP_E_HIP if event creation
+ * fails). While on, every forward sweep (kind 0) and weight-gradient sweep
+ * (kind 1) launch is bracketed by an event pair, up to max_records pairs.
+ * plp_profile_stop(ms[2], count[2]): waits for the recorded events, returns
+ * per kind the summed milliseconds and the number of launches, destroys the
+ * events and turns recording off. Process-global; not for concurrent use. */
+PLP_API int plp_profile_start(int32_t max_records);
+PLP_API int plp_profile_stop(double* ms_out, int32_t* count_out);
+
 #ifdef __cplusplus
 }
 #endif

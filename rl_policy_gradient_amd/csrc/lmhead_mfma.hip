@@ -118,6 +118,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
   constexpr int DB = 2 * KB;   // 16-wide column blocks per wave
   __shared__ f32x4 s_part[NW][2][4][64];
   __shared__ bf16x8 s_p[4][64];
+  __shared__ bf16x8 s_q[NW][4][KB][64];  // resident h fragments, per wave, in fragment order
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -128,14 +129,14 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
   const int t_begin = sv * tiles_per_split;
   const int t_end = min(n_tiles, t_begin + tiles_per_split);
 
-  // Resident h fragments (B operand of S^T): rows q0+16nb+c16, cols d0+32kb+8g.
-  bf16x8 qf[4][KB];
+  // Resident h fragments (B operand of S^T): rows q0+16nb+c16, cols
+  // d0+32kb+8g. Each wave reads back only its own slice, so no barrier.
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int64_t row = min(q0 + 16 * nb + c16, N - 1);
     const __bf16* src = h + row * H + d0 + 8 * g;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qf[nb][kb] = ld16(src + 32 * kb);
+    for (int kb = 0; kb < KB; ++kb) s_q[w][nb][kb][lane] = ld16(src + 32 * kb);
   }
 
   f32x4 o[4][WITH_O ? DB : 1];
@@ -153,8 +154,36 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
   float zy = 0.f;
   bool have_y = false, flag = false;
 
+  // Operand fragments of one tile: a = W rows (A of S^T), bt = blocked W^T
+  // (B of P KV). Loads run one phase ahead of their use: a for tile t+1 is
+  // issued right after the S^T product of tile t, bt for tile t+1 right after
+  // the P KV product of tile t, so their latency overlaps compute.
+  auto load_a = [&](int t, bf16x8 (&a)[2][KB]) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int v = min(t * BK + 16 * mb + c16, V - 1);  // rows past V are masked in the epilogue
+      const __bf16* src = W + (int64_t)v * H + d0 + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) a[mb][kb] = ld16(src + 32 * kb);
+    }
+  };
+  auto load_b = [&](int t, bf16x8 (&b)[WITH_O ? DB : 1]) {
+    if constexpr (WITH_O) {
+      const __bf16* src = Wt + (((int64_t)t * 4 + g) * H + d0 + c16) * 8;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) b[db] = ld16(src + 16 * 8 * db);
+    }
+  };
+  bf16x8 a[2][KB];
+  bf16x8 bt[WITH_O ? DB : 1];
+  if (t_begin < t_end) {
+    load_a(t_begin, a);
+    load_b(t_begin, bt);
+  }
+
   for (int t = t_begin; t < t_end; ++t) {
     const int v0 = t * BK;
+    const int tn = min(t + 1, t_end - 1);
     // ---- S^T partial over this wave's columns --------------------------------
     f32x4 acc[2][4];
 #pragma unroll
@@ -162,25 +191,17 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero4();
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int v = min(v0 + 16 * mb + c16, V - 1);  // rows past V are masked in the epilogue
-      const __bf16* src = W + (int64_t)v * H + d0 + 8 * g;
+    for (int kb = 0; kb < KB; ++kb) {
+      bf16x8 q[4];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 a = ld16(src + 32 * kb);
+      for (int nb = 0; nb < 4; ++nb) q[nb] = s_q[w][nb][kb][lane];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a, qf[nb][kb], acc[mb][nb]);
-      }
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb][kb], q[nb], acc[mb][nb]);
     }
-    // keep the accumulator-operand loads below the logit MFMAs: both operand
-    // sets live at once would not fit the register file
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8 bt[WITH_O ? DB : 1];
-    if constexpr (WITH_O) {
-      const __bf16* src = Wt + (((int64_t)t * 4 + g) * H + d0 + c16) * 8;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) bt[db] = ld16(src + 16 * 8 * db);
-    }
+    load_a(tn, a);
     // ---- reduce-scatter: wave w collects row block w -------------------------
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -252,6 +273,8 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], bt[db], o[qb][db]);
+      __builtin_amdgcn_sched_barrier(0);
+      load_b(tn, bt);
     }
   }
 
@@ -306,6 +329,7 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
   __shared__ f32x4 s_part[NW][2][4][64];
   __shared__ bf16x8 s_p[4][64];
   __shared__ TokData s_tok[BK];
+  __shared__ bf16x8 s_q[NW][4][KB][64];  // resident W fragments, per wave, in fragment order
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -314,13 +338,12 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
   const int n_tok = *count_dev;
   const int n_tiles = (n_tok + BK - 1) / BK;
 
-  bf16x8 qf[4][KB];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int v = min(q0 + 16 * nb + c16, V - 1);
     const __bf16* src = W + (int64_t)v * H + d0 + 8 * g;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qf[nb][kb] = ld16(src + 32 * kb);
+    for (int kb = 0; kb < KB; ++kb) s_q[w][nb][kb][lane] = ld16(src + 32 * kb);
   }
   f32x4 o[4][DB];
 #pragma unroll
@@ -332,8 +355,30 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
   const float bv = bias ? (float)bias[min(my_v, V - 1)] : 0.f;
   double gb_run = 0.0;
 
+  // Loads one phase ahead of their use, as in the forward sweep.
+  auto load_a = [&](int t, bf16x8 (&a)[2][KB]) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const __bf16* src = hc + (int64_t)(t * BK + 16 * mb + c16) * H + d0 + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) a[mb][kb] = ld16(src + 32 * kb);
+    }
+  };
+  auto load_b = [&](int t, bf16x8 (&b)[DB]) {
+    const __bf16* src = ht + (((int64_t)t * 4 + g) * H + d0 + c16) * 8;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) b[db] = ld16(src + 16 * 8 * db);
+  };
+  bf16x8 a[2][KB];
+  bf16x8 bt[DB];
+  if (n_tiles > 0) {
+    load_a(0, a);
+    load_b(0, bt);
+  }
+
   for (int t = 0; t < n_tiles; ++t) {
     const int t0 = t * BK;
+    const int tn = min(t + 1, n_tiles - 1);
     if (w == 0 && lane < BK) s_tok[lane] = tok[t0 + lane];
     f32x4 acc[2][4];
 #pragma unroll
@@ -341,21 +386,17 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero4();
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const __bf16* src = hc + (int64_t)(t0 + 16 * mb + c16) * H + d0 + 8 * g;
+    for (int kb = 0; kb < KB; ++kb) {
+      bf16x8 q[4];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 a = ld16(src + 32 * kb);
+      for (int nb = 0; nb < 4; ++nb) q[nb] = s_q[w][nb][kb][lane];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a, qf[nb][kb], acc[mb][nb]);
-      }
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb][kb], q[nb], acc[mb][nb]);
     }
-    bf16x8 bt[DB];
-    {
-      const __bf16* src = ht + (((int64_t)t * 4 + g) * H + d0 + c16) * 8;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) bt[db] = ld16(src + 16 * 8 * db);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(tn, a);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -393,6 +434,8 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], bt[db], o[qb][db]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(tn, bt);
   }
 
   // grad_b: the four lane groups of a row hold disjoint token subsets

@@ -6,7 +6,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/plp.h"
 #include "common.h"
@@ -156,6 +158,26 @@ size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
   return c.off + kAlign;
 }
 
+// Optional event timing of the two sweeps (plp_profile_start/stop).
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> kind;
+  size_t used = 0;
+};
+Profiler g_prof;
+
+// Returns the event pair for one launch of `k`, or nullptr when not recording.
+hipEvent_t* prof_slot(int k) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.on || 2 * (g_prof.used + 1) > g_prof.ev.size()) return nullptr;
+  hipEvent_t* p = &g_prof.ev[2 * g_prof.used];
+  g_prof.kind[g_prof.used] = k;
+  ++g_prof.used;
+  return p;
+}
+
 #define HIP_TRY(expr)                                                                   \
   do {                                                                                  \
     hipError_t e_ = (expr);                                                             \
@@ -236,8 +258,11 @@ int forward_rows(const plp_args* a, const Plan& p, Bufs& b, int64_t r0, int64_t 
   const int64_t* y = a->targets + r0;
   const float inv_tau = (float)(1.0 / a->temperature);
   if (p.mfma) {
+    hipEvent_t* ev = prof_slot(0);
+    if (ev) HIP_TRY(hipEventRecord(ev[0], st));
     HIP_TRY(launch_fwd_mfma((const __bf16*)h, (const __bf16*)a->weight, b.Wt, (const __bf16*)a->bias, y, n, a->H,
                             a->V, inv_tau, p.Sv, with_o, b.stats, with_o ? b.O : nullptr, st));
+    if (ev) HIP_TRY(hipEventRecord(ev[1], st));
   } else {
     HIP_TRY(launch_fwd_generic(a->dtype, h, a->weight, a->bias, y, n, a->H, a->V, inv_tau, with_o, b.stats,
                                with_o ? b.O : nullptr, st));
@@ -252,6 +277,49 @@ int forward_rows(const plp_args* a, const Plan& p, Bufs& b, int64_t r0, int64_t 
 extern "C" {
 
 PLP_API int plp_abi_version(void) { return PLP_ABI_VERSION; }
+
+PLP_API int plp_profile_start(int32_t max_records) {
+  if (max_records < 1) return fail(PLP_E_INVALID, "max_records must be >= 1");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.assign(2 * (size_t)max_records, nullptr);
+  g_prof.kind.assign((size_t)max_records, 0);
+  g_prof.used = 0;
+  for (auto& e : g_prof.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      g_prof.on = false;
+      return fail(PLP_E_HIP, "hipEventCreate: %s", hipGetErrorString(r));
+    }
+  }
+  g_prof.on = true;
+  return ok();
+}
+
+PLP_API int plp_profile_stop(double* ms_out, int32_t* count_out) {
+  if (!ms_out || !count_out) return fail(PLP_E_INVALID, "ms_out and count_out are required");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  ms_out[0] = ms_out[1] = 0.0;
+  count_out[0] = count_out[1] = 0;
+  int rc = PLP_OK;
+  for (size_t i = 0; i < g_prof.used; ++i) {
+    float ms = 0.f;
+    hipError_t r = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+    if (r != hipSuccess) {
+      rc = fail(PLP_E_HIP, "event timing: %s", hipGetErrorString(r));
+      break;
+    }
+    ms_out[g_prof.kind[i]] += ms;
+    count_out[g_prof.kind[i]] += 1;
+  }
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.kind.clear();
+  g_prof.used = 0;
+  g_prof.on = false;
+  return rc == PLP_OK ? ok() : rc;
+}
 
 PLP_API const char* plp_last_error(void) { return g_last_error.c_str(); }
 
@@ -343,11 +411,14 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
       else
         HIP_TRY(launch_gather_rows(a->dtype, hsrc, b.idx, b.count, p.cap, H, b.hc, st));
       const int mode = p.nchunks == 1 ? 0 : (c == 0 ? 1 : (c == p.nchunks - 1 ? 3 : 2));
-      if (p.mfma)
+      if (p.mfma) {
+        hipEvent_t* ev = prof_slot(1);
+        if (ev) HIP_TRY(hipEventRecord(ev[0], st));
         HIP_TRY(launch_bwd_mfma((const __bf16*)a->weight, (const __bf16*)a->bias, (const __bf16*)b.hc, b.ht, b.tok,
                                 b.count, p.cap, H, V, inv_tau, mode, b.gW_acc, b.gb_acc, (__bf16*)out->grad_weight,
                                 (__bf16*)out->grad_bias, st));
-      else
+        if (ev) HIP_TRY(hipEventRecord(ev[1], st));
+      } else
         HIP_TRY(launch_bwd_generic(a->dtype, a->weight, a->bias, b.hc, b.tok, b.count, H, V, inv_tau, mode, b.gW_acc,
                                    b.gb_acc, out->grad_weight, out->grad_bias, st));
     }

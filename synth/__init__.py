@@ -96,12 +96,25 @@ def _rng(spec: Spec, stream: int) -> np.random.Generator:
 
 
 def round_bf16_bits(x32: np.ndarray) -> np.ndarray:
-    """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
-    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    nan = np.isnan(x32)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    out = u.astype(np.uint16)
-    out[nan] = 0x7FC0
+    """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even.
+
+    Adds 0x7FFF plus the lowest kept bit and truncates; in uint32 this cannot
+    wrap for any non-NaN input (NaNs are set to the canonical quiet NaN)."""
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    out = np.empty(x32.shape, dtype=np.uint16)
+    flat_in = x32.reshape(-1).view(np.uint32)
+    flat_out = out.reshape(-1)
+    step = 1 << 22
+    for a in range(0, flat_in.size, step):
+        u = flat_in[a:a + step]
+        r = (u >> np.uint32(16)) & np.uint32(1)
+        r += np.uint32(0x7FFF)
+        r += u
+        r >>= np.uint32(16)
+        flat_out[a:a + step] = r
+        nan = np.isnan(x32.reshape(-1)[a:a + step])
+        if nan.any():
+            flat_out[a:a + step][nan] = 0x7FC0
     return out
 
 
