@@ -57,7 +57,28 @@ __device__ __forceinline__ bf16x8 ld16(const __bf16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
-__device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
+// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 lane swaps: permlane16_swap(x, x) hands every lane the
+// values of rows {0,1} or {2,3} as (even row, odd row), permlane32_swap(y, y)
+// the values of halves (low, high). Every lane combines the same operands in
+// the same order, so all four lanes hold bitwise-identical results.
+__device__ __forceinline__ float xg_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const unsigned v = __float_as_uint(y);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+__device__ __forceinline__ float xg_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const unsigned v = __float_as_uint(y);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -103,11 +124,28 @@ __global__ __launch_bounds__(256) void blocked_copy_kernel(const __bf16* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Forward sweep: per token row, running (m, sum e^{z-m}, sum e^{z-m} z), the
-// target logit, and (WITH_O) the accumulator O = sum_v e^{z-m} W_v.
-// Grid: (row blocks) x Sv vocabulary splits, block id = rb * Sv + split.
+// Schedule shared by both sweeps (per workgroup, per tile t of the sweep):
+//
+//   prologue: S^T(t0) -> LDS partials, barrier, reduce -> sf
+//   loop t:   S^T(t+1) MFMAs          | interleaved with the epilogue of tile t
+//             loads for tile t+2         (VALU on sf, the reduced logits of t)
+//             barrier
+//             P(t) -> LDS, partials of t+1 -> LDS
+//             barrier
+//             P KV(t) MFMAs            | interleaved with the reduce of t+1
+//             loads for tile t+1 (KV^T)
+//
+// so the matrix cores work while the vector unit runs the epilogue, and every
+// load has a whole phase to arrive. Two barriers per tile; the partials and P
+// buffers are reused every tile (each write follows a barrier that all reads
+// of the previous contents precede).
 // ---------------------------------------------------------------------------
-template <int KB, bool WITH_O>
+
+// Forward sweep: per token row, running (sum e^{z-m}, sum e^{z-m} z) against
+// the reference m, the target logit, and (WITH_O) the accumulator
+// O = sum_v e^{z-m} W_v. Grid: (row blocks) x Sv vocabulary splits, block
+// id = rb * Sv + split.
+template <int KB, bool WITH_O, bool HAS_BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
                      const __bf16* __restrict__ Wt, const __bf16* __restrict__ bias,
@@ -140,12 +178,10 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
   }
 
   f32x4 o[4][WITH_O ? DB : 1];
-  if constexpr (WITH_O) {
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+  for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[qb][db] = zero4();
-  }
+    for (int db = 0; db < (WITH_O ? DB : 1); ++db) o[qb][db] = zero4();
 
   const int64_t my_row = q0 + 16 * w + c16;  // row whose epilogue this lane runs
   const int64_t yv = (y != nullptr && my_row < N) ? y[my_row] : -1;
@@ -154,10 +190,6 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
   float zy = 0.f;
   bool have_y = false, flag = false;
 
-  // Operand fragments of one tile: a = W rows (A of S^T), bt = blocked W^T
-  // (B of P KV). Loads run one phase ahead of their use: a for tile t+1 is
-  // issued right after the S^T product of tile t, bt for tile t+1 right after
-  // the P KV product of tile t, so their latency overlaps compute.
   auto load_a = [&](int t, bf16x8 (&a)[2][KB]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -174,18 +206,11 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
       for (int db = 0; db < DB; ++db) b[db] = ld16(src + 16 * 8 * db);
     }
   };
-  bf16x8 a[2][KB];
-  bf16x8 bt[WITH_O ? DB : 1];
-  if (t_begin < t_end) {
-    load_a(t_begin, a);
-    load_b(t_begin, bt);
-  }
-
-  for (int t = t_begin; t < t_end; ++t) {
-    const int v0 = t * BK;
-    const int tn = min(t + 1, t_end - 1);
-    // ---- S^T partial over this wave's columns --------------------------------
-    f32x4 acc[2][4];
+  auto load_bias = [&](int t, float (&bv)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bv[j] = HAS_BIAS ? (float)bias[min(t * BK + kv_of(g, j), V - 1)] : 0.f;
+  };
+  auto s_mfma = [&](const bf16x8 (&a)[2][KB], f32x4 (&acc)[2][4]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -200,15 +225,14 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb][kb], q[nb], acc[mb][nb]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(tn, a);
-    // ---- reduce-scatter: wave w collects row block w -------------------------
+  };
+  auto write_part = [&](const f32x4 (&acc)[2][4]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) s_part[w][mb][nb][lane] = acc[mb][nb];
-    __syncthreads();
-    f32x4 sf[2];
+  };
+  auto reduce_part = [&](f32x4 (&sf)[2]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       f32x4 r = s_part[0][mb][w][lane];
@@ -216,7 +240,32 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
       for (int src = 1; src < NW; ++src) r += s_part[src][mb][w][lane];
       sf[mb] = r;
     }
-    // ---- epilogue on row my_row, tile rows kv(g, j) -------------------------
+  };
+
+  bf16x8 a[2][KB];
+  bf16x8 bt[WITH_O ? DB : 1];
+  f32x4 acc[2][4], sf[2];
+  float bv[8];
+  if (t_begin < t_end) {
+    load_a(t_begin, a);
+    load_b(t_begin, bt);
+    load_bias(t_begin, bv);
+    s_mfma(a, acc);
+    load_a(min(t_begin + 1, t_end - 1), a);
+    write_part(acc);
+  }
+  __syncthreads();
+  if (t_begin < t_end) reduce_part(sf);
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int v0 = t * BK;
+    const int tn = min(t + 1, t_end - 1);
+    const int tnn = min(t + 2, t_end - 1);
+    // ---- logits of tile t+1 on the matrix cores ----------------------------
+    s_mfma(a, acc);
+    float bvn[8];
+    load_bias(tn, bvn);
+    // ---- epilogue of tile t on row my_row, tile rows kv(g, j) -------------
     float z[8];
     bool ok[8];
 #pragma unroll
@@ -224,15 +273,13 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
       const int v = v0 + kv_of(g, j);
       ok[j] = v < V;
       const float sv_ = j < 4 ? sf[0][j] : sf[1][j - 4];
-      const float bv = bias ? (float)bias[min(v, V - 1)] : 0.f;
-      z[j] = ok[j] ? (sv_ + bv) * inv_tau : -INFINITY;
+      z[j] = ok[j] ? (sv_ + bv[j]) * inv_tau : -INFINITY;
     }
     float mx = z[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    if (t == t_begin) m_ref = mx;
+    mx = xg_max(mx);
+    m_ref = t == t_begin ? mx : m_ref;
     flag |= mx > m_ref + kRefSlack;
     float p[8], sp = 0.f, szp = 0.f;
 #pragma unroll
@@ -241,30 +288,26 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
       sp += p[j];
       szp += ok[j] ? p[j] * z[j] : 0.f;
     }
-    sp += shfl_xor_f(sp, 16);
-    sp += shfl_xor_f(sp, 32);
-    szp += shfl_xor_f(szp, 16);
-    szp += shfl_xor_f(szp, 32);
-    s_run += (double)sp;
-    sz_run += (double)szp;
+    s_run += (double)xg_sum(sp);
+    sz_run += (double)xg_sum(szp);
     {
       const int64_t rel = yv - v0;
-      if (rel >= 0 && rel < BK) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (kv_of(g, j) == (int)rel) {
-            zy = z[j];
-            have_y = true;
-          }
+      for (int j = 0; j < 8; ++j) {
+        const bool hit = (int64_t)kv_of(g, j) == rel;
+        zy = hit ? z[j] : zy;
+        have_y |= hit;
       }
     }
-    if constexpr (WITH_O) {
-      bf16x8 pa;
+    bf16x8 pa;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pa[j] = (__bf16)p[j];
-      s_p[w][lane] = pa;
-    }
+    for (int j = 0; j < 8; ++j) pa[j] = (__bf16)p[j];
+    load_a(tnn, a);
     __syncthreads();
+    if constexpr (WITH_O) s_p[w][lane] = pa;
+    write_part(acc);
+    __syncthreads();
+    // ---- accumulator product of tile t, reduce of tile t+1 -----------------
     if constexpr (WITH_O) {
       bf16x8 pf[4];
 #pragma unroll
@@ -273,15 +316,15 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], bt[db], o[qb][db]);
-      __builtin_amdgcn_sched_barrier(0);
       load_b(tn, bt);
     }
+    reduce_part(sf);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bv[j] = bvn[j];
   }
 
   // ---- results ---------------------------------------------------------------
-  float zyv = have_y ? zy : 0.f;
-  zyv += shfl_xor_f(zyv, 16);
-  zyv += shfl_xor_f(zyv, 32);
+  const float zyv = xg_sum(have_y ? zy : 0.f);
   if (g == 0 && my_row < N) {
     RowStats rs;
     rs.m = m_ref;
@@ -315,7 +358,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
 // acc_mode: 0 write the output dtype; 1 store fp32 accumulator; 2 add into it;
 // 3 add the fp32 accumulator and write the output dtype.
 // ---------------------------------------------------------------------------
-template <int KB>
+template <int KB, bool HAS_BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bias,
                      const __bf16* __restrict__ hc, const __bf16* __restrict__ ht,
@@ -328,7 +371,7 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
   constexpr int DB = 2 * KB;
   __shared__ f32x4 s_part[NW][2][4][64];
   __shared__ bf16x8 s_p[4][64];
-  __shared__ TokData s_tok[BK];
+  __shared__ TokData s_tok[2][BK];
   __shared__ bf16x8 s_q[NW][4][KB][64];  // resident W fragments, per wave, in fragment order
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -352,10 +395,9 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
     for (int db = 0; db < DB; ++db) o[qb][db] = zero4();
 
   const int my_v = q0 + 16 * w + c16;
-  const float bv = bias ? (float)bias[min(my_v, V - 1)] : 0.f;
+  const float bvl = HAS_BIAS ? (float)bias[min(my_v, V - 1)] : 0.f;
   double gb_run = 0.0;
 
-  // Loads one phase ahead of their use, as in the forward sweep.
   auto load_a = [&](int t, bf16x8 (&a)[2][KB]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -369,18 +411,10 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
 #pragma unroll
     for (int db = 0; db < DB; ++db) b[db] = ld16(src + 16 * 8 * db);
   };
-  bf16x8 a[2][KB];
-  bf16x8 bt[DB];
-  if (n_tiles > 0) {
-    load_a(0, a);
-    load_b(0, bt);
-  }
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int t0 = t * BK;
-    const int tn = min(t + 1, n_tiles - 1);
-    if (w == 0 && lane < BK) s_tok[lane] = tok[t0 + lane];
-    f32x4 acc[2][4];
+  auto stage_tok = [&](int t) {
+    if (w == 0 && lane < BK) s_tok[t & 1][lane] = tok[t * BK + lane];
+  };
+  auto s_mfma = [&](const bf16x8 (&a)[2][KB], f32x4 (&acc)[2][4]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -395,14 +429,14 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb][kb], q[nb], acc[mb][nb]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(tn, a);
+  };
+  auto write_part = [&](const f32x4 (&acc)[2][4]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) s_part[w][mb][nb][lane] = acc[mb][nb];
-    __syncthreads();
-    f32x4 sf[2];
+  };
+  auto reduce_part = [&](f32x4 (&sf)[2]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       f32x4 r = s_part[0][mb][w][lane];
@@ -410,14 +444,35 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
       for (int src = 1; src < NW; ++src) r += s_part[src][mb][w][lane];
       sf[mb] = r;
     }
+  };
+
+  bf16x8 a[2][KB];
+  bf16x8 bt[DB];
+  f32x4 acc[2][4], sf[2];
+  if (n_tiles > 0) {
+    stage_tok(0);
+    load_a(0, a);
+    load_b(0, bt);
+    s_mfma(a, acc);
+    load_a(min(1, n_tiles - 1), a);
+    write_part(acc);
+  }
+  __syncthreads();
+  if (n_tiles > 0) reduce_part(sf);
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int t0 = t * BK;
+    const int tn = min(t + 1, n_tiles - 1);
+    const int tnn = min(t + 2, n_tiles - 1);
+    s_mfma(a, acc);
     bf16x8 pa;
     float gsum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int kv = kv_of(g, j);
-      const TokData td = s_tok[kv];
+      const TokData td = s_tok[t & 1][kv];
       const float sv_ = j < 4 ? sf[0][j] : sf[1][j - 4];
-      const float z = (sv_ + bv) * inv_tau;
+      const float z = (sv_ + bvl) * inv_tau;
       const float pr = __expf(z - td.lse);
       float dz = td.gs * ((td.y == my_v ? 1.f : 0.f) - pr);
       dz = (t0 + kv < n_tok && my_v < V) ? dz : 0.f;
@@ -425,7 +480,11 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
       pa[j] = (__bf16)dz;
     }
     gb_run += (double)gsum;
+    load_a(tnn, a);
+    __syncthreads();
     s_p[w][lane] = pa;
+    write_part(acc);
+    stage_tok(tn);
     __syncthreads();
     bf16x8 pf[4];
 #pragma unroll
@@ -434,8 +493,8 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], bt[db], o[qb][db]);
-    __builtin_amdgcn_sched_barrier(0);
     load_b(tn, bt);
+    reduce_part(sf);
   }
 
   // grad_b: the four lane groups of a row hold disjoint token subsets
@@ -476,11 +535,17 @@ hipError_t fwd_dispatch(const __bf16* h, const __bf16* W, const __bf16* Wt, cons
                         RowStats* stats, float* O, hipStream_t st) {
   const int64_t nrb = (N + BQ - 1) / BQ;
   dim3 grid((unsigned)(nrb * Sv)), block(256);
-  if (with_o)
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true>), grid, block, 0, st, h, W, Wt, b, y, N, V, inv_tau, Sv,
+  if (with_o && b)
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true, true>), grid, block, 0, st, h, W, Wt, b, y, N, V, inv_tau, Sv,
+                       tps, stats, O);
+  else if (with_o)
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true, false>), grid, block, 0, st, h, W, Wt, b, y, N, V, inv_tau, Sv,
+                       tps, stats, O);
+  else if (b)
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false, true>), grid, block, 0, st, h, W, Wt, b, y, N, V, inv_tau, Sv,
                        tps, stats, O);
   else
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false>), grid, block, 0, st, h, W, Wt, b, y, N, V, inv_tau, Sv,
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false, false>), grid, block, 0, st, h, W, Wt, b, y, N, V, inv_tau, Sv,
                        tps, stats, O);
   return hipGetLastError();
 }
@@ -490,8 +555,12 @@ hipError_t bwd_dispatch(const __bf16* W, const __bf16* b, const __bf16* hc, cons
                         const TokData* tok, const int* count_dev, int V, float inv_tau, int acc_mode,
                         float* gW_acc, float* gb_acc, __bf16* gW_out, __bf16* gb_out, hipStream_t st) {
   dim3 grid((unsigned)((V + BQ - 1) / BQ)), block(256);
-  hipLaunchKernelGGL((bwd_mfma_kernel<KB>), grid, block, 0, st, W, b, hc, ht, tok, count_dev, V, inv_tau,
-                     acc_mode, gW_acc, gb_acc, gW_out, gb_out);
+  if (b)
+    hipLaunchKernelGGL((bwd_mfma_kernel<KB, true>), grid, block, 0, st, W, b, hc, ht, tok, count_dev, V, inv_tau,
+                       acc_mode, gW_acc, gb_acc, gW_out, gb_out);
+  else
+    hipLaunchKernelGGL((bwd_mfma_kernel<KB, false>), grid, block, 0, st, W, b, hc, ht, tok, count_dev, V, inv_tau,
+                       acc_mode, gW_acc, gb_acc, gW_out, gb_out);
   return hipGetLastError();
 }
 
