@@ -191,6 +191,12 @@ def hidden(spec: Spec, rows: Optional[np.ndarray] = None):
     return _store(spec, out)
 
 
+def hidden_block(spec: Spec, bi: int):
+    """Rows [4096 bi, 4096 bi + 4096) of the hidden states, as (fp32 values,
+    raw storage); blocks are independent, so they can be drawn in parallel."""
+    return _store(spec, _hidden_block(spec, bi))
+
+
 def _hidden_block(spec: Spec, bi: int) -> np.ndarray:
     rng = np.random.default_rng(np.random.SeedSequence([spec.seed, spec.cfg_id, _S_H, bi]))
     rows = min(4096, spec.N - bi * 4096)
