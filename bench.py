@@ -12,7 +12,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -84,14 +83,6 @@ def _workload(cfg: int, device):
                       old_logp=old, ref_logp=ref)
 
 
-def _kernel_src_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("lmhead_mfma.hip", "loss_stage.hip", "plp_api.cpp"):
-        with open(os.path.join(ROOT, "rl_policy_gradient_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def _traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE and
     WRITE_SIZE, scaled by a plain-copy calibration), read from the committed
@@ -104,7 +95,9 @@ def _traffic_from_profiles(kernel: str, workload: str):
             d = json.load(fh)
     except (OSError, ValueError):
         return None
-    if d.get("kernel_src_hash") != _kernel_src_hash():
+    from rl_policy_gradient_amd.profsum import kernel_src_hash
+
+    if d.get("kernel_src_hash") != kernel_src_hash():
         return None
     return d.get("bytes_per_launch")
 
@@ -207,7 +200,7 @@ def main() -> int:
     dom = "fwd_sweep" if ms[0] >= ms[1] else "wgrad_sweep"
     flops, avg_ms = per_launch[dom]
     achieved = flops / (avg_ms * 1e-3) / 1e12
-    workload = f"cfg{args.config}_{spec.name}"
+    workload = spec.name
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": _traffic_from_profiles(dom, workload),

@@ -1,0 +1,195 @@
+"""Summaries of rocprofv3 CSV output for the library's kernels.
+
+    python -m rl_policy_gradient_amd.profsum copy --mib 1024 --reps 4
+        a plain streaming kernel of known size (torch's elementwise negation:
+        reads and writes each byte once), to run under
+        ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE``: the counters'
+        reading for it gives the factor from counter KiB to bytes moved.
+    python -m rl_policy_gradient_amd.profsum stats TRACE_CSV --command "..."
+        per-kernel count / average / min / max duration from a
+        ``--kernel-trace`` CSV (text table).
+    python -m rl_policy_gradient_amd.profsum traffic --fetch CSV --write CSV
+            --copy-fetch CSV --copy-write CSV --copy-bytes B --kernel NAME
+            --match SUBSTR --workload W --out JSON --command "..."
+        HBM bytes per launch of one kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+        dispatch) averaged over its dispatches, each scaled by the factor the
+        same counter shows on the plain copy.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ("lmhead_mfma.hip", "loss_stage.hip", "plp_api.cpp", "common.h")
+
+
+def kernel_src_hash() -> str:
+    """Hash of the sources that define the sweeps' code and launch shapes; a
+    traffic summary taken on other sources is stale."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "rl_policy_gradient_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _demangle(names):
+    """Demangled kernel names (c++filt when present, else unchanged)."""
+    import shutil
+    import subprocess
+
+    import re
+
+    names = [n.strip('"') for n in names]
+    if shutil.which("c++filt"):
+        out = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True).stdout.split("\n")
+        if len(out) >= len(names):
+            names = out[: len(names)]
+    # names c++filt leaves mangled (bf16 parameters): namespace, name and the
+    # integer / bool template arguments
+    pretty = []
+    for n in names:
+        m = re.match(r"_ZN3plp12_GLOBAL__N_1(\d+)", n)
+        if not m:
+            pretty.append(n)
+            continue
+        k = int(m.group(1))
+        base = n[m.end(): m.end() + k]
+        rest = n[m.end() + k:]
+        targs = []
+        if rest.startswith("I"):
+            for t, v in re.findall(r"L(i|b)(\d+)E", rest.split("EEv")[0]):
+                targs.append(v if t == "i" else ("true" if v == "1" else "false"))
+        pretty.append("plp::" + base + (f"<{', '.join(targs)}>" if targs else ""))
+    return pretty
+
+
+def _short(name: str, width: int = 90) -> str:
+    name = name.strip('"')
+    if name.startswith("void "):
+        name = name[5:]
+    return name if len(name) <= width else name[: width - 3] + "..."
+
+
+def _rows(path):
+    with open(path, newline="") as fh:
+        yield from csv.DictReader(fh)
+
+
+def kernel_durations(trace_csv: str) -> dict:
+    """{kernel name: [duration ns, ...]} from a rocprofv3 kernel-trace CSV."""
+    out = {}
+    for r in _rows(trace_csv):
+        d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        out.setdefault(r["Kernel_Name"], []).append(d)
+    return out
+
+
+def counter_per_dispatch(pmc_csv: str, counter: str, match: str) -> list:
+    """Values of `counter` for every dispatch whose kernel name contains `match`."""
+    vals = {}
+    for r in _rows(pmc_csv):
+        if r["Counter_Name"] != counter or match not in r["Kernel_Name"]:
+            continue
+        key = r["Dispatch_Id"]
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return [vals[k] for k in sorted(vals, key=int)]
+
+
+def cmd_copy(args) -> int:
+    import torch
+
+    n = args.mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(args.reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"streamed {n} bytes in and out x {args.reps}", flush=True)
+    return 0
+
+
+def cmd_stats(args) -> int:
+    d = kernel_durations(args.trace)
+    total = sum(sum(v) for v in d.values())
+    lines = [f"# rocprofv3 kernel trace summary", f"# command: {args.command}", "",
+             f"{'kernel':<92} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10} {'pct':>6}"]
+    items = sorted(d.items(), key=lambda kv: -sum(kv[1]))
+    for name, (_, v) in zip(_demangle([k for k, _ in items]), items):
+        lines.append(f"{_short(name):<92} {len(v):>6} {statistics.mean(v) / 1e3:>10.2f} {min(v) / 1e3:>10.2f} "
+                     f"{max(v) / 1e3:>10.2f} {sum(v) / 1e6:>10.3f} {100.0 * sum(v) / total:>6.2f}")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as fh:
+            fh.write(text)
+    sys.stdout.write(text)
+    return 0
+
+
+def cmd_traffic(args) -> int:
+    fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE", args.match)
+    write = counter_per_dispatch(args.write, "WRITE_SIZE", args.match)
+    cf = counter_per_dispatch(args.copy_fetch, "FETCH_SIZE", args.copy_match)
+    cw = counter_per_dispatch(args.copy_write, "WRITE_SIZE", args.copy_match)
+    if not (fetch and write and cf and cw):
+        print("missing dispatches: fetch %d write %d copy %d/%d" % (len(fetch), len(write), len(cf), len(cw)))
+        return 1
+    # the largest copy dispatches are the timed copies (fills and warm-up aside)
+    f_factor = args.copy_bytes / (1024.0 * max(cf))
+    w_factor = args.copy_bytes / (1024.0 * max(cw))
+    fb = statistics.mean(fetch) * 1024.0 * f_factor
+    wb = statistics.mean(write) * 1024.0 * w_factor
+    d = {
+        "kernel": args.kernel,
+        "match": args.match,
+        "workload": args.workload,
+        "dispatches": [len(fetch), len(write)],
+        "fetch_kib_per_dispatch": statistics.mean(fetch),
+        "write_kib_per_dispatch": statistics.mean(write),
+        "copy_bytes": args.copy_bytes,
+        "copy_fetch_kib": max(cf),
+        "copy_write_kib": max(cw),
+        "fetch_factor": f_factor,
+        "write_factor": w_factor,
+        "fetch_bytes_per_launch": fb,
+        "write_bytes_per_launch": wb,
+        "bytes_per_launch": fb + wb,
+        "kernel_src_hash": kernel_src_hash(),
+        "command": args.command,
+    }
+    with open(args.out, "w") as fh:
+        json.dump(d, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(d))
+    return 0
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("copy")
+    c.add_argument("--mib", type=int, default=1024)
+    c.add_argument("--reps", type=int, default=4)
+    s = sub.add_parser("stats")
+    s.add_argument("trace")
+    s.add_argument("--out")
+    s.add_argument("--command", default="")
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "match", "workload", "out"):
+        t.add_argument("--" + k.replace("_", "-"), required=True)
+    t.add_argument("--copy-bytes", type=float, required=True)
+    t.add_argument("--copy-match", default="neg")
+    t.add_argument("--command", default="")
+    args = ap.parse_args(argv)
+    return {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[args.cmd](args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
