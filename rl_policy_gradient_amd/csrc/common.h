@@ -73,24 +73,19 @@ struct LossParams {
 // Launchers (each enqueues on `st`; return hipError_t of the launch)
 // ---------------------------------------------------------------------------
 
-// Blocked transposed copy used as the second MFMA operand of the
-// probability-weighted sums: rows [0, rows_pad) of X (or X[idx[k]] when idx
-// is given; rows beyond `rows` are zero) into Xt[rows_pad/32][4][H][8], and,
-// when Xc is not NULL, a compact natural-layout copy Xc[rows_pad][H].
-hipError_t launch_blocked_copy_bf16(const __bf16* X, const int* idx, const int* count_dev,
-                                    int64_t rows, int64_t rows_pad, int H, __bf16* Xt, __bf16* Xc,
-                                    hipStream_t st);
+// Row gather of bf16 rows for the weight-gradient sweep: Xc[k] = X[idx[k]]
+// for k < *count_dev, zero rows up to the next multiple of 32 (at most cap).
+hipError_t launch_gather_bf16(const __bf16* X, const int* idx, const int* count_dev, int64_t cap, int H,
+                              __bf16* Xc, hipStream_t st);
 
 // Forward sweep on MFMA (bf16, H a multiple of 128, H <= 896).
-hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* W, const __bf16* Wt, const __bf16* b,
-                           const int64_t* y, int64_t N, int H, int V, float inv_tau, int Sv,
-                           bool with_o, RowStats* stats, float* O, hipStream_t st);
+hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* W, const __bf16* b, const int64_t* y, int64_t N, int H,
+                           int V, float inv_tau, int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st);
 
-// Weight-gradient sweep on MFMA over compacted tokens.
-hipError_t launch_bwd_mfma(const __bf16* W, const __bf16* b, const __bf16* hc, const __bf16* ht,
-                           const TokData* tok, const int* count_dev, int64_t n_cap, int H, int V,
-                           float inv_tau, int acc_mode, float* gW_acc, float* gb_acc, __bf16* gW_out,
-                           __bf16* gb_out, hipStream_t st);
+// Weight-gradient sweep on MFMA over the compacted tokens hc.
+hipError_t launch_bwd_mfma(const __bf16* W, const __bf16* b, const __bf16* hc, const TokData* tok,
+                           const int* count_dev, int H, int V, float inv_tau, int acc_mode, float* gW_acc,
+                           float* gb_acc, __bf16* gW_out, __bf16* gb_out, hipStream_t st);
 
 // Generic (VALU) forward and weight-gradient sweeps for any H and fp32 or bf16.
 hipError_t launch_fwd_generic(int dtype, const void* h, const void* W, const void* b, const int64_t* y,

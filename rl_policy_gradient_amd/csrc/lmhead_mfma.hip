@@ -7,21 +7,28 @@
 //   streamed tiles KV[32, H]        (forward: 32 vocabulary rows of W;
 //                                     weight grad: 32 compacted token rows of h)
 //   S^T = KV Q^T                    logits of the tile, contraction over H
-//   P   = epilogue(S)               forward: exp(z - m) with the running max m
+//   P   = epilogue(S)               forward: exp(z - m) with the row's reference m
 //                                   weight grad: g (onehot - softmax) / tau
 //   Acc += P KV                     forward: sum_v e^{z-m} W_v (for grad_h)
 //                                   weight grad: sum_t dz h_t  (grad_W)
 //
 // H is split across the 4 waves of a workgroup: wave w owns columns
-// [w*H/4, (w+1)*H/4) of Q, of every KV tile and of Acc, so a wave only ever
-// touches its own slice of the streamed tile. The partial S^T of each wave
-// (its slice of the contraction) is reduce-scattered through LDS: wave w ends
-// up with the complete logits of resident-row block w, runs the epilogue on
-// them, and the bf16 P fragments are all-gathered through LDS for the P KV
-// product. The P KV product contracts over tile rows, so its KV operand comes
-// from a blocked transposed copy KVt[tile][g][H][8] (see
-// launch_blocked_copy_bf16) in which the 8 tile rows a lane needs for one
-// column are contiguous.
+// [w*H/4, (w+1)*H/4) of Q, of every KV tile and of Acc. Its slice of Q stays
+// in registers for the whole sweep and Acc in accumulation registers. The
+// partial S^T of each wave (its slice of the contraction) is reduce-scattered
+// through LDS: wave w ends up with the complete logits of resident-row block
+// w, runs the epilogue on them, and the bf16 P fragments are all-gathered
+// through LDS for the P KV product.
+//
+// Each KV tile is read from global memory once. The P KV product contracts
+// over tile rows, so its KV operand needs the 8 tile rows of one column in a
+// lane: after a wave has used its slice of the tile for S^T, it stores that
+// slice row-major into a wave-private LDS buffer and reads it back with the
+// gfx950 transposing load ds_read_b64_tr_b16, which, within each 16-lane
+// group, hands lane l element l%4 of the 64-bit chunk that lane 4j + l/4
+// addressed, for j = 0..3. Pointing lane p at row r0 + p/4, columns
+// c0 + 4(p%4) .. +3 gives lane l the column c0 + l of rows r0 .. r0 + 3, the
+// MFMA B-operand layout.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16. Lane l holds A[l%16][8(l/16)+j],
 // B[8(l/16)+j][l%16] (j = 0..7) and D[4(l/16)+i][l%16] (i = 0..3).
@@ -47,6 +54,10 @@ constexpr int NW = 4;    // waves per workgroup
 // running sum far inside fp32 and bf16 range.
 constexpr float kRefSlack = 64.0f;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -55,6 +66,15 @@ __device__ __forceinline__ int kv_of(int g, int j) { return j < 4 ? 4 * g + j : 
 
 __device__ __forceinline__ bf16x8 ld16(const __bf16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// Two transposing LDS loads (rows r0..r0+3 and r0+16..r0+19 of a row-major
+// bf16 tile, see the header) form one B-operand fragment.
+__device__ __forceinline__ bf16x8 ld_tr(const unsigned short* p0, const unsigned short* p1) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
@@ -82,44 +102,32 @@ __device__ __forceinline__ float xg_max(float x) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Row stride (elements) of a wave's staged tile slice: the slice width plus
+// 16 elements, so the four rows one 16-lane group reads in a transposing
+// load fall on distinct banks.
+template <int KB>
+struct Stage {
+  static constexpr int DS = 32 * KB;
+  static constexpr int TS = DS + 16;
+};
+
 // ---------------------------------------------------------------------------
-// Blocked transposed copy: Xt[tile][g][d][j] = X[src(32*tile + kv(g,j))][d]
+// Row gather: Xc[k] = X[idx[k]] for k < count, zero rows up to the next
+// multiple of 32 (16-byte vector copies).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void blocked_copy_kernel(const __bf16* __restrict__ X,
-                                                           const int* __restrict__ idx,
-                                                           const int* __restrict__ count_dev,
-                                                           int64_t rows_host, int H,
-                                                           __bf16* __restrict__ Xt,
-                                                           __bf16* __restrict__ Xc) {
-  extern __shared__ uint4 smem_u4[];
-  unsigned short* tile = reinterpret_cast<unsigned short*>(smem_u4);  // [32][H]
-  const int64_t rows = count_dev ? (int64_t)(*count_dev) : rows_host;
-  const int64_t t0 = (int64_t)blockIdx.x * BK;
-  if (t0 >= rows) return;  // tile entirely past the last row (block-uniform)
-  const int cpr = H / 8;   // 16-byte chunks per row
-  for (int c = threadIdx.x; c < BK * cpr; c += blockDim.x) {
-    const int r = c / cpr, cc = c - r * cpr;
-    const int64_t k = t0 + r;
+__global__ __launch_bounds__(256) void gather16_kernel(const __bf16* __restrict__ X, const int* __restrict__ idx,
+                                                       const int* __restrict__ count_dev, int64_t cap, int H,
+                                                       __bf16* __restrict__ Xc) {
+  const int64_t n = *count_dev;
+  const int64_t rows = min(cap, (n + BK - 1) / BK * BK);
+  const int cpr = H / 8;
+  const int64_t total = rows * cpr;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t k = e / cpr;
+    const int c = (int)(e - k * cpr);
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (k < rows) {
-      const int64_t src = idx ? (int64_t)idx[k] : k;
-      v = *reinterpret_cast<const uint4*>(X + src * H + cc * 8);
-    }
-    *reinterpret_cast<uint4*>(tile + r * H + cc * 8) = v;
-    if (Xc) *reinterpret_cast<uint4*>(Xc + k * H + cc * 8) = v;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 4 * H; e += blockDim.x) {
-    const int g = e / H, d = e - g * H;
-    unsigned short u[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) u[j] = tile[kv_of(g, j) * H + d];
-    uint4 v;
-    v.x = u[0] | ((unsigned)u[1] << 16);
-    v.y = u[2] | ((unsigned)u[3] << 16);
-    v.z = u[4] | ((unsigned)u[5] << 16);
-    v.w = u[6] | ((unsigned)u[7] << 16);
-    *reinterpret_cast<uint4*>(Xt + (((int64_t)blockIdx.x * 4 + g) * H + d) * 8) = v;
+    if (k < n) v = *reinterpret_cast<const uint4*>(X + (int64_t)idx[k] * H + c * 8);
+    *reinterpret_cast<uint4*>(Xc + k * H + c * 8) = v;
   }
 }
 
@@ -128,17 +136,18 @@ __global__ __launch_bounds__(256) void blocked_copy_kernel(const __bf16* __restr
 //
 //   prologue: S^T(t0) -> LDS partials, barrier, reduce -> sf
 //   loop t:   S^T(t+1) MFMAs          | interleaved with the epilogue of tile t
-//             loads for tile t+2         (VALU on sf, the reduced logits of t)
+//             stage tile t+1 for the transposing load, loads for tile t+2
 //             barrier
 //             P(t) -> LDS, partials of t+1 -> LDS
 //             barrier
 //             P KV(t) MFMAs            | interleaved with the reduce of t+1
-//             loads for tile t+1 (KV^T)
 //
 // so the matrix cores work while the vector unit runs the epilogue, and every
 // load has a whole phase to arrive. Two barriers per tile; the partials and P
 // buffers are reused every tile (each write follows a barrier that all reads
-// of the previous contents precede).
+// of the previous contents precede). The staged tile slices are double
+// buffered per wave: slice t+1 is written after the wave's last read of the
+// buffer (P KV of tile t-1), and read in P KV(t+1).
 // ---------------------------------------------------------------------------
 
 // Forward sweep: per token row, running (sum e^{z-m}, sum e^{z-m} z) against
@@ -148,15 +157,16 @@ __global__ __launch_bounds__(256) void blocked_copy_kernel(const __bf16* __restr
 template <int KB, bool WITH_O, bool HAS_BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
-                     const __bf16* __restrict__ Wt, const __bf16* __restrict__ bias,
-                     const int64_t* __restrict__ y, int64_t N, int V, float inv_tau, int Sv,
-                     int tiles_per_split, RowStats* __restrict__ stats, float* __restrict__ O) {
+                     const __bf16* __restrict__ bias, const int64_t* __restrict__ y, int64_t N, int V,
+                     float inv_tau, int Sv, int tiles_per_split, RowStats* __restrict__ stats,
+                     float* __restrict__ O) {
   constexpr int H = 128 * KB;
-  constexpr int DS = 32 * KB;  // columns per wave
-  constexpr int DB = 2 * KB;   // 16-wide column blocks per wave
+  constexpr int DS = Stage<KB>::DS;  // columns per wave
+  constexpr int TS = Stage<KB>::TS;
+  constexpr int DB = 2 * KB;         // 16-wide column blocks per wave
   __shared__ f32x4 s_part[NW][2][4][64];
   __shared__ bf16x8 s_p[4][64];
-  __shared__ bf16x8 s_q[NW][4][KB][64];  // resident h fragments, per wave, in fragment order
+  __shared__ unsigned short s_t[WITH_O ? NW : 1][2][BK][WITH_O ? TS : 8];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -167,14 +177,14 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
   const int t_begin = sv * tiles_per_split;
   const int t_end = min(n_tiles, t_begin + tiles_per_split);
 
-  // Resident h fragments (B operand of S^T): rows q0+16nb+c16, cols
-  // d0+32kb+8g. Each wave reads back only its own slice, so no barrier.
+  // Resident h fragments (B operand of S^T), rows q0+16nb+c16, cols d0+32kb+8g.
+  bf16x8 q[4][KB];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int64_t row = min(q0 + 16 * nb + c16, N - 1);
     const __bf16* src = h + row * H + d0 + 8 * g;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s_q[w][nb][kb][lane] = ld16(src + 32 * kb);
+    for (int kb = 0; kb < KB; ++kb) q[nb][kb] = ld16(src + 32 * kb);
   }
 
   f32x4 o[4][WITH_O ? DB : 1];
@@ -199,11 +209,13 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
       for (int kb = 0; kb < KB; ++kb) a[mb][kb] = ld16(src + 32 * kb);
     }
   };
-  auto load_b = [&](int t, bf16x8 (&b)[WITH_O ? DB : 1]) {
+  auto stage = [&](int buf, const bf16x8 (&a)[2][KB]) {
     if constexpr (WITH_O) {
-      const __bf16* src = Wt + (((int64_t)t * 4 + g) * H + d0 + c16) * 8;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) b[db] = ld16(src + 16 * 8 * db);
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          *reinterpret_cast<bf16x8*>(&s_t[w][buf][16 * mb + c16][32 * kb + 8 * g]) = a[mb][kb];
     }
   };
   auto load_bias = [&](int t, float (&bv)[8]) {
@@ -216,15 +228,11 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero4();
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      bf16x8 q[4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) q[nb] = s_q[w][nb][kb][lane];
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb][kb], q[nb], acc[mb][nb]);
-    }
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb][kb], q[nb][kb], acc[mb][nb]);
   };
   auto write_part = [&](const f32x4 (&acc)[2][4]) {
 #pragma unroll
@@ -241,16 +249,29 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
       sf[mb] = r;
     }
   };
+  auto pv_mfma = [&](int buf) {
+    if constexpr (WITH_O) {
+      bf16x8 pf[4];
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) pf[qb] = s_p[qb][lane];
+      const unsigned short* base = &s_t[w][buf][4 * g + (c16 >> 2)][4 * (c16 & 3)];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 bt = ld_tr(base + 16 * db, base + 16 * TS + 16 * db);
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], bt, o[qb][db]);
+      }
+    }
+  };
 
   bf16x8 a[2][KB];
-  bf16x8 bt[WITH_O ? DB : 1];
   f32x4 acc[2][4], sf[2];
   float bv[8];
   if (t_begin < t_end) {
     load_a(t_begin, a);
-    load_b(t_begin, bt);
     load_bias(t_begin, bv);
     s_mfma(a, acc);
+    stage(t_begin & 1, a);
     load_a(min(t_begin + 1, t_end - 1), a);
     write_part(acc);
   }
@@ -302,22 +323,14 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
     bf16x8 pa;
 #pragma unroll
     for (int j = 0; j < 8; ++j) pa[j] = (__bf16)p[j];
+    if (t + 1 < t_end) stage((t + 1) & 1, a);
     load_a(tnn, a);
     __syncthreads();
     if constexpr (WITH_O) s_p[w][lane] = pa;
     write_part(acc);
     __syncthreads();
     // ---- accumulator product of tile t, reduce of tile t+1 -----------------
-    if constexpr (WITH_O) {
-      bf16x8 pf[4];
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) pf[qb] = s_p[qb][lane];
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], bt[db], o[qb][db]);
-      load_b(tn, bt);
-    }
+    pv_mfma(t & 1);
     reduce_part(sf);
 #pragma unroll
     for (int j = 0; j < 8; ++j) bv[j] = bvn[j];
@@ -361,18 +374,18 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
 template <int KB, bool HAS_BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bias,
-                     const __bf16* __restrict__ hc, const __bf16* __restrict__ ht,
-                     const TokData* __restrict__ tok, const int* __restrict__ count_dev, int V,
-                     float inv_tau, int acc_mode, float* __restrict__ gW_acc,
-                     float* __restrict__ gb_acc, __bf16* __restrict__ gW_out,
+                     const __bf16* __restrict__ hc, const TokData* __restrict__ tok,
+                     const int* __restrict__ count_dev, int V, float inv_tau, int acc_mode,
+                     float* __restrict__ gW_acc, float* __restrict__ gb_acc, __bf16* __restrict__ gW_out,
                      __bf16* __restrict__ gb_out) {
   constexpr int H = 128 * KB;
-  constexpr int DS = 32 * KB;
+  constexpr int DS = Stage<KB>::DS;
+  constexpr int TS = Stage<KB>::TS;
   constexpr int DB = 2 * KB;
   __shared__ f32x4 s_part[NW][2][4][64];
   __shared__ bf16x8 s_p[4][64];
   __shared__ TokData s_tok[2][BK];
-  __shared__ bf16x8 s_q[NW][4][KB][64];  // resident W fragments, per wave, in fragment order
+  __shared__ unsigned short s_t[NW][2][BK][TS];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -381,12 +394,14 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
   const int n_tok = *count_dev;
   const int n_tiles = (n_tok + BK - 1) / BK;
 
+  // Resident W fragments (B operand of S^T), rows q0+16nb+c16, cols d0+32kb+8g.
+  bf16x8 q[4][KB];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int v = min(q0 + 16 * nb + c16, V - 1);
     const __bf16* src = W + (int64_t)v * H + d0 + 8 * g;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s_q[w][nb][kb][lane] = ld16(src + 32 * kb);
+    for (int kb = 0; kb < KB; ++kb) q[nb][kb] = ld16(src + 32 * kb);
   }
   f32x4 o[4][DB];
 #pragma unroll
@@ -406,10 +421,12 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
       for (int kb = 0; kb < KB; ++kb) a[mb][kb] = ld16(src + 32 * kb);
     }
   };
-  auto load_b = [&](int t, bf16x8 (&b)[DB]) {
-    const __bf16* src = ht + (((int64_t)t * 4 + g) * H + d0 + c16) * 8;
+  auto stage = [&](int buf, const bf16x8 (&a)[2][KB]) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) b[db] = ld16(src + 16 * 8 * db);
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        *reinterpret_cast<bf16x8*>(&s_t[w][buf][16 * mb + c16][32 * kb + 8 * g]) = a[mb][kb];
   };
   auto stage_tok = [&](int t) {
     if (w == 0 && lane < BK) s_tok[t & 1][lane] = tok[t * BK + lane];
@@ -420,15 +437,11 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero4();
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      bf16x8 q[4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) q[nb] = s_q[w][nb][kb][lane];
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb][kb], q[nb], acc[mb][nb]);
-    }
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb][kb], q[nb][kb], acc[mb][nb]);
   };
   auto write_part = [&](const f32x4 (&acc)[2][4]) {
 #pragma unroll
@@ -445,15 +458,26 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
       sf[mb] = r;
     }
   };
+  auto pv_mfma = [&](int buf) {
+    bf16x8 pf[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) pf[qb] = s_p[qb][lane];
+    const unsigned short* base = &s_t[w][buf][4 * g + (c16 >> 2)][4 * (c16 & 3)];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 bt = ld_tr(base + 16 * db, base + 16 * TS + 16 * db);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], bt, o[qb][db]);
+    }
+  };
 
   bf16x8 a[2][KB];
-  bf16x8 bt[DB];
   f32x4 acc[2][4], sf[2];
   if (n_tiles > 0) {
     stage_tok(0);
     load_a(0, a);
-    load_b(0, bt);
     s_mfma(a, acc);
+    stage(0, a);
     load_a(min(1, n_tiles - 1), a);
     write_part(acc);
   }
@@ -480,20 +504,14 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
       pa[j] = (__bf16)dz;
     }
     gb_run += (double)gsum;
+    if (t + 1 < n_tiles) stage((t + 1) & 1, a);
     load_a(tnn, a);
     __syncthreads();
     s_p[w][lane] = pa;
     write_part(acc);
     stage_tok(tn);
     __syncthreads();
-    bf16x8 pf[4];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) pf[qb] = s_p[qb][lane];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], bt[db], o[qb][db]);
-    load_b(tn, bt);
+    pv_mfma(t & 1);
     reduce_part(sf);
   }
 
@@ -530,82 +548,78 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
 }
 
 template <int KB>
-hipError_t fwd_dispatch(const __bf16* h, const __bf16* W, const __bf16* Wt, const __bf16* b,
-                        const int64_t* y, int64_t N, int V, float inv_tau, int Sv, int tps, bool with_o,
-                        RowStats* stats, float* O, hipStream_t st) {
+hipError_t fwd_dispatch(const __bf16* h, const __bf16* W, const __bf16* b, const int64_t* y, int64_t N, int V,
+                        float inv_tau, int Sv, int tps, bool with_o, RowStats* stats, float* O, hipStream_t st) {
   const int64_t nrb = (N + BQ - 1) / BQ;
   dim3 grid((unsigned)(nrb * Sv)), block(256);
   if (with_o && b)
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true, true>), grid, block, 0, st, h, W, Wt, b, y, N, V, inv_tau, Sv,
-                       tps, stats, O);
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true, true>), grid, block, 0, st, h, W, b, y, N, V, inv_tau, Sv, tps,
+                       stats, O);
   else if (with_o)
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true, false>), grid, block, 0, st, h, W, Wt, b, y, N, V, inv_tau, Sv,
-                       tps, stats, O);
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true, false>), grid, block, 0, st, h, W, b, y, N, V, inv_tau, Sv, tps,
+                       stats, O);
   else if (b)
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false, true>), grid, block, 0, st, h, W, Wt, b, y, N, V, inv_tau, Sv,
-                       tps, stats, O);
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false, true>), grid, block, 0, st, h, W, b, y, N, V, inv_tau, Sv, tps,
+                       stats, O);
   else
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false, false>), grid, block, 0, st, h, W, Wt, b, y, N, V, inv_tau, Sv,
-                       tps, stats, O);
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false, false>), grid, block, 0, st, h, W, b, y, N, V, inv_tau, Sv, tps,
+                       stats, O);
   return hipGetLastError();
 }
 
 template <int KB>
-hipError_t bwd_dispatch(const __bf16* W, const __bf16* b, const __bf16* hc, const __bf16* ht,
-                        const TokData* tok, const int* count_dev, int V, float inv_tau, int acc_mode,
-                        float* gW_acc, float* gb_acc, __bf16* gW_out, __bf16* gb_out, hipStream_t st) {
+hipError_t bwd_dispatch(const __bf16* W, const __bf16* b, const __bf16* hc, const TokData* tok, const int* count_dev,
+                        int V, float inv_tau, int acc_mode, float* gW_acc, float* gb_acc, __bf16* gW_out,
+                        __bf16* gb_out, hipStream_t st) {
   dim3 grid((unsigned)((V + BQ - 1) / BQ)), block(256);
   if (b)
-    hipLaunchKernelGGL((bwd_mfma_kernel<KB, true>), grid, block, 0, st, W, b, hc, ht, tok, count_dev, V, inv_tau,
+    hipLaunchKernelGGL((bwd_mfma_kernel<KB, true>), grid, block, 0, st, W, b, hc, tok, count_dev, V, inv_tau,
                        acc_mode, gW_acc, gb_acc, gW_out, gb_out);
   else
-    hipLaunchKernelGGL((bwd_mfma_kernel<KB, false>), grid, block, 0, st, W, b, hc, ht, tok, count_dev, V, inv_tau,
+    hipLaunchKernelGGL((bwd_mfma_kernel<KB, false>), grid, block, 0, st, W, b, hc, tok, count_dev, V, inv_tau,
                        acc_mode, gW_acc, gb_acc, gW_out, gb_out);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_blocked_copy_bf16(const __bf16* X, const int* idx, const int* count_dev, int64_t rows,
-                                    int64_t rows_pad, int H, __bf16* Xt, __bf16* Xc, hipStream_t st) {
-  const int64_t tiles = rows_pad / BK;
-  if (tiles <= 0) return hipSuccess;
-  const size_t lds = (size_t)BK * H * sizeof(__bf16);
-  hipLaunchKernelGGL(blocked_copy_kernel, dim3((unsigned)tiles), dim3(256), lds, st, X, idx, count_dev, rows, H,
-                     Xt, Xc);
+hipError_t launch_gather_bf16(const __bf16* X, const int* idx, const int* count_dev, int64_t cap, int H, __bf16* Xc,
+                              hipStream_t st) {
+  if (cap <= 0) return hipSuccess;
+  const int64_t chunks = cap * (H / 8);
+  const int64_t blocks = (chunks + 255) / 256;
+  const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
+  hipLaunchKernelGGL(gather16_kernel, dim3(grid), dim3(256), 0, st, X, idx, count_dev, cap, H, Xc);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* W, const __bf16* Wt, const __bf16* b,
-                           const int64_t* y, int64_t N, int H, int V, float inv_tau, int Sv, bool with_o,
-                           RowStats* stats, float* O, hipStream_t st) {
+hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* W, const __bf16* b, const int64_t* y, int64_t N, int H,
+                           int V, float inv_tau, int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st) {
   const int n_tiles = (V + BK - 1) / BK;
   const int tps = (n_tiles + Sv - 1) / Sv;
   switch (H / 128) {
-    case 1: return fwd_dispatch<1>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 2: return fwd_dispatch<2>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 3: return fwd_dispatch<3>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 4: return fwd_dispatch<4>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 5: return fwd_dispatch<5>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 6: return fwd_dispatch<6>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 7: return fwd_dispatch<7>(h, W, Wt, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 1: return fwd_dispatch<1>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 2: return fwd_dispatch<2>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 3: return fwd_dispatch<3>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 4: return fwd_dispatch<4>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 5: return fwd_dispatch<5>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 6: return fwd_dispatch<6>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 7: return fwd_dispatch<7>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd_mfma(const __bf16* W, const __bf16* b, const __bf16* hc, const __bf16* ht,
-                           const TokData* tok, const int* count_dev, int64_t n_cap, int H, int V,
-                           float inv_tau, int acc_mode, float* gW_acc, float* gb_acc, __bf16* gW_out,
-                           __bf16* gb_out, hipStream_t st) {
-  (void)n_cap;
+hipError_t launch_bwd_mfma(const __bf16* W, const __bf16* b, const __bf16* hc, const TokData* tok,
+                           const int* count_dev, int H, int V, float inv_tau, int acc_mode, float* gW_acc,
+                           float* gb_acc, __bf16* gW_out, __bf16* gb_out, hipStream_t st) {
   switch (H / 128) {
-    case 1: return bwd_dispatch<1>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 2: return bwd_dispatch<2>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 3: return bwd_dispatch<3>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 4: return bwd_dispatch<4>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 5: return bwd_dispatch<5>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 6: return bwd_dispatch<6>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 7: return bwd_dispatch<7>(W, b, hc, ht, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 1: return bwd_dispatch<1>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 2: return bwd_dispatch<2>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 3: return bwd_dispatch<3>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 4: return bwd_dispatch<4>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 5: return bwd_dispatch<5>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 6: return bwd_dispatch<6>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 7: return bwd_dispatch<7>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -83,7 +83,6 @@ struct Plan {
 };
 
 struct Bufs {
-  __bf16* Wt = nullptr;
   RowStats* stats = nullptr;
   float* O = nullptr;
   float* v = nullptr;
@@ -99,7 +98,6 @@ struct Bufs {
   int* count = nullptr;
   void* cscratch = nullptr;
   void* hc = nullptr;
-  __bf16* ht = nullptr;
   float* gW_acc = nullptr;
   float* gb_acc = nullptr;
 };
@@ -128,7 +126,6 @@ Plan make_plan(const plp_args* a, bool need_o, bool need_gw, bool need_gb) {
 size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
   Carver c(ws);
   const int H = a->H, V = a->V;
-  if (p.mfma && p.need_o) b.Wt = c.take<__bf16>((size_t)round_up(V, kBK) * H);
   b.stats = c.take<RowStats>((size_t)p.Sv * p.Nc);
   if (p.need_o) {
     b.O = c.take<float>((size_t)p.Sv * p.Nc * H);
@@ -149,7 +146,6 @@ size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
     b.count = c.take<int>(1);
     b.cscratch = c.take<char>(compact_scratch_bytes(p.Nc));
     b.hc = c.take<char>((size_t)p.cap * H * esize(a->dtype));
-    if (p.mfma) b.ht = c.take<__bf16>((size_t)p.cap * H);
     if (p.nchunks > 1) {
       b.gW_acc = c.take<float>((size_t)V * H);
       if (p.need_gb) b.gb_acc = c.take<float>(V);
@@ -260,8 +256,8 @@ int forward_rows(const plp_args* a, const Plan& p, Bufs& b, int64_t r0, int64_t 
   if (p.mfma) {
     hipEvent_t* ev = prof_slot(0);
     if (ev) HIP_TRY(hipEventRecord(ev[0], st));
-    HIP_TRY(launch_fwd_mfma((const __bf16*)h, (const __bf16*)a->weight, b.Wt, (const __bf16*)a->bias, y, n, a->H,
-                            a->V, inv_tau, p.Sv, with_o, b.stats, with_o ? b.O : nullptr, st));
+    HIP_TRY(launch_fwd_mfma((const __bf16*)h, (const __bf16*)a->weight, (const __bf16*)a->bias, y, n, a->H, a->V,
+                            inv_tau, p.Sv, with_o, b.stats, with_o ? b.O : nullptr, st));
     if (ev) HIP_TRY(hipEventRecord(ev[1], st));
   } else {
     HIP_TRY(launch_fwd_generic(a->dtype, h, a->weight, a->bias, y, n, a->H, a->V, inv_tau, with_o, b.stats,
@@ -361,9 +357,6 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
   const LossParams lpar = loss_params(a);
 
   HIP_TRY(launch_loss_zero(b.acc, st));
-  if (b.Wt)
-    HIP_TRY(launch_blocked_copy_bf16((const __bf16*)a->weight, nullptr, nullptr, V, round_up(V, kBK), H, b.Wt,
-                                     nullptr, st));
 
   bool first_chunk_done = false;
   if (p.entropy) {
@@ -407,15 +400,15 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
       HIP_TRY(launch_compact(g, b.lse + r0, a->targets + r0, n, inv_tau, b.idx, b.tok, b.count, b.cscratch, st));
       const char* hsrc = (const char*)a->hidden + (size_t)r0 * H * es;
       if (p.mfma)
-        HIP_TRY(launch_blocked_copy_bf16((const __bf16*)hsrc, b.idx, b.count, n, p.cap, H, b.ht, (__bf16*)b.hc, st));
+        HIP_TRY(launch_gather_bf16((const __bf16*)hsrc, b.idx, b.count, p.cap, H, (__bf16*)b.hc, st));
       else
         HIP_TRY(launch_gather_rows(a->dtype, hsrc, b.idx, b.count, p.cap, H, b.hc, st));
       const int mode = p.nchunks == 1 ? 0 : (c == 0 ? 1 : (c == p.nchunks - 1 ? 3 : 2));
       if (p.mfma) {
         hipEvent_t* ev = prof_slot(1);
         if (ev) HIP_TRY(hipEventRecord(ev[0], st));
-        HIP_TRY(launch_bwd_mfma((const __bf16*)a->weight, (const __bf16*)a->bias, (const __bf16*)b.hc, b.ht, b.tok,
-                                b.count, p.cap, H, V, inv_tau, mode, b.gW_acc, b.gb_acc, (__bf16*)out->grad_weight,
+        HIP_TRY(launch_bwd_mfma((const __bf16*)a->weight, (const __bf16*)a->bias, (const __bf16*)b.hc, b.tok, b.count,
+                                H, V, inv_tau, mode, b.gW_acc, b.gb_acc, (__bf16*)out->grad_weight,
                                 (__bf16*)out->grad_bias, st));
         if (ev) HIP_TRY(hipEventRecord(ev[1], st));
       } else
@@ -461,8 +454,8 @@ PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const 
   const int64_t* y = targets;  // may be NULL: no target logit is gathered
   const float inv_tau = 1.0f / temperature;
   if (mfma)
-    HIP_TRY(launch_fwd_mfma((const __bf16*)hidden, (const __bf16*)weight, nullptr, (const __bf16*)bias, y, N, H, V,
-                            inv_tau, sv, false, stats, nullptr, st));
+    HIP_TRY(launch_fwd_mfma((const __bf16*)hidden, (const __bf16*)weight, (const __bf16*)bias, y, N, H, V, inv_tau,
+                            sv, false, stats, nullptr, st));
   else
     HIP_TRY(launch_fwd_generic(dtype, hidden, weight, bias, y, N, H, V, inv_tau, false, stats, nullptr, st));
   HIP_TRY(launch_combine(dtype, stats, nullptr, sv, N, H, V, hidden, weight, bias, inv_tau, y,

@@ -107,12 +107,15 @@ def test_full_size_sampled(cfg):
         kept = ref["entropy_mask"].sum()
         assert 0 < kept < comp.sum()
 
-    # clip predicates: no active log-ratio within the log-prob tolerance of a bound
+    # clip predicates: every active log-ratio sits further from a bound than
+    # the GPU's log-prob differs from the oracle's, so no decision can differ
     if spec.loss_type == synth.GMPO:
         lr = fwd["logp"] - d["old"].astype(np.float64)
         m_hi = np.abs(lr - np.float32(spec.eps_high))[comp].min()
         m_lo = np.abs(lr + np.float32(spec.eps_low))[comp].min()
-        assert min(m_hi, m_lo) > 10 * LP_TOL
+        dlp = float(np.abs(gpu["logp"].astype(np.float64) - fwd["logp"])[comp].max())
+        print(f"[info] cfg{cfg}: clip margin {min(m_hi, m_lo):.2e}, max |dlogp| {dlp:.2e}", flush=True)
+        assert min(m_hi, m_lo) > 2 * dlp
 
     # loss and metrics
     w = 1.0 / (spec.B * np.maximum(1, comp.reshape(spec.B, spec.T).sum(1)))
@@ -199,6 +202,9 @@ def test_cfg5_largest_single_gpu_shape():
                                                chunk_sequences=spec.chunk_sequences, **kw)
     torch.cuda.synchronize()
     for k, v in out.items():
+        if k == "metrics":   # the entropy threshold is NaN by definition when q = 1
+            assert bool(torch.isnan(v[4])) and bool(torch.isfinite(v[torch.arange(8, device=dev) != 4]).all())
+            continue
         assert bool(torch.isfinite(v.float()).all()), k
 
     # sums over the vocabulary vanish: sum_v dz[t,v] = g_t (1 - sum_v p[t,v]) / tau = 0
