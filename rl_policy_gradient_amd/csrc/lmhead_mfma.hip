@@ -103,8 +103,8 @@ __device__ __forceinline__ float xg_max(float x) {
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Row stride (elements) of a wave's staged tile slice: the slice width plus
-// 16 elements, so the four rows one 16-lane group reads in a transposing
-// load fall on distinct banks.
+// 16 elements, so the rows a 16-lane group writes and the four rows each
+// quarter of it reads in a transposing load start on different banks.
 template <int KB>
 struct Stage {
   static constexpr int DS = 32 * KB;
@@ -209,30 +209,59 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
       for (int kb = 0; kb < KB; ++kb) a[mb][kb] = ld16(src + 32 * kb);
     }
   };
-  auto stage = [&](int buf, const bf16x8 (&a)[2][KB]) {
-    if constexpr (WITH_O) {
+  // Bias of tile rows kv(g, 0..7), kept as packed bf16 (two groups of four
+  // consecutive rows, one 8-byte load each when inside the vocabulary).
+  auto load_bias = [&](int t, uint2 (&bv)[2]) {
+    if constexpr (HAS_BIAS) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r0 = t * BK + 16 * hf + 4 * g;
+        if (r0 + 3 < V) {
+          bv[hf] = *reinterpret_cast<const uint2*>(bias + r0);
+        } else {
+          unsigned short e[4];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          *reinterpret_cast<bf16x8*>(&s_t[w][buf][16 * mb + c16][32 * kb + 8 * g]) = a[mb][kb];
+          for (int j = 0; j < 4; ++j) e[j] = __builtin_bit_cast(unsigned short, bias[min(r0 + j, V - 1)]);
+          bv[hf] = make_uint2(e[0] | ((unsigned)e[1] << 16), e[2] | ((unsigned)e[3] << 16));
+        }
+      }
+    } else {
+      bv[0] = bv[1] = make_uint2(0u, 0u);
     }
   };
-  auto load_bias = [&](int t, float (&bv)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) bv[j] = HAS_BIAS ? (float)bias[min(t * BK + kv_of(g, j), V - 1)] : 0.f;
+  auto bias_at = [&](const uint2 (&bv)[2], int j) -> float {
+    const uint2 u = bv[j >> 2];
+    const unsigned wd = (j & 2) ? u.y : u.x;
+    return __uint_as_float((j & 1) ? (wd & 0xffff0000u) : (wd << 16));
   };
-  auto s_mfma = [&](const bf16x8 (&a)[2][KB], f32x4 (&acc)[2][4]) {
+  // S^T of the tile held in `a`; each k-slice of `a`, once its MFMAs are
+  // issued, is staged for the transposing load (WITH_O) and reloaded with
+  // the same slice of tile `t_next`.
+  auto s_step = [&](bf16x8 (&a)[2][KB], f32x4 (&acc)[2][4], int buf, int t_next) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero4();
+    const __bf16* src[2];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int mb = 0; mb < 2; ++mb) {
+      const int v = min(t_next * BK + 16 * mb + c16, V - 1);
+      src[mb] = W + (int64_t)v * H + d0 + 8 * g;
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb][kb], q[nb][kb], acc[mb][nb]);
+      if constexpr (WITH_O) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          *reinterpret_cast<bf16x8*>(&s_t[w][buf][16 * mb + c16][32 * kb + 8 * g]) = a[mb][kb];
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) a[mb][kb] = ld16(src[mb] + 32 * kb);
+    }
   };
   auto write_part = [&](const f32x4 (&acc)[2][4]) {
 #pragma unroll
@@ -242,37 +271,56 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
   };
   auto reduce_part = [&](f32x4 (&sf)[2]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x4 r = s_part[0][mb][w][lane];
-#pragma unroll
-      for (int src = 1; src < NW; ++src) r += s_part[src][mb][w][lane];
-      sf[mb] = r;
-    }
+    for (int mb = 0; mb < 2; ++mb)
+      sf[mb] = (s_part[0][mb][w][lane] + s_part[1][mb][w][lane]) + (s_part[2][mb][w][lane] + s_part[3][mb][w][lane]);
   };
-  auto pv_mfma = [&](int buf) {
+  // P KV of the staged tile in `buf`, with the reduce of the next tile's
+  // partials issued four column blocks before the end.
+  auto pv_reduce = [&](int buf, f32x4 (&sf)[2]) {
+    f32x4 r[NW];
     if constexpr (WITH_O) {
       bf16x8 pf[4];
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) pf[qb] = s_p[qb][lane];
       const unsigned short* base = &s_t[w][buf][4 * g + (c16 >> 2)][4 * (c16 & 3)];
+      // operand fragments two column blocks ahead of the MFMAs that use them
+      bf16x8 b0 = ld_tr(base, base + 16 * TS);
+      bf16x8 b1 = ld_tr(base + 16, base + 16 * TS + 16);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 bt = ld_tr(base + 16 * db, base + 16 * TS + 16 * db);
+        const int dn = db + 2 < DB ? db + 2 : DB - 1;
+        const bf16x8 b2 = ld_tr(base + 16 * dn, base + 16 * TS + 16 * dn);
+        if (db == (DB > 4 ? DB - 4 : 0)) {
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], bt, o[qb][db]);
+          for (int src = 0; src < NW; ++src) r[src] = s_part[src][0][w][lane];
+        }
+        if (db == (DB > 2 ? DB - 2 : 0)) {
+          sf[0] = (r[0] + r[1]) + (r[2] + r[3]);
+#pragma unroll
+          for (int src = 0; src < NW; ++src) r[src] = s_part[src][1][w][lane];
+        }
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], b0, o[qb][db]);
+        b0 = b1;
+        b1 = b2;
       }
+    } else {
+#pragma unroll
+      for (int src = 0; src < NW; ++src) r[src] = s_part[src][0][w][lane];
+      sf[0] = (r[0] + r[1]) + (r[2] + r[3]);
+#pragma unroll
+      for (int src = 0; src < NW; ++src) r[src] = s_part[src][1][w][lane];
     }
+    sf[1] = (r[0] + r[1]) + (r[2] + r[3]);
   };
 
   bf16x8 a[2][KB];
   f32x4 acc[2][4], sf[2];
-  float bv[8];
+  uint2 bv[2];
   if (t_begin < t_end) {
     load_a(t_begin, a);
     load_bias(t_begin, bv);
-    s_mfma(a, acc);
-    stage(t_begin & 1, a);
-    load_a(min(t_begin + 1, t_end - 1), a);
+    s_step(a, acc, t_begin & 1, min(t_begin + 1, t_end - 1));
     write_part(acc);
   }
   __syncthreads();
@@ -282,9 +330,9 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
     const int v0 = t * BK;
     const int tn = min(t + 1, t_end - 1);
     const int tnn = min(t + 2, t_end - 1);
-    // ---- logits of tile t+1 on the matrix cores ----------------------------
-    s_mfma(a, acc);
-    float bvn[8];
+    // ---- logits of tile t+1 on the matrix cores, stage t+1, load t+2 -------
+    s_step(a, acc, (t + 1) & 1, tnn);
+    uint2 bvn[2];
     load_bias(tn, bvn);
     // ---- epilogue of tile t on row my_row, tile rows kv(g, j) -------------
     float z[8];
@@ -294,7 +342,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
       const int v = v0 + kv_of(g, j);
       ok[j] = v < V;
       const float sv_ = j < 4 ? sf[0][j] : sf[1][j - 4];
-      z[j] = ok[j] ? (sv_ + bv[j]) * inv_tau : -INFINITY;
+      z[j] = ok[j] ? (sv_ + bias_at(bv, j)) * inv_tau : -INFINITY;
     }
     float mx = z[0];
 #pragma unroll
@@ -323,17 +371,14 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
     bf16x8 pa;
 #pragma unroll
     for (int j = 0; j < 8; ++j) pa[j] = (__bf16)p[j];
-    if (t + 1 < t_end) stage((t + 1) & 1, a);
-    load_a(tnn, a);
     __syncthreads();
     if constexpr (WITH_O) s_p[w][lane] = pa;
     write_part(acc);
     __syncthreads();
     // ---- accumulator product of tile t, reduce of tile t+1 -----------------
-    pv_mfma(t & 1);
-    reduce_part(sf);
+    pv_reduce(t & 1, sf);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bv[j] = bvn[j];
+    for (int hf = 0; hf < 2; ++hf) bv[hf] = bvn[hf];
   }
 
   // ---- results ---------------------------------------------------------------
@@ -421,27 +466,29 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
       for (int kb = 0; kb < KB; ++kb) a[mb][kb] = ld16(src + 32 * kb);
     }
   };
-  auto stage = [&](int buf, const bf16x8 (&a)[2][KB]) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        *reinterpret_cast<bf16x8*>(&s_t[w][buf][16 * mb + c16][32 * kb + 8 * g]) = a[mb][kb];
-  };
   auto stage_tok = [&](int t) {
     if (w == 0 && lane < BK) s_tok[t & 1][lane] = tok[t * BK + lane];
   };
-  auto s_mfma = [&](const bf16x8 (&a)[2][KB], f32x4 (&acc)[2][4]) {
+  auto s_step = [&](bf16x8 (&a)[2][KB], f32x4 (&acc)[2][4], int buf, int t_next) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero4();
+    const __bf16* src[2];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int mb = 0; mb < 2; ++mb) src[mb] = hc + (int64_t)(t_next * BK + 16 * mb + c16) * H + d0 + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb][kb], q[nb][kb], acc[mb][nb]);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        *reinterpret_cast<bf16x8*>(&s_t[w][buf][16 * mb + c16][32 * kb + 8 * g]) = a[mb][kb];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) a[mb][kb] = ld16(src[mb] + 32 * kb);
+    }
   };
   auto write_part = [&](const f32x4 (&acc)[2][4]) {
 #pragma unroll
@@ -451,24 +498,36 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
   };
   auto reduce_part = [&](f32x4 (&sf)[2]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x4 r = s_part[0][mb][w][lane];
-#pragma unroll
-      for (int src = 1; src < NW; ++src) r += s_part[src][mb][w][lane];
-      sf[mb] = r;
-    }
+    for (int mb = 0; mb < 2; ++mb)
+      sf[mb] = (s_part[0][mb][w][lane] + s_part[1][mb][w][lane]) + (s_part[2][mb][w][lane] + s_part[3][mb][w][lane]);
   };
-  auto pv_mfma = [&](int buf) {
+  auto pv_reduce = [&](int buf, f32x4 (&sf)[2]) {
+    f32x4 r[NW];
     bf16x8 pf[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) pf[qb] = s_p[qb][lane];
     const unsigned short* base = &s_t[w][buf][4 * g + (c16 >> 2)][4 * (c16 & 3)];
+    bf16x8 b0 = ld_tr(base, base + 16 * TS);
+    bf16x8 b1 = ld_tr(base + 16, base + 16 * TS + 16);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const bf16x8 bt = ld_tr(base + 16 * db, base + 16 * TS + 16 * db);
+      const int dn = db + 2 < DB ? db + 2 : DB - 1;
+      const bf16x8 b2 = ld_tr(base + 16 * dn, base + 16 * TS + 16 * dn);
+      if (db == (DB > 4 ? DB - 4 : 0)) {
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], bt, o[qb][db]);
+        for (int src = 0; src < NW; ++src) r[src] = s_part[src][0][w][lane];
+      }
+      if (db == (DB > 2 ? DB - 2 : 0)) {
+        sf[0] = (r[0] + r[1]) + (r[2] + r[3]);
+#pragma unroll
+        for (int src = 0; src < NW; ++src) r[src] = s_part[src][1][w][lane];
+      }
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], b0, o[qb][db]);
+      b0 = b1;
+      b1 = b2;
     }
+    sf[1] = (r[0] + r[1]) + (r[2] + r[3]);
   };
 
   bf16x8 a[2][KB];
@@ -476,9 +535,7 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
   if (n_tiles > 0) {
     stage_tok(0);
     load_a(0, a);
-    s_mfma(a, acc);
-    stage(0, a);
-    load_a(min(1, n_tiles - 1), a);
+    s_step(a, acc, 0, min(1, n_tiles - 1));
     write_part(acc);
   }
   __syncthreads();
@@ -488,7 +545,7 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
     const int t0 = t * BK;
     const int tn = min(t + 1, n_tiles - 1);
     const int tnn = min(t + 2, n_tiles - 1);
-    s_mfma(a, acc);
+    s_step(a, acc, (t + 1) & 1, tnn);
     bf16x8 pa;
     float gsum = 0.f;
 #pragma unroll
@@ -504,15 +561,12 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
       pa[j] = (__bf16)dz;
     }
     gb_run += (double)gsum;
-    if (t + 1 < n_tiles) stage((t + 1) & 1, a);
-    load_a(tnn, a);
     __syncthreads();
     s_p[w][lane] = pa;
     write_part(acc);
     stage_tok(tn);
     __syncthreads();
-    pv_mfma(t & 1);
-    reduce_part(sf);
+    pv_reduce(t & 1, sf);
   }
 
   // grad_b: the four lane groups of a row hold disjoint token subsets
