@@ -12,9 +12,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Per (vocabulary split, row) result of the forward sweep: the reference m
-// all exponentials are taken against, sum exp(z-m), sum exp(z-m) z, the
-// target logit when the target falls in the split, and a flag asking the
-// merge to recompute the row exactly (a logit far above the reference).
+// all exponentials are taken against, sum exp(z-m), sum exp(z-m) z, and a
+// flag asking the merge to recompute the row exactly (a logit far above the
+// reference). zy is not read (the merge takes the target logit itself).
 struct alignas(8) RowStats {
   float m;
   float zy;
@@ -73,17 +73,20 @@ struct LossParams {
 // Launchers (each enqueues on `st`; return hipError_t of the launch)
 // ---------------------------------------------------------------------------
 
-// Row gather of bf16 rows for the weight-gradient sweep: Xc[k] = X[idx[k]]
-// for k < *count_dev, zero rows up to the next multiple of 32 (at most cap).
-hipError_t launch_gather_bf16(const __bf16* X, const int* idx, const int* count_dev, int64_t cap, int H,
-                              __bf16* Xc, hipStream_t st);
+// Fragment-major copy of bf16 rows for the MFMA sweeps (the layout is given
+// in lmhead_mfma.hip): `tiles` 32-row tiles of X, or of X[idx[k]] when idx is
+// given; rows at or past `rows` (*count_dev when given) are zero.
+hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_dev, int64_t rows, int64_t tiles, int H,
+                            __bf16* Xf, hipStream_t st);
 
-// Forward sweep on MFMA (bf16, H a multiple of 128, H <= 896).
-hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* W, const __bf16* b, const int64_t* y, int64_t N, int H,
-                           int V, float inv_tau, int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st);
+// Forward sweep on MFMA (bf16, H a multiple of 128, H <= 896); Wf is the
+// fragment-major copy of W.
+hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
+                           int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st);
 
-// Weight-gradient sweep on MFMA over the compacted tokens hc.
-hipError_t launch_bwd_mfma(const __bf16* W, const __bf16* b, const __bf16* hc, const TokData* tok,
+// Weight-gradient sweep on MFMA over the compacted tokens (hcf and Wf are
+// fragment-major).
+hipError_t launch_bwd_mfma(const __bf16* Wf, const __bf16* b, const __bf16* hcf, const TokData* tok,
                            const int* count_dev, int H, int V, float inv_tau, int acc_mode, float* gW_acc,
                            float* gb_acc, __bf16* gW_out, __bf16* gb_out, hipStream_t st);
 

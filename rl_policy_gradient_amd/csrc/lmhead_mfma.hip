@@ -12,29 +12,34 @@
 //   Acc += P KV                     forward: sum_v e^{z-m} W_v (for grad_h)
 //                                   weight grad: sum_t dz h_t  (grad_W)
 //
+// MFMA: v_mfma_f32_32x32x16_bf16, the bf16 shape that runs at the full dense
+// rate on gfx950 (the 16x16x32 shape issues at half of it). Lane l, with
+// h = l/32 and c = l%32, holds A[c][8h+j], B[8h+j][c] (j = 0..7) and
+// D[8(i/4)+4h+i%4][c] (i = 0..15).
+//
 // H is split across the 4 waves of a workgroup: wave w owns columns
 // [w*H/4, (w+1)*H/4) of Q, of every KV tile and of Acc. Its slice of Q stays
 // in registers for the whole sweep and Acc in accumulation registers. The
 // partial S^T of each wave (its slice of the contraction) is reduce-scattered
-// through LDS: wave w ends up with the complete logits of resident-row block
-// w, runs the epilogue on them, and the bf16 P fragments are all-gathered
-// through LDS for the P KV product.
+// through LDS: wave w = nb + 2kh ends up with the complete logits of one
+// quarter of the tile, resident-row block nb (32 rows) and tile-row half kh
+// (16 rows); lane (h, c) holds resident row 32nb + c and the eight tile rows
+// kvq(kh, h, e) = 16kh + 8(e/4) + 4h + e%4. Those eight values are exactly
+// lane (h, c)'s A operand of the P KV product for row block nb and
+// contraction step kh, so the bf16 P fragments are all-gathered through LDS
+// unchanged, and the same tile-row order is the contraction index of the KV
+// operand. A resident row's values are spread over four lanes (two lane
+// halves of two waves); its running sums are kept per lane against a
+// reference fixed before the sweep and combined once at the end.
 //
 // Each KV tile is read from global memory once. The P KV product contracts
-// over tile rows, so its KV operand needs the 8 tile rows of one column in a
-// lane: after a wave has used its slice of the tile for S^T, it stores that
-// slice row-major into a wave-private LDS buffer and reads it back with the
-// gfx950 transposing load ds_read_b64_tr_b16, which, within each 16-lane
-// group, hands lane l element l%4 of the 64-bit chunk that lane 4j + l/4
-// addressed, for j = 0..3. Pointing lane p at row r0 + p/4, columns
-// c0 + 4(p%4) .. +3 gives lane l the column c0 + l of rows r0 .. r0 + 3, the
-// MFMA B-operand layout.
-//
-// MFMA: v_mfma_f32_16x16x32_bf16. Lane l holds A[l%16][8(l/16)+j],
-// B[8(l/16)+j][l%16] (j = 0..7) and D[4(l/16)+i][l%16] (i = 0..3).
-// The rows of a 32-row tile that lane-group g = l/16 holds after the S^T
-// product are kv(g,j) = 4g+j (j<4) and 16+4g+(j-4) (j>=4); the same order is
-// used as the contraction index of the P KV product, for both operands.
+// over tile rows, so its KV operand needs tile rows of one column in a lane:
+// after a wave has used its slice of the tile for S^T, it stores that slice
+// row-major into a wave-private LDS buffer and reads it back with the gfx950
+// transposing load ds_read_b64_tr_b16, which, within each 16-lane group,
+// hands lane l element l%4 of the 64-bit chunk that lane 4j + l/4 addressed,
+// for j = 0..3. Pointing lane p at row r0 + p/4, columns c0 + 4(p%4) .. +3
+// gives lane l the column c0 + l of rows r0 .. r0 + 3, the B-operand layout.
 #include "common.h"
 
 #include <math.h>
@@ -43,7 +48,7 @@ namespace plp {
 
 namespace {
 
-constexpr int BQ = 64;   // resident rows per workgroup
+constexpr int BQ = 64;   // resident rows per workgroup (two 32-row blocks)
 constexpr int BK = 32;   // streamed rows per tile
 constexpr int NW = 4;    // waves per workgroup
 // The forward sweep fixes each row's exponent reference m at the max of the
@@ -53,22 +58,35 @@ constexpr int NW = 4;    // waves per workgroup
 // flagged and the merge kernel recomputes it exactly. e^64 ~ 6e27 keeps every
 // running sum far inside fp32 and bf16 range.
 constexpr float kRefSlack = 64.0f;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr double kLn2 = 0.693147180559945309417;
+constexpr float kRefSlack2 = kRefSlack * kLog2e;  // the slack in base-2 units
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int kv_of(int g, int j) { return j < 4 ? 4 * g + j : 12 + 4 * g + j; }
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Tile row held in element e (0..7) by lane half h of the wave that owns
+// tile-row half kh after the reduce (see the header comment).
+__device__ __forceinline__ int kvq(int kh, int h, int e) { return 16 * kh + 8 * (e >> 2) + 4 * h + (e & 3); }
 
 __device__ __forceinline__ bf16x8 ld16(const __bf16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
-// Two transposing LDS loads (rows r0..r0+3 and r0+16..r0+19 of a row-major
+// Two transposing LDS loads (rows r0..r0+3 and r0+8..r0+11 of a row-major
 // bf16 tile, see the header) form one B-operand fragment.
 __device__ __forceinline__ bf16x8 ld_tr(const unsigned short* p0, const unsigned short* p1) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
@@ -77,57 +95,69 @@ __device__ __forceinline__ bf16x8 ld_tr(const unsigned short* p0, const unsigned
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
-// l^48) with the gfx950 lane swaps: permlane16_swap(x, x) hands every lane the
-// values of rows {0,1} or {2,3} as (even row, odd row), permlane32_swap(y, y)
-// the values of halves (low, high). Every lane combines the same operands in
-// the same order, so all four lanes hold bitwise-identical results.
-__device__ __forceinline__ float xg_sum(float x) {
+// Values of the other lane half (l ^ 32) with the gfx950 lane swap:
+// permlane32_swap(x, x) returns (low-half value, high-half value) in every lane.
+__device__ __forceinline__ float other_half(float x, int h) {
   const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  const unsigned v = __float_as_uint(y);
-  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(h ? r[0] : r[1]);
 }
 
-__device__ __forceinline__ float xg_max(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  const unsigned v = __float_as_uint(y);
-  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
-}
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// Row stride (elements) of a wave's staged tile slice: the slice width plus
-// 16 elements, so the rows a 16-lane group writes and the four rows each
-// quarter of it reads in a transposing load start on different banks.
+// Layout of a wave's staged tile slice: 32 rows of TS elements; the 16-byte
+// chunk k of row r sits at chunk position k ^ ((r >> 2) & 3). With 64 banks
+// of 4 bytes, the stage writes (16 lanes: rows 0..15 or 16..31, one chunk
+// each) and the transposing loads (32 lanes: four rows x 64 bytes) then touch
+// 64 distinct banks. Rows are padded by 32 elements for even KB so that four
+// consecutive rows start 16 banks apart.
 template <int KB>
 struct Stage {
   static constexpr int DS = 32 * KB;
-  static constexpr int TS = DS + 16;
+  static constexpr int TS = DS + ((KB & 1) ? 0 : 32);
 };
 
+// Fragment-major copies: the operand a wave loads for one 16-wide contraction
+// step of a 32-row tile is one contiguous kilobyte, lane-ordered:
+//   Xf[((tile * 4 + w) * KS + ks) * 64 + lane][0..7]
+//     = X[32 tile + lane % 32][w * DS + 16 ks + 8 (lane / 32) + 0..7].
+template <int KB>
+__device__ __forceinline__ const __bf16* frag_ptr(const __bf16* Xf, int64_t tile, int w, int ks, int lane) {
+  constexpr int KS = 2 * KB;
+  return Xf + ((((tile * 4 + w) * KS) + ks) * 64 + lane) * 8;
+}
+
 // ---------------------------------------------------------------------------
-// Row gather: Xc[k] = X[idx[k]] for k < count, zero rows up to the next
-// multiple of 32 (16-byte vector copies).
+// Fragment-major copy of 32-row tiles of X (rows X[idx[k]] when idx is given),
+// rows at or past `rows` (= *count_dev when given) zero. One block per tile:
+// coalesced row loads into LDS (rows padded by one 16-byte chunk so the
+// fragment-order reads spread over the banks), fragment-order stores.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gather16_kernel(const __bf16* __restrict__ X, const int* __restrict__ idx,
-                                                       const int* __restrict__ count_dev, int64_t cap, int H,
-                                                       __bf16* __restrict__ Xc) {
-  const int64_t n = *count_dev;
-  const int64_t rows = min(cap, (n + BK - 1) / BK * BK);
-  const int cpr = H / 8;
-  const int64_t total = rows * cpr;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t k = e / cpr;
-    const int c = (int)(e - k * cpr);
+__global__ __launch_bounds__(256) void frag_copy_kernel(const __bf16* __restrict__ X, const int* __restrict__ idx,
+                                                        const int* __restrict__ count_dev, int64_t rows_host, int H,
+                                                        __bf16* __restrict__ Xf) {
+  extern __shared__ uint4 smem_u4[];
+  const int64_t rows = count_dev ? (int64_t)(*count_dev) : rows_host;
+  const int64_t t = blockIdx.x;
+  const int64_t r0 = t * BK;
+  if (count_dev && r0 >= rows) return;  // tiles past the gathered rows are never read (block-uniform)
+  const int cpr = H / 8;                // 16-byte chunks per row
+  const int rs = cpr + 1;               // padded LDS row stride in chunks
+  for (int e = threadIdx.x; e < BK * cpr; e += blockDim.x) {
+    const int r = e / cpr, cc = e - r * cpr;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (k < n) v = *reinterpret_cast<const uint4*>(X + (int64_t)idx[k] * H + c * 8);
-    *reinterpret_cast<uint4*>(Xc + k * H + c * 8) = v;
+    if (r0 + r < rows) {
+      const int64_t src = idx ? (int64_t)idx[r0 + r] : r0 + r;
+      v = *reinterpret_cast<const uint4*>(X + src * H + cc * 8);
+    }
+    smem_u4[r * rs + cc] = v;
+  }
+  __syncthreads();
+  const int ks_per_wave = H / 64;  // 16-wide steps in a quarter of H
+  for (int o = threadIdx.x; o < BK * cpr; o += blockDim.x) {
+    const int lane = o & 63;
+    const int rem = o >> 6;          // (w * KS + ks)
+    const int w = rem / ks_per_wave, ks = rem - w * ks_per_wave;
+    const int chunk = w * (H / 32) + 2 * ks + (lane >> 5);
+    *reinterpret_cast<uint4*>(Xf + (t * BK * cpr + o) * 8) = smem_u4[(lane & 31) * rs + chunk];
   }
 }
 
@@ -135,8 +165,9 @@ __global__ __launch_bounds__(256) void gather16_kernel(const __bf16* __restrict_
 // Schedule shared by both sweeps (per workgroup, per tile t of the sweep):
 //
 //   prologue: S^T(t0) -> LDS partials, barrier, reduce -> sf
-//   loop t:   S^T(t+1) MFMAs          | interleaved with the epilogue of tile t
-//             stage tile t+1 for the transposing load, loads for tile t+2
+//   loop t:   epilogue of tile t (vector ALU)   | interleaved with
+//             S^T(t+1) MFMAs, staging of tile t+1 for the transposing load
+//             and the loads of tile t+2
 //             barrier
 //             P(t) -> LDS, partials of t+1 -> LDS
 //             barrier
@@ -150,72 +181,94 @@ __global__ __launch_bounds__(256) void gather16_kernel(const __bf16* __restrict_
 // buffer (P KV of tile t-1), and read in P KV(t+1).
 // ---------------------------------------------------------------------------
 
-// Forward sweep: per token row, running (sum e^{z-m}, sum e^{z-m} z) against
-// the reference m, the target logit, and (WITH_O) the accumulator
+// Forward sweep: per token row, running (sum 2^{z2-m2}, sum 2^{z2-m2} z2)
+// against the reference m2 (z2 = z log2 e), and (WITH_O) the accumulator
 // O = sum_v e^{z-m} W_v. Grid: (row blocks) x Sv vocabulary splits, block
 // id = rb * Sv + split.
 template <int KB, bool WITH_O, bool HAS_BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
-                     const __bf16* __restrict__ bias, const int64_t* __restrict__ y, int64_t N, int V,
-                     float inv_tau, int Sv, int tiles_per_split, RowStats* __restrict__ stats,
-                     float* __restrict__ O) {
+void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf,
+                     const __bf16* __restrict__ bias, int64_t N, int V, float inv_tau, int Sv,
+                     int tiles_per_split, RowStats* __restrict__ stats, float* __restrict__ O) {
   constexpr int H = 128 * KB;
   constexpr int DS = Stage<KB>::DS;  // columns per wave
   constexpr int TS = Stage<KB>::TS;
-  constexpr int DB = 2 * KB;         // 16-wide column blocks per wave
+  constexpr int KS = DS / 16;        // 16-wide contraction steps per wave
+  constexpr int DB = DS / 32;        // 32-wide column blocks per wave
   __shared__ f32x4 s_part[NW][2][4][64];
   __shared__ bf16x8 s_p[4][64];
-  __shared__ unsigned short s_t[WITH_O ? NW : 1][2][BK][WITH_O ? TS : 8];
+  __shared__ unsigned short s_t[WITH_O ? NW : 1][2][WITH_O ? BK * TS : 8];
+  // cross-wave exchanges of per-row values reuse the P buffer (before the
+  // sweep) and the partials buffer (after it)
+  float* s_x = reinterpret_cast<float*>(&s_p[0][0]);              // [NW][64]
+  double* s_xd = reinterpret_cast<double*>(&s_part[0][0][0][0]);   // [NW][2][64]
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int hh = lane >> 5, c = lane & 31;
+  const int nbq = w & 1, kh = w >> 1;  // quarter this wave reduces: row block nbq, tile-row half kh
   const int rb = blockIdx.x / Sv, sv = blockIdx.x - rb * Sv;
   const int64_t q0 = (int64_t)rb * BQ;
   const int d0 = w * DS;
+  // Stage write offsets (element) of lane (hh, c) for even / odd k-step:
+  // row c, chunk 2ks + hh at position (2ks + hh) ^ f(c), f(c) = (c >> 2) & 3.
+  int sw_base[2];
+  {
+    const int f = (c >> 2) & 3;
+    const int b = c * TS + 8 * (hh ^ (f & 1));
+    sw_base[0] = b + 16 * (f >> 1);
+    sw_base[1] = b - 16 * (f >> 1);
+  }
+  // Transposing-load offsets: provider lane p of 16-lane group G reads row
+  // 4(G/2) + p/4 (and 8 further down) of contraction step ks, chunk
+  // 4db + 2(G%2) + (p%4)/2 of column block db, half p%2.
+  int tr_base[2];
+  {
+    const int p = lane & 15, G = lane >> 4;
+    const int r = 4 * (G >> 1) + (p >> 2);
+    const int b = 2 * (G & 1) + ((p >> 1) & 1);
+    const int f = (r >> 2) & 3;  // rows r and r + 8: f and f ^ 2
+    tr_base[0] = r * TS + 8 * (b ^ f) + 4 * (p & 1);
+    tr_base[1] = (r + 8) * TS + 8 * (b ^ f ^ 2) + 4 * (p & 1);
+  }
   const int n_tiles = (V + BK - 1) / BK;
   const int t_begin = sv * tiles_per_split;
   const int t_end = min(n_tiles, t_begin + tiles_per_split);
 
-  // Resident h fragments (B operand of S^T), rows q0+16nb+c16, cols d0+32kb+8g.
-  bf16x8 q[4][KB];
+  // Resident h fragments (B operand of S^T): rows q0 + 32nb + c, cols d0 + 16ks + 8hh.
+  bf16x8 q[2][KS];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int64_t row = min(q0 + 16 * nb + c16, N - 1);
-    const __bf16* src = h + row * H + d0 + 8 * g;
+  for (int nb = 0; nb < 2; ++nb) {
+    const int64_t row = min(q0 + 32 * nb + c, N - 1);
+    const __bf16* src = h + row * H + d0 + 8 * hh;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) q[nb][kb] = ld16(src + 32 * kb);
+    for (int ks = 0; ks < KS; ++ks) q[nb][ks] = ld16(src + 16 * ks);
   }
 
-  f32x4 o[4][WITH_O ? DB : 1];
+  f32x16 o[2][WITH_O ? DB : 1];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int db = 0; db < (WITH_O ? DB : 1); ++db) o[qb][db] = zero4();
+    for (int db = 0; db < (WITH_O ? DB : 1); ++db) o[qb][db] = zero16();
 
-  const int64_t my_row = q0 + 16 * w + c16;  // row whose epilogue this lane runs
-  const int64_t yv = (y != nullptr && my_row < N) ? y[my_row] : -1;
-  float m_ref = -INFINITY;
-  double s_run = 0.0, sz_run = 0.0;
-  float zy = 0.f;
-  bool have_y = false, flag = false;
+  const int64_t my_row = q0 + 32 * nbq + c;  // row whose epilogue this lane runs (with 3 other lanes)
+  // The epilogue works in base 2: z2 = z log2(e), p = 2^(z2 - m2).
+  const float c2 = inv_tau * kLog2e;
+  float m2 = -INFINITY;
+  double s_acc = 0.0, sz_acc = 0.0;  // this lane's share of sum p, sum p z2
+  bool flag = false;
 
-  auto load_a = [&](int t, bf16x8 (&a)[2][KB]) {
+  // rows past V are zero in the fragment-major copy and masked in the epilogue
+  auto load_a = [&](int t, bf16x8 (&a)[KS]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int v = min(t * BK + 16 * mb + c16, V - 1);  // rows past V are masked in the epilogue
-      const __bf16* src = W + (int64_t)v * H + d0 + 8 * g;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) a[mb][kb] = ld16(src + 32 * kb);
-    }
+    for (int ks = 0; ks < KS; ++ks) a[ks] = ld16(frag_ptr<KB>(Wf, t, w, ks, lane));
   };
-  // Bias of tile rows kv(g, 0..7), kept as packed bf16 (two groups of four
-  // consecutive rows, one 8-byte load each when inside the vocabulary).
+  // Bias of tile rows kvq(kh, hh, 0..7), kept as packed bf16 (two groups of
+  // four consecutive rows, one 8-byte load each when inside the vocabulary).
   auto load_bias = [&](int t, uint2 (&bv)[2]) {
     if constexpr (HAS_BIAS) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int r0 = t * BK + 16 * hf + 4 * g;
+        const int r0 = t * BK + 16 * kh + 8 * hf + 4 * hh;
         if (r0 + 3 < V) {
           bv[hf] = *reinterpret_cast<const uint2*>(bias + r0);
         } else {
@@ -237,85 +290,95 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
   // S^T of the tile held in `a`; each k-slice of `a`, once its MFMAs are
   // issued, is staged for the transposing load (WITH_O) and reloaded with
   // the same slice of tile `t_next`.
-  auto s_step = [&](bf16x8 (&a)[2][KB], f32x4 (&acc)[2][4], int buf, int t_next) {
+  auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int buf, int t_next) {
+    acc[0] = zero16();
+    acc[1] = zero16();
+    const __bf16* src = frag_ptr<KB>(Wf, t_next, w, 0, lane);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero4();
-    const __bf16* src[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int v = min(t_next * BK + 16 * mb + c16, V - 1);
-      src[mb] = W + (int64_t)v * H + d0 + 8 * g;
-    }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb][kb], q[nb][kb], acc[mb][nb]);
-      if constexpr (WITH_O) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          *reinterpret_cast<bf16x8*>(&s_t[w][buf][16 * mb + c16][32 * kb + 8 * g]) = a[mb][kb];
-      }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) a[mb][kb] = ld16(src[mb] + 32 * kb);
+      for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a[ks], q[nb][ks], acc[nb]);
+      if constexpr (WITH_O)
+        *reinterpret_cast<bf16x8*>(&s_t[w][buf][sw_base[ks & 1] + 16 * ks]) = a[ks];
+      a[ks] = ld16(src + 512 * ks);
     }
   };
-  auto write_part = [&](const f32x4 (&acc)[2][4]) {
+  // The partial S^T in four groups of four rows per row block; the wave
+  // reducing quarter (nb, kh) reads groups 2kh and 2kh+1 of block nb.
+  auto write_part = [&](const f32x16 (&acc)[2]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) s_part[w][mb][nb][lane] = acc[mb][nb];
+      for (int ig = 0; ig < 4; ++ig)
+        s_part[w][nb][ig][lane] = f32x4{acc[nb][4 * ig], acc[nb][4 * ig + 1], acc[nb][4 * ig + 2], acc[nb][4 * ig + 3]};
   };
   auto reduce_part = [&](f32x4 (&sf)[2]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-      sf[mb] = (s_part[0][mb][w][lane] + s_part[1][mb][w][lane]) + (s_part[2][mb][w][lane] + s_part[3][mb][w][lane]);
+    for (int e = 0; e < 2; ++e)
+      sf[e] = (s_part[0][nbq][2 * kh + e][lane] + s_part[1][nbq][2 * kh + e][lane]) +
+              (s_part[2][nbq][2 * kh + e][lane] + s_part[3][nbq][2 * kh + e][lane]);
   };
-  // P KV of the staged tile in `buf`, with the reduce of the next tile's
-  // partials issued four column blocks before the end.
+  // P KV of the staged tile in `buf` (A = P of row block qb, k-step ks from
+  // the wave that reduced quarter (qb, ks); B = staged rows kvq(ks, hh, *),
+  // columns 32db + c), with the reduce of the next tile's partials issued
+  // near the end.
   auto pv_reduce = [&](int buf, f32x4 (&sf)[2]) {
     f32x4 r[NW];
     if constexpr (WITH_O) {
-      bf16x8 pf[4];
+      bf16x8 pf[2][2];
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) pf[qb] = s_p[qb][lane];
-      const unsigned short* base = &s_t[w][buf][4 * g + (c16 >> 2)][4 * (c16 & 3)];
-      // operand fragments two column blocks ahead of the MFMAs that use them
-      bf16x8 b0 = ld_tr(base, base + 16 * TS);
-      bf16x8 b1 = ld_tr(base + 16, base + 16 * TS + 16);
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int dn = db + 2 < DB ? db + 2 : DB - 1;
-        const bf16x8 b2 = ld_tr(base + 16 * dn, base + 16 * TS + 16 * dn);
-        if (db == (DB > 4 ? DB - 4 : 0)) {
+        for (int ks = 0; ks < 2; ++ks) pf[qb][ks] = s_p[qb + 2 * ks][lane];
+      const unsigned short* tb = &s_t[w][buf][0];
+      constexpr int NF = 2 * DB;  // fragments (db, ks) in order
+      auto frag = [&](int f) {
+        const int db = f >> 1, ks = f & 1;
+        return ld_tr(tb + tr_base[0] + 16 * ks * TS + 32 * db, tb + tr_base[1] + 16 * ks * TS + 32 * db);
+      };
+      bf16x8 b0 = frag(0), b1 = frag(1);
 #pragma unroll
-          for (int src = 0; src < NW; ++src) r[src] = s_part[src][0][w][lane];
+      for (int f = 0; f < NF; ++f) {
+        const bf16x8 b2 = frag(f + 2 < NF ? f + 2 : NF - 1);
+        if (f == (NF > 6 ? NF - 6 : 0)) {
+#pragma unroll
+          for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh][lane];
         }
-        if (db == (DB > 2 ? DB - 2 : 0)) {
+        if (f == (NF > 3 ? NF - 3 : 0)) {
           sf[0] = (r[0] + r[1]) + (r[2] + r[3]);
 #pragma unroll
-          for (int src = 0; src < NW; ++src) r[src] = s_part[src][1][w][lane];
+          for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh + 1][lane];
         }
+        const int db = f >> 1, ks = f & 1;
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], b0, o[qb][db]);
+        for (int qb = 0; qb < 2; ++qb) o[qb][db] = mfma32(pf[qb][ks], b0, o[qb][db]);
         b0 = b1;
         b1 = b2;
       }
     } else {
 #pragma unroll
-      for (int src = 0; src < NW; ++src) r[src] = s_part[src][0][w][lane];
+      for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh][lane];
       sf[0] = (r[0] + r[1]) + (r[2] + r[3]);
 #pragma unroll
-      for (int src = 0; src < NW; ++src) r[src] = s_part[src][1][w][lane];
+      for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh + 1][lane];
     }
     sf[1] = (r[0] + r[1]) + (r[2] + r[3]);
   };
+  // Logits (base 2) of the eight tile rows this lane holds; rows past the
+  // vocabulary get -1e30 (2^(-1e30 - m2) = 0 and 0 * z = 0).
+  auto logits = [&](int v0, const f32x4 (&sf)[2], const uint2 (&bv)[2], float (&z)[8]) {
+    const int lim = V - v0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float sv_ = sf[j >> 2][j & 3];
+      const float zz = HAS_BIAS ? (sv_ + bias_at(bv, j)) * c2 : sv_ * c2;
+      z[j] = kvq(kh, hh, j) < lim ? zz : -1e30f;
+    }
+  };
 
-  bf16x8 a[2][KB];
-  f32x4 acc[2][4], sf[2];
+  bf16x8 a[KS];
+  f32x16 acc[2];
+  f32x4 sf[2];
   uint2 bv[2];
   if (t_begin < t_end) {
     load_a(t_begin, a);
@@ -324,53 +387,45 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
     write_part(acc);
   }
   __syncthreads();
-  if (t_begin < t_end) reduce_part(sf);
+  if (t_begin < t_end) {
+    reduce_part(sf);
+    // reference m2: the row's max over its first tile, from the four lanes
+    // (two lane halves of two waves) that hold the row
+    float z[8];
+    logits(t_begin * BK, sf, bv, z);
+    float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+    mx = fmaxf(mx, other_half(mx, hh));
+    if (hh == 0) s_x[w * 64 + c] = mx;
+  }
+  __syncthreads();
+  if (t_begin < t_end) m2 = fmaxf(s_x[w * 64 + c], s_x[(w ^ 2) * 64 + c]);
+  __syncthreads();
 
   for (int t = t_begin; t < t_end; ++t) {
     const int v0 = t * BK;
     const int tn = min(t + 1, t_end - 1);
     const int tnn = min(t + 2, t_end - 1);
-    // ---- logits of tile t+1 on the matrix cores, stage t+1, load t+2 -------
-    s_step(a, acc, (t + 1) & 1, tnn);
     uint2 bvn[2];
     load_bias(tn, bvn);
-    // ---- epilogue of tile t on row my_row, tile rows kv(g, j) -------------
+    // ---- epilogue of tile t (vector ALU; the scheduler interleaves it with
+    //      the logit MFMAs of tile t+1 below) -------------------------------
     float z[8];
-    bool ok[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int v = v0 + kv_of(g, j);
-      ok[j] = v < V;
-      const float sv_ = j < 4 ? sf[0][j] : sf[1][j - 4];
-      z[j] = ok[j] ? (sv_ + bias_at(bv, j)) * inv_tau : -INFINITY;
-    }
-    float mx = z[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
-    mx = xg_max(mx);
-    m_ref = t == t_begin ? mx : m_ref;
-    flag |= mx > m_ref + kRefSlack;
-    float p[8], sp = 0.f, szp = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = ok[j] ? __expf(fminf(z[j] - m_ref, kRefSlack)) : 0.f;
-      sp += p[j];
-      szp += ok[j] ? p[j] * z[j] : 0.f;
-    }
-    s_run += (double)xg_sum(sp);
-    sz_run += (double)xg_sum(szp);
-    {
-      const int64_t rel = yv - v0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool hit = (int64_t)kv_of(g, j) == rel;
-        zy = hit ? z[j] : zy;
-        have_y |= hit;
-      }
-    }
+    logits(v0, sf, bv, z);
+    float sp = 0.f, szp = 0.f;
     bf16x8 pa;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pa[j] = (__bf16)p[j];
+    for (int j = 0; j < 8; ++j) {
+      flag |= z[j] > m2 + kRefSlack2;
+      const float pj = __builtin_amdgcn_exp2f(fminf(z[j] - m2, kRefSlack2));
+      sp += pj;
+      szp = fmaf(pj, z[j], szp);
+      pa[j] = (__bf16)pj;
+    }
+    s_acc += (double)sp;
+    sz_acc += (double)szp;
+    // ---- logits of tile t+1 on the matrix cores, stage t+1, load t+2 -------
+    s_step(a, acc, (t + 1) & 1, tnn);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     if constexpr (WITH_O) s_p[w][lane] = pa;
     write_part(acc);
@@ -381,29 +436,39 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
     for (int hf = 0; hf < 2; ++hf) bv[hf] = bvn[hf];
   }
 
-  // ---- results ---------------------------------------------------------------
-  const float zyv = xg_sum(have_y ? zy : 0.f);
-  if (g == 0 && my_row < N) {
+  // ---- results: combine the four holders of each row ----------------------
+  double sx = s_acc + (double)__shfl_xor(s_acc, 32, 64);
+  double szx = sz_acc + (double)__shfl_xor(sz_acc, 32, 64);
+  int fl = flag ? 1 : 0;
+  fl |= __shfl_xor(fl, 32, 64);
+  __syncthreads();
+  if (hh == 0) {
+    s_xd[(2 * w) * 64 + c] = sx;
+    s_xd[(2 * w + 1) * 64 + c] = szx;
+    s_x[w * 64 + c] = __int_as_float(fl);
+  }
+  __syncthreads();
+  if (kh == 0 && hh == 0 && my_row < N) {
     RowStats rs;
-    rs.m = m_ref;
-    rs.zy = zyv;
-    rs.s = s_run;
-    rs.sz = sz_run;
-    rs.flag = flag ? 1 : 0;
+    rs.m = (float)((double)m2 * kLn2);
+    rs.zy = 0.f;
+    rs.s = sx + s_xd[(2 * (w ^ 2)) * 64 + c];
+    rs.sz = (szx + s_xd[(2 * (w ^ 2) + 1) * 64 + c]) * kLn2;
+    rs.flag = (fl | __float_as_int(s_x[(w ^ 2) * 64 + c])) ? 1 : 0;
     rs.pad = 0;
     stats[(int64_t)sv * N + my_row] = rs;
   }
   if constexpr (WITH_O) {
     float* Ob = O + (int64_t)sv * N * H;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = q0 + 16 * qb + 4 * g + i;
+      for (int i = 0; i < 16; ++i) {
+        const int64_t row = q0 + 32 * qb + 8 * (i >> 2) + 4 * hh + (i & 3);
         if (row < N) {
-          float* dst = Ob + row * H + d0 + c16;
+          float* dst = Ob + row * H + d0 + c;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) dst[16 * db] = o[qb][db][i];
+          for (int db = 0; db < DB; ++db) dst[32 * db] = o[qb][db][i];
         }
       }
   }
@@ -418,120 +483,138 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ W,
 // ---------------------------------------------------------------------------
 template <int KB, bool HAS_BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bias,
-                     const __bf16* __restrict__ hc, const TokData* __restrict__ tok,
+void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bias,
+                     const __bf16* __restrict__ hcf, const TokData* __restrict__ tok,
                      const int* __restrict__ count_dev, int V, float inv_tau, int acc_mode,
                      float* __restrict__ gW_acc, float* __restrict__ gb_acc, __bf16* __restrict__ gW_out,
                      __bf16* __restrict__ gb_out) {
   constexpr int H = 128 * KB;
   constexpr int DS = Stage<KB>::DS;
   constexpr int TS = Stage<KB>::TS;
-  constexpr int DB = 2 * KB;
+  constexpr int KS = DS / 16;
+  constexpr int DB = DS / 32;
   __shared__ f32x4 s_part[NW][2][4][64];
   __shared__ bf16x8 s_p[4][64];
   __shared__ TokData s_tok[2][BK];
-  __shared__ unsigned short s_t[NW][2][BK][TS];
+  __shared__ unsigned short s_t[NW][2][BK * TS];
+  double* s_xd = reinterpret_cast<double*>(&s_part[0][0][0][0]);  // [NW][64], after the sweep
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int hh = lane >> 5, c = lane & 31;
+  const int nbq = w & 1, kh = w >> 1;
   const int q0 = blockIdx.x * BQ;
   const int d0 = w * DS;
+  // Stage write offsets (element) of lane (hh, c) for even / odd k-step:
+  // row c, chunk 2ks + hh at position (2ks + hh) ^ f(c), f(c) = (c >> 2) & 3.
+  int sw_base[2];
+  {
+    const int f = (c >> 2) & 3;
+    const int b = c * TS + 8 * (hh ^ (f & 1));
+    sw_base[0] = b + 16 * (f >> 1);
+    sw_base[1] = b - 16 * (f >> 1);
+  }
+  // Transposing-load offsets: provider lane p of 16-lane group G reads row
+  // 4(G/2) + p/4 (and 8 further down) of contraction step ks, chunk
+  // 4db + 2(G%2) + (p%4)/2 of column block db, half p%2.
+  int tr_base[2];
+  {
+    const int p = lane & 15, G = lane >> 4;
+    const int r = 4 * (G >> 1) + (p >> 2);
+    const int b = 2 * (G & 1) + ((p >> 1) & 1);
+    const int f = (r >> 2) & 3;  // rows r and r + 8: f and f ^ 2
+    tr_base[0] = r * TS + 8 * (b ^ f) + 4 * (p & 1);
+    tr_base[1] = (r + 8) * TS + 8 * (b ^ f ^ 2) + 4 * (p & 1);
+  }
   const int n_tok = *count_dev;
   const int n_tiles = (n_tok + BK - 1) / BK;
 
-  // Resident W fragments (B operand of S^T), rows q0+16nb+c16, cols d0+32kb+8g.
-  bf16x8 q[4][KB];
+  // Resident W fragments (B operand of S^T), rows q0 + 32nb + c, cols
+  // d0 + 16ks + 8hh, from the fragment-major copy (rows past V are zero).
+  bf16x8 q[2][KS];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int v = min(q0 + 16 * nb + c16, V - 1);
-    const __bf16* src = W + (int64_t)v * H + d0 + 8 * g;
+  for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) q[nb][kb] = ld16(src + 32 * kb);
-  }
-  f32x4 o[4][DB];
+    for (int ks = 0; ks < KS; ++ks) q[nb][ks] = ld16(frag_ptr<KB>(Wf, q0 / BK + nb, w, ks, lane));
+  f32x16 o[2][DB];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[qb][db] = zero4();
+    for (int db = 0; db < DB; ++db) o[qb][db] = zero16();
 
-  const int my_v = q0 + 16 * w + c16;
+  const int my_v = q0 + 32 * nbq + c;
   const float bvl = HAS_BIAS ? (float)bias[min(my_v, V - 1)] : 0.f;
   double gb_run = 0.0;
 
-  auto load_a = [&](int t, bf16x8 (&a)[2][KB]) {
+  auto load_a = [&](int t, bf16x8 (&a)[KS]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const __bf16* src = hc + (int64_t)(t * BK + 16 * mb + c16) * H + d0 + 8 * g;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) a[mb][kb] = ld16(src + 32 * kb);
-    }
+    for (int ks = 0; ks < KS; ++ks) a[ks] = ld16(frag_ptr<KB>(hcf, t, w, ks, lane));
   };
   auto stage_tok = [&](int t) {
     if (w == 0 && lane < BK) s_tok[t & 1][lane] = tok[t * BK + lane];
   };
-  auto s_step = [&](bf16x8 (&a)[2][KB], f32x4 (&acc)[2][4], int buf, int t_next) {
+  auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int buf, int t_next) {
+    acc[0] = zero16();
+    acc[1] = zero16();
+    const __bf16* src = frag_ptr<KB>(hcf, t_next, w, 0, lane);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero4();
-    const __bf16* src[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) src[mb] = hc + (int64_t)(t_next * BK + 16 * mb + c16) * H + d0 + 8 * g;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(a[mb][kb], q[nb][kb], acc[mb][nb]);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        *reinterpret_cast<bf16x8*>(&s_t[w][buf][16 * mb + c16][32 * kb + 8 * g]) = a[mb][kb];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) a[mb][kb] = ld16(src[mb] + 32 * kb);
+      for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a[ks], q[nb][ks], acc[nb]);
+      *reinterpret_cast<bf16x8*>(&s_t[w][buf][sw_base[ks & 1] + 16 * ks]) = a[ks];
+      a[ks] = ld16(src + 512 * ks);
     }
   };
-  auto write_part = [&](const f32x4 (&acc)[2][4]) {
+  auto write_part = [&](const f32x16 (&acc)[2]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) s_part[w][mb][nb][lane] = acc[mb][nb];
+      for (int ig = 0; ig < 4; ++ig)
+        s_part[w][nb][ig][lane] = f32x4{acc[nb][4 * ig], acc[nb][4 * ig + 1], acc[nb][4 * ig + 2], acc[nb][4 * ig + 3]};
   };
   auto reduce_part = [&](f32x4 (&sf)[2]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-      sf[mb] = (s_part[0][mb][w][lane] + s_part[1][mb][w][lane]) + (s_part[2][mb][w][lane] + s_part[3][mb][w][lane]);
+    for (int e = 0; e < 2; ++e)
+      sf[e] = (s_part[0][nbq][2 * kh + e][lane] + s_part[1][nbq][2 * kh + e][lane]) +
+              (s_part[2][nbq][2 * kh + e][lane] + s_part[3][nbq][2 * kh + e][lane]);
   };
   auto pv_reduce = [&](int buf, f32x4 (&sf)[2]) {
     f32x4 r[NW];
-    bf16x8 pf[4];
+    bf16x8 pf[2][2];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) pf[qb] = s_p[qb][lane];
-    const unsigned short* base = &s_t[w][buf][4 * g + (c16 >> 2)][4 * (c16 & 3)];
-    bf16x8 b0 = ld_tr(base, base + 16 * TS);
-    bf16x8 b1 = ld_tr(base + 16, base + 16 * TS + 16);
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int dn = db + 2 < DB ? db + 2 : DB - 1;
-      const bf16x8 b2 = ld_tr(base + 16 * dn, base + 16 * TS + 16 * dn);
-      if (db == (DB > 4 ? DB - 4 : 0)) {
+      for (int ks = 0; ks < 2; ++ks) pf[qb][ks] = s_p[qb + 2 * ks][lane];
+    const unsigned short* tb = &s_t[w][buf][0];
+    constexpr int NF = 2 * DB;
+    auto frag = [&](int f) {
+      const int db = f >> 1, ks = f & 1;
+      return ld_tr(tb + tr_base[0] + 16 * ks * TS + 32 * db, tb + tr_base[1] + 16 * ks * TS + 32 * db);
+    };
+    bf16x8 b0 = frag(0), b1 = frag(1);
 #pragma unroll
-        for (int src = 0; src < NW; ++src) r[src] = s_part[src][0][w][lane];
+    for (int f = 0; f < NF; ++f) {
+      const bf16x8 b2 = frag(f + 2 < NF ? f + 2 : NF - 1);
+      if (f == (NF > 6 ? NF - 6 : 0)) {
+#pragma unroll
+        for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh][lane];
       }
-      if (db == (DB > 2 ? DB - 2 : 0)) {
+      if (f == (NF > 3 ? NF - 3 : 0)) {
         sf[0] = (r[0] + r[1]) + (r[2] + r[3]);
 #pragma unroll
-        for (int src = 0; src < NW; ++src) r[src] = s_part[src][1][w][lane];
+        for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh + 1][lane];
       }
+      const int db = f >> 1, ks = f & 1;
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) o[qb][db] = mfma16(pf[qb], b0, o[qb][db]);
+      for (int qb = 0; qb < 2; ++qb) o[qb][db] = mfma32(pf[qb][ks], b0, o[qb][db]);
       b0 = b1;
       b1 = b2;
     }
     sf[1] = (r[0] + r[1]) + (r[2] + r[3]);
   };
 
-  bf16x8 a[2][KB];
-  f32x4 acc[2][4], sf[2];
+  bf16x8 a[KS];
+  f32x16 acc[2];
+  f32x4 sf[2];
   if (n_tiles > 0) {
     stage_tok(0);
     load_a(0, a);
@@ -545,14 +628,15 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
     const int t0 = t * BK;
     const int tn = min(t + 1, n_tiles - 1);
     const int tnn = min(t + 2, n_tiles - 1);
-    s_step(a, acc, (t + 1) & 1, tnn);
+    // ---- epilogue of tile t (vector ALU; the scheduler interleaves it with
+    //      the logit MFMAs of tile t+1 below) -------------------------------
     bf16x8 pa;
     float gsum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int kv = kv_of(g, j);
+      const int kv = kvq(kh, hh, j);
       const TokData td = s_tok[t & 1][kv];
-      const float sv_ = j < 4 ? sf[0][j] : sf[1][j - 4];
+      const float sv_ = sf[j >> 2][j & 3];
       const float z = (sv_ + bvl) * inv_tau;
       const float pr = __expf(z - td.lse);
       float dz = td.gs * ((td.y == my_v ? 1.f : 0.f) - pr);
@@ -561,6 +645,9 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
       pa[j] = (__bf16)dz;
     }
     gb_run += (double)gsum;
+    // ---- logits of tile t+1, stage t+1, load t+2 ---------------------------
+    s_step(a, acc, (t + 1) & 1, tnn);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     s_p[w][lane] = pa;
     write_part(acc);
@@ -569,30 +656,32 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
     pv_reduce(t & 1, sf);
   }
 
-  // grad_b: the four lane groups of a row hold disjoint token subsets
-  double gbv = gb_run;
-  gbv += __shfl_xor(gbv, 16, 64);
-  gbv += __shfl_xor(gbv, 32, 64);
+  // grad_b: the four holders of a vocabulary row (two lane halves of two
+  // waves) hold disjoint token subsets
+  double gbv = gb_run + __shfl_xor(gb_run, 32, 64);
+  __syncthreads();
+  if (hh == 0) s_xd[w * 64 + c] = gbv;
+  __syncthreads();
   const bool from_acc = acc_mode == 2 || acc_mode == 3;
   const bool to_acc = acc_mode == 1 || acc_mode == 2;
-  if (g == 0 && my_v < V && (to_acc ? gb_acc != nullptr : gb_out != nullptr)) {
-    double val = gbv;
+  if (kh == 0 && hh == 0 && my_v < V && (to_acc ? gb_acc != nullptr : gb_out != nullptr)) {
+    double val = gbv + s_xd[(w ^ 2) * 64 + c];
     if (from_acc) val += (double)gb_acc[my_v];
     if (to_acc) gb_acc[my_v] = (float)val;
     else gb_out[my_v] = (__bf16)(float)val;
   }
   if (to_acc ? gW_acc == nullptr : gW_out == nullptr) return;
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = q0 + 16 * qb + 4 * g + i;
+    for (int i = 0; i < 16; ++i) {
+      const int v = q0 + 32 * qb + 8 * (i >> 2) + 4 * hh + (i & 3);
       if (v < V) {
-        const int64_t base = (int64_t)v * H + d0 + c16;
+        const int64_t base = (int64_t)v * H + d0 + c;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           float val = o[qb][db][i];
-          const int64_t k = base + 16 * db;
+          const int64_t k = base + 32 * db;
           if (from_acc) val += gW_acc[k];
           if (to_acc) gW_acc[k] = val;
           else gW_out[k] = (__bf16)val;
@@ -602,78 +691,76 @@ void bwd_mfma_kernel(const __bf16* __restrict__ W, const __bf16* __restrict__ bi
 }
 
 template <int KB>
-hipError_t fwd_dispatch(const __bf16* h, const __bf16* W, const __bf16* b, const int64_t* y, int64_t N, int V,
-                        float inv_tau, int Sv, int tps, bool with_o, RowStats* stats, float* O, hipStream_t st) {
+hipError_t fwd_dispatch(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int V, float inv_tau, int Sv,
+                        int tps, bool with_o, RowStats* stats, float* O, hipStream_t st) {
   const int64_t nrb = (N + BQ - 1) / BQ;
   dim3 grid((unsigned)(nrb * Sv)), block(256);
   if (with_o && b)
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true, true>), grid, block, 0, st, h, W, b, y, N, V, inv_tau, Sv, tps,
-                       stats, O);
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true, true>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats,
+                       O);
   else if (with_o)
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true, false>), grid, block, 0, st, h, W, b, y, N, V, inv_tau, Sv, tps,
-                       stats, O);
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true, false>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats,
+                       O);
   else if (b)
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false, true>), grid, block, 0, st, h, W, b, y, N, V, inv_tau, Sv, tps,
-                       stats, O);
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false, true>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats,
+                       O);
   else
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false, false>), grid, block, 0, st, h, W, b, y, N, V, inv_tau, Sv, tps,
+    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false, false>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps,
                        stats, O);
   return hipGetLastError();
 }
 
 template <int KB>
-hipError_t bwd_dispatch(const __bf16* W, const __bf16* b, const __bf16* hc, const TokData* tok, const int* count_dev,
+hipError_t bwd_dispatch(const __bf16* Wf, const __bf16* b, const __bf16* hcf, const TokData* tok, const int* count_dev,
                         int V, float inv_tau, int acc_mode, float* gW_acc, float* gb_acc, __bf16* gW_out,
                         __bf16* gb_out, hipStream_t st) {
   dim3 grid((unsigned)((V + BQ - 1) / BQ)), block(256);
   if (b)
-    hipLaunchKernelGGL((bwd_mfma_kernel<KB, true>), grid, block, 0, st, W, b, hc, tok, count_dev, V, inv_tau,
+    hipLaunchKernelGGL((bwd_mfma_kernel<KB, true>), grid, block, 0, st, Wf, b, hcf, tok, count_dev, V, inv_tau,
                        acc_mode, gW_acc, gb_acc, gW_out, gb_out);
   else
-    hipLaunchKernelGGL((bwd_mfma_kernel<KB, false>), grid, block, 0, st, W, b, hc, tok, count_dev, V, inv_tau,
+    hipLaunchKernelGGL((bwd_mfma_kernel<KB, false>), grid, block, 0, st, Wf, b, hcf, tok, count_dev, V, inv_tau,
                        acc_mode, gW_acc, gb_acc, gW_out, gb_out);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gather_bf16(const __bf16* X, const int* idx, const int* count_dev, int64_t cap, int H, __bf16* Xc,
-                              hipStream_t st) {
-  if (cap <= 0) return hipSuccess;
-  const int64_t chunks = cap * (H / 8);
-  const int64_t blocks = (chunks + 255) / 256;
-  const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
-  hipLaunchKernelGGL(gather16_kernel, dim3(grid), dim3(256), 0, st, X, idx, count_dev, cap, H, Xc);
+hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_dev, int64_t rows, int64_t tiles, int H,
+                            __bf16* Xf, hipStream_t st) {
+  if (tiles <= 0) return hipSuccess;
+  const size_t lds = (size_t)BK * (H / 8 + 1) * 16;
+  hipLaunchKernelGGL(frag_copy_kernel, dim3((unsigned)tiles), dim3(256), lds, st, X, idx, count_dev, rows, H, Xf);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* W, const __bf16* b, const int64_t* y, int64_t N, int H,
-                           int V, float inv_tau, int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st) {
+hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
+                           int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st) {
   const int n_tiles = (V + BK - 1) / BK;
   const int tps = (n_tiles + Sv - 1) / Sv;
   switch (H / 128) {
-    case 1: return fwd_dispatch<1>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 2: return fwd_dispatch<2>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 3: return fwd_dispatch<3>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 4: return fwd_dispatch<4>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 5: return fwd_dispatch<5>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 6: return fwd_dispatch<6>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 7: return fwd_dispatch<7>(h, W, b, y, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 1: return fwd_dispatch<1>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 2: return fwd_dispatch<2>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 3: return fwd_dispatch<3>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 4: return fwd_dispatch<4>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 5: return fwd_dispatch<5>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 6: return fwd_dispatch<6>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
+    case 7: return fwd_dispatch<7>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd_mfma(const __bf16* W, const __bf16* b, const __bf16* hc, const TokData* tok,
+hipError_t launch_bwd_mfma(const __bf16* Wf, const __bf16* b, const __bf16* hcf, const TokData* tok,
                            const int* count_dev, int H, int V, float inv_tau, int acc_mode, float* gW_acc,
                            float* gb_acc, __bf16* gW_out, __bf16* gb_out, hipStream_t st) {
   switch (H / 128) {
-    case 1: return bwd_dispatch<1>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 2: return bwd_dispatch<2>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 3: return bwd_dispatch<3>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 4: return bwd_dispatch<4>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 5: return bwd_dispatch<5>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 6: return bwd_dispatch<6>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 7: return bwd_dispatch<7>(W, b, hc, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 1: return bwd_dispatch<1>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 2: return bwd_dispatch<2>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 3: return bwd_dispatch<3>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 4: return bwd_dispatch<4>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 5: return bwd_dispatch<5>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 6: return bwd_dispatch<6>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 7: return bwd_dispatch<7>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
     default: return hipErrorInvalidValue;
   }
 }

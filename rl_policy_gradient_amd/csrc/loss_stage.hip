@@ -18,34 +18,70 @@ __device__ __forceinline__ float ldf(const T* p, int64_t i) {
   return (float)p[i];
 }
 
+template <typename V_>
+__device__ V_ block_sum(V_ v, V_* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int s = NT / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  const V_ r = red[0];
+  __syncthreads();
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Merge of vocabulary splits (per row): lse = M + log sum_j e^{m_j-M} s_j,
 // lp = z_y - lse, H = lse - (sum_j e^{m_j-M} sz_j) / (sum_j e^{m_j-M} s_j)
 // (PR #1558: H = log_z - sum_exp_z / sum_exp), and v = W_y - O/s, so that
-// grad_h = (g / tau) v since d lp / d z_v = [v = y] - p_v.
-// A row any split flagged is recomputed exactly (row_exact).
+// grad_h = (g / tau) v since d lp / d z_v = [v = y] - p_v. The target logit
+// z_y = (h . W_y + b_y) / tau is one dot product per row, taken here rather
+// than gathered inside the sweeps. A row any split flagged is recomputed
+// exactly (row_exact).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict__ stats, const float* __restrict__ O,
-                                                     int Sv, int tps_tiles, int64_t N, int H, int V,
-                                                     const T* __restrict__ h, const T* __restrict__ W,
-                                                     const T* __restrict__ b, float inv_tau,
+                                                     int Sv, int64_t N, int H, int V, const T* __restrict__ h,
+                                                     const T* __restrict__ W, const T* __restrict__ b, float inv_tau,
                                                      const int64_t* __restrict__ y, float* __restrict__ lp,
                                                      float* __restrict__ ent, float* __restrict__ lse_out,
                                                      float* __restrict__ vout) {
   extern __shared__ float sm[];
   const int64_t row = blockIdx.x;
   __shared__ double s_c[64];  // per-split weights e^{m_j - M}, up to 64 splits
-  __shared__ double s_res[3];
+  __shared__ double s_red[NT];
+  __shared__ double s_res[4];
   __shared__ int s_flag;
   const int64_t yv = y ? y[row] : -1;
   // targets outside [0, V) are invalid input; clamp the index so they cannot
-  // address memory outside W or the split table
+  // address memory outside W
   const int64_t yc = yv < 0 ? 0 : (yv >= V ? V - 1 : yv);
-  if (threadIdx.x == 0) {
-    int f = 0;
-    for (int j = 0; j < Sv; ++j) f |= stats[(int64_t)j * N + row].flag;
-    s_flag = f;
+  if (threadIdx.x < 64) {
+    // one lane per split; butterfly reductions in a fixed order
+    const int j = threadIdx.x;
+    const bool have = j < Sv;
+    RowStats rs;
+    if (have) rs = stats[(int64_t)j * N + row];
+    int f = have ? rs.flag : 0;
+    float M = have ? rs.m : -INFINITY;
+    for (int o = 32; o > 0; o >>= 1) {
+      M = fmaxf(M, __shfl_xor(M, o, 64));
+      f |= __shfl_xor(f, o, 64);
+    }
+    const double c = (have && rs.s > 0.0) ? exp((double)rs.m - (double)M) : 0.0;
+    double cs = have ? c * rs.s : 0.0, csz = have ? c * rs.sz : 0.0;
+    for (int o = 32; o > 0; o >>= 1) {
+      cs += __shfl_xor(cs, o, 64);
+      csz += __shfl_xor(csz, o, 64);
+    }
+    s_c[j] = c;
+    if (j == 0) {
+      s_flag = f;
+      s_res[0] = (double)M;
+      s_res[1] = cs;
+      s_res[2] = csz;
+    }
   }
   __syncthreads();
   if (s_flag) {
@@ -64,29 +100,24 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
     }
     return;
   }
+  double zp = 0.0;
+  if (lp)
+    for (int d = threadIdx.x; d < H; d += NT) zp += (double)ldf<T>(h, row * H + d) * (double)ldf<T>(W, yc * H + d);
+  zp = block_sum(zp, s_red);
   if (threadIdx.x == 0) {
-    float M = -INFINITY;
-    for (int j = 0; j < Sv; ++j) M = fmaxf(M, stats[(int64_t)j * N + row].m);
-    double S = 0.0, SZ = 0.0;
-    for (int j = 0; j < Sv; ++j) {
-      const RowStats rs = stats[(int64_t)j * N + row];
-      const double c = rs.s > 0.0 ? exp((double)rs.m - (double)M) : 0.0;
-      s_c[j] = c;
-      S += c * rs.s;
-      SZ += c * rs.sz;
-    }
-    const double l = (double)M + log(S);
+    const double S = s_res[1], SZ = s_res[2];
+    const double l = s_res[0] + log(S);
     if (lp) {
-      const int jy = min(Sv - 1, (int)((yc / 32) / tps_tiles));
-      lp[row] = (float)((double)stats[(int64_t)jy * N + row].zy - l);
+      const float zy = (float)((zp + (b ? (double)ldf<T>(b, yc) : 0.0)) * (double)inv_tau);
+      lp[row] = (float)((double)zy - l);
     }
     ent[row] = (float)(l - SZ / S);
     if (lse_out) lse_out[row] = (float)l;
-    s_res[0] = 1.0 / S;
+    s_res[3] = 1.0 / S;
   }
   __syncthreads();
   if (vout) {
-    const double inv_s = s_res[0];
+    const double inv_s = s_res[3];
     for (int d = threadIdx.x; d < H; d += NT) {
       double o = 0.0;
       for (int j = 0; j < Sv; ++j)
@@ -135,19 +166,6 @@ __device__ __forceinline__ TokEval eval_tok(const LossParams& p, int64_t t, cons
     e.dkl = 0.0;
   }
   return e;
-}
-
-template <typename V_>
-__device__ V_ block_sum(V_ v, V_* red) {
-  red[threadIdx.x] = v;
-  __syncthreads();
-  for (int s = NT / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  const V_ r = red[0];
-  __syncthreads();
-  return r;
 }
 
 __global__ __launch_bounds__(NT) void zero_acc_kernel(LossAcc* acc) {
@@ -549,14 +567,12 @@ hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int 
                           const void* h, const void* W, const void* b, float inv_tau, const int64_t* y, float* lp,
                           float* ent, float* lse, float* vout, hipStream_t st) {
   if (N <= 0) return hipSuccess;
-  const int n_tiles = (V + 31) / 32;
-  const int tps = (n_tiles + Sv - 1) / Sv;
   const size_t lds = row_exact_smem_bytes(H);
   if (dtype == 0)
-    hipLaunchKernelGGL((combine_kernel<float>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, tps, N, H, V,
+    hipLaunchKernelGGL((combine_kernel<float>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H, V,
                        (const float*)h, (const float*)W, (const float*)b, inv_tau, y, lp, ent, lse, vout);
   else
-    hipLaunchKernelGGL((combine_kernel<__bf16>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, tps, N, H, V,
+    hipLaunchKernelGGL((combine_kernel<__bf16>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H, V,
                        (const __bf16*)h, (const __bf16*)W, (const __bf16*)b, inv_tau, y, lp, ent, lse, vout);
   return hipGetLastError();
 }

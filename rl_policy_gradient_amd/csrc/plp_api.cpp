@@ -83,6 +83,7 @@ struct Plan {
 };
 
 struct Bufs {
+  __bf16* Wf = nullptr;        // fragment-major copy of W (MFMA path)
   RowStats* stats = nullptr;
   float* O = nullptr;
   float* v = nullptr;
@@ -126,6 +127,7 @@ Plan make_plan(const plp_args* a, bool need_o, bool need_gw, bool need_gb) {
 size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
   Carver c(ws);
   const int H = a->H, V = a->V;
+  if (p.mfma) b.Wf = c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H);
   b.stats = c.take<RowStats>((size_t)p.Sv * p.Nc);
   if (p.need_o) {
     b.O = c.take<float>((size_t)p.Sv * p.Nc * H);
@@ -256,8 +258,8 @@ int forward_rows(const plp_args* a, const Plan& p, Bufs& b, int64_t r0, int64_t 
   if (p.mfma) {
     hipEvent_t* ev = prof_slot(0);
     if (ev) HIP_TRY(hipEventRecord(ev[0], st));
-    HIP_TRY(launch_fwd_mfma((const __bf16*)h, (const __bf16*)a->weight, (const __bf16*)a->bias, y, n, a->H, a->V,
-                            inv_tau, p.Sv, with_o, b.stats, with_o ? b.O : nullptr, st));
+    HIP_TRY(launch_fwd_mfma((const __bf16*)h, b.Wf, (const __bf16*)a->bias, n, a->H, a->V, inv_tau, p.Sv, with_o,
+                            b.stats, with_o ? b.O : nullptr, st));
     if (ev) HIP_TRY(hipEventRecord(ev[1], st));
   } else {
     HIP_TRY(launch_fwd_generic(a->dtype, h, a->weight, a->bias, y, n, a->H, a->V, inv_tau, with_o, b.stats,
@@ -357,6 +359,8 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
   const LossParams lpar = loss_params(a);
 
   HIP_TRY(launch_loss_zero(b.acc, st));
+  if (p.mfma)
+    HIP_TRY(launch_frag_copy((const __bf16*)a->weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H, b.Wf, st));
 
   bool first_chunk_done = false;
   if (p.entropy) {
@@ -400,16 +404,15 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
       HIP_TRY(launch_compact(g, b.lse + r0, a->targets + r0, n, inv_tau, b.idx, b.tok, b.count, b.cscratch, st));
       const char* hsrc = (const char*)a->hidden + (size_t)r0 * H * es;
       if (p.mfma)
-        HIP_TRY(launch_gather_bf16((const __bf16*)hsrc, b.idx, b.count, p.cap, H, (__bf16*)b.hc, st));
+        HIP_TRY(launch_frag_copy((const __bf16*)hsrc, b.idx, b.count, n, p.cap / kBK, H, (__bf16*)b.hc, st));
       else
         HIP_TRY(launch_gather_rows(a->dtype, hsrc, b.idx, b.count, p.cap, H, b.hc, st));
       const int mode = p.nchunks == 1 ? 0 : (c == 0 ? 1 : (c == p.nchunks - 1 ? 3 : 2));
       if (p.mfma) {
         hipEvent_t* ev = prof_slot(1);
         if (ev) HIP_TRY(hipEventRecord(ev[0], st));
-        HIP_TRY(launch_bwd_mfma((const __bf16*)a->weight, (const __bf16*)a->bias, (const __bf16*)b.hc, b.tok, b.count,
-                                H, V, inv_tau, mode, b.gW_acc, b.gb_acc, (__bf16*)out->grad_weight,
-                                (__bf16*)out->grad_bias, st));
+        HIP_TRY(launch_bwd_mfma(b.Wf, (const __bf16*)a->bias, (const __bf16*)b.hc, b.tok, b.count, H, V, inv_tau, mode,
+                                b.gW_acc, b.gb_acc, (__bf16*)out->grad_weight, (__bf16*)out->grad_bias, st));
         if (ev) HIP_TRY(hipEventRecord(ev[1], st));
       } else
         HIP_TRY(launch_bwd_generic(a->dtype, a->weight, a->bias, b.hc, b.tok, b.count, H, V, inv_tau, mode, b.gW_acc,
@@ -429,8 +432,10 @@ PLP_API int plp_selective_entropy_workspace_size(int64_t N, int32_t H, int32_t V
   if (!bytes) return fail(PLP_E_INVALID, "bytes is NULL");
   if (N < 1 || N >= kMaxRows || H < 1 || V < 1) return fail(PLP_E_INVALID, "bad sizes N=%lld H=%d V=%d", (long long)N, H, V);
   if (dtype != PLP_DTYPE_F32 && dtype != PLP_DTYPE_BF16) return fail(PLP_E_INVALID, "unknown dtype %d", dtype);
-  const int sv = choose_splits(N, V, mfma_eligible(dtype, H));
+  const bool mfma = mfma_eligible(dtype, H);
+  const int sv = choose_splits(N, V, mfma);
   *bytes = align_up((size_t)sv * N * sizeof(RowStats)) + align_up((size_t)N * sizeof(float)) + kAlign;
+  if (mfma) *bytes += align_up((size_t)round_up(V, 2 * kBK) * H * sizeof(__bf16));
   return ok();
 }
 
@@ -451,11 +456,14 @@ PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const 
   Carver c(ws);
   RowStats* stats = c.take<RowStats>((size_t)sv * N);
   float* scratch_lp = c.take<float>(N);
-  const int64_t* y = targets;  // may be NULL: no target logit is gathered
+  __bf16* Wf = mfma ? c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H) : nullptr;
+  const int64_t* y = targets;  // may be NULL: no target logit is taken
   const float inv_tau = 1.0f / temperature;
-  if (mfma)
-    HIP_TRY(launch_fwd_mfma((const __bf16*)hidden, (const __bf16*)weight, (const __bf16*)bias, y, N, H, V, inv_tau,
-                            sv, false, stats, nullptr, st));
+  if (mfma) {
+    HIP_TRY(launch_frag_copy((const __bf16*)weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H, Wf, st));
+    HIP_TRY(launch_fwd_mfma((const __bf16*)hidden, Wf, (const __bf16*)bias, N, H, V, inv_tau, sv, false, stats, nullptr,
+                            st));
+  }
   else
     HIP_TRY(launch_fwd_generic(dtype, hidden, weight, bias, y, N, H, V, inv_tau, false, stats, nullptr, st));
   HIP_TRY(launch_combine(dtype, stats, nullptr, sv, N, H, V, hidden, weight, bias, inv_tau, y,
