@@ -125,6 +125,29 @@ __device__ __forceinline__ const __bf16* frag_ptr(const __bf16* Xf, int64_t tile
   return Xf + ((((tile * 4 + w) * KS) + ks) * 64 + lane) * 8;
 }
 
+// Store of a wave's accumulator (rows 32qb + 8(i/4) + 4h + i%4 of the
+// resident block, columns 32db + c of the wave's slice) through a wave-private
+// LDS buffer of 32 x DS floats, one 32-row half at a time, so that the global
+// accesses are 16-byte chunks along rows: emit(qb, row, col, f32x4) is called
+// once per chunk. Every wave of the block must call it (it synchronises).
+template <int DS, int DB, typename Emit>
+__device__ __forceinline__ void store_acc(const f32x16 (&o)[2][DB], float* buf, int hh, int c, int lane, Emit&& emit) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    __syncthreads();
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) buf[(8 * (i >> 2) + 4 * hh + (i & 3)) * DS + 32 * db + c] = o[qb][db][i];
+    __syncthreads();
+    const f32x4* b4 = reinterpret_cast<const f32x4*>(buf);
+    for (int q = lane; q < 32 * DS / 4; q += 64) {
+      const int r = q / (DS / 4), c4 = q - r * (DS / 4);
+      emit(qb, r, 4 * c4, b4[q]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Fragment-major copy of 32-row tiles of X (rows X[idx[k]] when idx is given),
 // rows at or past `rows` (= *count_dev when given) zero. One block per tile:
@@ -549,8 +572,14 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) a[ks] = ld16(frag_ptr<KB>(hcf, t, w, ks, lane));
   };
+  // Per-token data of tile t, loaded into a register one phase before it is
+  // written to LDS (wave 0, lanes < 32), so the load latency stays hidden.
+  TokData tk;
+  auto load_tok = [&](int t) {
+    if (w == 0 && lane < BK) tk = tok[t * BK + lane];
+  };
   auto stage_tok = [&](int t) {
-    if (w == 0 && lane < BK) s_tok[t & 1][lane] = tok[t * BK + lane];
+    if (w == 0 && lane < BK) s_tok[t & 1][lane] = tk;
   };
   auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int buf, int t_next) {
     acc[0] = zero16();
@@ -616,7 +645,9 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
   f32x16 acc[2];
   f32x4 sf[2];
   if (n_tiles > 0) {
+    load_tok(0);
     stage_tok(0);
+    load_tok(min(1, n_tiles - 1));
     load_a(0, a);
     s_step(a, acc, 0, min(1, n_tiles - 1));
     write_part(acc);
@@ -653,6 +684,7 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
     write_part(acc);
     stage_tok(tn);
     __syncthreads();
+    load_tok(tnn);
     pv_reduce(t & 1, sf);
   }
 
@@ -670,24 +702,24 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
     if (to_acc) gb_acc[my_v] = (float)val;
     else gb_out[my_v] = (__bf16)(float)val;
   }
-  if (to_acc ? gW_acc == nullptr : gW_out == nullptr) return;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int v = q0 + 32 * qb + 8 * (i >> 2) + 4 * hh + (i & 3);
-      if (v < V) {
-        const int64_t base = (int64_t)v * H + d0 + c;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          float val = o[qb][db][i];
-          const int64_t k = base + 32 * db;
-          if (from_acc) val += gW_acc[k];
-          if (to_acc) gW_acc[k] = val;
-          else gW_out[k] = (__bf16)val;
-        }
-      }
-    }
+  if (to_acc ? gW_acc == nullptr : gW_out == nullptr) return;  // uniform: every wave returns
+  store_acc<DS, DB>(o, reinterpret_cast<float*>(&s_t[w][0][0]), hh, c, lane,
+                    [&](int qb, int r, int col, f32x4 v) {
+                      const int vr = q0 + 32 * qb + r;
+                      if (vr >= V) return;
+                      const int64_t k = (int64_t)vr * H + d0 + col;
+                      if (from_acc) v += *reinterpret_cast<const f32x4*>(gW_acc + k);
+                      if (to_acc) {
+                        *reinterpret_cast<f32x4*>(gW_acc + k) = v;
+                      } else {
+                        bf16x4 u;
+                        u[0] = (__bf16)v[0];
+                        u[1] = (__bf16)v[1];
+                        u[2] = (__bf16)v[2];
+                        u[3] = (__bf16)v[3];
+                        *reinterpret_cast<bf16x4*>(gW_out + k) = u;
+                      }
+                    });
 }
 
 template <int KB>
