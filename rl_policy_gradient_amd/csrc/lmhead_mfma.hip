@@ -150,37 +150,31 @@ __device__ __forceinline__ void store_acc(const f32x16 (&o)[2][DB], float* buf, 
 
 // ---------------------------------------------------------------------------
 // Fragment-major copy of 32-row tiles of X (rows X[idx[k]] when idx is given),
-// rows at or past `rows` (= *count_dev when given) zero. One block per tile:
-// coalesced row loads into LDS (rows padded by one 16-byte chunk so the
-// fragment-order reads spread over the banks), fragment-order stores.
+// rows at or past `rows` (= *count_dev when given) zero. One thread per output
+// chunk: the stores are contiguous; each wave's loads touch 32 rows, and
+// every source line is used whole by the waves of the block.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void frag_copy_kernel(const __bf16* __restrict__ X, const int* __restrict__ idx,
-                                                        const int* __restrict__ count_dev, int64_t rows_host, int H,
-                                                        __bf16* __restrict__ Xf) {
-  extern __shared__ uint4 smem_u4[];
+                                                               const int* __restrict__ count_dev, int64_t rows_host,
+                                                               int H, int64_t tiles, __bf16* __restrict__ Xf) {
   const int64_t rows = count_dev ? (int64_t)(*count_dev) : rows_host;
-  const int64_t t = blockIdx.x;
-  const int64_t r0 = t * BK;
-  if (count_dev && r0 >= rows) return;  // tiles past the gathered rows are never read (block-uniform)
-  const int cpr = H / 8;                // 16-byte chunks per row
-  const int rs = cpr + 1;               // padded LDS row stride in chunks
-  for (int e = threadIdx.x; e < BK * cpr; e += blockDim.x) {
-    const int r = e / cpr, cc = e - r * cpr;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r0 + r < rows) {
-      const int64_t src = idx ? (int64_t)idx[r0 + r] : r0 + r;
-      v = *reinterpret_cast<const uint4*>(X + src * H + cc * 8);
-    }
-    smem_u4[r * rs + cc] = v;
-  }
-  __syncthreads();
-  const int ks_per_wave = H / 64;  // 16-wide steps in a quarter of H
-  for (int o = threadIdx.x; o < BK * cpr; o += blockDim.x) {
-    const int lane = o & 63;
-    const int rem = o >> 6;          // (w * KS + ks)
+  const int cpr = H / 8;
+  // with a device row count, tiles past the last gathered row are never read
+  const int64_t used = count_dev ? min(tiles, (rows + BK - 1) / BK) : tiles;
+  const int64_t total = used * BK * cpr;
+  const int ks_per_wave = H / 64;
+  for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
+    const int64_t t = o / (BK * cpr);
+    const int oo = (int)(o - t * BK * cpr);
+    const int lane = oo & 63, rem = oo >> 6;
     const int w = rem / ks_per_wave, ks = rem - w * ks_per_wave;
-    const int chunk = w * (H / 32) + 2 * ks + (lane >> 5);
-    *reinterpret_cast<uint4*>(Xf + (t * BK * cpr + o) * 8) = smem_u4[(lane & 31) * rs + chunk];
+    const int64_t r = t * BK + (lane & 31);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rows) {
+      const int64_t src = idx ? (int64_t)idx[r] : r;
+      v = *reinterpret_cast<const uint4*>(X + src * H + (w * (H / 32) + 2 * ks + (lane >> 5)) * 8);
+    }
+    *reinterpret_cast<uint4*>(Xf + o * 8) = v;
   }
 }
 
@@ -761,8 +755,10 @@ hipError_t bwd_dispatch(const __bf16* Wf, const __bf16* b, const __bf16* hcf, co
 hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_dev, int64_t rows, int64_t tiles, int H,
                             __bf16* Xf, hipStream_t st) {
   if (tiles <= 0) return hipSuccess;
-  const size_t lds = (size_t)BK * (H / 8 + 1) * 16;
-  hipLaunchKernelGGL(frag_copy_kernel, dim3((unsigned)tiles), dim3(256), lds, st, X, idx, count_dev, rows, H, Xf);
+  const int64_t total = tiles * BK * (H / 8);
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(frag_copy_kernel, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(256), 0, st, X, idx,
+                     count_dev, rows, H, tiles, Xf);
   return hipGetLastError();
 }
 

@@ -118,10 +118,12 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
   __syncthreads();
   if (vout) {
     const double inv_s = s_res[3];
+    const float* Orow = O + row * H;
+    const int64_t sstride = N * H;
     for (int d = threadIdx.x; d < H; d += NT) {
       double o = 0.0;
-      for (int j = 0; j < Sv; ++j)
-        if (s_c[j] != 0.0) o += s_c[j] * (double)O[((int64_t)j * N + row) * H + d];
+#pragma unroll 8
+      for (int j = 0; j < Sv; ++j) o += s_c[j] * (double)Orow[j * sstride + d];
       vout[row * H + d] = (float)((double)ldf<T>(W, yc * H + d) - o * inv_s);
     }
   }
