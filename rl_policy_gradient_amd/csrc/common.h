@@ -106,29 +106,25 @@ hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int 
                           const void* h, const void* W, const void* b, float inv_tau, const int64_t* y,
                           float* lp, float* ent, float* lse, float* vout, hipStream_t st);
 
-// Loss stage.
-hipError_t launch_loss_zero(LossAcc* acc, hipStream_t st);
+// Loss stage (per outer chunk): per-sequence partial sums, the per-sequence
+// merge (accumulators set on the first chunk; loss and metrics written on the
+// last, with the threshold from thr_dev or NaN), then per-token dL/dlogp with
+// per-32-token counts of nonzero gradients and grad_h = g / tau * v (gh and v
+// may be NULL), and the in-order compaction of the tokens with g != 0.
 hipError_t launch_loss_seq_partial(const LossParams& p, int64_t Bc, const float* lp, const float* old,
                                    const float* ref, const uint8_t* comp, const uint8_t* ratio,
                                    const uint8_t* emask, const float* adv, int St, SeqPart* part,
                                    hipStream_t st);
 hipError_t launch_loss_seq_final(const LossParams& p, int64_t Bc, int St, const SeqPart* part, const float* adv,
-                                 SeqCoef* coef, LossAcc* acc, hipStream_t st);
-hipError_t launch_loss_token_grad(const LossParams& p, int64_t Bc, const float* lp, const float* old,
-                                  const float* ref, const uint8_t* comp, const uint8_t* ratio,
-                                  const uint8_t* emask, const SeqCoef* coef, float* g, hipStream_t st);
-hipError_t launch_loss_finalize(const LossAcc* acc, int64_t B_total, float* loss, float* metrics,
-                                hipStream_t st);
-
-// grad_h = g / tau * v, cast to dtype.
-hipError_t launch_grad_h(int dtype, const float* g, const float* v, int64_t N, int H, float inv_tau,
-                         void* gh, hipStream_t st);
-
-// Token compaction for the weight-gradient sweep: idx of tokens with g != 0
-// in order, their count (device), and the per-token data.
+                                 SeqCoef* coef, LossAcc* acc, bool init, const float* thr_dev, float* loss_out,
+                                 float* metrics, hipStream_t st);
+hipError_t launch_loss_tokens(int dtype, const LossParams& p, int64_t Bc, const float* lp, const float* old,
+                              const float* ref, const uint8_t* comp, const uint8_t* ratio, const uint8_t* emask,
+                              const SeqCoef* coef, float* g, int* cnt32, const float* v, int H, float inv_tau,
+                              void* gh, hipStream_t st);
 size_t compact_scratch_bytes(int64_t N);
-hipError_t launch_compact(const float* g, const float* lse, const int64_t* y, int64_t N, float inv_tau,
-                          int* idx, TokData* tok, int* count_dev, void* scratch, hipStream_t st);
+hipError_t launch_compact_scatter(const float* g, const float* lse, const int64_t* y, int64_t N, float inv_tau,
+                                  const int* cnt32, int* idx, TokData* tok, int* count_dev, hipStream_t st);
 hipError_t launch_gather_rows(int dtype, const void* X, const int* idx, const int* count_dev, int64_t cap,
                               int H, void* Xc, hipStream_t st);
 
@@ -138,7 +134,7 @@ hipError_t launch_entropy_select(const float* ent, const uint8_t* active, int64_
                                  float* thr_dev, void* scratch, hipStream_t st);
 hipError_t launch_entropy_mask(const float* ent, const uint8_t* active, int64_t N, const float* thr_dev,
                                uint8_t* mask, hipStream_t st);
-hipError_t launch_store_thr(const float* thr_dev, LossAcc* acc, float* thr_out, hipStream_t st);
+hipError_t launch_store_thr(const float* thr_dev, float* thr_out, hipStream_t st);
 hipError_t launch_copy_mask(const uint8_t* src, int64_t N, uint8_t* dst, hipStream_t st);
 hipError_t launch_set_nan(float* dst, hipStream_t st);
 

@@ -170,17 +170,6 @@ __device__ __forceinline__ TokEval eval_tok(const LossParams& p, int64_t t, cons
   return e;
 }
 
-__global__ __launch_bounds__(NT) void zero_acc_kernel(LossAcc* acc) {
-  if (threadIdx.x == 0) {
-    acc->loss = 0.0;
-    acc->slr = 0.0;
-    acc->mkl = 0.0;
-    acc->n_active = acc->n_clip = acc->n_kept = acc->n_clipseq = 0ull;
-    acc->thr = __int_as_float(0x7fc00000);
-    acc->pad = 0;
-  }
-}
-
 // grid (Bc, St): partial sums of sequence i over token segment s.
 __global__ __launch_bounds__(NT) void seq_partial_kernel(LossParams p, const float* __restrict__ lp,
                                                          const float* __restrict__ old, const float* __restrict__ ref,
@@ -225,11 +214,16 @@ __global__ __launch_bounds__(NT) void seq_partial_kernel(LossParams p, const flo
 }
 
 // One block: per-sequence scalars (GMPO r_i, GSPO s_i), gradient
-// coefficients, loss and metric contributions of the chunk.
+// coefficients, loss and metric contributions of the chunk. The first chunk
+// (init) sets the batch accumulators instead of adding to them; the last one
+// (loss_out != NULL) also writes the loss and the metrics, with the entropy
+// threshold from thr_dev (NaN when NULL: the mask is off).
 __global__ __launch_bounds__(NT) void seq_final_kernel(LossParams p, int64_t Bc, int St,
                                                        const SeqPart* __restrict__ part,
                                                        const float* __restrict__ adv, SeqCoef* __restrict__ coef,
-                                                       LossAcc* __restrict__ acc) {
+                                                       LossAcc* __restrict__ acc, int init,
+                                                       const float* __restrict__ thr_dev, float* __restrict__ loss_out,
+                                                       float* __restrict__ metrics) {
   __shared__ double redd[NT];
   __shared__ unsigned long long redu[NT];
   double loss = 0.0, slr = 0.0, mkl = 0.0;
@@ -296,114 +290,121 @@ __global__ __launch_bounds__(NT) void seq_final_kernel(LossParams p, int64_t Bc,
   nk = block_sum(nk, redu);
   ncs = block_sum(ncs, redu);
   if (threadIdx.x == 0) {
-    acc->loss += loss;
-    acc->slr += slr;
-    acc->mkl += mkl;
-    acc->n_active += na;
-    acc->n_clip += nc;
-    acc->n_kept += nk;
-    acc->n_clipseq += ncs;
-  }
-}
-
-// g_t = dL/dlp_t. GMPO: pol on unclipped ratio tokens; GSPO-token: pol on
-// kept completion tokens; plus w beta (1 - e^{ref - lp}) on completion tokens.
-__global__ __launch_bounds__(NT) void token_grad_kernel(LossParams p, int64_t Nc, const float* __restrict__ lp,
-                                                        const float* __restrict__ old, const float* __restrict__ ref,
-                                                        const uint8_t* __restrict__ comp,
-                                                        const uint8_t* __restrict__ ratio,
-                                                        const uint8_t* __restrict__ emask,
-                                                        const SeqCoef* __restrict__ coef, float* __restrict__ g) {
-  for (int64_t t = (int64_t)blockIdx.x * NT + threadIdx.x; t < Nc; t += (int64_t)gridDim.x * NT) {
-    const int64_t i = t / p.T;
-    const SeqCoef c = coef[i];
-    const TokEval e = eval_tok(p, t, lp, old, ref, comp, ratio, emask, c.adv);
-    double gv = 0.0;
-    if (p.loss_type == 0) {
-      if (e.R && !e.clipped) gv = c.pol;
+    LossAcc a;
+    if (init) {
+      a.loss = loss;
+      a.slr = slr;
+      a.mkl = mkl;
+      a.n_active = na;
+      a.n_clip = nc;
+      a.n_kept = nk;
+      a.n_clipseq = ncs;
     } else {
-      if (e.M && e.E) gv = c.pol;
+      a = *acc;
+      a.loss += loss;
+      a.slr += slr;
+      a.mkl += mkl;
+      a.n_active += na;
+      a.n_clip += nc;
+      a.n_kept += nk;
+      a.n_clipseq += ncs;
     }
-    if (e.M) gv += c.wbeta * e.dkl;
-    g[t] = (float)gv;
+    a.thr = 0.f;
+    a.pad = 0;
+    *acc = a;
+    if (loss_out) {
+      loss_out[0] = (float)a.loss;
+      const float den = (float)(a.n_active > 0 ? a.n_active : 1ull);
+      metrics[0] = (float)a.n_clip / den;
+      metrics[1] = (float)(a.slr / (double)p.B_total);
+      metrics[2] = (float)((double)a.n_clipseq / (double)p.B_total);
+      metrics[3] = (float)(a.mkl / (double)p.B_total);
+      metrics[4] = thr_dev ? *thr_dev : __int_as_float(0x7fc00000);
+      metrics[5] = a.n_active > 0 ? (float)a.n_kept / den : 0.f;
+      metrics[6] = (float)a.n_active;
+      metrics[7] = (float)a.n_clip;
+    }
   }
 }
 
-__global__ void finalize_kernel(const LossAcc* __restrict__ acc, int64_t B_total, float* __restrict__ loss,
-                                float* __restrict__ metrics) {
-  if (threadIdx.x != 0) return;
-  const LossAcc a = *acc;
-  loss[0] = (float)a.loss;
-  const float den = (float)(a.n_active > 0 ? a.n_active : 1ull);
-  metrics[0] = (float)a.n_clip / den;
-  metrics[1] = (float)(a.slr / (double)B_total);
-  metrics[2] = (float)((double)a.n_clipseq / (double)B_total);
-  metrics[3] = (float)(a.mkl / (double)B_total);
-  metrics[4] = a.thr;
-  metrics[5] = a.n_active > 0 ? (float)a.n_kept / den : 0.f;
-  metrics[6] = (float)a.n_active;
-  metrics[7] = (float)a.n_clip;
-}
+// Per 32-token block: g_t = dL/dlp_t (GMPO: pol on unclipped ratio tokens;
+// GSPO-token: pol on kept completion tokens; plus w beta (1 - e^{ref - lp})
+// on completion tokens), the block's count of g != 0 (cnt32, when given) and,
+// when gh is given, grad_h = (g / tau) v for its rows.
+constexpr int TB = 32;  // tokens per block of the token kernel
 
-// ---------------------------------------------------------------------------
-// grad_h = (g / tau) v
-// ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(NT) void grad_h_kernel(const float* __restrict__ g, const float* __restrict__ v,
-                                                    int64_t N, int H, float inv_tau, T* __restrict__ gh) {
-  const int64_t total = N * H;
-  for (int64_t k = ((int64_t)blockIdx.x * NT + threadIdx.x) * 4; k < total; k += (int64_t)gridDim.x * NT * 4) {
-    if (k + 3 < total && (H % 4) == 0) {
-      const float s = g[k / H] * inv_tau;
-      const float4 x = *reinterpret_cast<const float4*>(v + k);
-      gh[k] = (T)(s * x.x);
-      gh[k + 1] = (T)(s * x.y);
-      gh[k + 2] = (T)(s * x.z);
-      gh[k + 3] = (T)(s * x.w);
-    } else {
-      for (int64_t e = k; e < min(total, k + 4); ++e) gh[e] = (T)(g[e / H] * inv_tau * v[e]);
+__global__ __launch_bounds__(NT) void token_kernel(LossParams p, int64_t Nc, const float* __restrict__ lp,
+                                                   const float* __restrict__ old, const float* __restrict__ ref,
+                                                   const uint8_t* __restrict__ comp, const uint8_t* __restrict__ ratio,
+                                                   const uint8_t* __restrict__ emask,
+                                                   const SeqCoef* __restrict__ coef, float* __restrict__ g,
+                                                   int* __restrict__ cnt32, const float* __restrict__ v, int H,
+                                                   float inv_tau, T* __restrict__ gh) {
+  __shared__ float s_g[TB];
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  if (threadIdx.x < TB) {
+    const int64_t t = t0 + threadIdx.x;
+    float gv32 = 0.f;
+    if (t < Nc) {
+      const int64_t i = t / p.T;
+      const SeqCoef c = coef[i];
+      const TokEval e = eval_tok(p, t, lp, old, ref, comp, ratio, emask, c.adv);
+      double gv = 0.0;
+      if (p.loss_type == 0) {
+        if (e.R && !e.clipped) gv = c.pol;
+      } else {
+        if (e.M && e.E) gv = c.pol;
+      }
+      if (e.M) gv += c.wbeta * e.dkl;
+      gv32 = (float)gv;
+      g[t] = gv32;
     }
+    s_g[threadIdx.x] = gv32;
+    if (cnt32) {
+      const unsigned long long m = __ballot(gv32 != 0.f);
+      if (threadIdx.x == 0) cnt32[blockIdx.x] = __popcll(m);
+    }
+  }
+  if (gh == nullptr) return;  // uniform
+  __syncthreads();
+  const int rows = (int)min((int64_t)TB, Nc - t0);
+  const int64_t base = t0 * H;
+  if ((H & 3) == 0) {
+    for (int e = threadIdx.x * 4; e < rows * H; e += NT * 4) {
+      const int r = e / H;
+      const float sc = s_g[r] * inv_tau;
+      const float4 x = *reinterpret_cast<const float4*>(v + base + e);
+      gh[base + e] = (T)(sc * x.x);
+      gh[base + e + 1] = (T)(sc * x.y);
+      gh[base + e + 2] = (T)(sc * x.z);
+      gh[base + e + 3] = (T)(sc * x.w);
+    }
+  } else {
+    for (int e = threadIdx.x; e < rows * H; e += NT) gh[base + e] = (T)(s_g[e / H] * inv_tau * v[base + e]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Token compaction: tokens with g != 0, in order.
 // ---------------------------------------------------------------------------
-constexpr int CB = 1024;  // tokens per compaction block
+constexpr int CB = 1024;  // tokens per compaction block (32 token-kernel blocks)
 
-__global__ __launch_bounds__(NT) void compact_count_kernel(const float* __restrict__ g, int64_t N,
-                                                           int* __restrict__ cnt) {
-  __shared__ int red[NT];
-  const int64_t base = (int64_t)blockIdx.x * CB;
-  int c = 0;
-  for (int k = threadIdx.x; k < CB; k += NT) {
-    const int64_t t = base + k;
-    c += (t < N && g[t] != 0.f) ? 1 : 0;
-  }
-  c = block_sum(c, red);
-  if (threadIdx.x == 0) cnt[blockIdx.x] = c;
-}
-
-__global__ __launch_bounds__(NT) void compact_scan_kernel(const int* __restrict__ cnt, int nb, int* __restrict__ off,
-                                                          int* __restrict__ total) {
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int b = 0; b < nb; ++b) {
-      off[b] = run;
-      run += cnt[b];
-    }
-    *total = run;
-  }
-}
-
+// Each block sums the g != 0 counts of the 32-token blocks before it (fixed
+// order), then each thread owns CB/NT = 4 consecutive tokens; an exclusive
+// scan of the per-thread counts gives every kept token its slot. The last
+// block writes the total.
 __global__ __launch_bounds__(NT) void compact_scatter_kernel(const float* __restrict__ g, const float* __restrict__ lse,
                                                              const int64_t* __restrict__ y, int64_t N, float inv_tau,
-                                                             const int* __restrict__ off, int* __restrict__ idx,
-                                                             TokData* __restrict__ tok) {
-  // Each thread owns CB/NT = 4 consecutive tokens; an exclusive scan of the
-  // per-thread counts (fixed order) gives every kept token its slot.
+                                                             const int* __restrict__ cnt32, int* __restrict__ idx,
+                                                             TokData* __restrict__ tok, int* __restrict__ total) {
   __shared__ int sc[NT];
+  __shared__ int red[NT];
   constexpr int PER = CB / NT;
+  const int nprev = blockIdx.x * (CB / TB);
+  int pre = 0;
+  for (int k = threadIdx.x; k < nprev; k += NT) pre += cnt32[k];
+  pre = block_sum(pre, red);
   const int64_t base = (int64_t)blockIdx.x * CB + (int64_t)threadIdx.x * PER;
   int c = 0;
   bool f[PER];
@@ -421,7 +422,8 @@ __global__ __launch_bounds__(NT) void compact_scatter_kernel(const float* __rest
     sc[threadIdx.x] += v;
     __syncthreads();
   }
-  int pos = off[blockIdx.x] + sc[threadIdx.x] - c;
+  int pos = pre + sc[threadIdx.x] - c;
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == NT - 1) *total = pre + sc[NT - 1];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     if (f[k]) {
@@ -538,12 +540,8 @@ __global__ __launch_bounds__(NT) void mask_kernel(const float* __restrict__ ent,
     mask[t] = (active[t] != 0 && ent[t] >= thr) ? 1 : 0;
 }
 
-__global__ void store_thr_kernel(const float* __restrict__ thr_dev, LossAcc* __restrict__ acc,
-                                 float* __restrict__ thr_out) {
-  if (threadIdx.x == 0) {
-    if (acc) acc->thr = *thr_dev;
-    if (thr_out) *thr_out = *thr_dev;
-  }
+__global__ void store_thr_kernel(const float* __restrict__ thr_dev, float* __restrict__ thr_out) {
+  if (threadIdx.x == 0) *thr_out = *thr_dev;
 }
 
 __global__ __launch_bounds__(NT) void copy_mask_kernel(const uint8_t* __restrict__ src, int64_t N,
@@ -579,11 +577,6 @@ hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int 
   return hipGetLastError();
 }
 
-hipError_t launch_loss_zero(LossAcc* acc, hipStream_t st) {
-  hipLaunchKernelGGL(zero_acc_kernel, dim3(1), dim3(64), 0, st, acc);
-  return hipGetLastError();
-}
-
 hipError_t launch_loss_seq_partial(const LossParams& p, int64_t Bc, const float* lp, const float* old,
                                    const float* ref, const uint8_t* comp, const uint8_t* ratio,
                                    const uint8_t* emask, const float* adv, int St, SeqPart* part,
@@ -594,49 +587,35 @@ hipError_t launch_loss_seq_partial(const LossParams& p, int64_t Bc, const float*
 }
 
 hipError_t launch_loss_seq_final(const LossParams& p, int64_t Bc, int St, const SeqPart* part, const float* adv,
-                                 SeqCoef* coef, LossAcc* acc, hipStream_t st) {
-  hipLaunchKernelGGL(seq_final_kernel, dim3(1), dim3(NT), 0, st, p, Bc, St, part, adv, coef, acc);
+                                 SeqCoef* coef, LossAcc* acc, bool init, const float* thr_dev, float* loss_out,
+                                 float* metrics, hipStream_t st) {
+  hipLaunchKernelGGL(seq_final_kernel, dim3(1), dim3(NT), 0, st, p, Bc, St, part, adv, coef, acc, init ? 1 : 0,
+                     thr_dev, loss_out, metrics);
   return hipGetLastError();
 }
 
-hipError_t launch_loss_token_grad(const LossParams& p, int64_t Bc, const float* lp, const float* old,
-                                  const float* ref, const uint8_t* comp, const uint8_t* ratio,
-                                  const uint8_t* emask, const SeqCoef* coef, float* g, hipStream_t st) {
+hipError_t launch_loss_tokens(int dtype, const LossParams& p, int64_t Bc, const float* lp, const float* old,
+                              const float* ref, const uint8_t* comp, const uint8_t* ratio, const uint8_t* emask,
+                              const SeqCoef* coef, float* g, int* cnt32, const float* v, int H, float inv_tau,
+                              void* gh, hipStream_t st) {
   const int64_t Nc = Bc * p.T;
-  hipLaunchKernelGGL(token_grad_kernel, dim3(grid_for(Nc, NT)), dim3(NT), 0, st, p, Nc, lp, old, ref, comp, ratio,
-                     emask, coef, g);
-  return hipGetLastError();
-}
-
-hipError_t launch_loss_finalize(const LossAcc* acc, int64_t B_total, float* loss, float* metrics, hipStream_t st) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(64), 0, st, acc, B_total, loss, metrics);
-  return hipGetLastError();
-}
-
-hipError_t launch_grad_h(int dtype, const float* g, const float* v, int64_t N, int H, float inv_tau, void* gh,
-                         hipStream_t st) {
-  const unsigned grid = grid_for(N * H, NT * 4 * 4);
+  const unsigned grid = (unsigned)((Nc + TB - 1) / TB);
   if (dtype == 0)
-    hipLaunchKernelGGL((grad_h_kernel<float>), dim3(grid), dim3(NT), 0, st, g, v, N, H, inv_tau, (float*)gh);
+    hipLaunchKernelGGL((token_kernel<float>), dim3(grid), dim3(NT), 0, st, p, Nc, lp, old, ref, comp, ratio, emask,
+                       coef, g, cnt32, v, H, inv_tau, (float*)gh);
   else
-    hipLaunchKernelGGL((grad_h_kernel<__bf16>), dim3(grid), dim3(NT), 0, st, g, v, N, H, inv_tau, (__bf16*)gh);
+    hipLaunchKernelGGL((token_kernel<__bf16>), dim3(grid), dim3(NT), 0, st, p, Nc, lp, old, ref, comp, ratio, emask,
+                       coef, g, cnt32, v, H, inv_tau, (__bf16*)gh);
   return hipGetLastError();
 }
 
-size_t compact_scratch_bytes(int64_t N) {
-  const int64_t nb = (N + CB - 1) / CB;
-  return (size_t)(2 * nb) * sizeof(int);
-}
+size_t compact_scratch_bytes(int64_t N) { return (size_t)((N + TB - 1) / TB) * sizeof(int); }
 
-hipError_t launch_compact(const float* g, const float* lse, const int64_t* y, int64_t N, float inv_tau, int* idx,
-                          TokData* tok, int* count_dev, void* scratch, hipStream_t st) {
+hipError_t launch_compact_scatter(const float* g, const float* lse, const int64_t* y, int64_t N, float inv_tau,
+                                  const int* cnt32, int* idx, TokData* tok, int* count_dev, hipStream_t st) {
   const int64_t nb = (N + CB - 1) / CB;
-  int* cnt = (int*)scratch;
-  int* off = cnt + nb;
-  hipLaunchKernelGGL(compact_count_kernel, dim3((unsigned)nb), dim3(NT), 0, st, g, N, cnt);
-  hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(64), 0, st, cnt, (int)nb, off, count_dev);
-  hipLaunchKernelGGL(compact_scatter_kernel, dim3((unsigned)nb), dim3(NT), 0, st, g, lse, y, N, inv_tau, off, idx,
-                     tok);
+  hipLaunchKernelGGL(compact_scatter_kernel, dim3((unsigned)nb), dim3(NT), 0, st, g, lse, y, N, inv_tau, cnt32, idx,
+                     tok, count_dev);
   return hipGetLastError();
 }
 
@@ -667,8 +646,8 @@ hipError_t launch_entropy_mask(const float* ent, const uint8_t* active, int64_t 
   return hipGetLastError();
 }
 
-hipError_t launch_store_thr(const float* thr_dev, LossAcc* acc, float* thr_out, hipStream_t st) {
-  hipLaunchKernelGGL(store_thr_kernel, dim3(1), dim3(64), 0, st, thr_dev, acc, thr_out);
+hipError_t launch_store_thr(const float* thr_dev, float* thr_out, hipStream_t st) {
+  hipLaunchKernelGGL(store_thr_kernel, dim3(1), dim3(64), 0, st, thr_dev, thr_out);
   return hipGetLastError();
 }
 

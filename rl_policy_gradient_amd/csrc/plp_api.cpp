@@ -358,7 +358,6 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
   const float inv_tau = (float)(1.0 / a->temperature);
   const LossParams lpar = loss_params(a);
 
-  HIP_TRY(launch_loss_zero(b.acc, st));
   if (p.mfma)
     HIP_TRY(launch_frag_copy((const __bf16*)a->weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H, b.Wf, st));
 
@@ -378,7 +377,6 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
     HIP_TRY(launch_entropy_select(b.ent, a->completion_mask, p.N, (float)(1.0 - a->top_entropy_quantile), b.thr,
                                   nullptr, st));
     HIP_TRY(launch_entropy_mask(b.ent, a->completion_mask, p.N, b.thr, b.emask, st));
-    HIP_TRY(launch_store_thr(b.thr, b.acc, nullptr, st));
   }
 
   for (int64_t c = 0; c < p.nchunks; ++c) {
@@ -395,13 +393,16 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
     const uint8_t* em = b.emask ? b.emask + r0 : nullptr;
     const float* adv = a->advantages + s0;
     HIP_TRY(launch_loss_seq_partial(lpar, bc, b.lp + r0, old, ref, comp, ratio, em, adv, p.St, b.part, st));
-    HIP_TRY(launch_loss_seq_final(lpar, bc, p.St, b.part, adv, b.coef, b.acc, st));
+    const bool last = c == p.nchunks - 1;
+    HIP_TRY(launch_loss_seq_final(lpar, bc, p.St, b.part, adv, b.coef, b.acc, c == 0, p.entropy ? b.thr : nullptr,
+                                  last ? out->loss : nullptr, last ? out->metrics : nullptr, st));
     float* g = out->dlogp_out ? out->dlogp_out + r0 : b.g;
-    HIP_TRY(launch_loss_token_grad(lpar, bc, b.lp + r0, old, ref, comp, ratio, em, b.coef, g, st));
-    if (p.need_o)
-      HIP_TRY(launch_grad_h(a->dtype, g, b.v, n, H, inv_tau, (char*)out->grad_hidden + (size_t)r0 * H * es, st));
+    int* cnt32 = p.need_gw ? (int*)b.cscratch : nullptr;
+    HIP_TRY(launch_loss_tokens(a->dtype, lpar, bc, b.lp + r0, old, ref, comp, ratio, em, b.coef, g, cnt32,
+                               p.need_o ? b.v : nullptr, H, inv_tau,
+                               p.need_o ? (char*)out->grad_hidden + (size_t)r0 * H * es : nullptr, st));
     if (p.need_gw) {
-      HIP_TRY(launch_compact(g, b.lse + r0, a->targets + r0, n, inv_tau, b.idx, b.tok, b.count, b.cscratch, st));
+      HIP_TRY(launch_compact_scatter(g, b.lse + r0, a->targets + r0, n, inv_tau, cnt32, b.idx, b.tok, b.count, st));
       const char* hsrc = (const char*)a->hidden + (size_t)r0 * H * es;
       if (p.mfma)
         HIP_TRY(launch_frag_copy((const __bf16*)hsrc, b.idx, b.count, n, p.cap / kBK, H, (__bf16*)b.hc, st));
@@ -419,7 +420,6 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
                                    b.gb_acc, out->grad_weight, out->grad_bias, st));
     }
   }
-  HIP_TRY(launch_loss_finalize(b.acc, p.B, out->loss, out->metrics, st));
   if (out->logp_out) HIP_TRY(hipMemcpyAsync(out->logp_out, b.lp, p.N * sizeof(float), hipMemcpyDeviceToDevice, st));
   if (out->entropy_out)
     HIP_TRY(hipMemcpyAsync(out->entropy_out, b.ent, p.N * sizeof(float), hipMemcpyDeviceToDevice, st));
@@ -496,7 +496,7 @@ PLP_API int plp_entropy_quantile_mask(const float* entropy, const uint8_t* activ
   }
   HIP_TRY(launch_entropy_select(entropy, active, N, (float)(1.0 - q), thr, nullptr, st));
   if (N > 0) HIP_TRY(launch_entropy_mask(entropy, active, N, thr, mask_out, st));
-  if (threshold_out) HIP_TRY(launch_store_thr(thr, nullptr, threshold_out, st));
+  if (threshold_out) HIP_TRY(launch_store_thr(thr, threshold_out, st));
   return ok();
 }
 
@@ -541,20 +541,18 @@ PLP_API int plp_policy_loss_from_logprobs(const plp_args* a, const float* logp, 
   LossAcc* acc = c.take<LossAcc>(1);
   float* thr = c.take<float>(1);
   const LossParams lpar = loss_params(a);
-  HIP_TRY(launch_loss_zero(acc, st));
   if (q_on) {
     HIP_TRY(launch_entropy_select(entropy, a->completion_mask, N, (float)(1.0 - a->top_entropy_quantile), thr, nullptr, st));
     HIP_TRY(launch_entropy_mask(entropy, a->completion_mask, N, thr, emask, st));
-    HIP_TRY(launch_store_thr(thr, acc, nullptr, st));
   }
   const uint8_t* em = q_on ? emask : nullptr;
   HIP_TRY(launch_loss_seq_partial(lpar, a->B, logp, a->old_logp, a->ref_logp, a->completion_mask, a->ratio_mask, em,
                                   a->advantages, St, part, st));
-  HIP_TRY(launch_loss_seq_final(lpar, a->B, St, part, a->advantages, coef, acc, st));
+  HIP_TRY(launch_loss_seq_final(lpar, a->B, St, part, a->advantages, coef, acc, true, q_on ? thr : nullptr, out->loss,
+                                out->metrics, st));
   float* g = out->dlogp_out ? out->dlogp_out : gbuf;
-  HIP_TRY(launch_loss_token_grad(lpar, a->B, logp, a->old_logp, a->ref_logp, a->completion_mask, a->ratio_mask, em,
-                                 coef, g, st));
-  HIP_TRY(launch_loss_finalize(acc, a->B, out->loss, out->metrics, st));
+  HIP_TRY(launch_loss_tokens(PLP_DTYPE_F32, lpar, a->B, logp, a->old_logp, a->ref_logp, a->completion_mask,
+                             a->ratio_mask, em, coef, g, nullptr, nullptr, 0, 1.0f, nullptr, st));
   if (out->entropy_mask_out) HIP_TRY(launch_copy_mask(q_on ? emask : a->completion_mask, N, out->entropy_mask_out, st));
   return ok();
 }
