@@ -308,13 +308,11 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   // issued, is staged for the transposing load (WITH_O) and reloaded with
   // the same slice of tile `t_next`.
   auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int buf, int t_next) {
-    acc[0] = zero16();
-    acc[1] = zero16();
     const __bf16* src = frag_ptr<KB>(Wf, t_next, w, 0, lane);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a[ks], q[nb][ks], acc[nb]);
+      for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a[ks], q[nb][ks], ks == 0 ? zero16() : acc[nb]);
       if constexpr (WITH_O)
         *reinterpret_cast<bf16x8*>(&s_t[w][buf][sw_base[ks & 1] + 16 * ks]) = a[ks];
       a[ks] = ld16(src + 512 * ks);
@@ -576,13 +574,11 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
     if (w == 0 && lane < BK) s_tok[t & 1][lane] = tk;
   };
   auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int buf, int t_next) {
-    acc[0] = zero16();
-    acc[1] = zero16();
     const __bf16* src = frag_ptr<KB>(hcf, t_next, w, 0, lane);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a[ks], q[nb][ks], acc[nb]);
+      for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a[ks], q[nb][ks], ks == 0 ? zero16() : acc[nb]);
       *reinterpret_cast<bf16x8*>(&s_t[w][buf][sw_base[ks & 1] + 16 * ks]) = a[ks];
       a[ks] = ld16(src + 512 * ks);
     }
