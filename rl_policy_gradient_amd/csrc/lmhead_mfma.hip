@@ -63,6 +63,8 @@ constexpr double kLn2 = 0.693147180559945309417;
 constexpr float kRefSlack2 = kRefSlack * kLog2e;  // the slack in base-2 units
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -77,6 +79,13 @@ __device__ __forceinline__ f32x16 zero16() {
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
   return z;
 }
+
+// Workgroup execution barrier without a memory fence. It orders the
+// exchange writes after the previous tile's exchange reads: every wave has
+// already consumed the values it read (they fed its MFMAs and epilogue), so
+// no LDS access of another wave is outstanding on those buffers, and the
+// wave's own stage writes, which only it reads back, need not drain first.
+__device__ __forceinline__ void exec_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Tile row held in element e (0..7) by lane half h of the wave that owns
 // tile-row half kh after the reduce (see the header comment).
@@ -172,7 +181,9 @@ __global__ __launch_bounds__(256) void frag_copy_kernel(const __bf16* __restrict
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (r < rows) {
       const int64_t src = idx ? (int64_t)idx[r] : r;
-      v = *reinterpret_cast<const uint4*>(X + src * H + (w * (H / 32) + 2 * ks + (lane >> 5)) * 8);
+      // each source row is read once: stream it past the caches
+      v = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                        reinterpret_cast<const u32x4*>(X + src * H + (w * (H / 32) + 2 * ks + (lane >> 5)) * 8)));
     }
     *reinterpret_cast<uint4*>(Xf + o * 8) = v;
   }
@@ -441,7 +452,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
     // ---- logits of tile t+1 on the matrix cores, stage t+1, load t+2 -------
     s_step(a, acc, (t + 1) & 1, tnn);
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    exec_barrier();
     if constexpr (WITH_O) s_p[w][lane] = pa;
     write_part(acc);
     __syncthreads();
@@ -669,7 +680,7 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
     // ---- logits of tile t+1, stage t+1, load t+2 ---------------------------
     s_step(a, acc, (t + 1) & 1, tnn);
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    exec_barrier();
     s_p[w][lane] = pa;
     write_part(acc);
     stage_tok(tn);
@@ -707,7 +718,8 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
                         u[1] = (__bf16)v[1];
                         u[2] = (__bf16)v[2];
                         u[3] = (__bf16)v[3];
-                        *reinterpret_cast<bf16x4*>(gW_out + k) = u;
+                        // written once, read by nobody in this call: stream past the caches
+                        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, u), reinterpret_cast<u32x2*>(gW_out + k));
                       }
                     });
 }
