@@ -15,6 +15,9 @@ Sources it follows (the pages):
     before the KL penalty.
   * Tinker "GSPO" page, the sequence ratio, the GSPO-token ratio and the GSPO
     objective equations, and "Choosing clipping thresholds".
+  * The token-level clipped losses GRPO, BNPO and DAPO, which Liger PR #1558
+    (Testing) and PR #1320 (Testing) name without printing them: the Tinker
+    page's clipped objective with a per-token ratio (readings R15-R17).
 
 Every function in ``core`` states the passage it follows and, where the pages
 are silent, the reading it takes.
@@ -30,6 +33,13 @@ from .core import (  # noqa: F401
     grad_w_rows,
     run,
     finalize_metrics,
+    token_normaliser,
     LossConfig,
     METRIC_NAMES,
+    GMPO,
+    GSPO_TOKEN,
+    GRPO,
+    BNPO,
+    DAPO,
+    PPO_CLIP_LOSSES,
 )

@@ -41,6 +41,20 @@ Readings taken where the pages are silent (each also listed in the design doc):
       token gives an all-false mask and a NaN threshold. q = 1 turns the mask
       off entirely.
   R10 old_logp absent means on-policy (lr = 0); ratio_mask absent means R = M.
+  R15 GRPO, BNPO and DAPO (named as loss types by Liger PR #1558, Testing,
+      and PR #1320, Testing; their formulas are not printed): the token-level
+      clipped surrogate of the Tinker GSPO page's objective with the token
+      ratio rho_t = exp(lr_t) in place of the sequence ratio,
+      policy_t = -min(rho_t A_i, clip(rho_t, 1-eps_low, 1+eps_high) A_i),
+      over the completion tokens M (the ratio mask plays no part).
+  R16 Their normalisations: GRPO the per-sample reduction of R5; BNPO the sum
+      over every completion token of the batch divided by the number of those
+      tokens; DAPO the same sum divided by a caller-given global token count
+      (for gradient accumulation over several calls), defaulting to the
+      batch's own count, where it equals BNPO.
+  R17 Their clip predicate is decided on exp(lr32) in fp64 against
+      fp32(1-eps_low) and fp32(1+eps_high); a clipped token takes the bound's
+      value and no gradient.
 """
 from __future__ import annotations
 
@@ -63,6 +77,10 @@ METRIC_NAMES = (
 
 GMPO = "gmpo"
 GSPO_TOKEN = "gspo_token"
+GRPO = "grpo"
+BNPO = "bnpo"
+DAPO = "dapo"
+PPO_CLIP_LOSSES = (GRPO, BNPO, DAPO)
 
 
 @dataclass(frozen=True)
@@ -75,15 +93,17 @@ class LossConfig:
     beta: float = 0.0
     temperature: float = 1.0
     top_entropy_quantile: float = 1.0
-    reduction: str = "seq_mean"      # "seq_mean" (per-sample) or "token_sum"
+    reduction: str = "seq_mean"      # "seq_mean" (per-sample) or "token_sum"; GMPO / GSPO only
     chunk_sequences: int = 0         # 0 = whole batch
+    global_tokens: int = 0           # DAPO normaliser; 0 = the batch's completion tokens
 
     @staticmethod
     def from_spec(spec) -> "LossConfig":
         return LossConfig(B=spec.B, T=spec.T, loss_type=spec.loss_type, eps_low=spec.eps_low,
                           eps_high=spec.eps_high, beta=spec.beta, temperature=spec.temperature,
                           top_entropy_quantile=spec.top_entropy_quantile,
-                          reduction=spec.reduction, chunk_sequences=spec.chunk_sequences)
+                          reduction=spec.reduction, chunk_sequences=spec.chunk_sequences,
+                          global_tokens=getattr(spec, "global_tokens", 0))
 
 
 # ---------------------------------------------------------------------------
@@ -186,13 +206,23 @@ def entropy_quantile_mask(H32, active, q: float):
 # Policy loss from per-token log-probs: GMPO, GSPO-token, K3 KL
 # ---------------------------------------------------------------------------
 
+def token_normaliser(cfg: LossConfig, completion_mask) -> int:
+    """BNPO / DAPO divisor (R16): the caller's global token count for DAPO
+    when given, else the number of completion tokens of the whole batch."""
+    if cfg.loss_type == DAPO and cfg.global_tokens > 0:
+        return int(cfg.global_tokens)
+    return max(1, int((np.asarray(completion_mask) != 0).sum()))
+
+
 def policy_loss(cfg: LossConfig, lp, old, ref, completion_mask, ratio_mask, advantages,
-                entropy_mask=None, seq_offset: int = 0, B_total: Optional[int] = None) -> dict:
+                entropy_mask=None, seq_offset: int = 0, B_total: Optional[int] = None,
+                tokens_total: Optional[int] = None) -> dict:
     """Loss, metrics and g = dL/dlp for a run of whole sequences.
 
     lp: fp64 (or fp32) [b*T]; old, ref: fp32 [b*T] or None; masks u8/bool
     [b*T]; advantages fp32 [b]; entropy_mask bool [b*T] or None (= all ones).
-    B_total is the batch size that divides the per-sample reduction (R5).
+    B_total is the batch size that divides the per-sample reduction (R5);
+    tokens_total the BNPO / DAPO divisor (R16; default: from this run).
 
     GMPO (Liger PR #1320): c_t clipped per R1; r_i = exp(mean_{R_i} c);
     per-token policy term -A_i r_i.  GSPO-token (Tinker GSPO page): sequence
@@ -216,7 +246,12 @@ def policy_loss(cfg: LossConfig, lp, old, ref, completion_mask, ratio_mask, adva
     A = np.asarray(advantages, np.float32).astype(np.float64).reshape(b)
     n = np.maximum(1, M.sum(axis=1)).astype(np.float64)
     nt = np.maximum(1, R.sum(axis=1)).astype(np.float64)
-    if cfg.reduction == "seq_mean":
+    if cfg.loss_type == GRPO:
+        w = 1.0 / (Bt * n)
+    elif cfg.loss_type in (BNPO, DAPO):
+        G = token_normaliser(cfg, M) if tokens_total is None else tokens_total
+        w = np.full(b, 1.0 / G)
+    elif cfg.reduction == "seq_mean":
         w = 1.0 / (Bt * n)
     elif cfg.reduction == "token_sum":
         w = np.ones(b)
@@ -253,10 +288,32 @@ def policy_loss(cfg: LossConfig, lp, old, ref, completion_mask, ratio_mask, adva
         clipped_tok = np.broadcast_to(clipped_seq[:, None], (b, T)) & M
         seq_ratio = s
         clipped_seq_any = (s < lo) | (s > hi)
+    elif cfg.loss_type in PPO_CLIP_LOSSES:
+        lo = np.float32(1.0 - cfg.eps_low)
+        hi = np.float32(1.0 + cfg.eps_high)
+        Ac = A[:, None]
+        with np.errstate(over="ignore"):
+            rho_pred = np.exp(lr32.astype(np.float64))      # R17
+            rho = np.exp(lr)
+        clip_hi = M & (Ac > 0) & (rho_pred > float(hi))
+        clip_lo = M & (Ac < 0) & (rho_pred < float(lo))
+        clipped_tok = clip_hi | clip_lo
+        live = (Ac != 0) & ~clipped_tok                      # A = 0: no term, no gradient (R2)
+        rho_l = np.where(live, rho, 0.0)
+        # -min(rho A, clip(rho, lo, hi) A): the bound where the clip binds
+        pol_ppo = np.where(clip_hi, -float(hi) * Ac, np.where(clip_lo, -float(lo) * Ac, -rho_l * Ac))
+        g_pol = np.where(e & M & live, -rho_l * Ac, 0.0)
+        with np.errstate(over="ignore"):
+            seq_ratio = np.exp(seq_log_ratio)
+        clipped_seq = np.zeros(b, bool)
+        clipped_seq_any = np.zeros(b, bool)
     else:
         raise ValueError(cfg.loss_type)
 
-    policy_tok = np.broadcast_to(policy_seq[:, None], (b, T))
+    if cfg.loss_type in PPO_CLIP_LOSSES:
+        policy_tok = pol_ppo
+    else:
+        policy_tok = np.broadcast_to(policy_seq[:, None], (b, T))
     if ref is not None:
         x = np.asarray(ref, np.float32).astype(np.float64).reshape(b, T) - lp
         kl = np.exp(x) - x - 1.0
@@ -408,6 +465,7 @@ def run(cfg: LossConfig, h, W, b, targets, old, ref, completion_mask, ratio_mask
     else:
         emask, thr = None, np.float32(np.nan)
     cs = cfg.chunk_sequences if cfg.chunk_sequences > 0 else B
+    G = token_normaliser(cfg, completion_mask)   # batch-global, like B (R16)
     parts = []
     g = np.zeros(B * T)
     for s0 in range(0, B, cs):
@@ -415,7 +473,8 @@ def run(cfg: LossConfig, h, W, b, targets, old, ref, completion_mask, ratio_mask
         sl = slice(s0 * T, s1 * T)
         p = policy_loss(cfg, lp[sl], None if old is None else old[sl], None if ref is None else ref[sl],
                         completion_mask[sl], None if ratio_mask is None else ratio_mask[sl],
-                        advantages[s0:s1], None if emask is None else emask[sl], B_total=B)
+                        advantages[s0:s1], None if emask is None else emask[sl], B_total=B,
+                        tokens_total=G)
         g[sl] = p["g"]
         parts.append(p)
     loss, metrics = finalize_metrics(parts, thr)
