@@ -57,7 +57,7 @@ extern "C" {
 #endif
 
 #define PLP_API __attribute__((visibility("default")))
-#define PLP_ABI_VERSION 1
+#define PLP_ABI_VERSION 2
 
 /* Return codes. */
 #define PLP_OK 0
@@ -68,26 +68,47 @@ extern "C" {
 
 typedef enum { PLP_DTYPE_F32 = 0, PLP_DTYPE_BF16 = 1 } plp_dtype;
 
-/* GMPO: Liger PR #1320. GSPO_TOKEN: Tinker GSPO page (GSPO-token variant). */
-typedef enum { PLP_LOSS_GMPO = 0, PLP_LOSS_GSPO_TOKEN = 1 } plp_loss_type;
+/* GMPO: Liger PR #1320. GSPO_TOKEN: Tinker GSPO page (GSPO-token variant).
+ * GRPO, BNPO, DAPO: the token-level clipped surrogate that Liger PR #1558
+ * (Testing) and PR #1320 (Testing) name as loss types without printing it,
+ * read as the Tinker GSPO page's objective with each token's own ratio
+ * rho_t = exp(lp_t - old_t): per completion token
+ * -min(rho_t A_i, clip(rho_t, 1-eps_low, 1+eps_high) A_i), a token held at a
+ * bound passing no gradient (the predicate is exp(fp32(lp - old)) in fp64
+ * against fp32(1-eps_low) and fp32(1+eps_high); ties are not clipped). They
+ * differ only in the divisor of the token sum: GRPO the per-sample reduction
+ * (masked mean per sequence, mean over B); BNPO the number of completion
+ * tokens of the batch; DAPO args->global_tokens when > 0 (a count over a
+ * larger accumulated batch), else the same as BNPO. The `reduction` field
+ * does not apply to them; the ratio mask plays no part. */
+typedef enum {
+  PLP_LOSS_GMPO = 0,
+  PLP_LOSS_GSPO_TOKEN = 1,
+  PLP_LOSS_GRPO = 2,
+  PLP_LOSS_BNPO = 3,
+  PLP_LOSS_DAPO = 4
+} plp_loss_type;
 
 /* Importance-sampling level. GMPO rejects SEQUENCE (PR #1320: it clips at
  * token level before the sequence aggregation); GSPO_TOKEN is inherently a
- * sequence-level ratio and takes SEQUENCE. */
+ * sequence-level ratio and takes SEQUENCE; GRPO, BNPO and DAPO take TOKEN
+ * (their sequence-level form is GSPO_TOKEN). */
 typedef enum { PLP_IS_TOKEN = 0, PLP_IS_SEQUENCE = 1 } plp_is_level;
 
 /* SEQ_MEAN: masked mean over each sequence's completion tokens, then the mean
  * over the B sequences (the per-sample reduction PR #1320 reuses).
- * TOKEN_SUM: plain sum over completion tokens (the Tinker page's loss:sum). */
+ * TOKEN_SUM: plain sum over completion tokens (the Tinker page's loss:sum).
+ * For GMPO and GSPO_TOKEN only. */
 typedef enum { PLP_REDUCE_SEQ_MEAN = 0, PLP_REDUCE_TOKEN_SUM = 1 } plp_reduction;
 
 /* Metrics layout (fp32, PLP_NUM_METRICS entries). */
 enum {
   PLP_M_CLIP_FRACTION = 0,        /* clipped completion tokens / completion tokens (GSPO: a
-                                     sequence's verdict counts for each of its tokens) */
+                                     sequence's verdict counts for each of its tokens; GRPO,
+                                     BNPO, DAPO: tokens whose ratio is held at a bound) */
   PLP_M_SEQ_LOG_RATIO_MEAN = 1,   /* mean over sequences of mean_{ratio tokens} (lp - old) */
   PLP_M_CLIPPED_SEQ_FRACTION = 2, /* GSPO: share of sequences whose ratio left the clip range
-                                     (either side); GMPO: 0 */
+                                     (either side); other loss types: 0 */
   PLP_M_MEAN_KL = 3,              /* mean over sequences of the masked-mean K3 KL (0 without ref) */
   PLP_M_ENTROPY_THRESHOLD = 4,    /* batch-global entropy threshold; NaN when q = 1 or no
                                      completion token */
@@ -98,7 +119,8 @@ enum {
 };
 
 /* Inputs of the fused call. Versioned by struct_size (set it to
- * sizeof(plp_args)); fields are only ever appended. */
+ * sizeof(plp_args)); fields are only ever appended, and a struct_size that
+ * ends before an appended field leaves that field at its default. */
 typedef struct plp_args {
   uint32_t struct_size;
   int32_t dtype;                /* plp_dtype of hidden, weight, bias and the gradients */
@@ -124,6 +146,9 @@ typedef struct plp_args {
   double temperature;           /* logits are divided by it (> 0) */
   double top_entropy_quantile;  /* q in [0,1]; 1 = no entropy mask */
   int64_t chunk_sequences;      /* outer chunk in whole sequences; 0 = all B at once */
+  /* ---- ABI version 2 ---- */
+  int64_t global_tokens;        /* DAPO divisor (>= 0); 0 = the batch's completion tokens.
+                                   Ignored by the other loss types. Default 0. */
 } plp_args;
 
 /* Outputs of the fused call. Every pointer except loss and metrics may be
@@ -160,8 +185,9 @@ PLP_API int plp_workspace_size(const plp_args* args, size_t* bytes);
  * threshold and the batch mean are global, so results do not depend on the
  * chunk size beyond rounding. Errors: PLP_E_INVALID (shapes, NULLs, q outside
  * [0,1], beta != 0 without ref_logp, temperature <= 0, negative eps or beta,
- * chunk_sequences < 0), PLP_E_UNSUPPORTED (GMPO with SEQUENCE importance
- * sampling; GSPO_TOKEN with TOKEN), PLP_E_WORKSPACE, PLP_E_HIP. */
+ * chunk_sequences < 0, global_tokens < 0), PLP_E_UNSUPPORTED (GMPO, GRPO,
+ * BNPO or DAPO with SEQUENCE importance sampling; GSPO_TOKEN with TOKEN),
+ * PLP_E_WORKSPACE, PLP_E_HIP. */
 PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* args, const plp_outputs* out,
                                                  void* workspace, size_t workspace_bytes,
                                                  hipStream_t stream);
@@ -191,7 +217,7 @@ PLP_API int plp_entropy_quantile_mask(const float* entropy, const uint8_t* activ
                                       size_t workspace_bytes, hipStream_t stream);
 
 /* The loss stage alone, from given per-token log-probs (the GMPO / GSPO-token
- * / K3 KL objective of the pages without the LM head). args: as for the fused
+ * / GRPO / BNPO / DAPO / K3 KL objective without the LM head). args: as for the fused
  * call; hidden, weight, bias and targets are ignored, H and V may be 0.
  * logp [N] fp32. entropy [N] fp32 is required iff top_entropy_quantile < 1.
  * out: loss and metrics required; dlogp_out and entropy_mask_out optional;

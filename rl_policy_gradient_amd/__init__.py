@@ -27,7 +27,8 @@ __all__ = [
     "PlpError",
 ]
 
-_LOSS = {"gmpo": _abi.LOSS_GMPO, "gspo_token": _abi.LOSS_GSPO_TOKEN}
+_LOSS = {"gmpo": _abi.LOSS_GMPO, "gspo_token": _abi.LOSS_GSPO_TOKEN, "grpo": _abi.LOSS_GRPO,
+         "bnpo": _abi.LOSS_BNPO, "dapo": _abi.LOSS_DAPO}
 _RED = {"seq_mean": _abi.REDUCE_SEQ_MEAN, "token_sum": _abi.REDUCE_TOKEN_SUM}
 
 
@@ -79,7 +80,7 @@ def _mask_u8(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
 
 def _fill_args(hidden, weight, bias, targets, old_logp, ref_logp, completion_mask, ratio_mask, advantages, B, T,
                loss_type, importance_sampling_level, reduction, epsilon_low, epsilon_high, beta, temperature,
-               top_entropy_quantile, chunk_sequences) -> _abi.PlpArgs:
+               top_entropy_quantile, chunk_sequences, global_tokens=0) -> _abi.PlpArgs:
     a = _abi.new_args()
     a.B, a.T = int(B), int(T)
     if hidden is not None:
@@ -100,6 +101,7 @@ def _fill_args(hidden, weight, bias, targets, old_logp, ref_logp, completion_mas
     a.beta, a.temperature = float(beta), float(temperature)
     a.top_entropy_quantile = float(top_entropy_quantile)
     a.chunk_sequences = int(chunk_sequences)
+    a.global_tokens = int(global_tokens)
     return a
 
 
@@ -128,11 +130,14 @@ def fused_lmhead_policy_loss_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor,
                                      importance_sampling_level: Optional[str] = None, reduction: str = "seq_mean",
                                      epsilon_low: float = 0.2, epsilon_high: float = 0.2, beta: float = 0.0,
                                      temperature: float = 1.0, top_entropy_quantile: float = 1.0,
-                                     chunk_sequences: int = 0, grad_hidden: bool = True, grad_weight: bool = True,
+                                     chunk_sequences: int = 0, global_tokens: int = 0,
+                                     grad_hidden: bool = True, grad_weight: bool = True,
                                      grad_bias: Optional[bool] = None, diagnostics: bool = False,
                                      workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
-    """Loss, metrics and gradients of the fused LM head + GMPO / GSPO-token
-    objective (plp_fused_lmhead_policy_loss_fwd_bwd). hidden: [B, T, H] or
+    """Loss, metrics and gradients of the fused LM head + GMPO / GSPO-token /
+    GRPO / BNPO / DAPO objective (plp_fused_lmhead_policy_loss_fwd_bwd);
+    global_tokens is DAPO's divisor (0 = the batch's completion tokens).
+    hidden: [B, T, H] or
     [B*T, H] (then pass B and T); weight [V, H]; targets int64 [B*T];
     masks bool/u8 [B*T]; advantages fp32 [B]. Returns a dict of tensors."""
     if hidden.dim() == 3:
@@ -154,7 +159,7 @@ def fused_lmhead_policy_loss_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor,
         grad_bias = bias is not None
     a = _fill_args(hidden, weight, bias, targets, old_logp, ref_logp, completion_mask, ratio_mask, advantages, B, T,
                    loss_type, importance_sampling_level, reduction, epsilon_low, epsilon_high, beta, temperature,
-                   top_entropy_quantile, chunk_sequences)
+                   top_entropy_quantile, chunk_sequences, global_tokens)
     L = _abi.lib()
     n = ctypes.c_size_t()
     _abi.check(L.plp_workspace_size(ctypes.byref(a), ctypes.byref(n)))
@@ -235,7 +240,7 @@ def policy_loss_from_logprobs(logp: torch.Tensor, completion_mask: torch.Tensor,
                               T: int, *, old_logp=None, ref_logp=None, ratio_mask=None, entropy=None,
                               loss_type: str = "gmpo", importance_sampling_level: Optional[str] = None,
                               reduction: str = "seq_mean", epsilon_low: float = 0.2, epsilon_high: float = 0.2,
-                              beta: float = 0.0, top_entropy_quantile: float = 1.0,
+                              beta: float = 0.0, top_entropy_quantile: float = 1.0, global_tokens: int = 0,
                               workspace: Optional[torch.Tensor] = None) -> dict:
     """The loss stage alone from per-token log-probs
     (plp_policy_loss_from_logprobs). Returns loss, metrics, dlogp and
@@ -248,7 +253,7 @@ def policy_loss_from_logprobs(logp: torch.Tensor, completion_mask: torch.Tensor,
     _check_vec(advantages, B, torch.float32, "advantages")
     a = _fill_args(None, None, None, None, old_logp, ref_logp, completion_mask, ratio_mask, advantages, B, T,
                    loss_type, importance_sampling_level, reduction, epsilon_low, epsilon_high, beta, 1.0,
-                   top_entropy_quantile, 0)
+                   top_entropy_quantile, 0, global_tokens)
     L = _abi.lib()
     n = ctypes.c_size_t()
     _abi.check(L.plp_policy_loss_workspace_size(ctypes.byref(a), ctypes.byref(n)))

@@ -16,7 +16,8 @@ PLP_E_WORKSPACE = -3
 PLP_E_HIP = -4
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
-LOSS_GMPO, LOSS_GSPO_TOKEN = 0, 1
+LOSS_GMPO, LOSS_GSPO_TOKEN, LOSS_GRPO, LOSS_BNPO, LOSS_DAPO = 0, 1, 2, 3, 4
+ABI_VERSION = 2
 IS_TOKEN, IS_SEQUENCE = 0, 1
 REDUCE_SEQ_MEAN, REDUCE_TOKEN_SUM = 0, 1
 
@@ -62,6 +63,7 @@ class PlpArgs(ctypes.Structure):
         ("temperature", ctypes.c_double),
         ("top_entropy_quantile", ctypes.c_double),
         ("chunk_sequences", ctypes.c_int64),
+        ("global_tokens", ctypes.c_int64),
     ]
 
 

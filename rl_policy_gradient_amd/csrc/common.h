@@ -62,12 +62,19 @@ struct SeqCoef {
 struct LossParams {
   int64_t B_total;     // batch size dividing the per-sample reduction
   int64_t T;
-  int loss_type;       // 0 GMPO, 1 GSPO_TOKEN
-  int reduction;       // 0 seq mean, 1 token sum
+  int loss_type;       // plp_loss_type: 0 GMPO, 1 GSPO_TOKEN, 2 GRPO, 3 BNPO, 4 DAPO
+  int reduction;       // GMPO / GSPO: 0 seq mean, 1 token sum
   float eh32, el32;    // fp32(eps_high), fp32(eps_low)
-  float lo32, hi32;    // GSPO ratio bounds fp32(1-eps_low), fp32(1+eps_high)
+  float lo32, hi32;    // ratio bounds fp32(1-eps_low), fp32(1+eps_high) (GSPO and the token-clip losses)
   double beta;
+  int64_t norm_tokens; // BNPO / DAPO divisor when > 0 (DAPO's global count)
+  const unsigned long long* ntok_dev;  // else: the batch's completion-token count (device)
 };
+
+// Token-level clipped losses (GRPO, BNPO, DAPO) share the per-token path.
+__host__ __device__ inline bool token_clip_loss(int loss_type) { return loss_type >= 2; }
+// Losses whose divisor is a token count rather than per-sample.
+__host__ __device__ inline bool token_mean_loss(int loss_type) { return loss_type == 3 || loss_type == 4; }
 
 // ---------------------------------------------------------------------------
 // Launchers (each enqueues on `st`; return hipError_t of the launch)
@@ -135,6 +142,8 @@ hipError_t launch_entropy_select(const float* ent, const uint8_t* active, int64_
 hipError_t launch_entropy_mask(const float* ent, const uint8_t* active, int64_t N, const float* thr_dev,
                                uint8_t* mask, hipStream_t st);
 hipError_t launch_store_thr(const float* thr_dev, float* thr_out, hipStream_t st);
+// Number of nonzero bytes of m[0, N) into *out (one block, fixed order).
+hipError_t launch_count_mask(const uint8_t* m, int64_t N, unsigned long long* out, hipStream_t st);
 hipError_t launch_copy_mask(const uint8_t* src, int64_t N, uint8_t* dst, hipStream_t st);
 hipError_t launch_set_nan(float* dst, hipStream_t st);
 

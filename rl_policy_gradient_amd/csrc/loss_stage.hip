@@ -134,15 +134,18 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
 // ---------------------------------------------------------------------------
 struct TokEval {
   bool M, R, E;
-  bool clipped;   // GMPO token predicate (ratio tokens only)
-  double c;       // GMPO clipped log-ratio value
+  bool clipped;   // GMPO: token predicate on ratio tokens; token-clip losses: ratio held at a bound
+  double c;       // GMPO: clipped log-ratio; token-clip losses: policy term -min(rho A, clip(rho) A)
+  double rho;     // token-clip losses: the token ratio exp(lr32)
   double lr;      // log-ratio value
   double kl, dkl;
 };
 
-// Per-token quantities (Liger PR #1320 GMPO clip in log space, advantage
-// dependent and one sided; K3 KL). lr32 = fp32(lp - old) is the predicate
-// operand, compared with fp32 bounds; ties are not clipped.
+// Per-token quantities. GMPO (Liger PR #1320): clip in log space, advantage
+// dependent and one sided. GRPO / BNPO / DAPO: the Tinker GSPO page's clipped
+// objective with the token's own ratio, decided on exp(lr32) in fp64 against
+// the fp32 ratio bounds. K3 KL. lr32 = fp32(lp - old) is the predicate
+// operand; ties are not clipped; A = 0 gives no term.
 __device__ __forceinline__ TokEval eval_tok(const LossParams& p, int64_t t, const float* lp, const float* old,
                                             const float* ref, const uint8_t* comp, const uint8_t* ratio,
                                             const uint8_t* emask, float A) {
@@ -154,10 +157,21 @@ __device__ __forceinline__ TokEval eval_tok(const LossParams& p, int64_t t, cons
   e.R = ratio ? ratio[t] != 0 : e.M;
   e.E = emask ? emask[t] != 0 : true;
   e.lr = (double)lr32;
-  const bool hi = A > 0.f && lr32 > p.eh32;
-  const bool lo = A < 0.f && lr32 < -p.el32;
-  e.clipped = e.R && (hi || lo);
-  e.c = hi ? (double)p.eh32 : (lo ? -(double)p.el32 : (double)lr32);
+  if (token_clip_loss(p.loss_type)) {
+    const double rho = exp((double)lr32);
+    const double hi64 = (double)p.hi32, lo64 = (double)p.lo32, A64 = (double)A;
+    const bool hi = A > 0.f && rho > hi64;
+    const bool lo = A < 0.f && rho < lo64;
+    e.clipped = e.M && (hi || lo);
+    e.rho = rho;
+    e.c = A == 0.f ? 0.0 : (hi ? -hi64 * A64 : (lo ? -lo64 * A64 : -rho * A64));
+  } else {
+    const bool hi = A > 0.f && lr32 > p.eh32;
+    const bool lo = A < 0.f && lr32 < -p.el32;
+    e.clipped = e.R && (hi || lo);
+    e.rho = 0.0;
+    e.c = hi ? (double)p.eh32 : (lo ? -(double)p.el32 : (double)lr32);
+  }
   if (ref) {
     const double x = (double)ref[t] - (double)lp32;
     const double ex = exp(x);
@@ -191,10 +205,11 @@ __global__ __launch_bounds__(NT) void seq_partial_kernel(LossParams p, const flo
     const int64_t t = (int64_t)i * T + k;
     const TokEval e = eval_tok(p, t, lp, old, ref, comp, ratio, emask, A);
     if (e.R) {
-      sc += e.c;
+      if (!token_clip_loss(p.loss_type)) sc += e.c;
       slr += e.lr;
       cr += 1;
     }
+    if (token_clip_loss(p.loss_type) && e.M && e.E) sc += e.c;
     if (e.M) {
       skl += e.kl;
       cm += 1;
@@ -213,8 +228,9 @@ __global__ __launch_bounds__(NT) void seq_partial_kernel(LossParams p, const flo
   if (threadIdx.x == 0) part[(int64_t)i * St + s] = out;
 }
 
-// One block: per-sequence scalars (GMPO r_i, GSPO s_i), gradient
-// coefficients, loss and metric contributions of the chunk. The first chunk
+// One block: per-sequence scalars (GMPO r_i, GSPO s_i; the token-clip
+// losses' masked sum of policy terms), gradient coefficients, loss and metric
+// contributions of the chunk. The first chunk
 // (init) sets the batch accumulators instead of adding to them; the last one
 // (loss_out != NULL) also writes the loss and the metrics, with the entropy
 // threshold from thr_dev (NaN when NULL: the mask is off).
@@ -246,12 +262,24 @@ __global__ __launch_bounds__(NT) void seq_final_kernel(LossParams p, int64_t Bc,
     const double K = (double)ck;
     const float A32 = adv[i];
     const double A = (double)A32;
-    const double w = p.reduction == 0 ? 1.0 / ((double)p.B_total * n) : 1.0;
+    double w;
+    if (token_mean_loss(p.loss_type))
+      w = 1.0 / (double)(p.norm_tokens > 0 ? (unsigned long long)p.norm_tokens
+                                           : (*p.ntok_dev > 0 ? *p.ntok_dev : 1ull));
+    else if (p.loss_type == 2 || p.reduction == 0)
+      w = 1.0 / ((double)p.B_total * n);
+    else
+      w = 1.0;
     const double seq_lr = sum_lr / nt;
     double policy_seq, pol;
     long long clip_tok;
     int clip_any = 0;
-    if (p.loss_type == 0) {
+    if (token_clip_loss(p.loss_type)) {
+      // GRPO / BNPO / DAPO: sum_c already holds the masked policy terms
+      policy_seq = 0.0;
+      pol = -A * w;  // times the token's ratio where it is not held at a bound
+      clip_tok = cc;
+    } else if (p.loss_type == 0) {
       // GMPO: r = exp(masked mean of the clipped log-ratios) (PR #1320)
       const double r = A32 != 0.f ? exp(sum_c / nt) : 1.0;
       policy_seq = A32 != 0.f ? -A * r : 0.0;
@@ -268,7 +296,7 @@ __global__ __launch_bounds__(NT) void seq_final_kernel(LossParams p, int64_t Bc,
       clip_tok = clipped ? cm : 0;
       clip_any = (sr < lo || sr > hi) ? 1 : 0;
     }
-    loss += w * (policy_seq * K + p.beta * sum_kl);
+    loss += token_clip_loss(p.loss_type) ? w * (sum_c + p.beta * sum_kl) : w * (policy_seq * K + p.beta * sum_kl);
     slr += seq_lr;
     mkl += sum_kl / n;
     na += (unsigned long long)cm;
@@ -328,7 +356,9 @@ __global__ __launch_bounds__(NT) void seq_final_kernel(LossParams p, int64_t Bc,
 }
 
 // Per 32-token block: g_t = dL/dlp_t (GMPO: pol on unclipped ratio tokens;
-// GSPO-token: pol on kept completion tokens; plus w beta (1 - e^{ref - lp})
+// GSPO-token: pol on kept completion tokens; GRPO / BNPO / DAPO: pol times the
+// token's ratio on kept completion tokens not held at a bound; plus
+// w beta (1 - e^{ref - lp})
 // on completion tokens), the block's count of g != 0 (cnt32, when given) and,
 // when gh is given, grad_h = (g / tau) v for its rows.
 constexpr int TB = 32;  // tokens per block of the token kernel
@@ -351,7 +381,9 @@ __global__ __launch_bounds__(NT) void token_kernel(LossParams p, int64_t Nc, con
       const SeqCoef c = coef[i];
       const TokEval e = eval_tok(p, t, lp, old, ref, comp, ratio, emask, c.adv);
       double gv = 0.0;
-      if (p.loss_type == 0) {
+      if (token_clip_loss(p.loss_type)) {
+        if (e.M && e.E && !e.clipped && c.pol != 0.0) gv = c.pol * e.rho;
+      } else if (p.loss_type == 0) {
         if (e.R && !e.clipped) gv = c.pol;
       } else {
         if (e.M && e.E) gv = c.pol;
@@ -540,6 +572,32 @@ __global__ __launch_bounds__(NT) void mask_kernel(const float* __restrict__ ent,
     mask[t] = (active[t] != 0 && ent[t] >= thr) ? 1 : 0;
 }
 
+// Number of nonzero mask bytes (one block, fixed-order sum): the batch's
+// completion tokens, the divisor of BNPO and of DAPO without a global count.
+__global__ __launch_bounds__(NT) void count_mask_kernel(const uint8_t* __restrict__ m, int64_t N,
+                                                        unsigned long long* __restrict__ out) {
+  __shared__ unsigned long long red[NT];
+  unsigned long long c = 0;
+  const int64_t n16 = N / 16;
+  const uint4* m16 = reinterpret_cast<const uint4*>(m);
+  const bool aligned = (reinterpret_cast<uintptr_t>(m) & 15) == 0;
+  int64_t done = 0;
+  if (aligned) {
+    for (int64_t k = threadIdx.x; k < n16; k += NT) {
+      const uint4 v = m16[k];
+      const unsigned w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) c += ((w4[j] >> (8 * b)) & 0xffu) != 0u;
+    }
+    done = n16 * 16;
+  }
+  for (int64_t k = done + threadIdx.x; k < N; k += NT) c += m[k] != 0;
+  c = block_sum(c, red);
+  if (threadIdx.x == 0) *out = c;
+}
+
 __global__ void store_thr_kernel(const float* __restrict__ thr_dev, float* __restrict__ thr_out) {
   if (threadIdx.x == 0) *thr_out = *thr_dev;
 }
@@ -643,6 +701,11 @@ hipError_t launch_entropy_select(const float* ent, const uint8_t* active, int64_
 hipError_t launch_entropy_mask(const float* ent, const uint8_t* active, int64_t N, const float* thr_dev,
                                uint8_t* mask, hipStream_t st) {
   hipLaunchKernelGGL(mask_kernel, dim3(grid_for(N, NT)), dim3(NT), 0, st, ent, active, N, thr_dev, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_count_mask(const uint8_t* m, int64_t N, unsigned long long* out, hipStream_t st) {
+  hipLaunchKernelGGL(count_mask_kernel, dim3(1), dim3(NT), 0, st, m, N, out);
   return hipGetLastError();
 }
 

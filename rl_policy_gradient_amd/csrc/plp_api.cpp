@@ -38,6 +38,13 @@ constexpr size_t kAlign = 256;
 constexpr int kBQ = 64, kBK = 32;
 constexpr int kMaxSplits = 64;
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
+// plp_args as of ABI version 1 (fields up to chunk_sequences); later fields
+// read as their defaults when struct_size ends before them.
+constexpr size_t kArgsV1Size = offsetof(plp_args, global_tokens);
+
+int64_t global_tokens(const plp_args* a) {
+  return a->struct_size >= offsetof(plp_args, global_tokens) + sizeof(int64_t) ? a->global_tokens : 0;
+}
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -94,6 +101,7 @@ struct Bufs {
   float* g = nullptr;
   LossAcc* acc = nullptr;
   float* thr = nullptr;
+  unsigned long long* ntok = nullptr;  // the batch's completion tokens (BNPO / DAPO divisor)
   int* idx = nullptr;
   TokData* tok = nullptr;
   int* count = nullptr;
@@ -142,6 +150,7 @@ size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
   b.g = c.take<float>(p.Nc);
   b.acc = c.take<LossAcc>(1);
   b.thr = c.take<float>(1);
+  b.ntok = c.take<unsigned long long>(1);
   if (p.need_gw) {
     b.idx = c.take<int>(p.cap);
     b.tok = c.take<TokData>(p.cap);
@@ -193,12 +202,12 @@ int check_ws(void* ws, size_t have, size_t need) {
 // check the required pointers (the workspace queries read sizes only).
 int check_loss_args(const plp_args* a, bool pointers = true) {
   if (!a) return fail(PLP_E_INVALID, "args is NULL");
-  if (a->struct_size < sizeof(plp_args)) return fail(PLP_E_INVALID, "args->struct_size %u < %zu", a->struct_size,
-                                                     sizeof(plp_args));
+  if (a->struct_size < kArgsV1Size)
+    return fail(PLP_E_INVALID, "args->struct_size %u < %zu", a->struct_size, kArgsV1Size);
   if (a->B < 1 || a->T < 1) return fail(PLP_E_INVALID, "B and T must be >= 1 (B=%lld T=%lld)", (long long)a->B,
                                         (long long)a->T);
   if (a->B > kMaxRows / a->T) return fail(PLP_E_INVALID, "B*T must be < 2^31");
-  if (a->loss_type != PLP_LOSS_GMPO && a->loss_type != PLP_LOSS_GSPO_TOKEN)
+  if (a->loss_type < PLP_LOSS_GMPO || a->loss_type > PLP_LOSS_DAPO)
     return fail(PLP_E_INVALID, "unknown loss_type %d", a->loss_type);
   if (a->is_level != PLP_IS_TOKEN && a->is_level != PLP_IS_SEQUENCE)
     return fail(PLP_E_INVALID, "unknown is_level %d", a->is_level);
@@ -207,6 +216,10 @@ int check_loss_args(const plp_args* a, bool pointers = true) {
                                    "sequence-level importance sampling is rejected");
   if (a->loss_type == PLP_LOSS_GSPO_TOKEN && a->is_level == PLP_IS_TOKEN)
     return fail(PLP_E_UNSUPPORTED, "GSPO_TOKEN uses the sequence-level ratio; set is_level = PLP_IS_SEQUENCE");
+  if (token_clip_loss(a->loss_type) && a->is_level == PLP_IS_SEQUENCE)
+    return fail(PLP_E_UNSUPPORTED, "GRPO, BNPO and DAPO clip each token's own ratio; their sequence-level form "
+                                   "is GSPO_TOKEN");
+  if (global_tokens(a) < 0) return fail(PLP_E_INVALID, "global_tokens must be >= 0");
   if (a->reduction != PLP_REDUCE_SEQ_MEAN && a->reduction != PLP_REDUCE_TOKEN_SUM)
     return fail(PLP_E_INVALID, "unknown reduction %d", a->reduction);
   if (!(a->epsilon_low >= 0.0) || !isfinite(a->epsilon_low) || !(a->epsilon_high >= 0.0) ||
@@ -235,7 +248,15 @@ int check_fused_args(const plp_args* a) {
   return PLP_OK;
 }
 
-LossParams loss_params(const plp_args* a) {
+// The batch's completion-token count, when the loss divides by it (BNPO, and
+// DAPO without a global count), into *ntok.
+int count_tokens_if_needed(const plp_args* a, unsigned long long* ntok, hipStream_t st) {
+  if (token_mean_loss(a->loss_type) && !(a->loss_type == PLP_LOSS_DAPO && global_tokens(a) > 0))
+    HIP_TRY(launch_count_mask(a->completion_mask, a->B * a->T, ntok, st));
+  return PLP_OK;
+}
+
+LossParams loss_params(const plp_args* a, const unsigned long long* ntok_dev) {
   LossParams p;
   p.B_total = a->B;
   p.T = a->T;
@@ -246,6 +267,8 @@ LossParams loss_params(const plp_args* a) {
   p.lo32 = (float)(1.0 - a->epsilon_low);
   p.hi32 = (float)(1.0 + a->epsilon_high);
   p.beta = a->beta;
+  p.norm_tokens = a->loss_type == PLP_LOSS_DAPO ? global_tokens(a) : 0;
+  p.ntok_dev = ntok_dev;
   return p;
 }
 
@@ -356,7 +379,9 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
   const int H = a->H, V = a->V;
   const size_t es = esize(a->dtype);
   const float inv_tau = (float)(1.0 / a->temperature);
-  const LossParams lpar = loss_params(a);
+  const LossParams lpar = loss_params(a, b.ntok);
+  rc = count_tokens_if_needed(a, b.ntok, st);
+  if (rc) return rc;
 
   if (p.mfma)
     HIP_TRY(launch_frag_copy((const __bf16*)a->weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H, b.Wf, st));
@@ -513,6 +538,7 @@ PLP_API int plp_policy_loss_workspace_size(const plp_args* a, size_t* bytes) {
   c.take<float>(N);
   c.take<LossAcc>(1);
   c.take<float>(1);
+  c.take<unsigned long long>(1);
   *bytes = c.off + kAlign;
   return ok();
 }
@@ -540,7 +566,10 @@ PLP_API int plp_policy_loss_from_logprobs(const plp_args* a, const float* logp, 
   float* gbuf = c.take<float>(N);
   LossAcc* acc = c.take<LossAcc>(1);
   float* thr = c.take<float>(1);
-  const LossParams lpar = loss_params(a);
+  unsigned long long* ntok = c.take<unsigned long long>(1);
+  const LossParams lpar = loss_params(a, ntok);
+  rc = count_tokens_if_needed(a, ntok, st);
+  if (rc) return rc;
   if (q_on) {
     HIP_TRY(launch_entropy_select(entropy, a->completion_mask, N, (float)(1.0 - a->top_entropy_quantile), thr, nullptr, st));
     HIP_TRY(launch_entropy_mask(entropy, a->completion_mask, N, thr, emask, st));

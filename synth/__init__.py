@@ -30,6 +30,9 @@ import numpy as np
 
 GMPO = "gmpo"
 GSPO_TOKEN = "gspo_token"
+GRPO = "grpo"
+BNPO = "bnpo"
+DAPO = "dapo"
 
 # Stream ids inside SeedSequence([seed, cfg_id, stream]).
 _S_H, _S_W, _S_B, _S_Y, _S_P, _S_A, _S_OLD, _S_REF, _S_ZERO = range(9)
@@ -65,6 +68,7 @@ class Spec:
     zero_adv_fraction: float = 0.0          # exact share of sequences with A=0
     chunk_sequences: int = 0                # 0: whole batch in one chunk
     reduction: str = "seq_mean"             # "seq_mean" or "token_sum"
+    global_tokens: int = 0                  # DAPO divisor; 0 = the batch's completion tokens
     seed: int = 0
 
     @property

@@ -54,7 +54,7 @@ def run_gpu(spec: synth.Spec, d: dict, **kw) -> dict:
     args = dict(B=spec.B, T=spec.T, loss_type=spec.loss_type, epsilon_low=spec.eps_low,
                 epsilon_high=spec.eps_high, beta=spec.beta, temperature=spec.temperature,
                 top_entropy_quantile=spec.top_entropy_quantile, chunk_sequences=spec.chunk_sequences,
-                reduction=spec.reduction, diagnostics=True)
+                reduction=spec.reduction, global_tokens=spec.global_tokens, diagnostics=True)
     args.update(kw)
     out = plp.fused_lmhead_policy_loss_fwd_bwd(g["hidden"], g["weight"], g["targets"], g["completion_mask"],
                                                g["advantages"], bias=g["bias"], old_logp=g["old_logp"],
@@ -86,14 +86,22 @@ def cosine(a, b) -> float:
 
 
 def clip_margin(spec: synth.Spec, d: dict, lp) -> float:
-    """Smallest distance of an active fp32 log-ratio to a GMPO bound (a
-    predicate closer than the log-prob tolerance could legitimately flip)."""
-    if spec.loss_type != synth.GMPO or d["old"] is None:
+    """Smallest distance of an active fp32 log-ratio to a token clip bound in
+    log space (GMPO: eps_high, -eps_low; GRPO / BNPO / DAPO: log of the fp32
+    ratio bounds). A predicate closer than the log-prob tolerance could
+    legitimately flip."""
+    if d["old"] is None:
+        return np.inf
+    if spec.loss_type == synth.GMPO:
+        hi, lo = float(np.float32(spec.eps_high)), -float(np.float32(spec.eps_low))
+    elif spec.loss_type in (synth.GRPO, synth.BNPO, synth.DAPO):
+        hi = np.log(float(np.float32(1 + spec.eps_high)))
+        lo = np.log(float(np.float32(1 - spec.eps_low)))
+    else:
         return np.inf
     lr = np.asarray(lp, np.float64) - d["old"].astype(np.float64)
     act = d["completion_mask"] != 0
-    b = np.concatenate([np.abs(lr - np.float32(spec.eps_high)), np.abs(lr + np.float32(spec.eps_low))])
-    return float(np.min(np.concatenate([b[: len(lr)][act], b[len(lr):][act]])))
+    return float(min(np.abs(lr - hi)[act].min(), np.abs(lr - lo)[act].min()))
 
 
 def grad_tol(spec: synth.Spec):

@@ -98,6 +98,11 @@ def _call(a, o=None, ws=None, ws_bytes=0):
     (lambda a: setattr(a, "completion_mask", None), abi.PLP_E_INVALID, "required"),
     (lambda a: setattr(a, "epsilon_low", -0.1), abi.PLP_E_INVALID, "epsilon"),
     (lambda a: setattr(a, "chunk_sequences", -1), abi.PLP_E_INVALID, "chunk_sequences"),
+    (lambda a: (setattr(a, "loss_type", abi.LOSS_GRPO), setattr(a, "is_level", abi.IS_SEQUENCE)),
+     abi.PLP_E_UNSUPPORTED, "GSPO_TOKEN"),
+    (lambda a: (setattr(a, "loss_type", abi.LOSS_DAPO), setattr(a, "global_tokens", -5)),
+     abi.PLP_E_INVALID, "global_tokens"),
+    (lambda a: setattr(a, "loss_type", 5), abi.PLP_E_INVALID, "loss_type"),
     (lambda a: setattr(a, "struct_size", 8), abi.PLP_E_INVALID, "struct_size"),
     (lambda a: setattr(a, "H", 5000), abi.PLP_E_UNSUPPORTED, "H=5000"),
     (lambda a: setattr(a, "dtype", 7), abi.PLP_E_INVALID, "dtype"),
@@ -108,6 +113,17 @@ def test_validation_rejects_before_launch(mutate, code, msg):
     rc, err = _call(a)
     assert rc == code, err
     assert msg in err
+
+
+def test_version_one_args_are_accepted():
+    """A caller built against ABI version 1 (struct_size ending before
+    global_tokens) passes validation; the field reads as its default."""
+    a = _valid_args()
+    a.struct_size = abi.PlpArgs.global_tokens.offset
+    a.global_tokens = -5  # beyond the caller's struct: must not be read
+    a.loss_type = abi.LOSS_DAPO
+    rc, err = _call(a, ws=None, ws_bytes=0)
+    assert rc == abi.PLP_E_WORKSPACE, err
 
 
 def test_workspace_checks():
@@ -146,4 +162,4 @@ def test_other_entry_points_validate():
     assert "q must lie" in L.plp_last_error().decode()
     a = _valid_args()
     assert L.plp_policy_loss_from_logprobs(ctypes.byref(a), None, None, None, None, 0, None) == abi.PLP_E_INVALID
-    assert L.plp_abi_version() == 1
+    assert L.plp_abi_version() == 2

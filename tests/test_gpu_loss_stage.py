@@ -83,14 +83,24 @@ def _loss_case(seed, B, T, loss_type, beta, q, ratio_mask, reduction, eps=(0.2, 
     ("gmpo", 0.0, 1.0, False, "token_sum", 3000),
     ("gspo_token", 0.0, 1.0, False, "seq_mean", 64),
     ("gspo_token", 0.04, 0.5, True, "token_sum", 4500),
+    ("grpo", 0.0, 1.0, False, "seq_mean", 41),
+    ("grpo", 0.04, 0.4, True, "seq_mean", 5000),
+    ("bnpo", 0.04, 1.0, False, "seq_mean", 3000),
+    ("bnpo", 0.0, 0.5, False, "seq_mean", 77),
+    ("dapo", 0.04, 0.5, False, "seq_mean", 4100),
+    ("dapo_global", 0.0, 1.0, True, "seq_mean", 300),
 ])
 def test_policy_loss_from_logprobs(loss_type, beta, q, ratio_mask, reduction, T):
     import rl_policy_gradient_amd as plp
     B = 7
-    eps = (0.2, 0.3) if loss_type == "gmpo" else (3e-2, 4e-2)
-    noise = 0.3 if loss_type == "gmpo" else 0.1
+    G = 0
+    if loss_type == "dapo_global":
+        loss_type, G = "dapo", 12345
+    eps = (0.2, 0.3) if loss_type in ("gmpo", "grpo", "bnpo", "dapo") else (3e-2, 4e-2)
+    noise = 0.3 if loss_type in ("gmpo", "grpo", "bnpo", "dapo") else 0.1
     cfg, lp, old, ref, comp, rm, A, ent = _loss_case(T, B, T, loss_type, beta, q, ratio_mask, reduction, eps, noise)
-    _say(f"loss stage {loss_type} beta={beta} q={q} ratio_mask={ratio_mask} {reduction} T={T}")
+    cfg = cfg.__class__(**{**cfg.__dict__, "global_tokens": G})
+    _say(f"loss stage {loss_type} beta={beta} q={q} ratio_mask={ratio_mask} {reduction} T={T} G={G}")
     emask, thr = (oracle.entropy_quantile_mask(ent, comp != 0, q) if q < 1 else (None, np.float32(np.nan)))
     p = oracle.policy_loss(cfg, lp.astype(np.float64), old, ref, comp, rm, A, emask)
     loss, metrics = oracle.finalize_metrics([p], thr)
@@ -98,7 +108,7 @@ def test_policy_loss_from_logprobs(loss_type, beta, q, ratio_mask, reduction, T)
                                         old_logp=dev_tensor(old), ref_logp=dev_tensor(ref),
                                         ratio_mask=dev_tensor(rm), entropy=dev_tensor(ent), loss_type=loss_type,
                                         reduction=reduction, epsilon_low=eps[0], epsilon_high=eps[1], beta=beta,
-                                        top_entropy_quantile=q)
+                                        top_entropy_quantile=q, global_tokens=G)
     torch.cuda.synchronize()
     gl = out["loss"].cpu().numpy()[0]
     assert abs(gl - loss) <= 1e-5 * max(1.0, abs(loss)), (gl, loss)
@@ -137,6 +147,42 @@ def test_policy_loss_exact_boundaries():
     m = out["metrics"].cpu().numpy()
     assert m[7] == metrics[7] == 6
     assert np.float32(m[0]).view(np.uint32) == np.float32(metrics[0]).view(np.uint32)
+    g = out["dlogp"].cpu().numpy()
+    np.testing.assert_array_equal(g != 0, p["g"] != 0)
+    assert abs(out["loss"].cpu().numpy()[0] - loss) <= 1e-6
+
+
+def test_token_clip_exact_boundaries():
+    """GRPO: fp32 log-ratios on either side of log(fp32(1 + eps_high)) and
+    log(fp32(1 - eps_low)) give the oracle's predicates bit for bit."""
+    import math
+    import rl_policy_gradient_amd as plp
+    _say("token-clip boundaries")
+    hi, lo = float(np.float32(1.3)), float(np.float32(0.8))
+
+    def around(bound):
+        x = np.float32(math.log(bound))
+        below = x if math.exp(float(x)) < bound else np.nextafter(x, np.float32(-10))
+        return [below, np.nextafter(below, np.float32(10))]
+
+    vals = around(hi) + around(lo)
+    B, T = 4, 3
+    lp = np.zeros(B * T, np.float32)
+    for i, v in enumerate(vals):
+        lp[i * T:(i + 1) * T] = v
+    old = np.zeros(B * T, np.float32)
+    A = np.array([1, 1, -1, -1], np.float32)
+    comp = np.ones(B * T, np.uint8)
+    cfg = oracle.LossConfig(B=B, T=T, loss_type="grpo", eps_low=0.2, eps_high=0.3)
+    p = oracle.policy_loss(cfg, lp.astype(np.float64), old, None, comp, None, A)
+    loss, metrics = oracle.finalize_metrics([p], np.float32(np.nan))
+    assert metrics[7] == 6  # above hi with A > 0 (3 tokens), below lo with A < 0 (3 tokens)
+    out = plp.policy_loss_from_logprobs(dev_tensor(lp), dev_tensor(comp), dev_tensor(A), B, T,
+                                        old_logp=dev_tensor(old), loss_type="grpo", epsilon_low=0.2,
+                                        epsilon_high=0.3)
+    torch.cuda.synchronize()
+    m = out["metrics"].cpu().numpy()
+    assert m[7] == metrics[7]
     g = out["dlogp"].cpu().numpy()
     np.testing.assert_array_equal(g != 0, p["g"] != 0)
     assert abs(out["loss"].cpu().numpy()[0] - loss) <= 1e-6
