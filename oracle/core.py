@@ -55,6 +55,12 @@ Readings taken where the pages are silent (each also listed in the design doc):
   R17 Their clip predicate is decided on exp(lr32) in fp64 against
       fp32(1-eps_low) and fp32(1+eps_high); a clipped token takes the bound's
       value and no gradient.
+  R18 Per-token advantages (Tinker GSPO page, "Input tensors": advantages
+      of shape (N,); "Building a datum" zeroes them off the completion): the
+      objective's min(s_t A_t, clip(s_t) A_t) takes each token's own A_t, so
+      the clip binds per token by the sign of A_t. Defined for GSPO-token and
+      the token-level clipped losses; GMPO's clip direction and geometric
+      mean belong to the sequence, so it keeps per-sequence advantages.
 """
 from __future__ import annotations
 
@@ -216,13 +222,15 @@ def token_normaliser(cfg: LossConfig, completion_mask) -> int:
 
 def policy_loss(cfg: LossConfig, lp, old, ref, completion_mask, ratio_mask, advantages,
                 entropy_mask=None, seq_offset: int = 0, B_total: Optional[int] = None,
-                tokens_total: Optional[int] = None) -> dict:
+                tokens_total: Optional[int] = None, token_advantages=None) -> dict:
     """Loss, metrics and g = dL/dlp for a run of whole sequences.
 
     lp: fp64 (or fp32) [b*T]; old, ref: fp32 [b*T] or None; masks u8/bool
     [b*T]; advantages fp32 [b]; entropy_mask bool [b*T] or None (= all ones).
     B_total is the batch size that divides the per-sample reduction (R5);
     tokens_total the BNPO / DAPO divisor (R16; default: from this run).
+    token_advantages fp32 [b*T] replaces `advantages` with one value per
+    token (R18; not for GMPO).
 
     GMPO (Liger PR #1320): c_t clipped per R1; r_i = exp(mean_{R_i} c);
     per-token policy term -A_i r_i.  GSPO-token (Tinker GSPO page): sequence
@@ -243,7 +251,14 @@ def policy_loss(cfg: LossConfig, lp, old, ref, completion_mask, ratio_mask, adva
     M = np.asarray(completion_mask).reshape(b, T) != 0
     R = M if ratio_mask is None else (np.asarray(ratio_mask).reshape(b, T) != 0)
     e = np.ones((b, T), bool) if entropy_mask is None else (np.asarray(entropy_mask).reshape(b, T) != 0)
-    A = np.asarray(advantages, np.float32).astype(np.float64).reshape(b)
+    if token_advantages is not None:
+        if cfg.loss_type == GMPO:
+            raise ValueError("GMPO takes per-sequence advantages (R18)")
+        At = np.asarray(token_advantages, np.float32).astype(np.float64).reshape(b, T)
+        A = None
+    else:
+        A = np.asarray(advantages, np.float32).astype(np.float64).reshape(b)
+        At = np.broadcast_to(A[:, None], (b, T))
     n = np.maximum(1, M.sum(axis=1)).astype(np.float64)
     nt = np.maximum(1, R.sum(axis=1)).astype(np.float64)
     if cfg.loss_type == GRPO:
@@ -276,6 +291,23 @@ def policy_loss(cfg: LossConfig, lp, old, ref, completion_mask, ratio_mask, adva
         seq_ratio = r
         clipped_seq = np.zeros(b, bool)
         clipped_seq_any = np.zeros(b, bool)
+    elif cfg.loss_type == GSPO_TOKEN and A is None:
+        # per-token advantages (R18): each token's min(s A_t, clip(s) A_t)
+        lo = np.float32(1.0 - cfg.eps_low)
+        hi = np.float32(1.0 + cfg.eps_high)
+        s = np.exp(seq_log_ratio)
+        sc = s[:, None]
+        held = ((At > 0) & (sc > float(hi))) | ((At < 0) & (sc < float(lo)))
+        clipped_tok = M & held
+        s_cl = np.clip(sc, float(lo), float(hi))
+        live = (At != 0) & ~held                             # A_t = 0: no term, no gradient
+        s_l = np.where(live, sc, 0.0)
+        # min(s A_t, clip(s) A_t) is the clipped value exactly where `held`
+        pol_tok_gspo = np.where(held, -s_cl * At, -s_l * At)
+        g_pol = np.where(e & M & live, -At * s_l, 0.0)
+        seq_ratio = s
+        clipped_seq = clipped_tok.any(axis=1)
+        clipped_seq_any = (s < lo) | (s > hi)
     elif cfg.loss_type == GSPO_TOKEN:
         lo = np.float32(1.0 - cfg.eps_low)
         hi = np.float32(1.0 + cfg.eps_high)
@@ -291,7 +323,7 @@ def policy_loss(cfg: LossConfig, lp, old, ref, completion_mask, ratio_mask, adva
     elif cfg.loss_type in PPO_CLIP_LOSSES:
         lo = np.float32(1.0 - cfg.eps_low)
         hi = np.float32(1.0 + cfg.eps_high)
-        Ac = A[:, None]
+        Ac = At
         with np.errstate(over="ignore"):
             rho_pred = np.exp(lr32.astype(np.float64))      # R17
             rho = np.exp(lr)
@@ -312,6 +344,8 @@ def policy_loss(cfg: LossConfig, lp, old, ref, completion_mask, ratio_mask, adva
 
     if cfg.loss_type in PPO_CLIP_LOSSES:
         policy_tok = pol_ppo
+    elif cfg.loss_type == GSPO_TOKEN and A is None:
+        policy_tok = pol_tok_gspo
     else:
         policy_tok = np.broadcast_to(policy_seq[:, None], (b, T))
     if ref is not None:
@@ -445,7 +479,7 @@ def grad_w_rows(h, W_rows, b_rows, tau, targets, lse, g, vrows, chunk: int = 655
 # ---------------------------------------------------------------------------
 
 def run(cfg: LossConfig, h, W, b, targets, old, ref, completion_mask, ratio_mask, advantages,
-        want_grads: bool = True, fwd: Optional[dict] = None) -> dict:
+        want_grads: bool = True, fwd: Optional[dict] = None, token_advantages=None) -> dict:
     """Forward statistics, batch-global entropy mask, loss and gradients.
 
     The outer loop walks chunks of whole sequences (PR #1320 tests outer chunk
@@ -473,8 +507,9 @@ def run(cfg: LossConfig, h, W, b, targets, old, ref, completion_mask, ratio_mask
         sl = slice(s0 * T, s1 * T)
         p = policy_loss(cfg, lp[sl], None if old is None else old[sl], None if ref is None else ref[sl],
                         completion_mask[sl], None if ratio_mask is None else ratio_mask[sl],
-                        advantages[s0:s1], None if emask is None else emask[sl], B_total=B,
-                        tokens_total=G)
+                        None if advantages is None else advantages[s0:s1],
+                        None if emask is None else emask[sl], B_total=B, tokens_total=G,
+                        token_advantages=None if token_advantages is None else token_advantages[sl])
         g[sl] = p["g"]
         parts.append(p)
     loss, metrics = finalize_metrics(parts, thr)
