@@ -135,7 +135,7 @@ typedef struct plp_args {
   const uint8_t* completion_mask; /* [N] nonzero = token enters the loss */
   const uint8_t* ratio_mask;    /* [N] nonzero = token enters the sequence ratio and clip;
                                    NULL = completion_mask (Tinker: sequence_ratio_mask) */
-  const float* advantages;      /* [B] per-sequence advantage */
+  const float* advantages;      /* [B] per-sequence advantage (NULL when token_advantages is given) */
   int32_t loss_type;            /* plp_loss_type */
   int32_t is_level;             /* plp_is_level */
   int32_t reduction;            /* plp_reduction */
@@ -149,6 +149,13 @@ typedef struct plp_args {
   /* ---- ABI version 2 ---- */
   int64_t global_tokens;        /* DAPO divisor (>= 0); 0 = the batch's completion tokens.
                                    Ignored by the other loss types. Default 0. */
+  const float* token_advantages;/* [N] one advantage per token (Tinker GSPO page, "Input
+                                   tensors": advantages (N,)), or NULL (default) to use
+                                   `advantages` [B]. When given, `advantages` is ignored and may
+                                   be NULL; each token's min(ratio A_t, clip(ratio) A_t) takes its
+                                   own A_t, so the clip binds per token by the sign of A_t.
+                                   GSPO_TOKEN, GRPO, BNPO and DAPO only (GMPO's clip direction
+                                   and geometric mean are per sequence: PLP_E_UNSUPPORTED). */
 } plp_args;
 
 /* Outputs of the fused call. Every pointer except loss and metrics may be

@@ -64,6 +64,7 @@ class PlpArgs(ctypes.Structure):
         ("top_entropy_quantile", ctypes.c_double),
         ("chunk_sequences", ctypes.c_int64),
         ("global_tokens", ctypes.c_int64),
+        ("token_advantages", _vp),
     ]
 
 

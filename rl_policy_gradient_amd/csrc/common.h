@@ -45,10 +45,14 @@ struct LossAcc {
 
 // Per-sequence partial sums of the loss stage.
 struct SeqPart {
-  double sum_c;        // GMPO: sum over ratio tokens of the clipped log-ratio
+  double sum_c;        // GMPO: sum over ratio tokens of the clipped log-ratio;
+                       // token-clip losses: sum over kept completion tokens of the policy term
   double sum_lr;       // sum over ratio tokens of the log-ratio
   double sum_kl;       // sum over completion tokens of the K3 KL
+  double sum_apos, sum_aneg;  // GSPO with per-token advantages: sums of A_t > 0 / A_t < 0 over kept
+                              // completion tokens
   int cnt_m, cnt_r, cnt_k, cnt_clip;
+  int cnt_pos, cnt_neg;       // completion tokens with A_t > 0 / A_t < 0 (per-token advantages)
 };
 
 // Per-sequence coefficients of dL/dlogp.
@@ -69,6 +73,8 @@ struct LossParams {
   double beta;
   int64_t norm_tokens; // BNPO / DAPO divisor when > 0 (DAPO's global count)
   const unsigned long long* ntok_dev;  // else: the batch's completion-token count (device)
+  int token_adv;       // advantages are per token (the kernels' tadv argument)
+  int pad;
 };
 
 // Token-level clipped losses (GRPO, BNPO, DAPO) share the per-token path.
@@ -118,17 +124,19 @@ hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int 
 // last, with the threshold from thr_dev or NaN), then per-token dL/dlogp with
 // per-32-token counts of nonzero gradients and grad_h = g / tau * v (gh and v
 // may be NULL), and the in-order compaction of the tokens with g != 0.
+// adv: per-sequence advantages [Bc]; tadv: per-token advantages [Bc*T] (used
+// instead of adv when p.token_adv).
 hipError_t launch_loss_seq_partial(const LossParams& p, int64_t Bc, const float* lp, const float* old,
                                    const float* ref, const uint8_t* comp, const uint8_t* ratio,
-                                   const uint8_t* emask, const float* adv, int St, SeqPart* part,
-                                   hipStream_t st);
+                                   const uint8_t* emask, const float* adv, const float* tadv, int St,
+                                   SeqPart* part, hipStream_t st);
 hipError_t launch_loss_seq_final(const LossParams& p, int64_t Bc, int St, const SeqPart* part, const float* adv,
                                  SeqCoef* coef, LossAcc* acc, bool init, const float* thr_dev, float* loss_out,
                                  float* metrics, hipStream_t st);
 hipError_t launch_loss_tokens(int dtype, const LossParams& p, int64_t Bc, const float* lp, const float* old,
                               const float* ref, const uint8_t* comp, const uint8_t* ratio, const uint8_t* emask,
-                              const SeqCoef* coef, float* g, int* cnt32, const float* v, int H, float inv_tau,
-                              void* gh, hipStream_t st);
+                              const float* tadv, const SeqCoef* coef, float* g, int* cnt32, const float* v, int H,
+                              float inv_tau, void* gh, hipStream_t st);
 size_t compact_scratch_bytes(int64_t N);
 hipError_t launch_compact_scatter(const float* g, const float* lse, const int64_t* y, int64_t N, float inv_tau,
                                   const int* cnt32, int* idx, TokData* tok, int* count_dev, hipStream_t st);

@@ -190,7 +190,8 @@ __global__ __launch_bounds__(NT) void seq_partial_kernel(LossParams p, const flo
                                                          const uint8_t* __restrict__ comp,
                                                          const uint8_t* __restrict__ ratio,
                                                          const uint8_t* __restrict__ emask,
-                                                         const float* __restrict__ adv, int St,
+                                                         const float* __restrict__ adv,
+                                                         const float* __restrict__ tadv, int St,
                                                          SeqPart* __restrict__ part) {
   __shared__ double redd[NT];
   __shared__ int redi[NT];
@@ -198,12 +199,21 @@ __global__ __launch_bounds__(NT) void seq_partial_kernel(LossParams p, const flo
   const int64_t T = p.T;
   const int64_t L = (T + St - 1) / St;
   const int64_t a = (int64_t)s * L, b = min(T, a + L);
-  const float A = adv[i];
-  double sc = 0.0, slr = 0.0, skl = 0.0;
-  int cm = 0, cr = 0, ck = 0, cc = 0;
+  const float Aseq = p.token_adv ? 0.f : adv[i];
+  double sc = 0.0, slr = 0.0, skl = 0.0, sap = 0.0, san = 0.0;
+  int cm = 0, cr = 0, ck = 0, cc = 0, cp = 0, cn = 0;
   for (int64_t k = a + threadIdx.x; k < b; k += NT) {
     const int64_t t = (int64_t)i * T + k;
+    const float A = p.token_adv ? tadv[t] : Aseq;
     const TokEval e = eval_tok(p, t, lp, old, ref, comp, ratio, emask, A);
+    if (p.token_adv && e.M) {
+      cp += A > 0.f ? 1 : 0;
+      cn += A < 0.f ? 1 : 0;
+      if (e.E) {
+        sap += A > 0.f ? (double)A : 0.0;
+        san += A < 0.f ? (double)A : 0.0;
+      }
+    }
     if (e.R) {
       if (!token_clip_loss(p.loss_type)) sc += e.c;
       slr += e.lr;
@@ -225,6 +235,10 @@ __global__ __launch_bounds__(NT) void seq_partial_kernel(LossParams p, const flo
   out.cnt_r = block_sum(cr, redi);
   out.cnt_k = block_sum(ck, redi);
   out.cnt_clip = block_sum(cc, redi);
+  out.sum_apos = block_sum(sap, redd);
+  out.sum_aneg = block_sum(san, redd);
+  out.cnt_pos = block_sum(cp, redi);
+  out.cnt_neg = block_sum(cn, redi);
   if (threadIdx.x == 0) part[(int64_t)i * St + s] = out;
 }
 
@@ -245,22 +259,26 @@ __global__ __launch_bounds__(NT) void seq_final_kernel(LossParams p, int64_t Bc,
   double loss = 0.0, slr = 0.0, mkl = 0.0;
   unsigned long long na = 0, nc = 0, nk = 0, ncs = 0;
   for (int64_t i = threadIdx.x; i < Bc; i += NT) {
-    double sum_c = 0.0, sum_lr = 0.0, sum_kl = 0.0;
-    long long cm = 0, cr = 0, ck = 0, cc = 0;
+    double sum_c = 0.0, sum_lr = 0.0, sum_kl = 0.0, sum_ap = 0.0, sum_an = 0.0;
+    long long cm = 0, cr = 0, ck = 0, cc = 0, cpos = 0, cneg = 0;
     for (int s = 0; s < St; ++s) {
       const SeqPart q = part[i * St + s];
       sum_c += q.sum_c;
       sum_lr += q.sum_lr;
       sum_kl += q.sum_kl;
+      sum_ap += q.sum_apos;
+      sum_an += q.sum_aneg;
       cm += q.cnt_m;
       cr += q.cnt_r;
       ck += q.cnt_k;
       cc += q.cnt_clip;
+      cpos += q.cnt_pos;
+      cneg += q.cnt_neg;
     }
     const double n = (double)(cm > 0 ? cm : 1);
     const double nt = (double)(cr > 0 ? cr : 1);
     const double K = (double)ck;
-    const float A32 = adv[i];
+    const float A32 = p.token_adv ? 0.f : adv[i];
     const double A = (double)A32;
     double w;
     if (token_mean_loss(p.loss_type))
@@ -274,11 +292,24 @@ __global__ __launch_bounds__(NT) void seq_final_kernel(LossParams p, int64_t Bc,
     double policy_seq, pol;
     long long clip_tok;
     int clip_any = 0;
+    int held = 0;  // GSPO with per-token advantages: bit 0 s > hi (A_t > 0 held), bit 1 s < lo (A_t < 0 held)
     if (token_clip_loss(p.loss_type)) {
       // GRPO / BNPO / DAPO: sum_c already holds the masked policy terms
       policy_seq = 0.0;
-      pol = -A * w;  // times the token's ratio where it is not held at a bound
+      pol = -w;  // times the token's A_t and ratio where it is not held at a bound
       clip_tok = cc;
+    } else if (p.token_adv) {
+      // GSPO-token with per-token advantages: min(s A_t, clip(s) A_t) is
+      // s A_t except min(s, hi) A_t for A_t > 0 and max(s, lo) A_t for A_t < 0
+      const double sr = exp(seq_lr);
+      const double lo = (double)p.lo32, hi = (double)p.hi32;
+      const bool hp = sr > hi, hn = sr < lo;
+      policy_seq = 0.0;
+      sum_c = (sum_ap != 0.0 ? -sum_ap * fmin(sr, hi) : 0.0) + (sum_an != 0.0 ? -sum_an * fmax(sr, lo) : 0.0);
+      pol = -sr * w;  // times A_t where the token is not held
+      clip_tok = (hp ? cpos : 0) + (hn ? cneg : 0);
+      clip_any = (hp || hn) ? 1 : 0;
+      held = (hp ? 1 : 0) | (hn ? 2 : 0);
     } else if (p.loss_type == 0) {
       // GMPO: r = exp(masked mean of the clipped log-ratios) (PR #1320)
       const double r = A32 != 0.f ? exp(sum_c / nt) : 1.0;
@@ -296,7 +327,8 @@ __global__ __launch_bounds__(NT) void seq_final_kernel(LossParams p, int64_t Bc,
       clip_tok = clipped ? cm : 0;
       clip_any = (sr < lo || sr > hi) ? 1 : 0;
     }
-    loss += token_clip_loss(p.loss_type) ? w * (sum_c + p.beta * sum_kl) : w * (policy_seq * K + p.beta * sum_kl);
+    const bool tok_terms = token_clip_loss(p.loss_type) || p.token_adv;
+    loss += tok_terms ? w * (sum_c + p.beta * sum_kl) : w * (policy_seq * K + p.beta * sum_kl);
     slr += seq_lr;
     mkl += sum_kl / n;
     na += (unsigned long long)cm;
@@ -307,7 +339,7 @@ __global__ __launch_bounds__(NT) void seq_final_kernel(LossParams p, int64_t Bc,
     sc.pol = pol;
     sc.wbeta = w * p.beta;
     sc.adv = A32;
-    sc.pad = 0;
+    sc.pad = held;
     coef[i] = sc;
   }
   loss = block_sum(loss, redd);
@@ -368,6 +400,7 @@ __global__ __launch_bounds__(NT) void token_kernel(LossParams p, int64_t Nc, con
                                                    const float* __restrict__ old, const float* __restrict__ ref,
                                                    const uint8_t* __restrict__ comp, const uint8_t* __restrict__ ratio,
                                                    const uint8_t* __restrict__ emask,
+                                                   const float* __restrict__ tadv,
                                                    const SeqCoef* __restrict__ coef, float* __restrict__ g,
                                                    int* __restrict__ cnt32, const float* __restrict__ v, int H,
                                                    float inv_tau, T* __restrict__ gh) {
@@ -379,10 +412,14 @@ __global__ __launch_bounds__(NT) void token_kernel(LossParams p, int64_t Nc, con
     if (t < Nc) {
       const int64_t i = t / p.T;
       const SeqCoef c = coef[i];
-      const TokEval e = eval_tok(p, t, lp, old, ref, comp, ratio, emask, c.adv);
+      const float A = p.token_adv ? tadv[t] : c.adv;
+      const TokEval e = eval_tok(p, t, lp, old, ref, comp, ratio, emask, A);
       double gv = 0.0;
       if (token_clip_loss(p.loss_type)) {
-        if (e.M && e.E && !e.clipped && c.pol != 0.0) gv = c.pol * e.rho;
+        if (e.M && e.E && !e.clipped && A != 0.f) gv = c.pol * (double)A * e.rho;
+      } else if (p.token_adv) {
+        const bool held = (A > 0.f && (c.pad & 1)) || (A < 0.f && (c.pad & 2));
+        if (e.M && e.E && !held && A != 0.f) gv = c.pol * (double)A;
       } else if (p.loss_type == 0) {
         if (e.R && !e.clipped) gv = c.pol;
       } else {
@@ -637,10 +674,10 @@ hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int 
 
 hipError_t launch_loss_seq_partial(const LossParams& p, int64_t Bc, const float* lp, const float* old,
                                    const float* ref, const uint8_t* comp, const uint8_t* ratio,
-                                   const uint8_t* emask, const float* adv, int St, SeqPart* part,
-                                   hipStream_t st) {
+                                   const uint8_t* emask, const float* adv, const float* tadv, int St,
+                                   SeqPart* part, hipStream_t st) {
   hipLaunchKernelGGL(seq_partial_kernel, dim3((unsigned)Bc, (unsigned)St), dim3(NT), 0, st, p, lp, old, ref, comp,
-                     ratio, emask, adv, St, part);
+                     ratio, emask, adv, tadv, St, part);
   return hipGetLastError();
 }
 
@@ -654,16 +691,16 @@ hipError_t launch_loss_seq_final(const LossParams& p, int64_t Bc, int St, const 
 
 hipError_t launch_loss_tokens(int dtype, const LossParams& p, int64_t Bc, const float* lp, const float* old,
                               const float* ref, const uint8_t* comp, const uint8_t* ratio, const uint8_t* emask,
-                              const SeqCoef* coef, float* g, int* cnt32, const float* v, int H, float inv_tau,
-                              void* gh, hipStream_t st) {
+                              const float* tadv, const SeqCoef* coef, float* g, int* cnt32, const float* v, int H,
+                              float inv_tau, void* gh, hipStream_t st) {
   const int64_t Nc = Bc * p.T;
   const unsigned grid = (unsigned)((Nc + TB - 1) / TB);
   if (dtype == 0)
     hipLaunchKernelGGL((token_kernel<float>), dim3(grid), dim3(NT), 0, st, p, Nc, lp, old, ref, comp, ratio, emask,
-                       coef, g, cnt32, v, H, inv_tau, (float*)gh);
+                       tadv, coef, g, cnt32, v, H, inv_tau, (float*)gh);
   else
     hipLaunchKernelGGL((token_kernel<__bf16>), dim3(grid), dim3(NT), 0, st, p, Nc, lp, old, ref, comp, ratio, emask,
-                       coef, g, cnt32, v, H, inv_tau, (__bf16*)gh);
+                       tadv, coef, g, cnt32, v, H, inv_tau, (__bf16*)gh);
   return hipGetLastError();
 }
 

@@ -46,6 +46,10 @@ int64_t global_tokens(const plp_args* a) {
   return a->struct_size >= offsetof(plp_args, global_tokens) + sizeof(int64_t) ? a->global_tokens : 0;
 }
 
+const float* token_advantages(const plp_args* a) {
+  return a->struct_size >= offsetof(plp_args, token_advantages) + sizeof(void*) ? a->token_advantages : nullptr;
+}
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -231,8 +235,11 @@ int check_loss_args(const plp_args* a, bool pointers = true) {
   if (!(a->top_entropy_quantile >= 0.0 && a->top_entropy_quantile <= 1.0))
     return fail(PLP_E_INVALID, "top_entropy_quantile must lie in [0, 1] (got %g)", a->top_entropy_quantile);
   if (a->chunk_sequences < 0) return fail(PLP_E_INVALID, "chunk_sequences must be >= 0");
-  if (pointers && (!a->completion_mask || !a->advantages))
-    return fail(PLP_E_INVALID, "completion_mask and advantages are required");
+  if (pointers && (!a->completion_mask || (!a->advantages && !token_advantages(a))))
+    return fail(PLP_E_INVALID, "completion_mask and advantages (or token_advantages) are required");
+  if (token_advantages(a) && a->loss_type == PLP_LOSS_GMPO)
+    return fail(PLP_E_UNSUPPORTED, "GMPO clips and averages per sequence and takes per-sequence advantages; "
+                                   "token_advantages is for GSPO_TOKEN, GRPO, BNPO and DAPO");
   return PLP_OK;
 }
 
@@ -269,6 +276,8 @@ LossParams loss_params(const plp_args* a, const unsigned long long* ntok_dev) {
   p.beta = a->beta;
   p.norm_tokens = a->loss_type == PLP_LOSS_DAPO ? global_tokens(a) : 0;
   p.ntok_dev = ntok_dev;
+  p.token_adv = token_advantages(a) != nullptr ? 1 : 0;
+  p.pad = 0;
   return p;
 }
 
@@ -416,14 +425,15 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
     const uint8_t* comp = a->completion_mask + r0;
     const uint8_t* ratio = a->ratio_mask ? a->ratio_mask + r0 : nullptr;
     const uint8_t* em = b.emask ? b.emask + r0 : nullptr;
-    const float* adv = a->advantages + s0;
-    HIP_TRY(launch_loss_seq_partial(lpar, bc, b.lp + r0, old, ref, comp, ratio, em, adv, p.St, b.part, st));
+    const float* adv = a->advantages ? a->advantages + s0 : nullptr;
+    const float* tadv = token_advantages(a) ? token_advantages(a) + r0 : nullptr;
+    HIP_TRY(launch_loss_seq_partial(lpar, bc, b.lp + r0, old, ref, comp, ratio, em, adv, tadv, p.St, b.part, st));
     const bool last = c == p.nchunks - 1;
     HIP_TRY(launch_loss_seq_final(lpar, bc, p.St, b.part, adv, b.coef, b.acc, c == 0, p.entropy ? b.thr : nullptr,
                                   last ? out->loss : nullptr, last ? out->metrics : nullptr, st));
     float* g = out->dlogp_out ? out->dlogp_out + r0 : b.g;
     int* cnt32 = p.need_gw ? (int*)b.cscratch : nullptr;
-    HIP_TRY(launch_loss_tokens(a->dtype, lpar, bc, b.lp + r0, old, ref, comp, ratio, em, b.coef, g, cnt32,
+    HIP_TRY(launch_loss_tokens(a->dtype, lpar, bc, b.lp + r0, old, ref, comp, ratio, em, tadv, b.coef, g, cnt32,
                                p.need_o ? b.v : nullptr, H, inv_tau,
                                p.need_o ? (char*)out->grad_hidden + (size_t)r0 * H * es : nullptr, st));
     if (p.need_gw) {
@@ -576,12 +586,12 @@ PLP_API int plp_policy_loss_from_logprobs(const plp_args* a, const float* logp, 
   }
   const uint8_t* em = q_on ? emask : nullptr;
   HIP_TRY(launch_loss_seq_partial(lpar, a->B, logp, a->old_logp, a->ref_logp, a->completion_mask, a->ratio_mask, em,
-                                  a->advantages, St, part, st));
+                                  a->advantages, token_advantages(a), St, part, st));
   HIP_TRY(launch_loss_seq_final(lpar, a->B, St, part, a->advantages, coef, acc, true, q_on ? thr : nullptr, out->loss,
                                 out->metrics, st));
   float* g = out->dlogp_out ? out->dlogp_out : gbuf;
   HIP_TRY(launch_loss_tokens(PLP_DTYPE_F32, lpar, a->B, logp, a->old_logp, a->ref_logp, a->completion_mask,
-                             a->ratio_mask, em, coef, g, nullptr, nullptr, 0, 1.0f, nullptr, st));
+                             a->ratio_mask, em, token_advantages(a), coef, g, nullptr, nullptr, 0, 1.0f, nullptr, st));
   if (out->entropy_mask_out) HIP_TRY(launch_copy_mask(q_on ? emask : a->completion_mask, N, out->entropy_mask_out, st));
   return ok();
 }

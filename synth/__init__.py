@@ -36,6 +36,7 @@ DAPO = "dapo"
 
 # Stream ids inside SeedSequence([seed, cfg_id, stream]).
 _S_H, _S_W, _S_B, _S_Y, _S_P, _S_A, _S_OLD, _S_REF, _S_ZERO = range(9)
+_S_TADV = 20
 
 
 @dataclass(frozen=True)
@@ -69,6 +70,7 @@ class Spec:
     chunk_sequences: int = 0                # 0: whole batch in one chunk
     reduction: str = "seq_mean"             # "seq_mean" or "token_sum"
     global_tokens: int = 0                  # DAPO divisor; 0 = the batch's completion tokens
+    token_adv: bool = False                 # one advantage per token (N,) instead of per sequence
     seed: int = 0
 
     @property
@@ -172,6 +174,13 @@ def advantages(spec: Spec) -> np.ndarray:
     return a.astype(np.float32)
 
 
+def token_advantages(spec: Spec, completion: np.ndarray) -> np.ndarray:
+    """Per-token advantages [N]: N(0,1) on completion tokens, 0 elsewhere (the
+    layout of a datum whose advantages are zeroed off the completion)."""
+    a = _rng(spec, _S_TADV).standard_normal(spec.N).astype(np.float32)
+    return np.where(np.asarray(completion) != 0, a, np.float32(0.0)).astype(np.float32)
+
+
 def targets(spec: Spec) -> np.ndarray:
     return _rng(spec, _S_Y).integers(0, spec.V, size=spec.N, dtype=np.int64)
 
@@ -260,6 +269,7 @@ def make(spec: Spec, with_hidden: bool = True) -> dict:
     d["targets"] = targets(spec)
     d["completion_mask"] = completion_mask(spec)
     d["advantages"] = advantages(spec)
+    d["token_advantages"] = token_advantages(spec, d["completion_mask"]) if spec.token_adv else None
     d["old_noise"] = old_noise(spec)
     d["ref_noise"] = ref_noise(spec)
     return d

@@ -42,7 +42,8 @@ def gpu_inputs(spec: synth.Spec, d: dict) -> dict:
         bias=dev_tensor(d["b_raw"], dt) if d["b_raw"] is not None else None,
         targets=dev_tensor(d["targets"]),
         completion_mask=dev_tensor(d["completion_mask"]),
-        advantages=dev_tensor(d["advantages"]),
+        advantages=dev_tensor(d["advantages"]) if d.get("token_advantages") is None else None,
+        token_advantages=dev_tensor(d.get("token_advantages")),
         old_logp=dev_tensor(d["old"]),
         ref_logp=dev_tensor(d["ref"]),
     )
@@ -54,7 +55,8 @@ def run_gpu(spec: synth.Spec, d: dict, **kw) -> dict:
     args = dict(B=spec.B, T=spec.T, loss_type=spec.loss_type, epsilon_low=spec.eps_low,
                 epsilon_high=spec.eps_high, beta=spec.beta, temperature=spec.temperature,
                 top_entropy_quantile=spec.top_entropy_quantile, chunk_sequences=spec.chunk_sequences,
-                reduction=spec.reduction, global_tokens=spec.global_tokens, diagnostics=True)
+                reduction=spec.reduction, global_tokens=spec.global_tokens,
+                token_advantages=g["token_advantages"], diagnostics=True)
     args.update(kw)
     out = plp.fused_lmhead_policy_loss_fwd_bwd(g["hidden"], g["weight"], g["targets"], g["completion_mask"],
                                                g["advantages"], bias=g["bias"], old_logp=g["old_logp"],
@@ -65,8 +67,10 @@ def run_gpu(spec: synth.Spec, d: dict, **kw) -> dict:
 
 def run_oracle(spec: synth.Spec, d: dict, want_grads=True) -> dict:
     cfg = oracle.LossConfig.from_spec(spec)
+    tadv = d.get("token_advantages")
     return oracle.run(cfg, d["h"], d["W"], d["b"], d["targets"], d["old"], d["ref"], d["completion_mask"], None,
-                      d["advantages"], want_grads=want_grads, fwd=d["fwd"])
+                      None if tadv is not None else d["advantages"], want_grads=want_grads, fwd=d["fwd"],
+                      token_advantages=tadv)
 
 
 def rel_l2(a, b) -> float:

@@ -186,3 +186,40 @@ def test_token_clip_exact_boundaries():
     g = out["dlogp"].cpu().numpy()
     np.testing.assert_array_equal(g != 0, p["g"] != 0)
     assert abs(out["loss"].cpu().numpy()[0] - loss) <= 1e-6
+
+
+@pytest.mark.parametrize("loss_type,reduction,q,T", [
+    ("gspo_token", "token_sum", 1.0, 50),
+    ("gspo_token", "seq_mean", 0.5, 4500),
+    ("grpo", "seq_mean", 1.0, 3000),
+    ("dapo", "seq_mean", 0.5, 90),
+])
+def test_policy_loss_token_advantages(loss_type, reduction, q, T):
+    """Per-token advantages (N,), both signs on the completion, zero
+    elsewhere: loss, metrics and dL/dlogp against the oracle."""
+    import rl_policy_gradient_amd as plp
+    B = 6
+    gspo = loss_type == "gspo_token"
+    eps = (2e-4, 2e-4) if gspo else (0.2, 0.3)
+    cfg, lp, old, ref, comp, rm, A, ent = _loss_case(T + 7, B, T, loss_type, 0.04, q, False, reduction, eps,
+                                                     0.01 if gspo else 0.3)
+    r = np.random.default_rng(T)
+    At = (r.standard_normal(B * T) * (comp != 0)).astype(np.float32)
+    _say(f"token advantages {loss_type} {reduction} q={q} T={T}")
+    emask, thr = (oracle.entropy_quantile_mask(ent, comp != 0, q) if q < 1 else (None, np.float32(np.nan)))
+    p = oracle.policy_loss(cfg, lp.astype(np.float64), old, ref, comp, None, None, emask, token_advantages=At)
+    assert p["clipped_tok"].any()
+    loss, metrics = oracle.finalize_metrics([p], thr)
+    out = plp.policy_loss_from_logprobs(dev_tensor(lp), dev_tensor(comp), None, B, T, old_logp=dev_tensor(old),
+                                        ref_logp=dev_tensor(ref), entropy=dev_tensor(ent), loss_type=loss_type,
+                                        reduction=reduction, epsilon_low=eps[0], epsilon_high=eps[1], beta=0.04,
+                                        top_entropy_quantile=q, token_advantages=dev_tensor(At))
+    torch.cuda.synchronize()
+    gl = out["loss"].cpu().numpy()[0]
+    assert abs(gl - loss) <= 1e-5 * max(1.0, abs(loss)), (gl, loss)
+    m = out["metrics"].cpu().numpy()
+    assert m[6] == metrics[6] and m[7] == metrics[7], (m, metrics)
+    assert np.float32(m[0]).view(np.uint32) == np.float32(metrics[0]).view(np.uint32)
+    np.testing.assert_allclose(m[[1, 2, 3, 5]], metrics[[1, 2, 3, 5]], rtol=1e-5, atol=1e-7)
+    g = out["dlogp"].cpu().numpy()
+    np.testing.assert_allclose(g, p["g"], rtol=1e-5, atol=1e-7 * np.abs(p["g"]).max())

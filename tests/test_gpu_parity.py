@@ -95,6 +95,14 @@ SMALL = {
     "generic_f32_dapo": synth.small("generic_dapo", cfg_id=114, dtype="f32", B=3, T=30, H=48, V=300,
                                     loss_type=synth.DAPO, eps_low=0.1, eps_high=0.12, chunk_sequences=2,
                                     top_entropy_quantile=0.3, beta=0.04, ref_noise_std=0.05),
+    # per-token advantages (N,), zero off the completion
+    "mfma_gspo_token_adv_sum": synth.small("mfma_gspo_tadv", cfg_id=115, B=3, T=64, H=256, V=1200,
+                                           loss_type=synth.GSPO_TOKEN, eps_low=2e-3, eps_high=2e-3,
+                                           old_noise_std=1e-2, token_adv=True, reduction="token_sum",
+                                           top_entropy_quantile=0.5),
+    "generic_f32_grpo_token_adv": synth.small("generic_grpo_tadv", cfg_id=116, dtype="f32", B=3, T=30, H=48,
+                                              V=300, loss_type=synth.GRPO, eps_low=0.1, eps_high=0.1,
+                                              token_adv=True, chunk_sequences=2, beta=0.04, ref_noise_std=0.05),
     # generic (vector ALU) path: fp32, and bf16 with H not a multiple of 128
     "generic_f32_cfg1": synth.CONFIGS[1],
     "generic_bf16_h96": synth.small("generic_h96", cfg_id=106, B=2, T=50, H=96, V=700, bias=True),
