@@ -134,6 +134,17 @@ __device__ __forceinline__ const __bf16* frag_ptr(const __bf16* Xf, int64_t tile
   return Xf + ((((tile * 4 + w) * KS) + ks) * 64 + lane) * 8;
 }
 
+// Loads of fragment-major data through a buffer resource: the workgroup-
+// uniform base (and a byte range that bounds the access) in scalar registers,
+// the lane's byte offset in one vector register, a constant byte offset in a
+// scalar register, so no 64-bit vector address per load is kept live.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t frag_rsrc(const __bf16* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ bf16x8 ld_buf(__amdgpu_buffer_rsrc_t r, int lane_bytes, int const_bytes) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_bytes, const_bytes, 0));
+}
+
 // Store of a wave's accumulator (rows 32qb + 8(i/4) + 4h + i%4 of the
 // resident block, columns 32db + c of the wave's slice) through a wave-private
 // LDS buffer of 32 x DS floats, one 32-row half at a time, so that the global
@@ -231,7 +242,8 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   float* s_x = reinterpret_cast<float*>(&s_p[0][0]);              // [NW][64]
   double* s_xd = reinterpret_cast<double*>(&s_part[0][0][0][0]);   // [NW][2][64]
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5, c = lane & 31;
   const int nbq = w & 1, kh = w >> 1;  // quarter this wave reduces: row block nbq, tile-row half kh
   const int rb = blockIdx.x / Sv, sv = blockIdx.x - rb * Sv;
@@ -266,10 +278,11 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   bf16x8 q[2][KS];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int64_t row = min(q0 + 32 * nb + c, N - 1);
-    const __bf16* src = h + row * H + d0 + 8 * hh;
+    // rows past N repeat row N - 1 (their results are never stored)
+    const int row = (int)min((int64_t)(32 * nb + c), N - 1 - q0);
+    const auto r = frag_rsrc(h + q0 * H, BQ * H * 2);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) q[nb][ks] = ld16(src + 16 * ks);
+    for (int ks = 0; ks < KS; ++ks) q[nb][ks] = ld_buf(r, (row * H + d0 + 8 * hh) * 2, 32 * ks);
   }
 
   f32x16 o[2][WITH_O ? DB : 1];
@@ -288,7 +301,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   // rows past V are zero in the fragment-major copy and masked in the epilogue
   auto load_a = [&](int t, bf16x8 (&a)[KS]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a[ks] = ld16(frag_ptr<KB>(Wf, t, w, ks, lane));
+    for (int ks = 0; ks < KS; ++ks) a[ks] = ld_buf(frag_rsrc(frag_ptr<KB>(Wf, t, w, 0, 0), KS * 1024), lane * 16, ks * 1024);
   };
   // Bias of tile rows kvq(kh, hh, 0..7), kept as packed bf16 (two groups of
   // four consecutive rows, one 8-byte load each when inside the vocabulary).
@@ -319,14 +332,14 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   // issued, is staged for the transposing load (WITH_O) and reloaded with
   // the same slice of tile `t_next`.
   auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int buf, int t_next) {
-    const __bf16* src = frag_ptr<KB>(Wf, t_next, w, 0, lane);
+    const auto r = frag_rsrc(frag_ptr<KB>(Wf, t_next, w, 0, 0), KS * 1024);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a[ks], q[nb][ks], ks == 0 ? zero16() : acc[nb]);
       if constexpr (WITH_O)
         *reinterpret_cast<bf16x8*>(&s_t[w][buf][sw_base[ks & 1] + 16 * ks]) = a[ks];
-      a[ks] = ld16(src + 512 * ks);
+      a[ks] = ld_buf(r, lane * 16, ks * 1024);
     }
   };
   // The partial S^T in four groups of four rows per row block; the wave
@@ -525,7 +538,8 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
   __shared__ unsigned short s_t[NW][2][BK * TS];
   double* s_xd = reinterpret_cast<double*>(&s_part[0][0][0][0]);  // [NW][64], after the sweep
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5, c = lane & 31;
   const int nbq = w & 1, kh = w >> 1;
   const int q0 = blockIdx.x * BQ;
@@ -560,7 +574,8 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) q[nb][ks] = ld16(frag_ptr<KB>(Wf, q0 / BK + nb, w, ks, lane));
+    for (int ks = 0; ks < KS; ++ks)
+      q[nb][ks] = ld_buf(frag_rsrc(frag_ptr<KB>(Wf, q0 / BK + nb, w, 0, 0), KS * 1024), lane * 16, ks * 1024);
   f32x16 o[2][DB];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
@@ -573,7 +588,7 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
 
   auto load_a = [&](int t, bf16x8 (&a)[KS]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a[ks] = ld16(frag_ptr<KB>(hcf, t, w, ks, lane));
+    for (int ks = 0; ks < KS; ++ks) a[ks] = ld_buf(frag_rsrc(frag_ptr<KB>(hcf, t, w, 0, 0), KS * 1024), lane * 16, ks * 1024);
   };
   // Per-token data of tile t, loaded into a register one phase before it is
   // written to LDS (wave 0, lanes < 32), so the load latency stays hidden.
@@ -585,13 +600,13 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
     if (w == 0 && lane < BK) s_tok[t & 1][lane] = tk;
   };
   auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int buf, int t_next) {
-    const __bf16* src = frag_ptr<KB>(hcf, t_next, w, 0, lane);
+    const auto r = frag_rsrc(frag_ptr<KB>(hcf, t_next, w, 0, 0), KS * 1024);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a[ks], q[nb][ks], ks == 0 ? zero16() : acc[nb]);
       *reinterpret_cast<bf16x8*>(&s_t[w][buf][sw_base[ks & 1] + 16 * ks]) = a[ks];
-      a[ks] = ld16(src + 512 * ks);
+      a[ks] = ld_buf(r, lane * 16, ks * 1024);
     }
   };
   auto write_part = [&](const f32x16 (&acc)[2]) {
