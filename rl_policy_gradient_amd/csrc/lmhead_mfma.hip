@@ -317,18 +317,23 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   };
   // Bias of tile rows kvq(kh, hh, 0..7), kept as packed bf16 (two groups of
   // four consecutive rows, one 8-byte load each when inside the vocabulary).
+  const auto bias_r = frag_rsrc(bias, HAS_BIAS ? V * 2 : 0);
   auto load_bias = [&](int t, uint2 (&bv)[2]) {
     if constexpr (HAS_BIAS) {
+      if ((t + 1) * BK <= V) {  // uniform: the whole tile lies inside the vocabulary
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int r0 = t * BK + 16 * kh + 8 * hf + 4 * hh;
-        if (r0 + 3 < V) {
-          bv[hf] = *reinterpret_cast<const uint2*>(bias + r0);
-        } else {
-          unsigned short e[4];
+        for (int hf = 0; hf < 2; ++hf) {
+          const int r0 = t * BK + 16 * kh + 8 * hf + 4 * hh;
+          bv[hf] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(bias_r, r0 * 2, 0, 0));
+        }
+      } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) e[j] = __builtin_bit_cast(unsigned short, bias[min(r0 + j, V - 1)]);
-          bv[hf] = make_uint2(e[0] | ((unsigned)e[1] << 16), e[2] | ((unsigned)e[3] << 16));
+        for (int hf = 0; hf < 2; ++hf) {
+          const int r0 = t * BK + 16 * kh + 8 * hf + 4 * hh;
+          unsigned e[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_raw_buffer_load_b16(bias_r, min(r0 + j, V - 1) * 2, 0, 0);
+          bv[hf] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
         }
       }
     } else {
