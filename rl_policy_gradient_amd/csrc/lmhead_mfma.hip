@@ -543,7 +543,8 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
                      const __bf16* __restrict__ hcf, const TokData* __restrict__ tok,
                      const int* __restrict__ count_dev, int V, float inv_tau, int acc_mode,
                      float* __restrict__ gW_acc, float* __restrict__ gb_acc, __bf16* __restrict__ gW_out,
-                     __bf16* __restrict__ gb_out) {
+                     __bf16* __restrict__ gb_out, int whole, int parts, float* __restrict__ part_w,
+                     float* __restrict__ part_b) {
   constexpr int H = 128 * KB;
   constexpr int DS = Stage<KB>::DS;
   constexpr int TS = Stage<KB>::TS;
@@ -559,7 +560,21 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5, c = lane & 31;
   const int nbq = w & 1, kh = w >> 1;
-  const int q0 = blockIdx.x * BQ;
+  const int n_tok = *count_dev;
+  const int n_tiles = (n_tok + BK - 1) / BK;
+  // Workgroups below `whole` take a vocabulary block and all token tiles.
+  // The blocks of the last, partial round are shared by `parts` workgroups
+  // each, which take contiguous thirds (or halves...) of the token tiles and
+  // write fp32 partial sums for tail_reduce_kernel.
+  int blk = blockIdx.x, t_lo = 0, t_hi = n_tiles, slot = -1;
+  if ((int)blockIdx.x >= whole) {
+    slot = (int)blockIdx.x - whole;
+    blk = whole + slot / parts;
+    const int part = slot - (slot / parts) * parts;
+    t_lo = (int)((int64_t)n_tiles * part / parts);
+    t_hi = (int)((int64_t)n_tiles * (part + 1) / parts);
+  }
+  const int q0 = blk * BQ;
   const int d0 = w * DS;
   // Stage write offsets (element) of lane (hh, c) for even / odd k-step:
   // row c, chunk 2ks + hh at position (2ks + hh) ^ f(c), f(c) = (c >> 2) & 3.
@@ -582,8 +597,6 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
     tr_base[0] = r * TS + 8 * (b ^ f) + 4 * (p & 1);
     tr_base[1] = (r + 8) * TS + 8 * (b ^ f ^ 2) + 4 * (p & 1);
   }
-  const int n_tok = *count_dev;
-  const int n_tiles = (n_tok + BK - 1) / BK;
 
   // Resident W fragments (B operand of S^T), rows q0 + 32nb + c, cols
   // d0 + 16ks + 8hh, from the fragment-major copy (rows past V are zero).
@@ -677,21 +690,21 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
   bf16x8 a[KS];
   f32x16 acc[2];
   f32x4 sf[2];
-  if (n_tiles > 0) {
-    load_tok(0);
-    stage_tok(0);
-    load_tok(min(1, n_tiles - 1));
-    load_a(0, a);
-    s_step(a, acc, 0, min(1, n_tiles - 1));
+  if (t_hi > t_lo) {
+    load_tok(t_lo);
+    stage_tok(t_lo);
+    load_tok(min(t_lo + 1, t_hi - 1));
+    load_a(t_lo, a);
+    s_step(a, acc, t_lo & 1, min(t_lo + 1, t_hi - 1));
     write_part(acc);
   }
   __syncthreads();
-  if (n_tiles > 0) reduce_part(sf);
+  if (t_hi > t_lo) reduce_part(sf);
 
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int t = t_lo; t < t_hi; ++t) {
     const int t0 = t * BK;
-    const int tn = min(t + 1, n_tiles - 1);
-    const int tnn = min(t + 2, n_tiles - 1);
+    const int tn = min(t + 1, t_hi - 1);
+    const int tnn = min(t + 2, t_hi - 1);
     // ---- epilogue of tile t (vector ALU; the scheduler interleaves it with
     //      the logit MFMAs of tile t+1 below) -------------------------------
     bf16x8 pa;
@@ -727,6 +740,15 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
   __syncthreads();
   if (hh == 0) s_xd[w * 64 + c] = gbv;
   __syncthreads();
+  if (slot >= 0) {  // a share of a tail block: fp32 partial sums, combined by tail_reduce_kernel
+    if (kh == 0 && hh == 0) part_b[slot * BQ + 32 * nbq + c] = (float)(gbv + s_xd[(w ^ 2) * 64 + c]);
+    float* pw = part_w + (int64_t)slot * BQ * H;
+    store_acc<DS, DB>(o, reinterpret_cast<float*>(&s_t[w][0][0]), hh, c, lane,
+                      [&](int qb, int r, int col, f32x4 v) {
+                        *reinterpret_cast<f32x4*>(pw + (int64_t)(32 * qb + r) * H + d0 + col) = v;
+                      });
+    return;  // uniform
+  }
   const bool from_acc = acc_mode == 2 || acc_mode == 3;
   const bool to_acc = acc_mode == 1 || acc_mode == 2;
   if (kh == 0 && hh == 0 && my_v < V && (to_acc ? gb_acc != nullptr : gb_out != nullptr)) {
@@ -776,17 +798,105 @@ hipError_t fwd_dispatch(const __bf16* h, const __bf16* Wf, const __bf16* b, int6
   return hipGetLastError();
 }
 
+constexpr int kTailParts = 4;     // workgroups sharing one tail block of the weight-gradient sweep
+constexpr int kMaxTailWGs = 256;  // bound of the partial-sum scratch (workgroups)
+
+// Workgroups of 256 threads of `kernel` the device holds at once (compute
+// units x workgroups per unit), computed once per device and kernel.
+template <typename K>
+hipError_t resident_workgroups(K kernel, int* out) {
+  constexpr int kMaxDevices = 64;
+  static int cache[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && cache[dev] > 0) {
+    *out = cache[dev];
+    return hipSuccess;
+  }
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0);
+  if (e != hipSuccess) return e;
+  const int n = cus * (per_cu > 0 ? per_cu : 1);
+  if (dev >= 0 && dev < kMaxDevices) cache[dev] = n;
+  *out = n;
+  return hipSuccess;
+}
+
+// Sum of the partial results of the tail blocks (fixed order over the parts)
+// and the same output step as the sweep's own: accumulate into / store the
+// fp32 accumulators or store bf16 grad_W and grad_b. One workgroup per row.
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restrict__ part_w,
+                                                          const float* __restrict__ part_b, int whole, int parts,
+                                                          int H, int V, int acc_mode, float* __restrict__ gW_acc,
+                                                          float* __restrict__ gb_acc, __bf16* __restrict__ gW_out,
+                                                          __bf16* __restrict__ gb_out) {
+  const int tb = blockIdx.x / BQ, r = blockIdx.x - tb * BQ;
+  const int vr = (whole + tb) * BQ + r;
+  if (vr >= V) return;  // uniform
+  const bool from_acc = acc_mode == 2 || acc_mode == 3;
+  const bool to_acc = acc_mode == 1 || acc_mode == 2;
+  const int64_t stride = (int64_t)BQ * H;
+  const float* src = part_w + ((int64_t)tb * parts * BQ + r) * H;
+  for (int c4 = threadIdx.x; c4 < H / 4; c4 += 256) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * c4);
+    for (int p = 1; p < parts; ++p) v += *reinterpret_cast<const f32x4*>(src + p * stride + 4 * c4);
+    const int64_t k = (int64_t)vr * H + 4 * c4;
+    if (to_acc ? gW_acc != nullptr : gW_out != nullptr) {
+      if (from_acc) v += *reinterpret_cast<const f32x4*>(gW_acc + k);
+      if (to_acc) {
+        *reinterpret_cast<f32x4*>(gW_acc + k) = v;
+      } else {
+        bf16x4 u;
+        u[0] = (__bf16)v[0];
+        u[1] = (__bf16)v[1];
+        u[2] = (__bf16)v[2];
+        u[3] = (__bf16)v[3];
+        *reinterpret_cast<bf16x4*>(gW_out + k) = u;
+      }
+    }
+  }
+  if (threadIdx.x == 0 && (to_acc ? gb_acc != nullptr : gb_out != nullptr)) {
+    double val = 0.0;
+    for (int p = 0; p < parts; ++p) val += (double)part_b[((int64_t)tb * parts + p) * BQ + r];
+    if (from_acc) val += (double)gb_acc[vr];
+    if (to_acc) gb_acc[vr] = (float)val;
+    else gb_out[vr] = (__bf16)(float)val;
+  }
+}
+
 template <int KB>
 hipError_t bwd_dispatch(const __bf16* Wf, const __bf16* b, const __bf16* hcf, const TokData* tok, const int* count_dev,
                         int V, float inv_tau, int acc_mode, float* gW_acc, float* gb_acc, __bf16* gW_out,
-                        __bf16* gb_out, hipStream_t st) {
-  dim3 grid((unsigned)((V + BQ - 1) / BQ)), block(256);
+                        __bf16* gb_out, float* tail_scratch, hipStream_t st) {
+  // Blocks of the last, partial round of workgroups are split over the token
+  // tiles so that round ends sooner: `parts` workgroups per block, as many as
+  // fit the free slots (at most kTailParts, and kMaxTailWGs in all).
+  const int nblk = (V + BQ - 1) / BQ;
+  int resident = 0;
+  hipError_t e = b ? resident_workgroups(bwd_mfma_kernel<KB, true>, &resident)
+                   : resident_workgroups(bwd_mfma_kernel<KB, false>, &resident);
+  if (e != hipSuccess) return e;
+  const int rem = resident > 0 ? nblk % resident : 0;
+  int parts = rem > 0 ? min(kTailParts, min(resident, kMaxTailWGs) / rem) : 1;
+  if (tail_scratch == nullptr || parts < 2) parts = 1;
+  const int whole = parts > 1 ? nblk - rem : nblk;
+  const int tail_wgs = parts > 1 ? rem * parts : 0;
+  float* part_w = tail_scratch;
+  float* part_b = tail_scratch ? tail_scratch + (size_t)kMaxTailWGs * BQ * (128 * KB) : nullptr;
+  dim3 grid((unsigned)(whole + tail_wgs)), block(256);
   if (b)
     hipLaunchKernelGGL((bwd_mfma_kernel<KB, true>), grid, block, 0, st, Wf, b, hcf, tok, count_dev, V, inv_tau,
-                       acc_mode, gW_acc, gb_acc, gW_out, gb_out);
+                       acc_mode, gW_acc, gb_acc, gW_out, gb_out, whole, parts, part_w, part_b);
   else
     hipLaunchKernelGGL((bwd_mfma_kernel<KB, false>), grid, block, 0, st, Wf, b, hcf, tok, count_dev, V, inv_tau,
-                       acc_mode, gW_acc, gb_acc, gW_out, gb_out);
+                       acc_mode, gW_acc, gb_acc, gW_out, gb_out, whole, parts, part_w, part_b);
+  e = hipGetLastError();
+  if (e != hipSuccess || tail_wgs == 0) return e;
+  hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)(rem * BQ)), dim3(256), 0, st, part_w, part_b, whole, parts,
+                     128 * KB, V, acc_mode, gW_acc, gb_acc, gW_out, gb_out);
   return hipGetLastError();
 }
 
@@ -819,17 +929,26 @@ hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const __bf16* b, i
 
 hipError_t launch_bwd_mfma(const __bf16* Wf, const __bf16* b, const __bf16* hcf, const TokData* tok,
                            const int* count_dev, int H, int V, float inv_tau, int acc_mode, float* gW_acc,
-                           float* gb_acc, __bf16* gW_out, __bf16* gb_out, hipStream_t st) {
+                           float* gb_acc, __bf16* gW_out, __bf16* gb_out, float* tail_scratch, hipStream_t st) {
   switch (H / 128) {
-    case 1: return bwd_dispatch<1>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 2: return bwd_dispatch<2>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 3: return bwd_dispatch<3>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 4: return bwd_dispatch<4>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 5: return bwd_dispatch<5>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 6: return bwd_dispatch<6>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
-    case 7: return bwd_dispatch<7>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out, st);
+    case 1: return bwd_dispatch<1>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+                                   tail_scratch, st);
+    case 2: return bwd_dispatch<2>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+                                   tail_scratch, st);
+    case 3: return bwd_dispatch<3>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+                                   tail_scratch, st);
+    case 4: return bwd_dispatch<4>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+                                   tail_scratch, st);
+    case 5: return bwd_dispatch<5>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+                                   tail_scratch, st);
+    case 6: return bwd_dispatch<6>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+                                   tail_scratch, st);
+    case 7: return bwd_dispatch<7>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+                                   tail_scratch, st);
     default: return hipErrorInvalidValue;
   }
 }
+
+size_t bwd_tail_scratch_floats(int H) { return (size_t)kMaxTailWGs * BQ * H + (size_t)kMaxTailWGs * BQ; }
 
 }  // namespace plp

@@ -111,6 +111,7 @@ struct Bufs {
   int* count = nullptr;
   void* cscratch = nullptr;
   void* hc = nullptr;
+  float* tail = nullptr;       // partial sums of the weight-gradient sweep's split tail blocks
   float* gW_acc = nullptr;
   float* gb_acc = nullptr;
 };
@@ -161,6 +162,7 @@ size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
     b.count = c.take<int>(1);
     b.cscratch = c.take<char>(compact_scratch_bytes(p.Nc));
     b.hc = c.take<char>((size_t)p.cap * H * esize(a->dtype));
+    if (p.mfma) b.tail = c.take<float>(bwd_tail_scratch_floats(H));
     if (p.nchunks > 1) {
       b.gW_acc = c.take<float>((size_t)V * H);
       if (p.need_gb) b.gb_acc = c.take<float>(V);
@@ -448,7 +450,7 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
         hipEvent_t* ev = prof_slot(1);
         if (ev) HIP_TRY(hipEventRecord(ev[0], st));
         HIP_TRY(launch_bwd_mfma(b.Wf, (const __bf16*)a->bias, (const __bf16*)b.hc, b.tok, b.count, H, V, inv_tau, mode,
-                                b.gW_acc, b.gb_acc, (__bf16*)out->grad_weight, (__bf16*)out->grad_bias, st));
+                                b.gW_acc, b.gb_acc, (__bf16*)out->grad_weight, (__bf16*)out->grad_bias, b.tail, st));
         if (ev) HIP_TRY(hipEventRecord(ev[1], st));
       } else
         HIP_TRY(launch_bwd_generic(a->dtype, a->weight, a->bias, b.hc, b.tok, b.count, H, V, inv_tau, mode, b.gW_acc,
