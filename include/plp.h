@@ -43,7 +43,9 @@
  *
  * Layouts: row-major. hidden [N,H] with the B sequences stored one after the
  * other, T rows each (row n = i*T + t); weight [V,H] (nn.Linear layout);
- * per-token arrays [N]; advantages [B].
+ * per-token arrays [N]; advantages [B]. hidden, weight, bias and the
+ * gradient outputs must be 16-byte aligned (the kernels move 16-byte
+ * chunks); a misaligned one is rejected with PLP_E_INVALID.
  */
 #ifndef PLP_H
 #define PLP_H

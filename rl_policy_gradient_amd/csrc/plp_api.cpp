@@ -251,6 +251,8 @@ int check_fused_args(const plp_args* a) {
   if (a->dtype != PLP_DTYPE_F32 && a->dtype != PLP_DTYPE_BF16) return fail(PLP_E_INVALID, "unknown dtype %d", a->dtype);
   if (a->H < 1 || a->V < 1) return fail(PLP_E_INVALID, "H and V must be >= 1");
   if (!a->hidden || !a->weight || !a->targets) return fail(PLP_E_INVALID, "hidden, weight and targets are required");
+  if (((uintptr_t)a->hidden | (uintptr_t)a->weight | (uintptr_t)a->bias) % 16 != 0)
+    return fail(PLP_E_INVALID, "hidden, weight and bias must be 16-byte aligned");
   if (!mfma_eligible(a->dtype, a->H) && !generic_eligible(a->H))
     return fail(PLP_E_UNSUPPORTED, "H=%d is not supported (bf16 MFMA path: H multiple of 128 up to 896; "
                                    "generic path: H <= 4096)", a->H);
@@ -375,6 +377,8 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
   if (!out || out->struct_size < sizeof(plp_outputs)) return fail(PLP_E_INVALID, "outputs NULL or struct_size too small");
   if (!out->loss || !out->metrics) return fail(PLP_E_INVALID, "loss and metrics outputs are required");
   if (out->grad_bias && !a->bias) return fail(PLP_E_INVALID, "grad_bias requested without bias");
+  if (((uintptr_t)out->grad_hidden | (uintptr_t)out->grad_weight | (uintptr_t)out->grad_bias) % 16 != 0)
+    return fail(PLP_E_INVALID, "gradient outputs must be 16-byte aligned");
   size_t need_full = 0;
   {
     Plan pf = make_plan(a, true, true, a->bias != nullptr);
@@ -483,6 +487,8 @@ PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const 
   int rc = plp_selective_entropy_workspace_size(N, H, V, dtype, &need);
   if (rc) return rc;
   if (!hidden || !weight || !entropy_out) return fail(PLP_E_INVALID, "hidden, weight and entropy_out are required");
+  if (((uintptr_t)hidden | (uintptr_t)weight | (uintptr_t)bias) % 16 != 0)
+    return fail(PLP_E_INVALID, "hidden, weight and bias must be 16-byte aligned");
   if (logp_out && !targets) return fail(PLP_E_INVALID, "logp_out needs targets");
   if (!(temperature > 0.f) || !isfinite(temperature)) return fail(PLP_E_INVALID, "temperature must be > 0");
   if (!mfma_eligible(dtype, H) && !generic_eligible(H)) return fail(PLP_E_UNSUPPORTED, "H=%d is not supported", H);

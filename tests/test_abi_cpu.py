@@ -103,6 +103,7 @@ def _call(a, o=None, ws=None, ws_bytes=0):
     (lambda a: (setattr(a, "loss_type", abi.LOSS_DAPO), setattr(a, "global_tokens", -5)),
      abi.PLP_E_INVALID, "global_tokens"),
     (lambda a: setattr(a, "loss_type", 5), abi.PLP_E_INVALID, "loss_type"),
+    (lambda a: setattr(a, "weight", 0x1008), abi.PLP_E_INVALID, "16-byte aligned"),
     (lambda a: setattr(a, "token_advantages", 0x4000), abi.PLP_E_UNSUPPORTED, "per-sequence advantages"),
     (lambda a: setattr(a, "advantages", None), abi.PLP_E_INVALID, "advantages"),
     (lambda a: setattr(a, "struct_size", 8), abi.PLP_E_INVALID, "struct_size"),
