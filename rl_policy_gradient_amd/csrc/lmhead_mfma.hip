@@ -170,45 +170,33 @@ __device__ __forceinline__ void store_acc(const f32x16 (&o)[2][DB], float* buf, 
 
 // ---------------------------------------------------------------------------
 // Fragment-major copy of 32-row tiles of X (rows X[idx[k]] when idx is given),
-// rows at or past `rows` (= *count_dev when given) zero. A workgroup stages
-// one tile in LDS: it reads the 32 source rows whole (each wave instruction a
-// run of 16-byte chunks along a row) and writes the tile in fragment-major
-// order (each wave instruction one contiguous kilobyte), so both sides move
-// full cache lines. Rows are padded by one chunk in LDS so that the
-// fragment-order reads (16 rows x one chunk per 16 lanes) hit distinct banks.
+// rows at or past `rows` (= *count_dev when given) zero. One thread per output
+// chunk: the stores are contiguous; each wave's loads touch 32 rows, and
+// every source line is used whole by the waves of the block.
 // ---------------------------------------------------------------------------
-constexpr int kCopyMaxChunks = 896 / 8;  // 16-byte chunks per row at the largest H of the MFMA path
-
 __global__ __launch_bounds__(256) void frag_copy_kernel(const __bf16* __restrict__ X, const int* __restrict__ idx,
-                                                        const int* __restrict__ count_dev, int64_t rows_host, int H,
-                                                        int64_t tiles, __bf16* __restrict__ Xf) {
-  __shared__ uint4 buf[BK * (kCopyMaxChunks + 1)];
+                                                               const int* __restrict__ count_dev, int64_t rows_host,
+                                                               int H, int64_t tiles, __bf16* __restrict__ Xf) {
   const int64_t rows = count_dev ? (int64_t)(*count_dev) : rows_host;
-  const int cpr = H / 8, stride = cpr + 1;
+  const int cpr = H / 8;
   // with a device row count, tiles past the last gathered row are never read
   const int64_t used = count_dev ? min(tiles, (rows + BK - 1) / BK) : tiles;
-  const int per_tile = BK * cpr;
+  const int64_t total = used * BK * cpr;
   const int ks_per_wave = H / 64;
-  for (int64_t t = blockIdx.x; t < used; t += gridDim.x) {
-    for (int q = threadIdx.x; q < per_tile; q += 256) {
-      const int r = q / cpr, k = q - r * cpr;
-      const int64_t row = t * BK + r;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (row < rows) {
-        const int64_t src = idx ? (int64_t)idx[row] : row;
-        // each source row is read once: stream it past the caches
-        v = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X + src * H) + k));
-      }
-      buf[r * stride + k] = v;
+  for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
+    const int64_t t = o / (BK * cpr);
+    const int oo = (int)(o - t * BK * cpr);
+    const int lane = oo & 63, rem = oo >> 6;
+    const int w = rem / ks_per_wave, ks = rem - w * ks_per_wave;
+    const int64_t r = t * BK + (lane & 31);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rows) {
+      const int64_t src = idx ? (int64_t)idx[r] : r;
+      // each source row is read once: stream it past the caches
+      v = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                        reinterpret_cast<const u32x4*>(X + src * H + (w * (H / 32) + 2 * ks + (lane >> 5)) * 8)));
     }
-    __syncthreads();
-    uint4* dst = reinterpret_cast<uint4*>(Xf) + t * per_tile;
-    for (int o = threadIdx.x; o < per_tile; o += 256) {
-      const int lane = o & 63, rem = o >> 6;
-      const int w = rem / ks_per_wave, ks = rem - w * ks_per_wave;
-      dst[o] = buf[(lane & 31) * stride + w * (H / 32) + 2 * ks + (lane >> 5)];
-    }
-    __syncthreads();
+    *reinterpret_cast<uint4*>(Xf + o * 8) = v;
   }
 }
 
@@ -905,8 +893,9 @@ hipError_t bwd_dispatch(const __bf16* Wf, const __bf16* b, const __bf16* hcf, co
 hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_dev, int64_t rows, int64_t tiles, int H,
                             __bf16* Xf, hipStream_t st) {
   if (tiles <= 0) return hipSuccess;
-  if (H / 8 > kCopyMaxChunks || H % 64 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(frag_copy_kernel, dim3((unsigned)(tiles < 8192 ? tiles : 8192)), dim3(256), 0, st, X, idx,
+  const int64_t total = tiles * BK * (H / 8);
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(frag_copy_kernel, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(256), 0, st, X, idx,
                      count_dev, rows, H, tiles, Xf);
   return hipGetLastError();
 }
