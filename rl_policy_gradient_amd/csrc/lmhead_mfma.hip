@@ -170,33 +170,38 @@ __device__ __forceinline__ void store_acc(const f32x16 (&o)[2][DB], float* buf, 
 
 // ---------------------------------------------------------------------------
 // Fragment-major copy of 32-row tiles of X (rows X[idx[k]] when idx is given),
-// rows at or past `rows` (= *count_dev when given) zero. One thread per output
-// chunk: the stores are contiguous; each wave's loads touch 32 rows, and
-// every source line is used whole by the waves of the block.
+// rows at or past `rows` (= *count_dev when given) zero. Each thread copies
+// the chunks of two consecutive k-steps of one row (two loads 32 bytes apart
+// in flight); each wave's stores are two contiguous kilobytes and its loads
+// touch 32 rows, every source line being used whole by neighbouring waves.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void frag_copy_kernel(const __bf16* __restrict__ X, const int* __restrict__ idx,
-                                                               const int* __restrict__ count_dev, int64_t rows_host,
-                                                               int H, int64_t tiles, __bf16* __restrict__ Xf) {
+                                                        const int* __restrict__ count_dev, int64_t rows_host, int H,
+                                                        int64_t tiles, __bf16* __restrict__ Xf) {
   const int64_t rows = count_dev ? (int64_t)(*count_dev) : rows_host;
   const int cpr = H / 8;
   // with a device row count, tiles past the last gathered row are never read
   const int64_t used = count_dev ? min(tiles, (rows + BK - 1) / BK) : tiles;
-  const int64_t total = used * BK * cpr;
   const int ks_per_wave = H / 64;
+  const int groups = ks_per_wave / 2;  // each thread copies the chunks of two consecutive k-steps
+  const int64_t total = used * 4 * groups * 64;  // (tile, wave slice, k-step pair, lane)
   for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
-    const int64_t t = o / (BK * cpr);
-    const int oo = (int)(o - t * BK * cpr);
-    const int lane = oo & 63, rem = oo >> 6;
-    const int w = rem / ks_per_wave, ks = rem - w * ks_per_wave;
+    const int lane = (int)(o & 63);
+    const int64_t rest = o >> 6;
+    const int gq = (int)(rest % (4 * groups));
+    const int64_t t = rest / (4 * groups);
+    const int w = gq / groups, ks0 = 2 * (gq - w * groups);
     const int64_t r = t * BK + (lane & 31);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
     if (r < rows) {
       const int64_t src = idx ? (int64_t)idx[r] : r;
-      // plain loads: the four waves reading one source line's 32-byte pieces
-      // find it in the cache (nontemporal loads re-fetch it, 40% slower)
-      v = *reinterpret_cast<const uint4*>(X + src * H + (w * (H / 32) + 2 * ks + (lane >> 5)) * 8);
+      const __bf16* base = X + src * H + (w * (H / 32) + 2 * ks0 + (lane >> 5)) * 8;
+      v0 = *reinterpret_cast<const uint4*>(base);
+      v1 = *reinterpret_cast<const uint4*>(base + 16);
     }
-    *reinterpret_cast<uint4*>(Xf + o * 8) = v;
+    uint4* dst = reinterpret_cast<uint4*>(Xf) + ((t * 4 + w) * ks_per_wave + ks0) * 64 + lane;
+    dst[0] = v0;
+    dst[64] = v1;
   }
 }
 
@@ -893,7 +898,7 @@ hipError_t bwd_dispatch(const __bf16* Wf, const __bf16* b, const __bf16* hcf, co
 hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_dev, int64_t rows, int64_t tiles, int H,
                             __bf16* Xf, hipStream_t st) {
   if (tiles <= 0) return hipSuccess;
-  const int64_t total = tiles * BK * (H / 8);
+  const int64_t total = tiles * BK * (H / 8) / 2;
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(frag_copy_kernel, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(256), 0, st, X, idx,
                      count_dev, rows, H, tiles, Xf);
