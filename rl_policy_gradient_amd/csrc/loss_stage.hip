@@ -406,6 +406,9 @@ __global__ __launch_bounds__(NT) void token_kernel(LossParams p, int64_t Nc, con
                                                    float inv_tau, T* __restrict__ gh) {
   __shared__ float s_g[TB];
   const int64_t t0 = (int64_t)blockIdx.x * TB;
+  // blockIdx.y = column slice of grad_h; every slice evaluates g for its 32
+  // tokens (cheap), slice 0 alone writes g and the counts
+  const bool writer = blockIdx.y == 0;
   if (threadIdx.x < TB) {
     const int64_t t = t0 + threadIdx.x;
     float gv32 = 0.f;
@@ -427,10 +430,10 @@ __global__ __launch_bounds__(NT) void token_kernel(LossParams p, int64_t Nc, con
       }
       if (e.M) gv += c.wbeta * e.dkl;
       gv32 = (float)gv;
-      g[t] = gv32;
+      if (writer) g[t] = gv32;
     }
     s_g[threadIdx.x] = gv32;
-    if (cnt32) {
+    if (cnt32 && writer) {
       const unsigned long long m = __ballot(gv32 != 0.f);
       if (threadIdx.x == 0) cnt32[blockIdx.x] = __popcll(m);
     }
@@ -438,19 +441,30 @@ __global__ __launch_bounds__(NT) void token_kernel(LossParams p, int64_t Nc, con
   if (gh == nullptr) return;  // uniform
   __syncthreads();
   const int rows = (int)min((int64_t)TB, Nc - t0);
-  const int64_t base = t0 * H;
-  if ((H & 3) == 0) {
-    for (int e = threadIdx.x * 4; e < rows * H; e += NT * 4) {
-      const int r = e / H;
+  const int HS = gridDim.y, Hs = H / HS, c0 = blockIdx.y * Hs;  // the launcher makes Hs a multiple of 4
+  const int64_t base = t0 * H + c0;
+  if ((Hs & 3) == 0) {
+    for (int e = threadIdx.x * 4; e < rows * Hs; e += NT * 4) {
+      const int r = e / Hs, col = e - r * Hs;
       const float sc = s_g[r] * inv_tau;
-      const float4 x = *reinterpret_cast<const float4*>(v + base + e);
-      gh[base + e] = (T)(sc * x.x);
-      gh[base + e + 1] = (T)(sc * x.y);
-      gh[base + e + 2] = (T)(sc * x.z);
-      gh[base + e + 3] = (T)(sc * x.w);
+      const int64_t k = base + (int64_t)r * H + col;
+      const float4 x = *reinterpret_cast<const float4*>(v + k);
+      if constexpr (sizeof(T) == 2) {
+        bf16x4 u;
+        u[0] = (__bf16)(sc * x.x);
+        u[1] = (__bf16)(sc * x.y);
+        u[2] = (__bf16)(sc * x.z);
+        u[3] = (__bf16)(sc * x.w);
+        *reinterpret_cast<bf16x4*>(gh + k) = u;
+      } else {
+        *reinterpret_cast<float4*>(gh + k) = make_float4(sc * x.x, sc * x.y, sc * x.z, sc * x.w);
+      }
     }
   } else {
-    for (int e = threadIdx.x; e < rows * H; e += NT) gh[base + e] = (T)(s_g[e / H] * inv_tau * v[base + e]);
+    for (int e = threadIdx.x; e < rows * Hs; e += NT) {
+      const int r = e / Hs, col = e - r * Hs;
+      gh[base + (int64_t)r * H + col] = (T)(s_g[r] * inv_tau * v[base + (int64_t)r * H + col]);
+    }
   }
 }
 
@@ -695,11 +709,17 @@ hipError_t launch_loss_tokens(int dtype, const LossParams& p, int64_t Bc, const 
                               float inv_tau, void* gh, hipStream_t st) {
   const int64_t Nc = Bc * p.T;
   const unsigned grid = (unsigned)((Nc + TB - 1) / TB);
+  // few token blocks: split grad_h's columns over more workgroups (slices of
+  // a multiple of 4 columns) so the copy-like part fills the chip
+  unsigned hs = 1;
+  if (gh != nullptr)
+    while (grid * hs * 2 <= 2048 && H % (int)(8 * hs) == 0) hs *= 2;
+  const dim3 grid2(grid, hs);
   if (dtype == 0)
-    hipLaunchKernelGGL((token_kernel<float>), dim3(grid), dim3(NT), 0, st, p, Nc, lp, old, ref, comp, ratio, emask,
+    hipLaunchKernelGGL((token_kernel<float>), grid2, dim3(NT), 0, st, p, Nc, lp, old, ref, comp, ratio, emask,
                        tadv, coef, g, cnt32, v, H, inv_tau, (float*)gh);
   else
-    hipLaunchKernelGGL((token_kernel<__bf16>), dim3(grid), dim3(NT), 0, st, p, Nc, lp, old, ref, comp, ratio, emask,
+    hipLaunchKernelGGL((token_kernel<__bf16>), grid2, dim3(NT), 0, st, p, Nc, lp, old, ref, comp, ratio, emask,
                        tadv, coef, g, cnt32, v, H, inv_tau, (__bf16*)gh);
   return hipGetLastError();
 }
