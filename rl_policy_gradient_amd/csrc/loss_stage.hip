@@ -18,15 +18,16 @@ __device__ __forceinline__ float ldf(const T* p, int64_t i) {
   return (float)p[i];
 }
 
+// Sum over the block's NT threads, the same order on every call: a butterfly
+// within each 64-lane wave, then the four wave sums as (w0 + w1) + (w2 + w3).
+static_assert(NT == 256, "block_sum combines four waves");
 template <typename V_>
 __device__ V_ block_sum(V_ v, V_* red) {
-  red[threadIdx.x] = v;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  for (int s = NT / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  const V_ r = red[0];
+  const V_ r = (red[0] + red[1]) + (red[2] + red[3]);
   __syncthreads();
   return r;
 }
