@@ -3,6 +3,11 @@
 MI355X, with the roofline of the dominant kernel and the CPU oracle beside it.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|4|5]
+                  [--loss gmpo|gspo_token|grpo|bnpo|dapo] [--token-advantages]
+
+--loss runs the workload's inputs under another loss type (same clip
+parameters); --token-advantages gives every completion token its own
+advantage (N(0,1), zero off the completion) instead of one per sequence.
 
 One step = one call of plp_fused_lmhead_policy_loss_fwd_bwd on one batch of
 synthetic inputs already resident in HBM: forward statistics, loss, metrics,
@@ -138,6 +143,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--loss", choices=["gmpo", "gspo_token", "grpo", "bnpo", "dapo"], default=None)
+    ap.add_argument("--token-advantages", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -154,6 +161,20 @@ def main() -> int:
     torch.cuda.set_device(dev)
     spec, inp = _workload(args.config, dev)
     N, H, V = spec.N, spec.H, spec.V
+    variant = ""
+    if args.loss and args.loss != spec.loss_type:
+        spec = spec.replace(loss_type=args.loss)
+        variant += "+" + args.loss
+    tadv = None
+    if args.token_advantages:
+        if spec.loss_type == "gmpo":
+            print("--token-advantages needs a loss other than gmpo (GMPO's advantages are per sequence)",
+                  file=sys.stderr)
+            return 2
+        g = torch.Generator(device=dev)
+        g.manual_seed(4242 + args.config)
+        tadv = (torch.randn(N, generator=g, device=dev) * (inp["completion_mask"] != 0)).float().contiguous()
+        variant += "+token_adv"
     kw = dict(B=spec.B, T=spec.T, loss_type=spec.loss_type, epsilon_low=spec.eps_low, epsilon_high=spec.eps_high,
               beta=spec.beta, temperature=spec.temperature, top_entropy_quantile=spec.top_entropy_quantile,
               chunk_sequences=spec.chunk_sequences, diagnostics=False)
@@ -162,7 +183,8 @@ def main() -> int:
                                         chunk_sequences=spec.chunk_sequences, loss_type=spec.loss_type),
                      dtype=torch.uint8, device=dev)
     call_args = (inp["hidden"], inp["weight"], inp["targets"], inp["completion_mask"], inp["advantages"])
-    call_kw = dict(bias=inp["bias"], old_logp=inp["old_logp"], ref_logp=inp["ref_logp"], workspace=ws, **kw)
+    call_kw = dict(bias=inp["bias"], old_logp=inp["old_logp"], ref_logp=inp["ref_logp"], workspace=ws,
+                   token_advantages=tadv, **kw)
     out = plp.fused_lmhead_policy_loss_fwd_bwd(*call_args, **call_kw)
     out["dlogp"] = torch.empty(N, dtype=torch.float32, device=dev)
     for _ in range(args.warmup):
@@ -200,7 +222,7 @@ def main() -> int:
     dom = "fwd_sweep" if ms[0] >= ms[1] else "wgrad_sweep"
     flops, avg_ms = per_launch[dom]
     achieved = flops / (avg_ms * 1e-3) / 1e12
-    workload = spec.name
+    workload = spec.name + variant
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": _traffic_from_profiles(dom, workload),
@@ -208,7 +230,8 @@ def main() -> int:
                 "launches": int(cnt[0] if dom == "fwd_sweep" else cnt[1]),
                 "other_sweep_ms_per_step": round((ms[1] if dom == "fwd_sweep" else ms[0]) / args.steps, 4)}
     line = {
-        "metric": METRIC,
+        "metric": METRIC if not variant else METRIC.replace(
+            "GMPO", spec.loss_type.upper() + (" (per-token advantages)" if tadv is not None else "")),
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -225,12 +248,13 @@ def main() -> int:
         "config": {"workload": workload, "B": spec.B, "T": spec.T, "H": H, "V": V,
                    "loss_type": spec.loss_type, "bias": spec.bias, "beta": spec.beta,
                    "top_entropy_quantile": spec.top_entropy_quantile, "chunk_sequences": spec.chunk_sequences,
+                   "token_advantages": tadv is not None,
                    "global_batch_tokens": N, "active_tokens_with_grad": n_active,
                    "event_ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4)},
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and tadv is None:
         line["cpu_baseline"] = _cpu_baseline(spec)
     print(json.dumps(line), flush=True)
     return 0
