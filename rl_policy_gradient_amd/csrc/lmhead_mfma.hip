@@ -145,25 +145,51 @@ __device__ __forceinline__ bf16x8 ld_buf(__amdgpu_buffer_rsrc_t r, int lane_byte
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_bytes, const_bytes, 0));
 }
 
+// Ordering of one wave's own LDS accesses across its lanes. A wave's LDS
+// instructions execute in issue order, so a read that follows a write of
+// another lane of the same wave sees it; the fences keep the compiler from
+// moving the accesses across this point. No workgroup barrier: it would also
+// wait for the wave's outstanding global stores.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Store of a wave's accumulator (rows 32qb + 8(i/4) + 4h + i%4 of the
 // resident block, columns 32db + c of the wave's slice) through a wave-private
 // LDS buffer of 32 x DS floats, one 32-row half at a time, so that the global
-// accesses are 16-byte chunks along rows: emit(qb, row, col, f32x4) is called
-// once per chunk. Every wave of the block must call it (it synchronises).
-template <int DS, int DB, typename Emit>
+// accesses run along rows: emit(qb, row, col, v) is called once per CH
+// consecutive columns (CH = 4: v is one f32x4; CH = 8: v[0], v[1] hold
+// columns col .. col+3, col+4 .. col+7). Row r sits at buffer row r ^ ((r >> 2)
+// & 1): the two lane halves write rows four apart, which then fall on
+// opposite halves of the 64 banks when a row holds an odd number of 32-float
+// blocks (H = 896: seven). The buffer must be one no other wave
+// touches from here on; the first half's global stores are still in flight
+// while the second half goes through the buffer.
+template <int CH, int DS, int DB, typename Emit>
 __device__ __forceinline__ void store_acc(const f32x16 (&o)[2][DB], float* buf, int hh, int c, int lane, Emit&& emit) {
+  static_assert(CH == 4 || CH == 8, "four or eight columns per call");
+  static_assert(DS % CH == 0 && (DS & 1) == 0, "rows split into whole chunks");
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * (i >> 2) + 4 * hh + (i & 3);
+      float* row = buf + (r ^ hh) * DS + c;  // (r >> 2) & 1 == hh
 #pragma unroll
-      for (int i = 0; i < 16; ++i) buf[(8 * (i >> 2) + 4 * hh + (i & 3)) * DS + 32 * db + c] = o[qb][db][i];
-    __syncthreads();
+      for (int db = 0; db < DB; ++db) row[32 * db] = o[qb][db][i];
+    }
+    wave_lds_sync();
     const f32x4* b4 = reinterpret_cast<const f32x4*>(buf);
-    for (int q = lane; q < 32 * DS / 4; q += 64) {
-      const int r = q / (DS / 4), c4 = q - r * (DS / 4);
-      emit(qb, r, 4 * c4, b4[q]);
+    for (int q = lane; q < 32 * DS / CH; q += 64) {
+      const int r = q / (DS / CH), cc = q - r * (DS / CH);
+      const f32x4* src = b4 + (r ^ ((r >> 2) & 1)) * (DS / 4) + cc * (CH / 4);
+      f32x4 v[CH / 4];
+#pragma unroll
+      for (int k = 0; k < CH / 4; ++k) v[k] = src[k];
+      emit(qb, r, CH * cc, v);
     }
   }
 }
@@ -736,10 +762,10 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
   if (slot >= 0) {  // a share of a tail block: fp32 partial sums, combined by tail_reduce_kernel
     if (kh == 0 && hh == 0) part_b[slot * BQ + 32 * nbq + c] = (float)(gbv + s_xd[(w ^ 2) * 64 + c]);
     float* pw = part_w + (int64_t)slot * BQ * H;
-    store_acc<DS, DB>(o, reinterpret_cast<float*>(&s_t[w][0][0]), hh, c, lane,
-                      [&](int qb, int r, int col, f32x4 v) {
-                        *reinterpret_cast<f32x4*>(pw + (int64_t)(32 * qb + r) * H + d0 + col) = v;
-                      });
+    store_acc<4, DS, DB>(o, reinterpret_cast<float*>(&s_t[w][0][0]), hh, c, lane,
+                         [&](int qb, int r, int col, const f32x4 (&v)[1]) {
+                           *reinterpret_cast<f32x4*>(pw + (int64_t)(32 * qb + r) * H + d0 + col) = v[0];
+                         });
     return;  // uniform
   }
   const bool from_acc = acc_mode == 2 || acc_mode == 3;
@@ -751,24 +777,33 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
     else gb_out[my_v] = (__bf16)(float)val;
   }
   if (to_acc ? gW_acc == nullptr : gW_out == nullptr) return;  // uniform: every wave returns
-  store_acc<DS, DB>(o, reinterpret_cast<float*>(&s_t[w][0][0]), hh, c, lane,
-                    [&](int qb, int r, int col, f32x4 v) {
-                      const int vr = q0 + 32 * qb + r;
-                      if (vr >= V) return;
-                      const int64_t k = (int64_t)vr * H + d0 + col;
-                      if (from_acc) v += *reinterpret_cast<const f32x4*>(gW_acc + k);
-                      if (to_acc) {
-                        *reinterpret_cast<f32x4*>(gW_acc + k) = v;
-                      } else {
-                        bf16x4 u;
-                        u[0] = (__bf16)v[0];
-                        u[1] = (__bf16)v[1];
-                        u[2] = (__bf16)v[2];
-                        u[3] = (__bf16)v[3];
-                        // written once, read by nobody in this call: stream past the caches
-                        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, u), reinterpret_cast<u32x2*>(gW_out + k));
-                      }
-                    });
+  float* sbuf = reinterpret_cast<float*>(&s_t[w][0][0]);
+  if (to_acc) {  // fp32 accumulator rows, one f32x4 per lane
+    store_acc<4, DS, DB>(o, sbuf, hh, c, lane, [&](int qb, int r, int col, const f32x4 (&v)[1]) {
+      const int vr = q0 + 32 * qb + r;
+      if (vr >= V) return;
+      f32x4* dst = reinterpret_cast<f32x4*>(gW_acc + (int64_t)vr * H + d0 + col);
+      *dst = from_acc ? *dst + v[0] : v[0];
+    });
+  } else {  // output dtype, eight bf16 (16 bytes) per lane
+    store_acc<8, DS, DB>(o, sbuf, hh, c, lane, [&](int qb, int r, int col, const f32x4 (&v)[2]) {
+      const int vr = q0 + 32 * qb + r;
+      if (vr >= V) return;
+      const int64_t k = (int64_t)vr * H + d0 + col;
+      f32x4 lo = v[0], hi = v[1];
+      if (from_acc) {
+        lo += *reinterpret_cast<const f32x4*>(gW_acc + k);
+        hi += *reinterpret_cast<const f32x4*>(gW_acc + k + 4);
+      }
+      bf16x8 u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u[j] = (__bf16)lo[j];
+        u[4 + j] = (__bf16)hi[j];
+      }
+      *reinterpret_cast<bf16x8*>(gW_out + k) = u;
+    });
+  }
 }
 
 template <int KB>
