@@ -305,15 +305,24 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   const int t_begin = sv * tiles_per_split;
   const int t_end = min(n_tiles, t_begin + tiles_per_split);
 
-  // Resident h fragments (B operand of S^T): rows q0 + 32nb + c, cols d0 + 16ks + 8hh.
+  // Resident h fragments (B operand of S^T): rows q0 + 32nb + c, cols
+  // d0 + 16ks + 8hh; rows past N repeat row N - 1 (their results are never
+  // stored). The first streamed tile is loaded in the same k-step order, so
+  // the first MFMAs wait only for their own operands.
+  const bool any = t_begin < t_end;
   bf16x8 q[2][KS];
+  bf16x8 a[KS];
+  {
+    const auto rh = frag_rsrc(h + q0 * H, BQ * H * 2);
+    const int row0 = (int)min((int64_t)c, N - 1 - q0), row1 = (int)min((int64_t)(32 + c), N - 1 - q0);
+    // an empty split loads nothing (zero range)
+    const auto ra = frag_rsrc(frag_ptr<KB>(Wf, any ? t_begin : 0, w, 0, 0), any ? KS * 1024 : 0);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    // rows past N repeat row N - 1 (their results are never stored)
-    const int row = (int)min((int64_t)(32 * nb + c), N - 1 - q0);
-    const auto r = frag_rsrc(h + q0 * H, BQ * H * 2);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) q[nb][ks] = ld_buf(r, (row * H + d0 + 8 * hh) * 2, 32 * ks);
+    for (int ks = 0; ks < KS; ++ks) {
+      q[0][ks] = ld_buf(rh, (row0 * H + d0 + 8 * hh) * 2, 32 * ks);
+      q[1][ks] = ld_buf(rh, (row1 * H + d0 + 8 * hh) * 2, 32 * ks);
+      a[ks] = ld_buf(ra, lane * 16, ks * 1024);
+    }
   }
 
   f32x16 o[2][WITH_O ? DB : 1];
@@ -329,11 +338,6 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   double s_acc = 0.0, sz_acc = 0.0;  // this lane's share of sum p, sum p z2
   bool flag = false;
 
-  // rows past V are zero in the fragment-major copy and masked in the epilogue
-  auto load_a = [&](int t, bf16x8 (&a)[KS]) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a[ks] = ld_buf(frag_rsrc(frag_ptr<KB>(Wf, t, w, 0, 0), KS * 1024), lane * 16, ks * 1024);
-  };
   // Bias of tile rows kvq(kh, hh, 0..7), kept as packed bf16 (two groups of
   // four consecutive rows, one 8-byte load each when inside the vocabulary).
   const auto bias_r = frag_rsrc(bias, HAS_BIAS ? V * 2 : 0);
@@ -364,7 +368,8 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
     const unsigned wd = (j & 2) ? u.y : u.x;
     return __uint_as_float((j & 1) ? (wd & 0xffff0000u) : (wd << 16));
   };
-  // S^T of the tile held in `a`; each k-slice of `a`, once its MFMAs are
+  // S^T of the tile held in `a` (tile rows past V are zero in the
+  // fragment-major copy and masked in the epilogue); each k-slice of `a`, once its MFMAs are
   // issued, is staged for the transposing load (WITH_O) and reloaded with
   // the same slice of tile `t_next`.
   auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int buf, int t_next) {
@@ -451,12 +456,10 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
     }
   };
 
-  bf16x8 a[KS];
   f32x16 acc[2];
   f32x4 sf[2];
   uint2 bv[2];
-  if (t_begin < t_end) {
-    load_a(t_begin, a);
+  if (any) {
     load_bias(t_begin, bv);
     s_step(a, acc, t_begin & 1, min(t_begin + 1, t_end - 1));
     write_part(acc);
@@ -617,14 +620,35 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
     tr_base[1] = (r + 8) * TS + 8 * (b ^ f ^ 2) + 4 * (p & 1);
   }
 
+  // Per-token data of tile t, loaded into a register one phase before it is
+  // written to LDS (wave 0, lanes < 32), so the load latency stays hidden.
+  const bool any = t_hi > t_lo;
+  TokData tk;
+  auto load_tok = [&](int t) {
+    if (w == 0 && lane < BK) tk = tok[t * BK + lane];
+  };
+  auto stage_tok = [&](int t) {
+    if (w == 0 && lane < BK) s_tok[t & 1][lane] = tk;
+  };
+  if (any) load_tok(t_lo);
   // Resident W fragments (B operand of S^T), rows q0 + 32nb + c, cols
-  // d0 + 16ks + 8hh, from the fragment-major copy (rows past V are zero).
+  // d0 + 16ks + 8hh, from the fragment-major copy (rows past V are zero),
+  // and the first token tile, in k-step order so that the first MFMAs wait
+  // only for their own operands.
   bf16x8 q[2][KS];
+  bf16x8 a[KS];
+  {
+    const auto rq0 = frag_rsrc(frag_ptr<KB>(Wf, q0 / BK, w, 0, 0), KS * 1024);
+    const auto rq1 = frag_rsrc(frag_ptr<KB>(Wf, q0 / BK + 1, w, 0, 0), KS * 1024);
+    // an empty token range loads nothing (zero range)
+    const auto ra = frag_rsrc(frag_ptr<KB>(hcf, any ? t_lo : 0, w, 0, 0), any ? KS * 1024 : 0);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      q[nb][ks] = ld_buf(frag_rsrc(frag_ptr<KB>(Wf, q0 / BK + nb, w, 0, 0), KS * 1024), lane * 16, ks * 1024);
+    for (int ks = 0; ks < KS; ++ks) {
+      q[0][ks] = ld_buf(rq0, lane * 16, ks * 1024);
+      q[1][ks] = ld_buf(rq1, lane * 16, ks * 1024);
+      a[ks] = ld_buf(ra, lane * 16, ks * 1024);
+    }
+  }
   f32x16 o[2][DB];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
@@ -635,19 +659,6 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
   const float bvl = HAS_BIAS ? (float)bias[min(my_v, V - 1)] : 0.f;
   double gb_run = 0.0;
 
-  auto load_a = [&](int t, bf16x8 (&a)[KS]) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a[ks] = ld_buf(frag_rsrc(frag_ptr<KB>(hcf, t, w, 0, 0), KS * 1024), lane * 16, ks * 1024);
-  };
-  // Per-token data of tile t, loaded into a register one phase before it is
-  // written to LDS (wave 0, lanes < 32), so the load latency stays hidden.
-  TokData tk;
-  auto load_tok = [&](int t) {
-    if (w == 0 && lane < BK) tk = tok[t * BK + lane];
-  };
-  auto stage_tok = [&](int t) {
-    if (w == 0 && lane < BK) s_tok[t & 1][lane] = tk;
-  };
   auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int buf, int t_next) {
     const auto r = frag_rsrc(frag_ptr<KB>(hcf, t_next, w, 0, 0), KS * 1024);
 #pragma unroll
@@ -706,14 +717,11 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
     sf[1] = (r[0] + r[1]) + (r[2] + r[3]);
   };
 
-  bf16x8 a[KS];
   f32x16 acc[2];
   f32x4 sf[2];
-  if (t_hi > t_lo) {
-    load_tok(t_lo);
+  if (any) {
     stage_tok(t_lo);
     load_tok(min(t_lo + 1, t_hi - 1));
-    load_a(t_lo, a);
     s_step(a, acc, t_lo & 1, min(t_lo + 1, t_hi - 1));
     write_part(acc);
   }
