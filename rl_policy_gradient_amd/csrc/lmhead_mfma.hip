@@ -144,6 +144,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t frag_rsrc(const __bf16* base, 
 __device__ __forceinline__ bf16x8 ld_buf(__amdgpu_buffer_rsrc_t r, int lane_bytes, int const_bytes) {
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_bytes, const_bytes, 0));
 }
+// The same with the non-temporal hint: for data read once (the resident
+// rows of the weight-gradient sweep), so that it does not push the token
+// tiles every workgroup re-reads out of L2.
+__device__ __forceinline__ bf16x8 ld_buf_nt(__amdgpu_buffer_rsrc_t r, int lane_bytes, int const_bytes) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_bytes, const_bytes, 2));
+}
 
 // Ordering of one wave's own LDS accesses across its lanes. A wave's LDS
 // instructions execute in issue order, so a read that follows a write of
@@ -644,8 +650,8 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
     const auto ra = frag_rsrc(frag_ptr<KB>(hcf, any ? t_lo : 0, w, 0, 0), any ? KS * 1024 : 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      q[0][ks] = ld_buf(rq0, lane * 16, ks * 1024);
-      q[1][ks] = ld_buf(rq1, lane * 16, ks * 1024);
+      q[0][ks] = ld_buf_nt(rq0, lane * 16, ks * 1024);
+      q[1][ks] = ld_buf_nt(rq1, lane * 16, ks * 1024);
       a[ks] = ld_buf(ra, lane * 16, ks * 1024);
     }
   }
@@ -809,7 +815,9 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
         u[j] = (__bf16)lo[j];
         u[4 + j] = (__bf16)hi[j];
       }
-      *reinterpret_cast<bf16x8*>(gW_out + k) = u;
+      // written once and read by nobody in this call: non-temporal, so that
+      // the token tiles stay in L2
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, u), reinterpret_cast<u32x4*>(gW_out + k));
     });
   }
 }
