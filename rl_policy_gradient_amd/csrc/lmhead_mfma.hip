@@ -113,11 +113,13 @@ __device__ __forceinline__ float other_half(float x, int h) {
 }
 
 // Layout of a wave's staged tile slice: 32 rows of TS elements; the 16-byte
-// chunk k of row r sits at chunk position k ^ ((r >> 2) & 3). With 64 banks
-// of 4 bytes, the stage writes (16 lanes: rows 0..15 or 16..31, one chunk
-// each) and the transposing loads (32 lanes: four rows x 64 bytes) then touch
-// 64 distinct banks. Rows are padded by 32 elements for even KB so that four
-// consecutive rows start 16 banks apart.
+// chunk k of row r sits at chunk position k ^ s(r), s(r) = (r >> 1) & 3. The
+// LDS serves 128 bytes (32 banks of 4 bytes) per pass, and a 16-byte store or
+// an 8-byte transposing load is served eight lanes at a time: the eight stage
+// writes of a pass (rows 8m .. 8m+7, one chunk each) and the eight loads of a
+// pass (two rows, two chunks, two halves) then touch 32 distinct banks. A row
+// spans 4 (mod 8) chunks, so rows of opposite parity start 64 bytes apart;
+// rows are padded by 32 elements for even KB to keep that.
 template <int KB>
 struct Stage {
   static constexpr int DS = 32 * KB;
@@ -167,10 +169,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // LDS buffer of 32 x DS floats, one 32-row half at a time, so that the global
 // accesses run along rows: emit(qb, row, col, v) is called once per CH
 // consecutive columns (CH = 4: v is one f32x4; CH = 8: v[0], v[1] hold
-// columns col .. col+3, col+4 .. col+7). Row r sits at buffer row r ^ ((r >> 2)
-// & 1): the two lane halves write rows four apart, which then fall on
-// opposite halves of the 64 banks when a row holds an odd number of 32-float
-// blocks (H = 896: seven). The buffer must be one no other wave
+// columns col .. col+3, col+4 .. col+7). The buffer must be one no other wave
 // touches from here on; the first half's global stores are still in flight
 // while the second half goes through the buffer.
 template <int CH, int DS, int DB, typename Emit>
@@ -182,8 +181,7 @@ __device__ __forceinline__ void store_acc(const f32x16 (&o)[2][DB], float* buf, 
     wave_lds_sync();
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int r = 8 * (i >> 2) + 4 * hh + (i & 3);
-      float* row = buf + (r ^ hh) * DS + c;  // (r >> 2) & 1 == hh
+      float* row = buf + (8 * (i >> 2) + 4 * hh + (i & 3)) * DS + c;
 #pragma unroll
       for (int db = 0; db < DB; ++db) row[32 * db] = o[qb][db][i];
     }
@@ -191,7 +189,7 @@ __device__ __forceinline__ void store_acc(const f32x16 (&o)[2][DB], float* buf, 
     const f32x4* b4 = reinterpret_cast<const f32x4*>(buf);
     for (int q = lane; q < 32 * DS / CH; q += 64) {
       const int r = q / (DS / CH), cc = q - r * (DS / CH);
-      const f32x4* src = b4 + (r ^ ((r >> 2) & 1)) * (DS / 4) + cc * (CH / 4);
+      const f32x4* src = b4 + r * (DS / 4) + cc * (CH / 4);
       f32x4 v[CH / 4];
 #pragma unroll
       for (int k = 0; k < CH / 4; ++k) v[k] = src[k];
@@ -287,13 +285,12 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   const int64_t q0 = (int64_t)rb * BQ;
   const int d0 = w * DS;
   // Stage write offsets (element) of lane (hh, c) for even / odd k-step:
-  // row c, chunk 2ks + hh at position (2ks + hh) ^ f(c), f(c) = (c >> 2) & 3.
+  // row c, chunk 2ks + hh at position (2ks + hh) ^ s(c), s(c) = (c >> 1) & 3.
   int sw_base[2];
   {
-    const int f = (c >> 2) & 3;
-    const int b = c * TS + 8 * (hh ^ (f & 1));
-    sw_base[0] = b + 16 * (f >> 1);
-    sw_base[1] = b - 16 * (f >> 1);
+    const int x = hh ^ ((c >> 1) & 3);
+    sw_base[0] = c * TS + 8 * x;
+    sw_base[1] = c * TS + 8 * (x ^ 2) - 16;
   }
   // Transposing-load offsets: provider lane p of 16-lane group G reads row
   // 4(G/2) + p/4 (and 8 further down) of contraction step ks, chunk
@@ -303,9 +300,9 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
     const int p = lane & 15, G = lane >> 4;
     const int r = 4 * (G >> 1) + (p >> 2);
     const int b = 2 * (G & 1) + ((p >> 1) & 1);
-    const int f = (r >> 2) & 3;  // rows r and r + 8: f and f ^ 2
-    tr_base[0] = r * TS + 8 * (b ^ f) + 4 * (p & 1);
-    tr_base[1] = (r + 8) * TS + 8 * (b ^ f ^ 2) + 4 * (p & 1);
+    const int s = (r >> 1) & 3;  // the same for rows r + 8 and r + 16
+    tr_base[0] = r * TS + 8 * (b ^ s) + 4 * (p & 1);
+    tr_base[1] = (r + 8) * TS + 8 * (b ^ s) + 4 * (p & 1);
   }
   const int n_tiles = (V + BK - 1) / BK;
   const int t_begin = sv * tiles_per_split;
@@ -605,13 +602,12 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
   const int q0 = blk * BQ;
   const int d0 = w * DS;
   // Stage write offsets (element) of lane (hh, c) for even / odd k-step:
-  // row c, chunk 2ks + hh at position (2ks + hh) ^ f(c), f(c) = (c >> 2) & 3.
+  // row c, chunk 2ks + hh at position (2ks + hh) ^ s(c), s(c) = (c >> 1) & 3.
   int sw_base[2];
   {
-    const int f = (c >> 2) & 3;
-    const int b = c * TS + 8 * (hh ^ (f & 1));
-    sw_base[0] = b + 16 * (f >> 1);
-    sw_base[1] = b - 16 * (f >> 1);
+    const int x = hh ^ ((c >> 1) & 3);
+    sw_base[0] = c * TS + 8 * x;
+    sw_base[1] = c * TS + 8 * (x ^ 2) - 16;
   }
   // Transposing-load offsets: provider lane p of 16-lane group G reads row
   // 4(G/2) + p/4 (and 8 further down) of contraction step ks, chunk
@@ -621,9 +617,9 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
     const int p = lane & 15, G = lane >> 4;
     const int r = 4 * (G >> 1) + (p >> 2);
     const int b = 2 * (G & 1) + ((p >> 1) & 1);
-    const int f = (r >> 2) & 3;  // rows r and r + 8: f and f ^ 2
-    tr_base[0] = r * TS + 8 * (b ^ f) + 4 * (p & 1);
-    tr_base[1] = (r + 8) * TS + 8 * (b ^ f ^ 2) + 4 * (p & 1);
+    const int s = (r >> 1) & 3;  // the same for rows r + 8 and r + 16
+    tr_base[0] = r * TS + 8 * (b ^ s) + 4 * (p & 1);
+    tr_base[1] = (r + 8) * TS + 8 * (b ^ s) + 4 * (p & 1);
   }
 
   // Per-token data of tile t, loaded into a register one phase before it is
