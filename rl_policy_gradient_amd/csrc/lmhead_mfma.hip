@@ -384,6 +384,11 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
       if constexpr (WITH_O)
         *reinterpret_cast<bf16x8*>(&s_t[w][buf][sw_base[ks & 1] + 16 * ks]) = a[ks];
       a[ks] = ld_buf(r, lane * 16, ks * 1024);
+      // keep the matrix, LDS and memory instructions of each k-step in this
+      // order (vector ALU work may move across): left to itself the compiler
+      // bunches the stage writes, and the waves then stall on the LDS queue
+      // (2 % faster here; the same fence slows the weight-gradient sweep)
+      __builtin_amdgcn_sched_barrier(0x002);
     }
   };
   // The partial S^T in four groups of four rows per row block; the wave
