@@ -627,15 +627,20 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
     tr_base[1] = (r + 8) * TS + 8 * (b ^ s) + 4 * (p & 1);
   }
 
-  // Per-token data of tile t, loaded into a register one phase before it is
+  // Per-token data of tile t, loaded into registers one phase before it is
   // written to LDS (wave 0, lanes < 32), so the load latency stays hidden.
+  // Held as a plain vector: a TokData variable was placed in LDS by the
+  // compiler, whose store right after the load then waited for every
+  // outstanding load of the wave, the token tiles included.
   const bool any = t_hi > t_lo;
-  TokData tk;
+  static_assert(sizeof(TokData) == 16, "one 16-byte record per token");
+  const auto tok_r = __builtin_amdgcn_make_buffer_rsrc(const_cast<TokData*>(tok), 0, 0x7ffffff0, 0x00020000);
+  u32x4 tk = {0u, 0u, 0u, 0u};
   auto load_tok = [&](int t) {
-    if (w == 0 && lane < BK) tk = tok[t * BK + lane];
+    if (w == 0 && lane < BK) tk = __builtin_amdgcn_raw_buffer_load_b128(tok_r, (t * BK + lane) * 16, 0, 0);
   };
   auto stage_tok = [&](int t) {
-    if (w == 0 && lane < BK) s_tok[t & 1][lane] = tk;
+    if (w == 0 && lane < BK) *reinterpret_cast<u32x4*>(&s_tok[t & 1][lane]) = tk;
   };
   if (any) load_tok(t_lo);
   // Resident W fragments (B operand of S^T), rows q0 + 32nb + c, cols
