@@ -76,6 +76,28 @@ def test_cfg2_full_against_live_oracle():
     _grad_ok(gpu["grad_weight"], ref["grad_W"], "grad_W")
 
 
+# The other loss types at the B=1 T=512 size (same inputs as cfg 2 but for
+# the loss settings), against the whole live oracle run.
+FULL2_VARIANTS = {
+    "grpo_token_adv": dict(loss_type=synth.GRPO, eps_low=0.2, eps_high=0.28, token_adv=True),
+    "bnpo_kl": dict(loss_type=synth.BNPO, eps_low=0.2, eps_high=0.28, beta=0.04, ref_noise_std=0.05),
+    "dapo_global": dict(loss_type=synth.DAPO, eps_low=0.2, eps_high=0.28, global_tokens=4096),
+    "gspo_token_adv": dict(loss_type=synth.GSPO_TOKEN, eps_low=3e-4, eps_high=4e-4, old_noise_std=1e-4,
+                           token_adv=True),
+}
+
+
+@pytest.mark.parametrize("variant", list(FULL2_VARIANTS))
+def test_cfg2_size_loss_types(variant):
+    from tests.test_gpu_parity import _check_fused
+    spec = synth.CONFIGS[2].replace(name=f"{variant}_bf16_b1_t512", **FULL2_VARIANTS[variant])
+    _say(f"cfg2-size {variant}")
+    d = make_case(spec)
+    ref = run_oracle(spec, d)
+    gpu = run_gpu(spec, d)
+    _check_fused(spec, d, gpu, ref, lp_tol=LP_TOL)
+
+
 @pytest.mark.parametrize("cfg", [3, 4])
 def test_full_size_sampled(cfg):
     spec = synth.CONFIGS[cfg]
