@@ -15,7 +15,13 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libplp.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["lmhead_mfma.hip", "lmhead_generic.hip", "loss_stage.hip", "plp_api.cpp"]
+SOURCES = ["lmhead_fwd.hip", "lmhead_mfma.hip", "lmhead_generic.hip", "loss_stage.hip", "plp_api.cpp"]
+
+# Per-source compiler options. The forward sweep is scheduled with LLVM's
+# iterative ILP strategy: 2-2.5 % faster than the default at 512 to 16384
+# tokens, measured on MI355X; the same strategy slows the weight-gradient
+# sweep, which keeps the default.
+EXTRA = {"lmhead_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [
@@ -29,7 +35,7 @@ COMMON = [
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -87,7 +87,7 @@ __host__ __device__ inline bool token_mean_loss(int loss_type) { return loss_typ
 // ---------------------------------------------------------------------------
 
 // Fragment-major copy of bf16 rows for the MFMA sweeps (the layout is given
-// in lmhead_mfma.hip): `tiles` 32-row tiles of X, or of X[idx[k]] when idx is
+// in mfma_tile.h): `tiles` 32-row tiles of X, or of X[idx[k]] when idx is
 // given; rows at or past `rows` (*count_dev when given) are zero.
 hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_dev, int64_t rows, int64_t tiles, int H,
                             __bf16* Xf, hipStream_t st);
