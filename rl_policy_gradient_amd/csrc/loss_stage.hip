@@ -12,10 +12,20 @@ namespace plp {
 namespace {
 
 constexpr int NT = 256;
+constexpr int kEarlySplits = 32;  // split accumulators a merge thread loads up front
 
 template <typename T>
 __device__ __forceinline__ float ldf(const T* p, int64_t i) {
   return (float)p[i];
+}
+
+// Four consecutive elements p[i .. i+3] as floats (i a multiple of 4, p
+// 16-byte aligned): one 16-byte load for fp32, one 8-byte load for bf16.
+__device__ __forceinline__ f32x4 ld4f(const float* p, int64_t i) { return *reinterpret_cast<const f32x4*>(p + i); }
+__device__ __forceinline__ f32x4 ld4f(const __bf16* p, int64_t i) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+  return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+               __uint_as_float(u.y & 0xffff0000u)};
 }
 
 // Sum over the block's NT threads, the same order on every call: a butterfly
@@ -41,7 +51,7 @@ __device__ V_ block_sum(V_ v, V_* red) {
 // than gathered inside the sweeps. A row any split flagged is recomputed
 // exactly (row_exact).
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool EARLY>
 __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict__ stats, const float* __restrict__ O,
                                                      int Sv, int64_t N, int H, int V, const T* __restrict__ h,
                                                      const T* __restrict__ W, const T* __restrict__ b, float inv_tau,
@@ -58,6 +68,18 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
   // targets outside [0, V) are invalid input; clamp the index so they cannot
   // address memory outside W
   const int64_t yc = yv < 0 ? 0 : (yv >= V ? V - 1 : yv);
+  // EARLY (several splits, up to 32, one 4-column group per thread): each
+  // thread's split accumulators are loaded first, so their latency overlaps
+  // the split statistics and the target-logit dot product below. It costs
+  // registers (two waves per SIMD), so a single split takes the plain form.
+  const bool vec = (H & 3) == 0;
+  const bool early = EARLY && vout != nullptr && vec && Sv <= kEarlySplits && H / 4 <= NT;
+  f32x4 opre[EARLY ? kEarlySplits : 1];
+  if (early && (int)threadIdx.x < H / 4) {
+#pragma unroll
+    for (int j = 0; j < (EARLY ? kEarlySplits : 1); ++j)
+      if (j < Sv) opre[j] = *reinterpret_cast<const f32x4*>(O + (int64_t)j * N * H + row * H + 4 * threadIdx.x);
+  }
   if (threadIdx.x < 64) {
     // one lane per split; butterfly reductions in a fixed order
     const int j = threadIdx.x;
@@ -101,9 +123,20 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
     }
     return;
   }
+  // Rows of H a multiple of 4 go four columns per thread and step (wide
+  // loads, more bytes in flight per thread); others one column at a time.
   double zp = 0.0;
-  if (lp)
-    for (int d = threadIdx.x; d < H; d += NT) zp += (double)ldf<T>(h, row * H + d) * (double)ldf<T>(W, yc * H + d);
+  if (lp) {
+    if (vec) {
+      for (int d4 = threadIdx.x; d4 < H / 4; d4 += NT) {
+        const f32x4 hv = ld4f(h, row * H + 4 * d4), wv = ld4f(W, yc * H + 4 * d4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) zp += (double)hv[k] * (double)wv[k];
+      }
+    } else {
+      for (int d = threadIdx.x; d < H; d += NT) zp += (double)ldf<T>(h, row * H + d) * (double)ldf<T>(W, yc * H + d);
+    }
+  }
   zp = block_sum(zp, s_red);
   if (threadIdx.x == 0) {
     const double S = s_res[1], SZ = s_res[2];
@@ -121,11 +154,47 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
     const double inv_s = s_res[3];
     const float* Orow = O + row * H;
     const int64_t sstride = N * H;
-    for (int d = threadIdx.x; d < H; d += NT) {
-      double o = 0.0;
+    if (early) {
+      const int d4 = threadIdx.x;
+      if (d4 < H / 4) {
+        double o[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int j = 0; j < (EARLY ? kEarlySplits : 1); ++j) {
+          if (j < Sv) {
+            const double c = s_c[j];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] += c * (double)opre[j][k];
+          }
+        }
+        const f32x4 wy = ld4f(W, yc * H + 4 * d4);
+        f32x4 r;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r[k] = (float)((double)wy[k] - o[k] * inv_s);
+        *reinterpret_cast<f32x4*>(vout + row * H + 4 * d4) = r;
+      }
+    } else if (vec) {
+      for (int d4 = threadIdx.x; d4 < H / 4; d4 += NT) {
+        double o[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 8
-      for (int j = 0; j < Sv; ++j) o += s_c[j] * (double)Orow[j * sstride + d];
-      vout[row * H + d] = (float)((double)ldf<T>(W, yc * H + d) - o * inv_s);
+        for (int j = 0; j < Sv; ++j) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(Orow + j * sstride + 4 * d4);
+          const double c = s_c[j];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) o[k] += c * (double)x[k];
+        }
+        const f32x4 wy = ld4f(W, yc * H + 4 * d4);
+        f32x4 r;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r[k] = (float)((double)wy[k] - o[k] * inv_s);
+        *reinterpret_cast<f32x4*>(vout + row * H + 4 * d4) = r;
+      }
+    } else {
+      for (int d = threadIdx.x; d < H; d += NT) {
+        double o = 0.0;
+#pragma unroll 8
+        for (int j = 0; j < Sv; ++j) o += s_c[j] * (double)Orow[j * sstride + d];
+        vout[row * H + d] = (float)((double)ldf<T>(W, yc * H + d) - o * inv_s);
+      }
     }
   }
 }
@@ -678,12 +747,24 @@ hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int 
                           float* ent, float* lse, float* vout, hipStream_t st) {
   if (N <= 0) return hipSuccess;
   const size_t lds = row_exact_smem_bytes(H);
-  if (dtype == 0)
-    hipLaunchKernelGGL((combine_kernel<float>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H, V,
-                       (const float*)h, (const float*)W, (const float*)b, inv_tau, y, lp, ent, lse, vout);
-  else
-    hipLaunchKernelGGL((combine_kernel<__bf16>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H, V,
-                       (const __bf16*)h, (const __bf16*)W, (const __bf16*)b, inv_tau, y, lp, ent, lse, vout);
+  const bool early = Sv > 1 && Sv <= kEarlySplits && vout != nullptr;
+  if (dtype == 0) {
+    const float *hh = (const float*)h, *WW = (const float*)W, *bb = (const float*)b;
+    if (early)
+      hipLaunchKernelGGL((combine_kernel<float, true>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H, V,
+                         hh, WW, bb, inv_tau, y, lp, ent, lse, vout);
+    else
+      hipLaunchKernelGGL((combine_kernel<float, false>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H, V,
+                         hh, WW, bb, inv_tau, y, lp, ent, lse, vout);
+  } else {
+    const __bf16 *hh = (const __bf16*)h, *WW = (const __bf16*)W, *bb = (const __bf16*)b;
+    if (early)
+      hipLaunchKernelGGL((combine_kernel<__bf16, true>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H, V,
+                         hh, WW, bb, inv_tau, y, lp, ent, lse, vout);
+    else
+      hipLaunchKernelGGL((combine_kernel<__bf16, false>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H,
+                         V, hh, WW, bb, inv_tau, y, lp, ent, lse, vout);
+  }
   return hipGetLastError();
 }
 
