@@ -624,11 +624,15 @@ __device__ __forceinline__ float key2f(unsigned k) {
 
 __global__ __launch_bounds__(SEL_NT) void select_kernel(const float* __restrict__ ent, const uint8_t* __restrict__ active,
                                                         int64_t N, float p32, float* __restrict__ thr_out) {
-  __shared__ unsigned hist[2][256];
+  // one pair of histograms per wave (LDS atomics of a pass then collide only
+  // within a wave); bins are integer counts, so the result is order free
+  constexpr int SEL_W = SEL_NT / 64;
+  __shared__ unsigned hist[SEL_W][2][256];
   __shared__ unsigned long long red[SEL_NT];
   __shared__ unsigned pre[2];
   __shared__ unsigned long long kk[2];
   unsigned long long c = 0;
+#pragma unroll 8
   for (int64_t t = threadIdx.x; t < N; t += SEL_NT) c += active[t] != 0 ? 1ull : 0ull;
   red[threadIdx.x] = c;
   __syncthreads();
@@ -653,24 +657,35 @@ __global__ __launch_bounds__(SEL_NT) void select_kernel(const float* __restrict_
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const unsigned hmask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
-    for (int k = threadIdx.x; k < 512; k += SEL_NT) (&hist[0][0])[k] = 0u;
+    for (int k = threadIdx.x; k < SEL_W * 512; k += SEL_NT) (&hist[0][0][0])[k] = 0u;
     __syncthreads();
     const unsigned p0 = pre[0], p1 = pre[1];
+    const bool same = p0 == p1;  // both ranks still share their prefix: one histogram serves both
+    unsigned (*wh)[256] = hist[threadIdx.x >> 6];
+#pragma unroll 8
     for (int64_t t = threadIdx.x; t < N; t += SEL_NT) {
       if (active[t] == 0) continue;
       const unsigned key = f2key(ent[t]);
       const unsigned d = (key >> shift) & 255u;
-      if ((key & hmask) == p0) atomicAdd(&hist[0][d], 1u);
-      if ((key & hmask) == p1) atomicAdd(&hist[1][d], 1u);
+      if ((key & hmask) == p0) atomicAdd(&wh[0][d], 1u);
+      if (!same && (key & hmask) == p1) atomicAdd(&wh[1][d], 1u);
+    }
+    __syncthreads();
+    // bin totals over the waves into wave 0's histograms
+    for (int k = threadIdx.x; k < 512; k += SEL_NT) {
+      unsigned tot = 0u;
+      for (int v = 0; v < SEL_W; ++v) tot += (&hist[v][0][0])[k];
+      (&hist[0][0][0])[k] = tot;
     }
     __syncthreads();
     if (threadIdx.x < 2) {
       const int which = threadIdx.x;
+      const unsigned* hw = hist[0][same ? 0 : which];
       unsigned long long cum = 0, k = kk[which];
       int b = 0;
       for (; b < 255; ++b) {
-        if (k < cum + hist[which][b]) break;
-        cum += hist[which][b];
+        if (k < cum + hw[b]) break;
+        cum += hw[b];
       }
       kk[which] = k - cum;
       pre[which] |= ((unsigned)b) << shift;
