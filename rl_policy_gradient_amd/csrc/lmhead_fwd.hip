@@ -1,352 +1,16 @@
-// Forward sweep of the LM head on the matrix cores (gfx950); the tile
-// machinery and the schedule are described in mfma_tile.h.
-#include "mfma_tile.h"
+// Forward sweep: the launcher, and the variants with a bias or without the
+// grad_h accumulator, compiled with the default scheduler and no per-k-step
+// fence (with a bias, the ILP strategy and the fence cost 11 %).
+#include "fwd_sweep.h"
 
 namespace plp {
 
-namespace {
-
-// Forward sweep: per token row, running (sum 2^{z2-m2}, sum 2^{z2-m2} z2)
-// against the reference m2 (z2 = z log2 e), and (WITH_O) the accumulator
-// O = sum_v e^{z-m} W_v. Grid: (row blocks) x Sv vocabulary splits, block
-// id = rb * Sv + split.
-template <int KB, bool WITH_O, bool HAS_BIAS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf,
-                     const __bf16* __restrict__ bias, int64_t N, int V, float inv_tau, int Sv,
-                     int tiles_per_split, RowStats* __restrict__ stats, float* __restrict__ O) {
-  constexpr int H = 128 * KB;
-  constexpr int DS = Stage<KB>::DS;  // columns per wave
-  constexpr int TS = Stage<KB>::TS;
-  constexpr int KS = DS / 16;        // 16-wide contraction steps per wave
-  constexpr int DB = DS / 32;        // 32-wide column blocks per wave
-  __shared__ f32x4 s_part[NW][2][4][64];
-  __shared__ bf16x8 s_p[4][64];
-  __shared__ unsigned short s_t[WITH_O ? NW : 1][2][WITH_O ? BK * TS : 8];
-  // cross-wave exchanges of per-row values reuse the P buffer (before the
-  // sweep) and the partials buffer (after it)
-  float* s_x = reinterpret_cast<float*>(&s_p[0][0]);              // [NW][64]
-  double* s_xd = reinterpret_cast<double*>(&s_part[0][0][0][0]);   // [NW][2][64]
-
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hh = lane >> 5, c = lane & 31;
-  const int nbq = w & 1, kh = w >> 1;  // quarter this wave reduces: row block nbq, tile-row half kh
-  const int rb = blockIdx.x / Sv, sv = blockIdx.x - rb * Sv;
-  const int64_t q0 = (int64_t)rb * BQ;
-  const int d0 = w * DS;
-  // Stage write offsets (element) of lane (hh, c) for even / odd k-step:
-  // row c, chunk 2ks + hh at position (2ks + hh) ^ s(c), s(c) = (c >> 1) & 3.
-  int sw_base[2];
-  {
-    const int x = hh ^ ((c >> 1) & 3);
-    sw_base[0] = c * TS + 8 * x;
-    sw_base[1] = c * TS + 8 * (x ^ 2) - 16;
-  }
-  // Transposing-load offsets: provider lane p of 16-lane group G reads row
-  // 4(G/2) + p/4 (and 8 further down) of contraction step ks, chunk
-  // 4db + 2(G%2) + (p%4)/2 of column block db, half p%2.
-  int tr_base[2];
-  {
-    const int p = lane & 15, G = lane >> 4;
-    const int r = 4 * (G >> 1) + (p >> 2);
-    const int b = 2 * (G & 1) + ((p >> 1) & 1);
-    const int s = (r >> 1) & 3;  // the same for rows r + 8 and r + 16
-    tr_base[0] = r * TS + 8 * (b ^ s) + 4 * (p & 1);
-    tr_base[1] = (r + 8) * TS + 8 * (b ^ s) + 4 * (p & 1);
-  }
-  const int n_tiles = (V + BK - 1) / BK;
-  const int t_begin = sv * tiles_per_split;
-  const int t_end = min(n_tiles, t_begin + tiles_per_split);
-
-  // Resident h fragments (B operand of S^T): rows q0 + 32nb + c, cols
-  // d0 + 16ks + 8hh; rows past N repeat row N - 1 (their results are never
-  // stored). The first streamed tile is loaded in the same k-step order, so
-  // the first MFMAs wait only for their own operands.
-  const bool any = t_begin < t_end;
-  bf16x8 q[2][KS];
-  bf16x8 a[KS];
-  {
-    const auto rh = frag_rsrc(h + q0 * H, BQ * H * 2);
-    const int row0 = (int)min((int64_t)c, N - 1 - q0), row1 = (int)min((int64_t)(32 + c), N - 1 - q0);
-    // an empty split loads nothing (zero range)
-    const auto ra = frag_rsrc(frag_ptr<KB>(Wf, any ? t_begin : 0, w, 0, 0), any ? KS * 1024 : 0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      q[0][ks] = ld_buf(rh, (row0 * H + d0 + 8 * hh) * 2, 32 * ks);
-      q[1][ks] = ld_buf(rh, (row1 * H + d0 + 8 * hh) * 2, 32 * ks);
-      a[ks] = ld_buf(ra, lane * 16, ks * 1024);
-    }
-  }
-
-  f32x16 o[2][WITH_O ? DB : 1];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < (WITH_O ? DB : 1); ++db) o[qb][db] = zero16();
-
-  const int64_t my_row = q0 + 32 * nbq + c;  // row whose epilogue this lane runs (with 3 other lanes)
-  // The epilogue works in base 2: z2 = z log2(e), p = 2^(z2 - m2).
-  const float c2 = inv_tau * kLog2e;
-  float m2 = -INFINITY;
-  double s_acc = 0.0, sz_acc = 0.0;  // this lane's share of sum p, sum p z2
-  bool flag = false;
-
-  // Bias of tile rows kvq(kh, hh, 0..7), kept as packed bf16 (two groups of
-  // four consecutive rows, one 8-byte load each when inside the vocabulary).
-  const auto bias_r = frag_rsrc(bias, HAS_BIAS ? V * 2 : 0);
-  auto load_bias = [&](int t, uint2 (&bv)[2]) {
-    if constexpr (HAS_BIAS) {
-      if ((t + 1) * BK <= V) {  // uniform: the whole tile lies inside the vocabulary
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int r0 = t * BK + 16 * kh + 8 * hf + 4 * hh;
-          bv[hf] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(bias_r, r0 * 2, 0, 0));
-        }
-      } else {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int r0 = t * BK + 16 * kh + 8 * hf + 4 * hh;
-          unsigned e[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_raw_buffer_load_b16(bias_r, min(r0 + j, V - 1) * 2, 0, 0);
-          bv[hf] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
-        }
-      }
-    } else {
-      bv[0] = bv[1] = make_uint2(0u, 0u);
-    }
-  };
-  auto bias_at = [&](const uint2 (&bv)[2], int j) -> float {
-    const uint2 u = bv[j >> 2];
-    const unsigned wd = (j & 2) ? u.y : u.x;
-    return __uint_as_float((j & 1) ? (wd & 0xffff0000u) : (wd << 16));
-  };
-  // S^T of the tile held in `a` (tile rows past V are zero in the
-  // fragment-major copy and masked in the epilogue); each k-slice of `a`, once its MFMAs are
-  // issued, is staged for the transposing load (WITH_O) and reloaded with
-  // the same slice of tile `t_next`.
-  auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int buf, int t_next) {
-    const auto r = frag_rsrc(frag_ptr<KB>(Wf, t_next, w, 0, 0), KS * 1024);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a[ks], q[nb][ks], ks == 0 ? zero16() : acc[nb]);
-      if constexpr (WITH_O)
-        *reinterpret_cast<bf16x8*>(&s_t[w][buf][sw_base[ks & 1] + 16 * ks]) = a[ks];
-      a[ks] = ld_buf(r, lane * 16, ks * 1024);
-      // keep the matrix, LDS and memory instructions of each k-step in this
-      // order (vector ALU work may move across): left to itself the compiler
-      // bunches the stage writes, and the waves then stall on the LDS queue
-      // (2 % faster here; the same fence slows the weight-gradient sweep)
-      __builtin_amdgcn_sched_barrier(0x002);
-    }
-  };
-  // The partial S^T in four groups of four rows per row block; the wave
-  // reducing quarter (nb, kh) reads groups 2kh and 2kh+1 of block nb.
-  auto write_part = [&](const f32x16 (&acc)[2]) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int ig = 0; ig < 4; ++ig)
-        s_part[w][nb][ig][lane] = f32x4{acc[nb][4 * ig], acc[nb][4 * ig + 1], acc[nb][4 * ig + 2], acc[nb][4 * ig + 3]};
-  };
-  auto reduce_part = [&](f32x4 (&sf)[2]) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      sf[e] = (s_part[0][nbq][2 * kh + e][lane] + s_part[1][nbq][2 * kh + e][lane]) +
-              (s_part[2][nbq][2 * kh + e][lane] + s_part[3][nbq][2 * kh + e][lane]);
-  };
-  // P KV of the staged tile in `buf` (A = P of row block qb, k-step ks from
-  // the wave that reduced quarter (qb, ks); B = staged rows kvq(ks, hh, *),
-  // columns 32db + c), with the reduce of the next tile's partials issued
-  // near the end.
-  auto pv_reduce = [&](int buf, f32x4 (&sf)[2]) {
-    f32x4 r[NW];
-    if constexpr (WITH_O) {
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) pf[qb][ks] = s_p[qb + 2 * ks][lane];
-      const unsigned short* tb = &s_t[w][buf][0];
-      constexpr int NF = 2 * DB;  // fragments (db, ks) in order
-      auto frag = [&](int f) {
-        const int db = f >> 1, ks = f & 1;
-        return ld_tr(tb + tr_base[0] + 16 * ks * TS + 32 * db, tb + tr_base[1] + 16 * ks * TS + 32 * db);
-      };
-      bf16x8 b0 = frag(0), b1 = frag(1);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const bf16x8 b2 = frag(f + 2 < NF ? f + 2 : NF - 1);
-        if (f == (NF > 6 ? NF - 6 : 0)) {
-#pragma unroll
-          for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh][lane];
-        }
-        if (f == (NF > 3 ? NF - 3 : 0)) {
-          sf[0] = (r[0] + r[1]) + (r[2] + r[3]);
-#pragma unroll
-          for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh + 1][lane];
-        }
-        const int db = f >> 1, ks = f & 1;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) o[qb][db] = mfma32(pf[qb][ks], b0, o[qb][db]);
-        b0 = b1;
-        b1 = b2;
-      }
-    } else {
-#pragma unroll
-      for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh][lane];
-      sf[0] = (r[0] + r[1]) + (r[2] + r[3]);
-#pragma unroll
-      for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh + 1][lane];
-    }
-    sf[1] = (r[0] + r[1]) + (r[2] + r[3]);
-  };
-  // Logits (base 2) of the eight tile rows this lane holds; rows past the
-  // vocabulary get -1e30 (2^(-1e30 - m2) = 0 and 0 * z = 0).
-  auto logits = [&](int v0, const f32x4 (&sf)[2], const uint2 (&bv)[2], float (&z)[8]) {
-    const int lim = V - v0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float sv_ = sf[j >> 2][j & 3];
-      const float zz = HAS_BIAS ? (sv_ + bias_at(bv, j)) * c2 : sv_ * c2;
-      z[j] = kvq(kh, hh, j) < lim ? zz : -1e30f;
-    }
-  };
-
-  f32x16 acc[2];
-  f32x4 sf[2];
-  uint2 bv[2];
-  if (any) {
-    load_bias(t_begin, bv);
-    s_step(a, acc, t_begin & 1, min(t_begin + 1, t_end - 1));
-    write_part(acc);
-  }
-  __syncthreads();
-  if (t_begin < t_end) {
-    reduce_part(sf);
-    // reference m2: the row's max over its first tile, from the four lanes
-    // (two lane halves of two waves) that hold the row
-    float z[8];
-    logits(t_begin * BK, sf, bv, z);
-    float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-    mx = fmaxf(mx, other_half(mx, hh));
-    if (hh == 0) s_x[w * 64 + c] = mx;
-  }
-  __syncthreads();
-  if (t_begin < t_end) m2 = fmaxf(s_x[w * 64 + c], s_x[(w ^ 2) * 64 + c]);
-  __syncthreads();
-
-  for (int t = t_begin; t < t_end; ++t) {
-    const int v0 = t * BK;
-    const int tn = min(t + 1, t_end - 1);
-    const int tnn = min(t + 2, t_end - 1);
-    uint2 bvn[2];
-    load_bias(tn, bvn);
-    // ---- epilogue of tile t (vector ALU; the scheduler interleaves it with
-    //      the logit MFMAs of tile t+1 below) -------------------------------
-    float z[8];
-    logits(v0, sf, bv, z);
-    float sp = 0.f, szp = 0.f;
-    bf16x8 pa;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      flag |= z[j] > m2 + kRefSlack2;
-      const float pj = __builtin_amdgcn_exp2f(fminf(z[j] - m2, kRefSlack2));
-      sp += pj;
-      szp = fmaf(pj, z[j], szp);
-      pa[j] = (__bf16)pj;
-    }
-    s_acc += (double)sp;
-    sz_acc += (double)szp;
-    // ---- logits of tile t+1 on the matrix cores, stage t+1, load t+2 -------
-    s_step(a, acc, (t + 1) & 1, tnn);
-    __builtin_amdgcn_sched_barrier(0);
-    exec_barrier();
-    if constexpr (WITH_O) s_p[w][lane] = pa;
-    write_part(acc);
-    __syncthreads();
-    // ---- accumulator product of tile t, reduce of tile t+1 -----------------
-    pv_reduce(t & 1, sf);
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) bv[hf] = bvn[hf];
-  }
-
-  // ---- results: combine the four holders of each row ----------------------
-  double sx = s_acc + (double)__shfl_xor(s_acc, 32, 64);
-  double szx = sz_acc + (double)__shfl_xor(sz_acc, 32, 64);
-  int fl = flag ? 1 : 0;
-  fl |= __shfl_xor(fl, 32, 64);
-  __syncthreads();
-  if (hh == 0) {
-    s_xd[(2 * w) * 64 + c] = sx;
-    s_xd[(2 * w + 1) * 64 + c] = szx;
-    s_x[w * 64 + c] = __int_as_float(fl);
-  }
-  __syncthreads();
-  if (kh == 0 && hh == 0 && my_row < N) {
-    RowStats rs;
-    rs.m = (float)((double)m2 * kLn2);
-    rs.zy = 0.f;
-    rs.s = sx + s_xd[(2 * (w ^ 2)) * 64 + c];
-    rs.sz = (szx + s_xd[(2 * (w ^ 2) + 1) * 64 + c]) * kLn2;
-    rs.flag = (fl | __float_as_int(s_x[(w ^ 2) * 64 + c])) ? 1 : 0;
-    rs.pad = 0;
-    stats[(int64_t)sv * N + my_row] = rs;
-  }
-  if constexpr (WITH_O) {
-    float* Ob = O + (int64_t)sv * N * H;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t row = q0 + 32 * qb + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (row < N) {
-          float* dst = Ob + row * H + d0 + c;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) dst[32 * db] = o[qb][db][i];
-        }
-      }
-  }
-}
-
-template <int KB>
-hipError_t fwd_dispatch(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int V, float inv_tau, int Sv,
-                        int tps, bool with_o, RowStats* stats, float* O, hipStream_t st) {
-  const int64_t nrb = (N + BQ - 1) / BQ;
-  dim3 grid((unsigned)(nrb * Sv)), block(256);
-  if (with_o && b)
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true, true>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats,
-                       O);
-  else if (with_o)
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, true, false>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats,
-                       O);
-  else if (b)
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false, true>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats,
-                       O);
-  else
-    hipLaunchKernelGGL((fwd_mfma_kernel<KB, false, false>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps,
-                       stats, O);
-  return hipGetLastError();
-}
-
-}  // namespace
-
 hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
                            int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st) {
-  const int n_tiles = (V + BK - 1) / BK;
-  const int tps = (n_tiles + Sv - 1) / Sv;
-  switch (H / 128) {
-    case 1: return fwd_dispatch<1>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 2: return fwd_dispatch<2>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 3: return fwd_dispatch<3>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 4: return fwd_dispatch<4>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 5: return fwd_dispatch<5>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 6: return fwd_dispatch<6>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    case 7: return fwd_dispatch<7>(h, Wf, b, N, V, inv_tau, Sv, tps, with_o, stats, O, st);
-    default: return hipErrorInvalidValue;
-  }
+  if (with_o && !b) return launch_fwd_mfma_o_nobias(h, Wf, N, H, V, inv_tau, Sv, stats, O, st);
+  if (with_o) return fwd_launch<true, true, false>(h, Wf, b, N, H, V, inv_tau, Sv, stats, O, st);
+  if (b) return fwd_launch<false, true, false>(h, Wf, b, N, H, V, inv_tau, Sv, stats, O, st);
+  return fwd_launch<false, false, false>(h, Wf, b, N, H, V, inv_tau, Sv, stats, O, st);
 }
 
 }  // namespace plp

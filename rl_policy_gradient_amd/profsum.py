@@ -26,7 +26,7 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCES = ("lmhead_fwd.hip", "lmhead_mfma.hip", "mfma_tile.h", "loss_stage.hip", "plp_api.cpp", "common.h")
+KERNEL_SOURCES = ("fwd_sweep.h", "lmhead_fwd.hip", "lmhead_fwd_o.hip", "lmhead_mfma.hip", "mfma_tile.h", "loss_stage.hip", "plp_api.cpp", "common.h")
 
 
 def kernel_src_hash() -> str:
