@@ -18,15 +18,10 @@ BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["lmhead_fwd.hip", "lmhead_fwd_o.hip", "lmhead_mfma.hip", "lmhead_generic.hip", "loss_stage.hip",
            "plp_api.cpp"]
 
-# Per-source compiler options. The forward sweep's no-bias variant with the
-# grad_h accumulator is scheduled with LLVM's iterative ILP strategy: 2-3.6 %
-# faster than the default at 512 to 16384 tokens, measured on MI355X; the
-# same strategy slows the biased variant and the weight-gradient sweep, which
-# keep the default. The weight-gradient sweep gains about 1 % at 512 to
-# 16384 tokens without the scheduler's unclustered high-register-pressure
-# rescheduling stage.
+# Per-source compiler options. The weight-gradient sweep gains about 1 % at
+# 512 to 16384 tokens without the scheduler's unclustered high-register-
+# pressure rescheduling stage (measured on MI355X).
 EXTRA = {
-    "lmhead_fwd_o.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "lmhead_mfma.hip": ["-mllvm", "-amdgpu-disable-unclustered-high-rp-reschedule"],
 }
 

@@ -1,14 +1,13 @@
-// Forward sweep, variant with the grad_h accumulator and no bias (the common
-// case). Compiled with LLVM's iterative ILP scheduling strategy; with it the
-// per-k-step fence pays (2-3.6 % faster at 512-16384 tokens on MI355X than
-// the default scheduler without the fence).
+// Forward sweep with the grad_h accumulator: the two-role kernel, with and
+// without a bias.
 #include "fwd_sweep.h"
 
 namespace plp {
 
-hipError_t launch_fwd_mfma_o_nobias(const __bf16* h, const __bf16* Wf, int64_t N, int H, int V, float inv_tau, int Sv,
-                                    RowStats* stats, float* O, hipStream_t st) {
-  return fwd_launch<true, false, true>(h, Wf, nullptr, N, H, V, inv_tau, Sv, stats, O, st);
+hipError_t launch_fwd_mfma_o(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
+                             int Sv, RowStats* stats, float* O, hipStream_t st) {
+  if (b) return fwd_pp_launch<true>(h, Wf, b, N, H, V, inv_tau, Sv, stats, O, st);
+  return fwd_pp_launch<false>(h, Wf, b, N, H, V, inv_tau, Sv, stats, O, st);
 }
 
 }  // namespace plp
