@@ -51,27 +51,38 @@ __global__ __launch_bounds__(256) void frag_copy_kernel(const __bf16* __restrict
 // acc_mode: 0 write the output dtype; 1 store fp32 accumulator; 2 add into it;
 // 3 add the fp32 accumulator and write the output dtype.
 // ---------------------------------------------------------------------------
+// Weight-gradient sweep as two roles per SIMD (eight waves, two per SIMD,
+// 256 registers each), like the forward sweep's accumulator passes: waves
+// 0-3 (S role) keep the resident W rows of their H quarter, compute the
+// logits of token tile t+1 with its stage writes and loads, reduce the
+// partials and run the epilogue (dz, grad_b); waves 4-7 (PV role) keep the
+// grad_W accumulator of the same quarter and compute dZ^T h of tile t, its
+// two contraction steps split over the two phases between the barriers.
+// P (dz) is double buffered; every sum runs in the same order as in a single
+// role, so results are bit-identical.
 template <int KB, bool HAS_BIAS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bias,
-                     const __bf16* __restrict__ hcf, const TokData* __restrict__ tok,
-                     const int* __restrict__ count_dev, int V, float inv_tau, int acc_mode,
-                     float* __restrict__ gW_acc, float* __restrict__ gb_acc, __bf16* __restrict__ gW_out,
-                     __bf16* __restrict__ gb_out, int whole, int parts, float* __restrict__ part_w,
-                     float* __restrict__ part_b) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bias,
+                   const __bf16* __restrict__ hcf, const TokData* __restrict__ tok,
+                   const int* __restrict__ count_dev, int V, float inv_tau, int acc_mode,
+                   float* __restrict__ gW_acc, float* __restrict__ gb_acc, __bf16* __restrict__ gW_out,
+                   __bf16* __restrict__ gb_out, int whole, int parts, float* __restrict__ part_w,
+                   float* __restrict__ part_b) {
   constexpr int H = 128 * KB;
   constexpr int DS = Stage<KB>::DS;
   constexpr int TS = Stage<KB>::TS;
   constexpr int KS = DS / 16;
   constexpr int DB = DS / 32;
   __shared__ f32x4 s_part[NW][2][4][64];
-  __shared__ bf16x8 s_p[4][64];
+  __shared__ bf16x8 s_p[2][4][64];
   __shared__ TokData s_tok[2][BK];
   __shared__ unsigned short s_t[NW][2][BK * TS];
   double* s_xd = reinterpret_cast<double*>(&s_part[0][0][0][0]);  // [NW][64], after the sweep
 
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wall = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool srole = wall < 4;
+  const int w = wall & 3;  // H quarter
   const int hh = lane >> 5, c = lane & 31;
   const int nbq = w & 1, kh = w >> 1;
   const int n_tok = *count_dev;
@@ -90,235 +101,242 @@ void bwd_mfma_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ b
   }
   const int q0 = blk * BQ;
   const int d0 = w * DS;
-  // Stage write offsets (element) of lane (hh, c) for even / odd k-step:
-  // row c, chunk 2ks + hh at position (2ks + hh) ^ s(c), s(c) = (c >> 1) & 3.
-  int sw_base[2];
-  {
-    const int x = hh ^ ((c >> 1) & 3);
-    sw_base[0] = c * TS + 8 * x;
-    sw_base[1] = c * TS + 8 * (x ^ 2) - 16;
-  }
-  // Transposing-load offsets: provider lane p of 16-lane group G reads row
-  // 4(G/2) + p/4 (and 8 further down) of contraction step ks, chunk
-  // 4db + 2(G%2) + (p%4)/2 of column block db, half p%2.
-  int tr_base[2];
-  {
-    const int p = lane & 15, G = lane >> 4;
-    const int r = 4 * (G >> 1) + (p >> 2);
-    const int b = 2 * (G & 1) + ((p >> 1) & 1);
-    const int s = (r >> 1) & 3;  // the same for rows r + 8 and r + 16
-    tr_base[0] = r * TS + 8 * (b ^ s) + 4 * (p & 1);
-    tr_base[1] = (r + 8) * TS + 8 * (b ^ s) + 4 * (p & 1);
-  }
-
-  // Per-token data of tile t, loaded into registers one phase before it is
-  // written to LDS (wave 0, lanes < 32), so the load latency stays hidden.
-  // Held as a plain vector: a TokData variable was placed in LDS by the
-  // compiler, whose store right after the load then waited for every
-  // outstanding load of the wave, the token tiles included.
   const bool any = t_hi > t_lo;
-  static_assert(sizeof(TokData) == 16, "one 16-byte record per token");
-  const auto tok_r = __builtin_amdgcn_make_buffer_rsrc(const_cast<TokData*>(tok), 0, 0x7ffffff0, 0x00020000);
-  u32x4 tk = {0u, 0u, 0u, 0u};
-  auto load_tok = [&](int t) {
-    if (w == 0 && lane < BK) tk = __builtin_amdgcn_raw_buffer_load_b128(tok_r, (t * BK + lane) * 16, 0, 0);
-  };
-  auto stage_tok = [&](int t) {
-    if (w == 0 && lane < BK) *reinterpret_cast<u32x4*>(&s_tok[t & 1][lane]) = tk;
-  };
-  if (any) load_tok(t_lo);
-  // Resident W fragments (B operand of S^T), rows q0 + 32nb + c, cols
-  // d0 + 16ks + 8hh, from the fragment-major copy (rows past V are zero),
-  // and the first token tile, in k-step order so that the first MFMAs wait
-  // only for their own operands.
-  bf16x8 q[2][KS];
-  bf16x8 a[KS];
-  {
-    const auto rq0 = frag_rsrc(frag_ptr<KB>(Wf, q0 / BK, w, 0, 0), KS * 1024);
-    const auto rq1 = frag_rsrc(frag_ptr<KB>(Wf, q0 / BK + 1, w, 0, 0), KS * 1024);
-    // an empty token range loads nothing (zero range)
-    const auto ra = frag_rsrc(frag_ptr<KB>(hcf, any ? t_lo : 0, w, 0, 0), any ? KS * 1024 : 0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      q[0][ks] = ld_buf_nt(rq0, lane * 16, ks * 1024);
-      q[1][ks] = ld_buf_nt(rq1, lane * 16, ks * 1024);
-      a[ks] = ld_buf(ra, lane * 16, ks * 1024);
-    }
-  }
-  f32x16 o[2][DB];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[qb][db] = zero16();
 
-  const int my_v = q0 + 32 * nbq + c;
-  const float bvl = HAS_BIAS ? (float)bias[min(my_v, V - 1)] : 0.f;
-  double gb_run = 0.0;
-
-  auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int buf, int t_next) {
-    const auto r = frag_rsrc(frag_ptr<KB>(hcf, t_next, w, 0, 0), KS * 1024);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a[ks], q[nb][ks], ks == 0 ? zero16() : acc[nb]);
-      *reinterpret_cast<bf16x8*>(&s_t[w][buf][sw_base[ks & 1] + 16 * ks]) = a[ks];
-      a[ks] = ld_buf(r, lane * 16, ks * 1024);
+  if (srole) {
+    // ======================= S role =======================
+    // Stage write offsets (element) of lane (hh, c) for even / odd k-step:
+    // row c, chunk 2ks + hh at position (2ks + hh) ^ s(c), s(c) = (c >> 1) & 3.
+    int sw_base[2];
+    {
+      const int x = hh ^ ((c >> 1) & 3);
+      sw_base[0] = c * TS + 8 * x;
+      sw_base[1] = c * TS + 8 * (x ^ 2) - 16;
     }
-  };
-  auto write_part = [&](const f32x16 (&acc)[2]) {
+    // Per-token data of tile t, loaded into registers one phase before it
+    // is written to LDS (wave 0, lanes < 32). Held as a plain vector: a
+    // TokData variable was placed in LDS by the compiler, whose store right
+    // after the load then waited for every outstanding load of the wave.
+    static_assert(sizeof(TokData) == 16, "one 16-byte record per token");
+    const auto tok_r = __builtin_amdgcn_make_buffer_rsrc(const_cast<TokData*>(tok), 0, 0x7ffffff0, 0x00020000);
+    u32x4 tk = {0u, 0u, 0u, 0u};
+    auto load_tok = [&](int t) {
+      if (w == 0 && lane < BK) tk = __builtin_amdgcn_raw_buffer_load_b128(tok_r, (t * BK + lane) * 16, 0, 0);
+    };
+    auto stage_tok = [&](int t) {
+      if (w == 0 && lane < BK) *reinterpret_cast<u32x4*>(&s_tok[t & 1][lane]) = tk;
+    };
+    if (any) load_tok(t_lo);
+    // Resident W fragments (B operand of S^T), rows q0 + 32nb + c, cols
+    // d0 + 16ks + 8hh, from the fragment-major copy (rows past V are zero),
+    // and the first token tile, in k-step order so that the first MFMAs
+    // wait only for their own operands.
+    bf16x8 q[2][KS];
+    bf16x8 a[KS];
+    {
+      const auto rq0 = frag_rsrc(frag_ptr<KB>(Wf, q0 / BK, w, 0, 0), KS * 1024);
+      const auto rq1 = frag_rsrc(frag_ptr<KB>(Wf, q0 / BK + 1, w, 0, 0), KS * 1024);
+      // an empty token range loads nothing (zero range)
+      const auto ra = frag_rsrc(frag_ptr<KB>(hcf, any ? t_lo : 0, w, 0, 0), any ? KS * 1024 : 0);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+      for (int ks = 0; ks < KS; ++ks) {
+        q[0][ks] = ld_buf_nt(rq0, lane * 16, ks * 1024);
+        q[1][ks] = ld_buf_nt(rq1, lane * 16, ks * 1024);
+        a[ks] = ld_buf(ra, lane * 16, ks * 1024);
+      }
+    }
+    const int my_v = q0 + 32 * nbq + c;
+    const float bvl = HAS_BIAS ? (float)bias[min(my_v, V - 1)] : 0.f;
+    double gb_run = 0.0;
+
+    auto s_step = [&](f32x16 (&acc)[2], int buf, int t_next) {
+      const auto r = frag_rsrc(frag_ptr<KB>(hcf, t_next, w, 0, 0), KS * 1024);
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig)
-        s_part[w][nb][ig][lane] = f32x4{acc[nb][4 * ig], acc[nb][4 * ig + 1], acc[nb][4 * ig + 2], acc[nb][4 * ig + 3]};
-  };
-  auto reduce_part = [&](f32x4 (&sf)[2]) {
+      for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
-      sf[e] = (s_part[0][nbq][2 * kh + e][lane] + s_part[1][nbq][2 * kh + e][lane]) +
-              (s_part[2][nbq][2 * kh + e][lane] + s_part[3][nbq][2 * kh + e][lane]);
-  };
-  auto pv_reduce = [&](int buf, f32x4 (&sf)[2]) {
-    f32x4 r[NW];
-    bf16x8 pf[2][2];
+        for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a[ks], q[nb][ks], ks == 0 ? zero16() : acc[nb]);
+        *reinterpret_cast<bf16x8*>(&s_t[w][buf][sw_base[ks & 1] + 16 * ks]) = a[ks];
+        a[ks] = ld_buf(r, lane * 16, ks * 1024);
+      }
+    };
+    auto write_part = [&](const f32x16 (&acc)[2]) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig)
+          s_part[w][nb][ig][lane] = f32x4{acc[nb][4 * ig], acc[nb][4 * ig + 1], acc[nb][4 * ig + 2], acc[nb][4 * ig + 3]};
+    };
+    auto reduce_part = [&](f32x4 (&sf)[2]) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        sf[e] = (s_part[0][nbq][2 * kh + e][lane] + s_part[1][nbq][2 * kh + e][lane]) +
+                (s_part[2][nbq][2 * kh + e][lane] + s_part[3][nbq][2 * kh + e][lane]);
+    };
+    // Epilogue of tile t: dz = g / tau ([v = y] - p) as bf16 P of this
+    // wave's quarter, and this lane's share of grad_b.
+    auto epilogue = [&](int t, const f32x4 (&sf)[2]) {
+      const int t0 = t * BK;
+      bf16x8 pa;
+      float gsum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kv = kvq(kh, hh, j);
+        const TokData td = s_tok[t & 1][kv];
+        const float sv_ = sf[j >> 2][j & 3];
+        const float z = (sv_ + bvl) * inv_tau;
+        const float pr = __expf(z - td.lse);
+        float dz = td.gs * ((td.y == my_v ? 1.f : 0.f) - pr);
+        dz = (t0 + kv < n_tok && my_v < V) ? dz : 0.f;
+        gsum += dz;
+        pa[j] = (__bf16)dz;
+      }
+      gb_run += (double)gsum;
+      s_p[t & 1][w][lane] = pa;
+    };
+
+    f32x16 acc[2];
+    f32x4 sf[2];
+    if (any) {
+      stage_tok(t_lo);
+      load_tok(min(t_lo + 1, t_hi - 1));
+      s_step(acc, t_lo & 1, min(t_lo + 1, t_hi - 1));
+      write_part(acc);
+    }
+    __syncthreads();  // P0
+    if (any) {
+      reduce_part(sf);
+      epilogue(t_lo, sf);
+    }
+    for (int t = t_lo; t < t_hi; ++t) {
+      __syncthreads();  // A
+      const bool more = t + 1 < t_hi;
+      if (more) {
+        stage_tok(t + 1);
+        load_tok(min(t + 2, t_hi - 1));
+        s_step(acc, (t + 1) & 1, min(t + 2, t_hi - 1));
+        write_part(acc);
+      }
+      __syncthreads();  // B
+      if (more) {
+        reduce_part(sf);
+        epilogue(t + 1, sf);
+      }
+    }
+
+    // grad_b: the four holders of a vocabulary row (two lane halves of two
+    // waves) hold disjoint token subsets
+    const double gbv = gb_run + __shfl_xor(gb_run, 32, 64);
+    __syncthreads();  // R0
+    if (hh == 0) s_xd[w * 64 + c] = gbv;
+    __syncthreads();  // R1
+    if (slot >= 0) {  // a share of a tail block: fp32 partial sum, combined by tail_reduce_kernel
+      if (kh == 0 && hh == 0) part_b[slot * BQ + 32 * nbq + c] = (float)(gbv + s_xd[(w ^ 2) * 64 + c]);
+      return;
+    }
+    const bool from_acc = acc_mode == 2 || acc_mode == 3;
+    const bool to_acc = acc_mode == 1 || acc_mode == 2;
+    if (kh == 0 && hh == 0 && my_v < V && (to_acc ? gb_acc != nullptr : gb_out != nullptr)) {
+      double val = gbv + s_xd[(w ^ 2) * 64 + c];
+      if (from_acc) val += (double)gb_acc[my_v];
+      if (to_acc) gb_acc[my_v] = (float)val;
+      else gb_out[my_v] = (__bf16)(float)val;
+    }
+  } else {
+    // ======================= PV role =======================
+    // Transposing-load offsets: provider lane p of 16-lane group G reads row
+    // 4(G/2) + p/4 (and 8 further down) of contraction step ks, chunk
+    // 4db + 2(G%2) + (p%4)/2 of column block db, half p%2.
+    int tr_base[2];
+    {
+      const int p = lane & 15, G = lane >> 4;
+      const int r = 4 * (G >> 1) + (p >> 2);
+      const int b = 2 * (G & 1) + ((p >> 1) & 1);
+      const int s = (r >> 1) & 3;  // the same for rows r + 8 and r + 16
+      tr_base[0] = r * TS + 8 * (b ^ s) + 4 * (p & 1);
+      tr_base[1] = (r + 8) * TS + 8 * (b ^ s) + 4 * (p & 1);
+    }
+    f32x16 o[2][DB];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) pf[qb][ks] = s_p[qb + 2 * ks][lane];
-    const unsigned short* tb = &s_t[w][buf][0];
-    constexpr int NF = 2 * DB;
-    auto frag = [&](int f) {
-      const int db = f >> 1, ks = f & 1;
-      return ld_tr(tb + tr_base[0] + 16 * ks * TS + 32 * db, tb + tr_base[1] + 16 * ks * TS + 32 * db);
+      for (int db = 0; db < DB; ++db) o[qb][db] = zero16();
+    // dZ^T h of tile t, contraction step ks (16 token rows)
+    auto pv = [&](int t, int ks) {
+      const int buf = t & 1;
+      const unsigned short* tb = &s_t[w][buf][0];
+      const bf16x8 p0 = s_p[buf][0 + 2 * ks][lane], p1 = s_p[buf][1 + 2 * ks][lane];
+      auto frag = [&](int db) {
+        return ld_tr(tb + tr_base[0] + 16 * ks * TS + 32 * db, tb + tr_base[1] + 16 * ks * TS + 32 * db);
+      };
+      bf16x8 b0 = frag(0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 b1 = frag(db + 1 < DB ? db + 1 : DB - 1);
+        o[0][db] = mfma32(p0, b0, o[0][db]);
+        o[1][db] = mfma32(p1, b0, o[1][db]);
+        b0 = b1;
+      }
     };
-    bf16x8 b0 = frag(0), b1 = frag(1);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const bf16x8 b2 = frag(f + 2 < NF ? f + 2 : NF - 1);
-      if (f == (NF > 6 ? NF - 6 : 0)) {
-#pragma unroll
-        for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh][lane];
-      }
-      if (f == (NF > 3 ? NF - 3 : 0)) {
-        sf[0] = (r[0] + r[1]) + (r[2] + r[3]);
-#pragma unroll
-        for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh + 1][lane];
-      }
-      const int db = f >> 1, ks = f & 1;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) o[qb][db] = mfma32(pf[qb][ks], b0, o[qb][db]);
-      b0 = b1;
-      b1 = b2;
+    __syncthreads();  // P0
+    for (int t = t_lo; t < t_hi; ++t) {
+      __syncthreads();  // A
+      pv(t, 0);
+      __syncthreads();  // B
+      pv(t, 1);
     }
-    sf[1] = (r[0] + r[1]) + (r[2] + r[3]);
-  };
-
-  f32x16 acc[2];
-  f32x4 sf[2];
-  if (any) {
-    stage_tok(t_lo);
-    load_tok(min(t_lo + 1, t_hi - 1));
-    s_step(a, acc, t_lo & 1, min(t_lo + 1, t_hi - 1));
-    write_part(acc);
-  }
-  __syncthreads();
-  if (t_hi > t_lo) reduce_part(sf);
-
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int t0 = t * BK;
-    const int tn = min(t + 1, t_hi - 1);
-    const int tnn = min(t + 2, t_hi - 1);
-    // ---- epilogue of tile t (vector ALU; the scheduler interleaves it with
-    //      the logit MFMAs of tile t+1 below) -------------------------------
-    bf16x8 pa;
-    float gsum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kv = kvq(kh, hh, j);
-      const TokData td = s_tok[t & 1][kv];
-      const float sv_ = sf[j >> 2][j & 3];
-      const float z = (sv_ + bvl) * inv_tau;
-      const float pr = __expf(z - td.lse);
-      float dz = td.gs * ((td.y == my_v ? 1.f : 0.f) - pr);
-      dz = (t0 + kv < n_tok && my_v < V) ? dz : 0.f;
-      gsum += dz;
-      pa[j] = (__bf16)dz;
+    __syncthreads();  // R0
+    __syncthreads();  // R1
+    // The accumulator leaves through this quarter's stage buffer (the S-role
+    // wave of the quarter no longer uses it).
+    float* sbuf = reinterpret_cast<float*>(&s_t[w][0][0]);
+    if (slot >= 0) {
+      float* pw = part_w + (int64_t)slot * BQ * H;
+      store_acc<4, DS, DB>(o, sbuf, hh, c, lane, [&](int qb, int r, int col, const f32x4 (&v)[1]) {
+        *reinterpret_cast<f32x4*>(pw + (int64_t)(32 * qb + r) * H + d0 + col) = v[0];
+      });
+      return;
     }
-    gb_run += (double)gsum;
-    // ---- logits of tile t+1, stage t+1, load t+2 ---------------------------
-    s_step(a, acc, (t + 1) & 1, tnn);
-    __builtin_amdgcn_sched_barrier(0);
-    exec_barrier();
-    s_p[w][lane] = pa;
-    write_part(acc);
-    stage_tok(tn);
-    __syncthreads();
-    load_tok(tnn);
-    pv_reduce(t & 1, sf);
-  }
-
-  // grad_b: the four holders of a vocabulary row (two lane halves of two
-  // waves) hold disjoint token subsets
-  double gbv = gb_run + __shfl_xor(gb_run, 32, 64);
-  __syncthreads();
-  if (hh == 0) s_xd[w * 64 + c] = gbv;
-  __syncthreads();
-  if (slot >= 0) {  // a share of a tail block: fp32 partial sums, combined by tail_reduce_kernel
-    if (kh == 0 && hh == 0) part_b[slot * BQ + 32 * nbq + c] = (float)(gbv + s_xd[(w ^ 2) * 64 + c]);
-    float* pw = part_w + (int64_t)slot * BQ * H;
-    store_acc<4, DS, DB>(o, reinterpret_cast<float*>(&s_t[w][0][0]), hh, c, lane,
-                         [&](int qb, int r, int col, const f32x4 (&v)[1]) {
-                           *reinterpret_cast<f32x4*>(pw + (int64_t)(32 * qb + r) * H + d0 + col) = v[0];
-                         });
-    return;  // uniform
-  }
-  const bool from_acc = acc_mode == 2 || acc_mode == 3;
-  const bool to_acc = acc_mode == 1 || acc_mode == 2;
-  if (kh == 0 && hh == 0 && my_v < V && (to_acc ? gb_acc != nullptr : gb_out != nullptr)) {
-    double val = gbv + s_xd[(w ^ 2) * 64 + c];
-    if (from_acc) val += (double)gb_acc[my_v];
-    if (to_acc) gb_acc[my_v] = (float)val;
-    else gb_out[my_v] = (__bf16)(float)val;
-  }
-  if (to_acc ? gW_acc == nullptr : gW_out == nullptr) return;  // uniform: every wave returns
-  float* sbuf = reinterpret_cast<float*>(&s_t[w][0][0]);
-  if (to_acc) {  // fp32 accumulator rows, one f32x4 per lane
-    store_acc<4, DS, DB>(o, sbuf, hh, c, lane, [&](int qb, int r, int col, const f32x4 (&v)[1]) {
-      const int vr = q0 + 32 * qb + r;
-      if (vr >= V) return;
-      f32x4* dst = reinterpret_cast<f32x4*>(gW_acc + (int64_t)vr * H + d0 + col);
-      *dst = from_acc ? *dst + v[0] : v[0];
-    });
-  } else {  // output dtype, eight bf16 (16 bytes) per lane
-    store_acc<8, DS, DB>(o, sbuf, hh, c, lane, [&](int qb, int r, int col, const f32x4 (&v)[2]) {
-      const int vr = q0 + 32 * qb + r;
-      if (vr >= V) return;
-      const int64_t k = (int64_t)vr * H + d0 + col;
-      f32x4 lo = v[0], hi = v[1];
-      if (from_acc) {
-        lo += *reinterpret_cast<const f32x4*>(gW_acc + k);
-        hi += *reinterpret_cast<const f32x4*>(gW_acc + k + 4);
-      }
-      bf16x8 u;
+    const bool from_acc = acc_mode == 2 || acc_mode == 3;
+    const bool to_acc = acc_mode == 1 || acc_mode == 2;
+    if (to_acc ? gW_acc == nullptr : gW_out == nullptr) return;  // uniform
+    if (to_acc) {  // fp32 accumulator rows, one f32x4 per lane
+      store_acc<4, DS, DB>(o, sbuf, hh, c, lane, [&](int qb, int r, int col, const f32x4 (&v)[1]) {
+        const int vr = q0 + 32 * qb + r;
+        if (vr >= V) return;
+        f32x4* dst = reinterpret_cast<f32x4*>(gW_acc + (int64_t)vr * H + d0 + col);
+        *dst = from_acc ? *dst + v[0] : v[0];
+      });
+    } else {  // output dtype, eight bf16 (16 bytes) per lane
+      store_acc<8, DS, DB>(o, sbuf, hh, c, lane, [&](int qb, int r, int col, const f32x4 (&v)[2]) {
+        const int vr = q0 + 32 * qb + r;
+        if (vr >= V) return;
+        const int64_t k = (int64_t)vr * H + d0 + col;
+        f32x4 lo = v[0], hi = v[1];
+        if (from_acc) {
+          lo += *reinterpret_cast<const f32x4*>(gW_acc + k);
+          hi += *reinterpret_cast<const f32x4*>(gW_acc + k + 4);
+        }
+        bf16x8 u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u[j] = (__bf16)lo[j];
-        u[4 + j] = (__bf16)hi[j];
-      }
-      // written once and read by nobody in this call: non-temporal, so that
-      // the token tiles stay in L2
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, u), reinterpret_cast<u32x4*>(gW_out + k));
-    });
+        for (int j = 0; j < 4; ++j) {
+          u[j] = (__bf16)lo[j];
+          u[4 + j] = (__bf16)hi[j];
+        }
+        // written once and read by nobody in this call: non-temporal, so
+        // that the token tiles stay in L2
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, u), reinterpret_cast<u32x4*>(gW_out + k));
+      });
+    }
   }
 }
 
 constexpr int kTailParts = 4;     // workgroups sharing one tail block of the weight-gradient sweep
 constexpr int kMaxTailWGs = 256;  // bound of the partial-sum scratch (workgroups)
 
-// Workgroups of 256 threads of `kernel` the device holds at once (compute
-// units x workgroups per unit), computed once per device and kernel.
+// Workgroups of `threads` threads of `kernel` the device holds at once
+// (compute units x workgroups per unit), computed once per device.
 template <typename K>
-hipError_t resident_workgroups(K kernel, int* out) {
+hipError_t resident_workgroups(K kernel, int threads, int* out) {
   constexpr int kMaxDevices = 64;
   static int cache[kMaxDevices] = {};
   int dev = 0;
@@ -331,7 +349,7 @@ hipError_t resident_workgroups(K kernel, int* out) {
   int cus = 0, per_cu = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
   if (e != hipSuccess) return e;
   const int n = cus * (per_cu > 0 ? per_cu : 1);
   if (dev >= 0 && dev < kMaxDevices) cache[dev] = n;
@@ -390,8 +408,8 @@ hipError_t bwd_dispatch(const __bf16* Wf, const __bf16* b, const __bf16* hcf, co
   // fit the free slots (at most kTailParts, and kMaxTailWGs in all).
   const int nblk = (V + BQ - 1) / BQ;
   int resident = 0;
-  hipError_t e = b ? resident_workgroups(bwd_mfma_kernel<KB, true>, &resident)
-                   : resident_workgroups(bwd_mfma_kernel<KB, false>, &resident);
+  hipError_t e = b ? resident_workgroups(bwd_pp_kernel<KB, true>, 512, &resident)
+                   : resident_workgroups(bwd_pp_kernel<KB, false>, 512, &resident);
   if (e != hipSuccess) return e;
   const int rem = resident > 0 ? nblk % resident : 0;
   int parts = rem > 0 ? min(kTailParts, min(resident, kMaxTailWGs) / rem) : 1;
@@ -400,12 +418,12 @@ hipError_t bwd_dispatch(const __bf16* Wf, const __bf16* b, const __bf16* hcf, co
   const int tail_wgs = parts > 1 ? rem * parts : 0;
   float* part_w = tail_scratch;
   float* part_b = tail_scratch ? tail_scratch + (size_t)kMaxTailWGs * BQ * (128 * KB) : nullptr;
-  dim3 grid((unsigned)(whole + tail_wgs)), block(256);
+  dim3 grid((unsigned)(whole + tail_wgs)), block(512);
   if (b)
-    hipLaunchKernelGGL((bwd_mfma_kernel<KB, true>), grid, block, 0, st, Wf, b, hcf, tok, count_dev, V, inv_tau,
+    hipLaunchKernelGGL((bwd_pp_kernel<KB, true>), grid, block, 0, st, Wf, b, hcf, tok, count_dev, V, inv_tau,
                        acc_mode, gW_acc, gb_acc, gW_out, gb_out, whole, parts, part_w, part_b);
   else
-    hipLaunchKernelGGL((bwd_mfma_kernel<KB, false>), grid, block, 0, st, Wf, b, hcf, tok, count_dev, V, inv_tau,
+    hipLaunchKernelGGL((bwd_pp_kernel<KB, false>), grid, block, 0, st, Wf, b, hcf, tok, count_dev, V, inv_tau,
                        acc_mode, gW_acc, gb_acc, gW_out, gb_out, whole, parts, part_w, part_b);
   e = hipGetLastError();
   if (e != hipSuccess || tail_wgs == 0) return e;
