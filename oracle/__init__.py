@@ -7,7 +7,8 @@ Sources it follows (the pages):
   * Liger-Kernel PR #1320 "Add GMPO to fused linear GRPO loss", Summary and
     "The implementation" bullets: advantage-dependent one-sided clipping of the
     per-token log-ratio in log space [-eps_low, +eps_high]; exp of the masked
-    mean per completion; per-sample reduction; K3 KL; clipping metric;
+    mean per completion; per-sample reduction; K3 KL (optionally bias
+    corrected, reading R19); clipping metric;
     chunking; input/weight/bias gradients.
   * Liger-Kernel PR #1558 "support top_entropy_quantile", Details bullets:
     entropy H = log_z - sum_exp_z / sum_exp; batch-global threshold

@@ -61,6 +61,16 @@ Readings taken where the pages are silent (each also listed in the design doc):
       the clip binds per token by the sign of A_t. Defined for GSPO-token and
       the token-level clipped losses; GMPO's clip direction and geometric
       mean belong to the sequence, so it keeps per-sequence advantages.
+  R19 Bias-corrected KL (Liger PR #1320, "The implementation" and
+      "Testing" name the option; no formula is printed): the K3 term of
+      every token is multiplied by that token's importance ratio
+      rho_t = exp(lp_t - old_t), unclipped and differentiated through, so
+      that its average over tokens drawn from the sampling policy is an
+      estimate of KL(pi_theta || pi_ref) rather than of the same divergence
+      weighted by the sampler. Without old log-probs rho_t = exp(lp - lp)
+      with the second lp held constant, as for the policy terms: the value
+      is plain K3 but the gradient keeps the ratio's own derivative, so it
+      is lp_t - ref_t. The mean_kl metric reports the corrected term.
 """
 from __future__ import annotations
 
@@ -102,6 +112,7 @@ class LossConfig:
     reduction: str = "seq_mean"      # "seq_mean" (per-sample) or "token_sum"; GMPO / GSPO only
     chunk_sequences: int = 0         # 0 = whole batch
     global_tokens: int = 0           # DAPO normaliser; 0 = the batch's completion tokens
+    kl_bias_correction: bool = False  # R19: KL term = rho_t * K3
 
     @staticmethod
     def from_spec(spec) -> "LossConfig":
@@ -109,7 +120,8 @@ class LossConfig:
                           eps_high=spec.eps_high, beta=spec.beta, temperature=spec.temperature,
                           top_entropy_quantile=spec.top_entropy_quantile,
                           reduction=spec.reduction, chunk_sequences=spec.chunk_sequences,
-                          global_tokens=getattr(spec, "global_tokens", 0))
+                          global_tokens=getattr(spec, "global_tokens", 0),
+                          kl_bias_correction=getattr(spec, "kl_bias_correction", False))
 
 
 # ---------------------------------------------------------------------------
@@ -237,7 +249,8 @@ def policy_loss(cfg: LossConfig, lp, old, ref, completion_mask, ratio_mask, adva
     log-ratio ls_i = mean_{R_i} lr; s_i = exp(ls_i); every token carries the
     value s_i with the gradient of its own log-prob; policy term
     -min(s A, clip(s, 1-eps_low, 1+eps_high) A).  Loss per token
-    l_t = e_t policy_t + beta kl_t (R6, R7), reduced per R5.
+    l_t = e_t policy_t + beta kl_t (R6, R7; kl_t = rho_t K3_t under R19),
+    reduced per R5.
     """
     T = cfg.T
     lp = np.asarray(lp, np.float64)
@@ -350,8 +363,18 @@ def policy_loss(cfg: LossConfig, lp, old, ref, completion_mask, ratio_mask, adva
         policy_tok = np.broadcast_to(policy_seq[:, None], (b, T))
     if ref is not None:
         x = np.asarray(ref, np.float32).astype(np.float64).reshape(b, T) - lp
-        kl = np.exp(x) - x - 1.0
-        dkl = 1.0 - np.exp(x)
+        k3 = np.exp(x) - x - 1.0
+        dk3 = 1.0 - np.exp(x)                                 # d K3 / d lp
+        if cfg.kl_bias_correction:
+            # R19: rho_t K3_t; d rho_t / d lp_t = rho_t (product rule), on
+            # policy too (rho = exp(lp - const) = 1)
+            with np.errstate(over="ignore"):
+                rho_kl = np.ones((b, T)) if old is None else np.exp(lr)
+            kl = rho_kl * k3
+            dkl = rho_kl * k3 + rho_kl * dk3
+        else:
+            kl = k3
+            dkl = dk3
     else:
         kl = np.zeros((b, T))
         dkl = np.zeros((b, T))

@@ -71,6 +71,7 @@ class Spec:
     reduction: str = "seq_mean"             # "seq_mean" or "token_sum"
     global_tokens: int = 0                  # DAPO divisor; 0 = the batch's completion tokens
     token_adv: bool = False                 # one advantage per token (N,) instead of per sequence
+    kl_bias_correction: bool = False        # KL term weighted by the token importance ratio
     seed: int = 0
 
     @property
