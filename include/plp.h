@@ -59,7 +59,7 @@ extern "C" {
 #endif
 
 #define PLP_API __attribute__((visibility("default")))
-#define PLP_ABI_VERSION 2
+#define PLP_ABI_VERSION 3
 
 /* Return codes. */
 #define PLP_OK 0
@@ -158,6 +158,15 @@ typedef struct plp_args {
                                    own A_t, so the clip binds per token by the sign of A_t.
                                    GSPO_TOKEN, GRPO, BNPO and DAPO only (GMPO's clip direction
                                    and geometric mean are per sequence: PLP_E_UNSUPPORTED). */
+  /* ---- ABI version 3 ---- */
+  int32_t kl_bias_correction;   /* nonzero: bias-corrected KL (Liger PR #1320, "The implementation"):
+                                   each token's K3 term is multiplied by its importance ratio
+                                   rho_t = exp(logp_t - old_logp_t), which is differentiated
+                                   through, so dKL_t/dlogp_t = rho_t (logp_t - ref_logp_t).
+                                   Without old_logp rho_t = 1 in value, its derivative still
+                                   taken. The mean_kl metric reports the corrected term. Only
+                                   read when beta != 0 or ref_logp is given. Default 0. */
+  int32_t pad1;
 } plp_args;
 
 /* Outputs of the fused call. Every pointer except loss and metrics may be

@@ -80,7 +80,8 @@ def _mask_u8(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
 
 def _fill_args(hidden, weight, bias, targets, old_logp, ref_logp, completion_mask, ratio_mask, advantages, B, T,
                loss_type, importance_sampling_level, reduction, epsilon_low, epsilon_high, beta, temperature,
-               top_entropy_quantile, chunk_sequences, global_tokens=0, token_advantages=None) -> _abi.PlpArgs:
+               top_entropy_quantile, chunk_sequences, global_tokens=0, token_advantages=None,
+               kl_bias_correction=False) -> _abi.PlpArgs:
     a = _abi.new_args()
     a.B, a.T = int(B), int(T)
     if hidden is not None:
@@ -103,6 +104,7 @@ def _fill_args(hidden, weight, bias, targets, old_logp, ref_logp, completion_mas
     a.chunk_sequences = int(chunk_sequences)
     a.global_tokens = int(global_tokens)
     a.token_advantages = _ptr(token_advantages)
+    a.kl_bias_correction = 1 if kl_bias_correction else 0
     return a
 
 
@@ -133,13 +135,15 @@ def fused_lmhead_policy_loss_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor,
                                      temperature: float = 1.0, top_entropy_quantile: float = 1.0,
                                      chunk_sequences: int = 0, global_tokens: int = 0,
                                      token_advantages: Optional[torch.Tensor] = None,
+                                     kl_bias_correction: bool = False,
                                      grad_hidden: bool = True, grad_weight: bool = True,
                                      grad_bias: Optional[bool] = None, diagnostics: bool = False,
                                      workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
     """Loss, metrics and gradients of the fused LM head + GMPO / GSPO-token /
     GRPO / BNPO / DAPO objective (plp_fused_lmhead_policy_loss_fwd_bwd);
     global_tokens is DAPO's divisor (0 = the batch's completion tokens);
-    token_advantages fp32 [B*T] replaces advantages [B] (pass None for it).
+    token_advantages fp32 [B*T] replaces advantages [B] (pass None for it);
+    kl_bias_correction weights each token's K3 term by its importance ratio.
     hidden: [B, T, H] or
     [B*T, H] (then pass B and T); weight [V, H]; targets int64 [B*T];
     masks bool/u8 [B*T]; advantages fp32 [B]. Returns a dict of tensors."""
@@ -163,7 +167,7 @@ def fused_lmhead_policy_loss_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor,
         grad_bias = bias is not None
     a = _fill_args(hidden, weight, bias, targets, old_logp, ref_logp, completion_mask, ratio_mask, advantages, B, T,
                    loss_type, importance_sampling_level, reduction, epsilon_low, epsilon_high, beta, temperature,
-                   top_entropy_quantile, chunk_sequences, global_tokens, token_advantages)
+                   top_entropy_quantile, chunk_sequences, global_tokens, token_advantages, kl_bias_correction)
     L = _abi.lib()
     n = ctypes.c_size_t()
     _abi.check(L.plp_workspace_size(ctypes.byref(a), ctypes.byref(n)))
@@ -246,6 +250,7 @@ def policy_loss_from_logprobs(logp: torch.Tensor, completion_mask: torch.Tensor,
                               reduction: str = "seq_mean", epsilon_low: float = 0.2, epsilon_high: float = 0.2,
                               beta: float = 0.0, top_entropy_quantile: float = 1.0, global_tokens: int = 0,
                               token_advantages: Optional[torch.Tensor] = None,
+                              kl_bias_correction: bool = False,
                               workspace: Optional[torch.Tensor] = None) -> dict:
     """The loss stage alone from per-token log-probs
     (plp_policy_loss_from_logprobs). Returns loss, metrics, dlogp and
@@ -259,7 +264,7 @@ def policy_loss_from_logprobs(logp: torch.Tensor, completion_mask: torch.Tensor,
     _check_vec(token_advantages, N, torch.float32, "token_advantages")
     a = _fill_args(None, None, None, None, old_logp, ref_logp, completion_mask, ratio_mask, advantages, B, T,
                    loss_type, importance_sampling_level, reduction, epsilon_low, epsilon_high, beta, 1.0,
-                   top_entropy_quantile, 0, global_tokens, token_advantages)
+                   top_entropy_quantile, 0, global_tokens, token_advantages, kl_bias_correction)
     L = _abi.lib()
     n = ctypes.c_size_t()
     _abi.check(L.plp_policy_loss_workspace_size(ctypes.byref(a), ctypes.byref(n)))

@@ -17,7 +17,7 @@ PLP_E_HIP = -4
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 LOSS_GMPO, LOSS_GSPO_TOKEN, LOSS_GRPO, LOSS_BNPO, LOSS_DAPO = 0, 1, 2, 3, 4
-ABI_VERSION = 2
+ABI_VERSION = 3
 IS_TOKEN, IS_SEQUENCE = 0, 1
 REDUCE_SEQ_MEAN, REDUCE_TOKEN_SUM = 0, 1
 
@@ -65,6 +65,8 @@ class PlpArgs(ctypes.Structure):
         ("chunk_sequences", ctypes.c_int64),
         ("global_tokens", ctypes.c_int64),
         ("token_advantages", _vp),
+        ("kl_bias_correction", ctypes.c_int32),
+        ("pad1", ctypes.c_int32),
     ]
 
 

@@ -74,7 +74,7 @@ struct LossParams {
   int64_t norm_tokens; // BNPO / DAPO divisor when > 0 (DAPO's global count)
   const unsigned long long* ntok_dev;  // else: the batch's completion-token count (device)
   int token_adv;       // advantages are per token (the kernels' tadv argument)
-  int pad;
+  int kl_bc;           // KL term weighted by the token importance ratio
 };
 
 // Token-level clipped losses (GRPO, BNPO, DAPO) share the per-token path.

@@ -214,7 +214,8 @@ struct TokEval {
 // Per-token quantities. GMPO (Liger PR #1320): clip in log space, advantage
 // dependent and one sided. GRPO / BNPO / DAPO: the Tinker GSPO page's clipped
 // objective with the token's own ratio, decided on exp(lr32) in fp64 against
-// the fp32 ratio bounds. K3 KL. lr32 = fp32(lp - old) is the predicate
+// the fp32 ratio bounds. K3 KL, optionally bias corrected (Liger PR #1320,
+// "The implementation"): weighted by the token's importance ratio. lr32 = fp32(lp - old) is the predicate
 // operand; ties are not clipped; A = 0 gives no term.
 __device__ __forceinline__ TokEval eval_tok(const LossParams& p, int64_t t, const float* lp, const float* old,
                                             const float* ref, const uint8_t* comp, const uint8_t* ratio,
@@ -245,8 +246,16 @@ __device__ __forceinline__ TokEval eval_tok(const LossParams& p, int64_t t, cons
   if (ref) {
     const double x = (double)ref[t] - (double)lp32;
     const double ex = exp(x);
-    e.kl = ex - x - 1.0;
-    e.dkl = 1.0 - ex;
+    const double k3 = ex - x - 1.0;
+    if (p.kl_bc) {
+      // rho K3 with rho = exp(lp - old): d/dlp = rho K3 + rho (1 - e^x) = -rho x
+      const double rho = old ? exp((double)lp32 - (double)old32) : 1.0;
+      e.kl = rho * k3;
+      e.dkl = -rho * x;
+    } else {
+      e.kl = k3;
+      e.dkl = 1.0 - ex;
+    }
   } else {
     e.kl = 0.0;
     e.dkl = 0.0;

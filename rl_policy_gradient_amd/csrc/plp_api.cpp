@@ -50,6 +50,10 @@ const float* token_advantages(const plp_args* a) {
   return a->struct_size >= offsetof(plp_args, token_advantages) + sizeof(void*) ? a->token_advantages : nullptr;
 }
 
+int kl_bias_correction(const plp_args* a) {
+  return a->struct_size >= offsetof(plp_args, kl_bias_correction) + sizeof(int32_t) && a->kl_bias_correction ? 1 : 0;
+}
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -281,7 +285,7 @@ LossParams loss_params(const plp_args* a, const unsigned long long* ntok_dev) {
   p.norm_tokens = a->loss_type == PLP_LOSS_DAPO ? global_tokens(a) : 0;
   p.ntok_dev = ntok_dev;
   p.token_adv = token_advantages(a) != nullptr ? 1 : 0;
-  p.pad = 0;
+  p.kl_bc = kl_bias_correction(a);
   return p;
 }
 

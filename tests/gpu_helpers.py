@@ -56,7 +56,8 @@ def run_gpu(spec: synth.Spec, d: dict, **kw) -> dict:
                 epsilon_high=spec.eps_high, beta=spec.beta, temperature=spec.temperature,
                 top_entropy_quantile=spec.top_entropy_quantile, chunk_sequences=spec.chunk_sequences,
                 reduction=spec.reduction, global_tokens=spec.global_tokens,
-                token_advantages=g["token_advantages"], diagnostics=True)
+                token_advantages=g["token_advantages"], kl_bias_correction=spec.kl_bias_correction,
+                diagnostics=True)
     args.update(kw)
     out = plp.fused_lmhead_policy_loss_fwd_bwd(g["hidden"], g["weight"], g["targets"], g["completion_mask"],
                                                g["advantages"], bias=g["bias"], old_logp=g["old_logp"],

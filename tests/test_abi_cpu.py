@@ -165,4 +165,4 @@ def test_other_entry_points_validate():
     assert "q must lie" in L.plp_last_error().decode()
     a = _valid_args()
     assert L.plp_policy_loss_from_logprobs(ctypes.byref(a), None, None, None, None, 0, None) == abi.PLP_E_INVALID
-    assert L.plp_abi_version() == 2
+    assert L.plp_abi_version() == 3

@@ -91,6 +91,24 @@ def _loss_case(seed, B, T, loss_type, beta, q, ratio_mask, reduction, eps=(0.2, 
     ("dapo_global", 0.0, 1.0, True, "seq_mean", 300),
 ])
 def test_policy_loss_from_logprobs(loss_type, beta, q, ratio_mask, reduction, T):
+    _loss_stage_case(loss_type, beta, q, ratio_mask, reduction, T)
+
+
+@pytest.mark.parametrize("loss_type,q,on_policy,T", [
+    ("gmpo", 1.0, False, 3000),
+    ("gmpo", 0.4, True, 77),
+    ("gspo_token", 0.5, False, 4500),
+    ("grpo", 1.0, False, 41),
+    ("grpo", 0.4, True, 5000),
+    ("dapo", 0.5, False, 300),
+])
+def test_policy_loss_kl_bias_correction(loss_type, q, on_policy, T):
+    """Bias-corrected KL (the K3 term weighted by the token importance
+    ratio, differentiated through) against the oracle, off and on policy."""
+    _loss_stage_case(loss_type, 0.1, q, False, "seq_mean", T, kl_bc=True, on_policy=on_policy)
+
+
+def _loss_stage_case(loss_type, beta, q, ratio_mask, reduction, T, kl_bc=False, on_policy=False):
     import rl_policy_gradient_amd as plp
     B = 7
     G = 0
@@ -99,8 +117,11 @@ def test_policy_loss_from_logprobs(loss_type, beta, q, ratio_mask, reduction, T)
     eps = (0.2, 0.3) if loss_type in ("gmpo", "grpo", "bnpo", "dapo") else (3e-2, 4e-2)
     noise = 0.3 if loss_type in ("gmpo", "grpo", "bnpo", "dapo") else 0.1
     cfg, lp, old, ref, comp, rm, A, ent = _loss_case(T, B, T, loss_type, beta, q, ratio_mask, reduction, eps, noise)
-    cfg = cfg.__class__(**{**cfg.__dict__, "global_tokens": G})
-    _say(f"loss stage {loss_type} beta={beta} q={q} ratio_mask={ratio_mask} {reduction} T={T} G={G}")
+    cfg = cfg.__class__(**{**cfg.__dict__, "global_tokens": G, "kl_bias_correction": kl_bc})
+    if on_policy:
+        old = None
+    _say(f"loss stage {loss_type} beta={beta} q={q} ratio_mask={ratio_mask} {reduction} T={T} G={G} "
+         f"kl_bc={kl_bc} on_policy={on_policy}")
     emask, thr = (oracle.entropy_quantile_mask(ent, comp != 0, q) if q < 1 else (None, np.float32(np.nan)))
     p = oracle.policy_loss(cfg, lp.astype(np.float64), old, ref, comp, rm, A, emask)
     loss, metrics = oracle.finalize_metrics([p], thr)
@@ -108,7 +129,7 @@ def test_policy_loss_from_logprobs(loss_type, beta, q, ratio_mask, reduction, T)
                                         old_logp=dev_tensor(old), ref_logp=dev_tensor(ref),
                                         ratio_mask=dev_tensor(rm), entropy=dev_tensor(ent), loss_type=loss_type,
                                         reduction=reduction, epsilon_low=eps[0], epsilon_high=eps[1], beta=beta,
-                                        top_entropy_quantile=q, global_tokens=G)
+                                        top_entropy_quantile=q, global_tokens=G, kl_bias_correction=kl_bc)
     torch.cuda.synchronize()
     gl = out["loss"].cpu().numpy()[0]
     assert abs(gl - loss) <= 1e-5 * max(1.0, abs(loss)), (gl, loss)

@@ -95,6 +95,18 @@ SMALL = {
     "generic_f32_dapo": synth.small("generic_dapo", cfg_id=114, dtype="f32", B=3, T=30, H=48, V=300,
                                     loss_type=synth.DAPO, eps_low=0.1, eps_high=0.12, chunk_sequences=2,
                                     top_entropy_quantile=0.3, beta=0.04, ref_noise_std=0.05),
+    # bias-corrected KL: K3 weighted by the token importance ratio
+    "mfma_gmpo_kl_bias_corrected": synth.small("mfma_gmpo_klbc", cfg_id=117, B=3, T=70, H=256, V=1000, bias=True,
+                                               beta=0.1, ref_noise_std=0.2, old_noise_std=0.3, eps_low=0.2,
+                                               eps_high=0.3, kl_bias_correction=True),
+    "mfma_grpo_kl_bias_corrected_q": synth.small("mfma_grpo_klbc", cfg_id=118, B=4, T=48, H=384, V=900,
+                                                 loss_type=synth.GRPO, eps_low=0.2, eps_high=0.28, beta=0.1,
+                                                 ref_noise_std=0.2, old_noise_std=0.3, top_entropy_quantile=0.5,
+                                                 chunk_sequences=3, kl_bias_correction=True),
+    "generic_f32_gspo_kl_bias_corrected": synth.small("generic_gspo_klbc", cfg_id=119, dtype="f32", B=3, T=30,
+                                                      H=48, V=300, loss_type=synth.GSPO_TOKEN, eps_low=0.01,
+                                                      eps_high=0.01, old_noise_std=0.01, beta=0.1,
+                                                      ref_noise_std=0.2, kl_bias_correction=True),
     # per-token advantages (N,), zero off the completion
     "mfma_gspo_token_adv_sum": synth.small("mfma_gspo_tadv", cfg_id=115, B=3, T=64, H=256, V=1200,
                                            loss_type=synth.GSPO_TOKEN, eps_low=2e-3, eps_high=2e-3,
