@@ -145,6 +145,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--loss", choices=["gmpo", "gspo_token", "grpo", "bnpo", "dapo"], default=None)
     ap.add_argument("--token-advantages", action="store_true")
+    ap.add_argument("--kl-bias-correction", action="store_true",
+                    help="K3 KL weighted by the token importance ratio (workloads with a KL term)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -175,9 +177,16 @@ def main() -> int:
         g.manual_seed(4242 + args.config)
         tadv = (torch.randn(N, generator=g, device=dev) * (inp["completion_mask"] != 0)).float().contiguous()
         variant += "+token_adv"
+    if args.kl_bias_correction:
+        if spec.beta == 0.0 or inp["ref_logp"] is None:
+            print("--kl-bias-correction needs a workload with a KL term (--config 3)", file=sys.stderr)
+            return 2
+        spec = spec.replace(kl_bias_correction=True)
+        variant += "+kl_bias_corrected"
     kw = dict(B=spec.B, T=spec.T, loss_type=spec.loss_type, epsilon_low=spec.eps_low, epsilon_high=spec.eps_high,
               beta=spec.beta, temperature=spec.temperature, top_entropy_quantile=spec.top_entropy_quantile,
-              chunk_sequences=spec.chunk_sequences, diagnostics=False)
+              chunk_sequences=spec.chunk_sequences, kl_bias_correction=spec.kl_bias_correction,
+              diagnostics=False)
     ws = torch.empty(plp.workspace_size(spec.B, spec.T, H, V, bias=spec.bias,
                                         top_entropy_quantile=spec.top_entropy_quantile,
                                         chunk_sequences=spec.chunk_sequences, loss_type=spec.loss_type),
@@ -231,7 +240,8 @@ def main() -> int:
                 "other_sweep_ms_per_step": round((ms[1] if dom == "fwd_sweep" else ms[0]) / args.steps, 4)}
     line = {
         "metric": METRIC if not variant else METRIC.replace(
-            "GMPO", spec.loss_type.upper() + (" (per-token advantages)" if tadv is not None else "")),
+            "GMPO", spec.loss_type.upper() + (" (per-token advantages)" if tadv is not None else "")
+            + (" (bias-corrected KL)" if spec.kl_bias_correction else "")),
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -248,7 +258,7 @@ def main() -> int:
         "config": {"workload": workload, "B": spec.B, "T": spec.T, "H": H, "V": V,
                    "loss_type": spec.loss_type, "bias": spec.bias, "beta": spec.beta,
                    "top_entropy_quantile": spec.top_entropy_quantile, "chunk_sequences": spec.chunk_sequences,
-                   "token_advantages": tadv is not None,
+                   "token_advantages": tadv is not None, "kl_bias_correction": spec.kl_bias_correction,
                    "global_batch_tokens": N, "active_tokens_with_grad": n_active,
                    "event_ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4)},
         "roofline": roofline,

@@ -123,8 +123,13 @@ void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bia
     auto load_tok = [&](int t) {
       if (w == 0 && lane < BK) tk = __builtin_amdgcn_raw_buffer_load_b128(tok_r, (t * BK + lane) * 16, 0, 0);
     };
+    // Tokens past the count get a neutral record (lse = +inf, gs = 0, y = -1)
+    // whose dz is exactly +0 with no per-element test in the epilogue.
     auto stage_tok = [&](int t) {
-      if (w == 0 && lane < BK) *reinterpret_cast<u32x4*>(&s_tok[t & 1][lane]) = tk;
+      if (w == 0 && lane < BK) {
+        const u32x4 pad = {0x7f800000u, 0u, 0xffffffffu, 0u};
+        *reinterpret_cast<u32x4*>(&s_tok[t & 1][lane]) = t * BK + lane < n_tok ? tk : pad;
+      }
     };
     if (any) load_tok(t_lo);
     // Resident W fragments (B operand of S^T), rows q0 + 32nb + c, cols
@@ -173,20 +178,27 @@ void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bia
                 (s_part[2][nbq][2 * kh + e][lane] + s_part[3][nbq][2 * kh + e][lane]);
     };
     // Epilogue of tile t: dz = g / tau ([v = y] - p) as bf16 P of this
-    // wave's quarter, and this lane's share of grad_b.
-    auto epilogue = [&](int t, const f32x4 (&sf)[2]) {
-      const int t0 = t * BK;
+    // wave's quarter, and this lane's share of grad_b. Every token record is
+    // read (padding included), so the reads are not guarded by branches;
+    // rows past V give values that only reach their own grad_W / grad_b
+    // rows, which are never stored.
+    // The eight records (lse, gs, y, pad) of the lane's tokens are read as
+    // plain vectors before the partial-logit reduce, so that all sixteen LDS
+    // reads of the phase are in flight together.
+    auto load_recs = [&](int t, f32x4 (&rec)[8]) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rec[j] = *reinterpret_cast<const f32x4*>(&s_tok[t & 1][kvq(kh, hh, j)]);
+    };
+    auto epilogue = [&](int t, const f32x4 (&sf)[2], const f32x4 (&rec)[8]) {
       bf16x8 pa;
       float gsum = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int kv = kvq(kh, hh, j);
-        const TokData td = s_tok[t & 1][kv];
-        const float sv_ = sf[j >> 2][j & 3];
-        const float z = (sv_ + bvl) * inv_tau;
-        const float pr = __expf(z - td.lse);
-        float dz = td.gs * ((td.y == my_v ? 1.f : 0.f) - pr);
-        dz = (t0 + kv < n_tok && my_v < V) ? dz : 0.f;
+        const float lse = rec[j][0], gs = rec[j][1];
+        const int y = __float_as_int(rec[j][2]);
+        const float z = (sf[j >> 2][j & 3] + bvl) * inv_tau;
+        const float pr = __expf(z - lse);
+        const float dz = gs * ((y == my_v ? 1.f : 0.f) - pr);
         gsum += dz;
         pa[j] = (__bf16)dz;
       }
@@ -204,8 +216,10 @@ void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bia
     }
     __syncthreads();  // P0
     if (any) {
+      f32x4 rec[8];
+      load_recs(t_lo, rec);
       reduce_part(sf);
-      epilogue(t_lo, sf);
+      epilogue(t_lo, sf, rec);
     }
     for (int t = t_lo; t < t_hi; ++t) {
       __syncthreads();  // A
@@ -218,8 +232,10 @@ void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bia
       }
       __syncthreads();  // B
       if (more) {
+        f32x4 rec[8];
+        load_recs(t + 1, rec);
         reduce_part(sf);
-        epilogue(t + 1, sf);
+        epilogue(t + 1, sf, rec);
       }
     }
 
