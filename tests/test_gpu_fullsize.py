@@ -84,6 +84,7 @@ FULL2_VARIANTS = {
     "dapo_global": dict(loss_type=synth.DAPO, eps_low=0.2, eps_high=0.28, global_tokens=4096),
     "gspo_token_adv": dict(loss_type=synth.GSPO_TOKEN, eps_low=3e-4, eps_high=4e-4, old_noise_std=1e-4,
                            token_adv=True),
+    "gmpo_kl_bias_corrected": dict(beta=0.04, ref_noise_std=0.05, kl_bias_correction=True),
 }
 
 
