@@ -187,6 +187,9 @@ def main() -> int:
               beta=spec.beta, temperature=spec.temperature, top_entropy_quantile=spec.top_entropy_quantile,
               chunk_sequences=spec.chunk_sequences, kl_bias_correction=spec.kl_bias_correction,
               diagnostics=False)
+    torch.cuda.synchronize()
+    mem_inputs = torch.cuda.memory_allocated(dev)  # inputs resident before the call's own memory
+    torch.cuda.reset_peak_memory_stats(dev)
     ws = torch.empty(plp.workspace_size(spec.B, spec.T, H, V, bias=spec.bias,
                                         top_entropy_quantile=spec.top_entropy_quantile,
                                         chunk_sequences=spec.chunk_sequences, loss_type=spec.loss_type),
@@ -221,6 +224,7 @@ def main() -> int:
     tokens_s = N * args.steps / elapsed
     flops_tok = 6.0 * H * V
     tflops = tokens_s * flops_tok / 1e12
+    peak_delta = torch.cuda.max_memory_allocated(dev) - mem_inputs
 
     # roofline of the dominant sweep
     n_active = int((out["dlogp"] != 0).sum().item())
@@ -255,6 +259,11 @@ def main() -> int:
         "data": "synthetic",
         "tflops_6nhv": round(tflops, 2),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        # what the path executes: the forward sweep's 4NHV plus the weight-gradient
+        # sweep's 4HV per token with a gradient (its logits are recomputed)
+        "executed_tflops": round(4.0 * H * V * (N + n_active) / (elapsed / args.steps) / 1e12, 2),
+        "memory": {"inputs_bytes": int(mem_inputs), "workspace_bytes": int(ws.numel()),
+                   "peak_bytes_beyond_inputs": int(peak_delta)},
         "config": {"workload": workload, "B": spec.B, "T": spec.T, "H": H, "V": V,
                    "loss_type": spec.loss_type, "bias": spec.bias, "beta": spec.beta,
                    "top_entropy_quantile": spec.top_entropy_quantile, "chunk_sequences": spec.chunk_sequences,

@@ -14,6 +14,10 @@
         HBM bytes per launch of one kernel: FETCH_SIZE and WRITE_SIZE (KiB per
         dispatch) averaged over its dispatches, each scaled by the factor the
         same counter shows on the plain copy.
+    python -m rl_policy_gradient_amd.profsum pmc PMC_CSV --match A,B --command "..."
+        per-dispatch averages of every counter in a ``--pmc`` CSV for the
+        kernels whose names contain A, B, ..., with the matrix-core and LDS
+        utilisation derived from them (formulas in the output).
 """
 from __future__ import annotations
 
@@ -116,6 +120,40 @@ def cmd_copy(args) -> int:
     return 0
 
 
+def cmd_pmc(args) -> int:
+    per = {}  # match -> dispatch id -> counter -> value (summed over the CSV's rows)
+    for r in _rows(args.csv):
+        for m in args.match.split(","):
+            if m in r["Kernel_Name"]:
+                d = per.setdefault(m, {}).setdefault(r["Dispatch_Id"], {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = ["# rocprofv3 counter summary (per-dispatch averages)", f"# command: {args.command}",
+             f"# wall cycles = GRBM_GUI_ACTIVE / {args.xcds} (the counter is summed over the XCDs);",
+             f"# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (wall x {args.cus} CUs x {args.simds} SIMDs);",
+             f"# LDS busy = SQ_LDS_IDX_ACTIVE / (wall x {args.cus} CUs); "
+             "bank-conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE", ""]
+    for m, disp in per.items():
+        names = sorted({k for d in disp.values() for k in d})
+        avg = {k: statistics.mean(d.get(k, 0.0) for d in disp.values()) for k in names}
+        lines.append(f"{m}: {len(disp)} dispatches")
+        for k in names:
+            lines.append(f"   {k:<28} {avg[k]:>14.4g}")
+        wall = avg.get("GRBM_GUI_ACTIVE", 0.0) / args.xcds
+        if wall > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            lines.append(f"   MFMA busy                    {100.0 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (wall * args.cus * args.simds):>13.1f} %")
+        if wall > 0 and "SQ_LDS_IDX_ACTIVE" in avg:
+            lines.append(f"   LDS busy                     {100.0 * avg['SQ_LDS_IDX_ACTIVE'] / (wall * args.cus):>13.1f} %")
+            if "SQ_LDS_BANK_CONFLICT" in avg and avg["SQ_LDS_IDX_ACTIVE"] > 0:
+                lines.append(f"   LDS bank-conflict share      "
+                             f"{100.0 * avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:>13.1f} %")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as fh:
+            fh.write(text)
+    sys.stdout.write(text)
+    return 0
+
+
 def cmd_stats(args) -> int:
     d = kernel_durations(args.trace)
     total = sum(sum(v) for v in d.values())
@@ -187,8 +225,16 @@ def main(argv=None) -> int:
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--copy-match", default="neg")
     t.add_argument("--command", default="")
+    q = sub.add_parser("pmc")
+    q.add_argument("csv")
+    q.add_argument("--match", required=True)
+    q.add_argument("--cus", type=int, default=256)
+    q.add_argument("--xcds", type=int, default=8)
+    q.add_argument("--simds", type=int, default=4)
+    q.add_argument("--out")
+    q.add_argument("--command", default="")
     args = ap.parse_args(argv)
-    return {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[args.cmd](args)
+    return {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic, "pmc": cmd_pmc}[args.cmd](args)
 
 
 if __name__ == "__main__":
