@@ -239,3 +239,50 @@ def test_selective_entropy(case):
     np.testing.assert_array_equal(ent.cpu().numpy(), ent2.cpu().numpy())
 
 
+
+
+# ---------------------------------------------------------------------------
+# Degenerate batches: no token carries a gradient, or a single token
+# ---------------------------------------------------------------------------
+
+DEGENERATE = {
+    # every advantage zero: the policy term and g vanish (no KL), so the
+    # weight-gradient sweep sees no token and every gradient is exactly zero
+    "all_zero_advantages": (synth.small("deg_zero_adv", cfg_id=121, B=3, T=40, H=256, V=1000, bias=True),
+                            lambda d: d["advantages"].fill(0.0)),
+    # no completion token at all
+    "empty_completion": (synth.small("deg_empty", cfg_id=122, B=2, T=48, H=128, V=700, bias=True,
+                                     loss_type=synth.GRPO, eps_low=0.2, eps_high=0.2),
+                         lambda d: d["completion_mask"].fill(0)),
+}
+
+
+@pytest.mark.parametrize("name", list(DEGENERATE))
+def test_fused_no_gradient_tokens(name):
+    spec, mutate = DEGENERATE[name]
+    _say(f"degenerate {name} B={spec.B} T={spec.T} H={spec.H} V={spec.V}")
+    d = make_case(spec)
+    mutate(d)
+    ref = run_oracle(spec, d)
+    gpu = run_gpu(spec, d)
+    assert ref["loss"] == 0.0 and gpu["loss"][0] == 0.0
+    assert not np.any(ref["g"]) and not np.any(gpu["dlogp"])
+    for k in ("grad_hidden", "grad_weight", "grad_bias"):
+        assert not np.any(gpu[k]), k                      # exactly zero, not merely small
+    m, mo = gpu["metrics"], ref["metrics"]
+    assert m[6] == mo[6] and m[7] == mo[7], (m, mo)
+    np.testing.assert_allclose(gpu["logp"], ref["logp"], rtol=0, atol=2e-5)
+
+
+def test_fused_single_token():
+    """B = T = 1: one completion token against the oracle (the smallest
+    problem: one partial row block, one token tile)."""
+    spec = synth.small("deg_one", cfg_id=123, B=1, T=1, H=256, V=1000, bias=True, prompt_lo=0, prompt_hi=0,
+                       eps_low=0.2, eps_high=0.3)
+    _say("degenerate single token")
+    d = make_case(spec)
+    d["completion_mask"][:] = 1
+    d["advantages"][:] = 0.75
+    ref = run_oracle(spec, d)
+    gpu = run_gpu(spec, d)
+    _check_fused(spec, d, gpu, ref)
