@@ -11,26 +11,20 @@ namespace plp {
 
 namespace {
 
-// Forward sweep: per token row, running (sum 2^{z2-m2}, sum 2^{z2-m2} z2)
-// against the reference m2 (z2 = z log2 e), and (WITH_O) the accumulator
-// O = sum_v e^{z-m} W_v. Grid: (row blocks) x Sv vocabulary splits, block
-// id = rb * Sv + split.
-template <int KB, bool WITH_O, bool HAS_BIAS>
+// Forward sweep, statistics only: per token row, running
+// (sum 2^{z2-m2}, sum 2^{z2-m2} z2) against the reference m2 (z2 = z log2 e).
+// Grid: (row blocks) x Sv vocabulary splits, block id = rb * Sv + split.
+template <int KB, bool HAS_BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf,
                      const __bf16* __restrict__ bias, int64_t N, int V, float inv_tau, int Sv,
-                     int tiles_per_split, RowStats* __restrict__ stats, float* __restrict__ O) {
+                     int tiles_per_split, RowStats* __restrict__ stats) {
   constexpr int H = 128 * KB;
   constexpr int DS = Stage<KB>::DS;  // columns per wave
-  constexpr int TS = Stage<KB>::TS;
   constexpr int KS = DS / 16;        // 16-wide contraction steps per wave
-  constexpr int DB = DS / 32;        // 32-wide column blocks per wave
   __shared__ f32x4 s_part[NW][2][4][64];
-  __shared__ bf16x8 s_p[4][64];
-  __shared__ unsigned short s_t[WITH_O ? NW : 1][2][WITH_O ? BK * TS : 8];
-  // cross-wave exchanges of per-row values reuse the P buffer (before the
-  // sweep) and the partials buffer (after it)
-  float* s_x = reinterpret_cast<float*>(&s_p[0][0]);              // [NW][64]
+  __shared__ float s_x[NW * 64];
+  // the partials buffer is reused for the final cross-wave sums
   double* s_xd = reinterpret_cast<double*>(&s_part[0][0][0][0]);   // [NW][2][64]
 
   const int lane = threadIdx.x & 63;
@@ -40,26 +34,6 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   const int rb = blockIdx.x / Sv, sv = blockIdx.x - rb * Sv;
   const int64_t q0 = (int64_t)rb * BQ;
   const int d0 = w * DS;
-  // Stage write offsets (element) of lane (hh, c) for even / odd k-step:
-  // row c, chunk 2ks + hh at position (2ks + hh) ^ s(c), s(c) = (c >> 1) & 3.
-  int sw_base[2];
-  {
-    const int x = hh ^ ((c >> 1) & 3);
-    sw_base[0] = c * TS + 8 * x;
-    sw_base[1] = c * TS + 8 * (x ^ 2) - 16;
-  }
-  // Transposing-load offsets: provider lane p of 16-lane group G reads row
-  // 4(G/2) + p/4 (and 8 further down) of contraction step ks, chunk
-  // 4db + 2(G%2) + (p%4)/2 of column block db, half p%2.
-  int tr_base[2];
-  {
-    const int p = lane & 15, G = lane >> 4;
-    const int r = 4 * (G >> 1) + (p >> 2);
-    const int b = 2 * (G & 1) + ((p >> 1) & 1);
-    const int s = (r >> 1) & 3;  // the same for rows r + 8 and r + 16
-    tr_base[0] = r * TS + 8 * (b ^ s) + 4 * (p & 1);
-    tr_base[1] = (r + 8) * TS + 8 * (b ^ s) + 4 * (p & 1);
-  }
   const int n_tiles = (V + BK - 1) / BK;
   const int t_begin = sv * tiles_per_split;
   const int t_end = min(n_tiles, t_begin + tiles_per_split);
@@ -83,12 +57,6 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
       a[ks] = ld_buf(ra, lane * 16, ks * 1024);
     }
   }
-
-  f32x16 o[2][WITH_O ? DB : 1];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < (WITH_O ? DB : 1); ++db) o[qb][db] = zero16();
 
   const int64_t my_row = q0 + 32 * nbq + c;  // row whose epilogue this lane runs (with 3 other lanes)
   // The epilogue works in base 2: z2 = z log2(e), p = 2^(z2 - m2).
@@ -128,17 +96,15 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
     return __uint_as_float((j & 1) ? (wd & 0xffff0000u) : (wd << 16));
   };
   // S^T of the tile held in `a` (tile rows past V are zero in the
-  // fragment-major copy and masked in the epilogue); each k-slice of `a`, once its MFMAs are
-  // issued, is staged for the transposing load (WITH_O) and reloaded with
-  // the same slice of tile `t_next`.
-  auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int buf, int t_next) {
+  // fragment-major copy and masked in the epilogue); each k-slice of `a`,
+  // once its MFMAs are issued, is reloaded with the same slice of tile
+  // `t_next`.
+  auto s_step = [&](bf16x8 (&a)[KS], f32x16 (&acc)[2], int t_next) {
     const auto r = frag_rsrc(frag_ptr<KB>(Wf, t_next, w, 0, 0), KS * 1024);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a[ks], q[nb][ks], ks == 0 ? zero16() : acc[nb]);
-      if constexpr (WITH_O)
-        *reinterpret_cast<bf16x8*>(&s_t[w][buf][sw_base[ks & 1] + 16 * ks]) = a[ks];
       a[ks] = ld_buf(r, lane * 16, ks * 1024);
     }
   };
@@ -157,52 +123,6 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
       sf[e] = (s_part[0][nbq][2 * kh + e][lane] + s_part[1][nbq][2 * kh + e][lane]) +
               (s_part[2][nbq][2 * kh + e][lane] + s_part[3][nbq][2 * kh + e][lane]);
   };
-  // P KV of the staged tile in `buf` (A = P of row block qb, k-step ks from
-  // the wave that reduced quarter (qb, ks); B = staged rows kvq(ks, hh, *),
-  // columns 32db + c), with the reduce of the next tile's partials issued
-  // near the end.
-  auto pv_reduce = [&](int buf, f32x4 (&sf)[2]) {
-    f32x4 r[NW];
-    if constexpr (WITH_O) {
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) pf[qb][ks] = s_p[qb + 2 * ks][lane];
-      const unsigned short* tb = &s_t[w][buf][0];
-      constexpr int NF = 2 * DB;  // fragments (db, ks) in order
-      auto frag = [&](int f) {
-        const int db = f >> 1, ks = f & 1;
-        return ld_tr(tb + tr_base[0] + 16 * ks * TS + 32 * db, tb + tr_base[1] + 16 * ks * TS + 32 * db);
-      };
-      bf16x8 b0 = frag(0), b1 = frag(1);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const bf16x8 b2 = frag(f + 2 < NF ? f + 2 : NF - 1);
-        if (f == (NF > 6 ? NF - 6 : 0)) {
-#pragma unroll
-          for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh][lane];
-        }
-        if (f == (NF > 3 ? NF - 3 : 0)) {
-          sf[0] = (r[0] + r[1]) + (r[2] + r[3]);
-#pragma unroll
-          for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh + 1][lane];
-        }
-        const int db = f >> 1, ks = f & 1;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) o[qb][db] = mfma32(pf[qb][ks], b0, o[qb][db]);
-        b0 = b1;
-        b1 = b2;
-      }
-    } else {
-#pragma unroll
-      for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh][lane];
-      sf[0] = (r[0] + r[1]) + (r[2] + r[3]);
-#pragma unroll
-      for (int src = 0; src < NW; ++src) r[src] = s_part[src][nbq][2 * kh + 1][lane];
-    }
-    sf[1] = (r[0] + r[1]) + (r[2] + r[3]);
-  };
   // Logits (base 2) of the eight tile rows this lane holds; rows past the
   // vocabulary get -1e30 (2^(-1e30 - m2) = 0 and 0 * z = 0).
   auto logits = [&](int v0, const f32x4 (&sf)[2], const uint2 (&bv)[2], float (&z)[8]) {
@@ -220,7 +140,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   uint2 bv[2];
   if (any) {
     load_bias(t_begin, bv);
-    s_step(a, acc, t_begin & 1, min(t_begin + 1, t_end - 1));
+    s_step(a, acc, min(t_begin + 1, t_end - 1));
     write_part(acc);
   }
   __syncthreads();
@@ -249,26 +169,23 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
     float z[8];
     logits(v0, sf, bv, z);
     float sp = 0.f, szp = 0.f;
-    bf16x8 pa;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       flag |= z[j] > m2 + kRefSlack2;
       const float pj = __builtin_amdgcn_exp2f(fminf(z[j] - m2, kRefSlack2));
       sp += pj;
       szp = fmaf(pj, z[j], szp);
-      pa[j] = (__bf16)pj;
     }
     s_acc += (double)sp;
     sz_acc += (double)szp;
-    // ---- logits of tile t+1 on the matrix cores, stage t+1, load t+2 -------
-    s_step(a, acc, (t + 1) & 1, tnn);
+    // ---- logits of tile t+1 on the matrix cores, load t+2 ------------------
+    s_step(a, acc, tnn);
     __builtin_amdgcn_sched_barrier(0);
     exec_barrier();
-    if constexpr (WITH_O) s_p[w][lane] = pa;
     write_part(acc);
     __syncthreads();
-    // ---- accumulator product of tile t, reduce of tile t+1 -----------------
-    pv_reduce(t & 1, sf);
+    // ---- reduce of tile t+1 ------------------------------------------------
+    reduce_part(sf);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) bv[hf] = bvn[hf];
   }
@@ -295,20 +212,6 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
     rs.pad = 0;
     stats[(int64_t)sv * N + my_row] = rs;
   }
-  if constexpr (WITH_O) {
-    float* Ob = O + (int64_t)sv * N * H;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t row = q0 + 32 * qb + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (row < N) {
-          float* dst = Ob + row * H + d0 + c;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) dst[32 * db] = o[qb][db][i];
-        }
-      }
-  }
 }
 
 // Forward sweep with the grad_h accumulator, as two roles on every SIMD
@@ -327,9 +230,9 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
 //            S: reduce of t+1, epilogue -> P(t+1)
 //            PV: P KV(t), second contraction step
 //
-// P is double buffered (P(t+1) is written while P KV(t) still reads P(t));
-// the staged tiles are double buffered as in the other form. Results are
-// bit-identical to the single-role form: every sum runs in the same order.
+// P is double buffered (P(t+1) is written while P KV(t) still reads P(t)),
+// and so are the staged tiles. The statistics are bit-identical to the
+// statistics-only kernel's: every sum runs in the same order.
 template <int KB, bool HAS_BIAS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, const __bf16* __restrict__ bias,
@@ -613,9 +516,9 @@ hipError_t fwd_pp_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int
   return hipGetLastError();
 }
 
-template <bool WITH_O, bool HAS_BIAS>
-hipError_t fwd_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
-                      int Sv, RowStats* stats, float* O, hipStream_t st) {
+template <bool HAS_BIAS>
+hipError_t fwd_stats_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V,
+                            float inv_tau, int Sv, RowStats* stats, hipStream_t st) {
   const int n_tiles = (V + BK - 1) / BK;
   const int tps = (n_tiles + Sv - 1) / Sv;
   const int64_t nrb = (N + BQ - 1) / BQ;
@@ -623,8 +526,7 @@ hipError_t fwd_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_
   switch (H / 128) {
 #define PLP_FWD_CASE(K)                                                                                              \
   case K:                                                                                                            \
-    hipLaunchKernelGGL((fwd_mfma_kernel<K, WITH_O, HAS_BIAS>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv,        \
-                       tps, stats, O);                                                                               \
+    hipLaunchKernelGGL((fwd_mfma_kernel<K, HAS_BIAS>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats); \
     break;
     PLP_FWD_CASE(1)
     PLP_FWD_CASE(2)

@@ -1,6 +1,8 @@
 // Weight-gradient sweep of the LM head on the matrix cores (gfx950), its
 // tail reduction, and the fragment-major copies both sweeps read; the tile
 // machinery and the schedule are described in mfma_tile.h.
+#include <atomic>
+
 #include "mfma_tile.h"
 
 namespace plp {
@@ -350,17 +352,22 @@ constexpr int kTailParts = 4;     // workgroups sharing one tail block of the we
 constexpr int kMaxTailWGs = 256;  // bound of the partial-sum scratch (workgroups)
 
 // Workgroups of `threads` threads of `kernel` the device holds at once
-// (compute units x workgroups per unit), computed once per device.
+// (compute units x workgroups per unit), computed once per device and
+// kernel (callers on several threads may compute it concurrently; they
+// store the same value).
 template <typename K>
 hipError_t resident_workgroups(K kernel, int threads, int* out) {
   constexpr int kMaxDevices = 64;
-  static int cache[kMaxDevices] = {};
+  static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < kMaxDevices && cache[dev] > 0) {
-    *out = cache[dev];
-    return hipSuccess;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) {
+      *out = v;
+      return hipSuccess;
+    }
   }
   int cus = 0, per_cu = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -368,7 +375,7 @@ hipError_t resident_workgroups(K kernel, int threads, int* out) {
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
   if (e != hipSuccess) return e;
   const int n = cus * (per_cu > 0 ? per_cu : 1);
-  if (dev >= 0 && dev < kMaxDevices) cache[dev] = n;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
   *out = n;
   return hipSuccess;
 }
