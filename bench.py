@@ -228,17 +228,34 @@ def main() -> int:
 
     # roofline of the dominant sweep
     n_active = int((out["dlogp"] != 0).sum().item())
+    # per launch: algorithmic FLOP (forward: logits + grad_h accumulator, 4HV
+    # per token; weight gradient: grad_W, 2HV per active token) and algorithmic
+    # HBM bytes (forward: W and the chunk's hidden rows read once, bf16;
+    # weight gradient: W read and grad_W written once, the active rows of h
+    # read once, bias and grad_b when present)
+    n_c, na_c = N / n_chunks, n_active / n_chunks
     per_launch = {
-        "fwd_sweep": (4.0 * H * V * N / n_chunks, ms[0] / max(1, cnt[0])),
-        "wgrad_sweep": (2.0 * H * V * n_active / n_chunks, ms[1] / max(1, cnt[1])),
+        "fwd_sweep": (4.0 * H * V * n_c, 2.0 * H * V + 2.0 * H * n_c + (2.0 * V if spec.bias else 0.0),
+                      ms[0] / max(1, cnt[0])),
+        "wgrad_sweep": (2.0 * H * V * na_c, 4.0 * H * V + 2.0 * H * na_c + (4.0 * V if spec.bias else 0.0),
+                        ms[1] / max(1, cnt[1])),
     }
     dom = "fwd_sweep" if ms[0] >= ms[1] else "wgrad_sweep"
-    flops, avg_ms = per_launch[dom]
-    achieved = flops / (avg_ms * 1e-3) / 1e12
+    flops, alg_bytes, avg_ms = per_launch[dom]
     workload = spec.name + variant
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+    # the roof that binds is the one the algorithmic intensity falls under
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops / alg_bytes >= ridge:
+        achieved = flops / (avg_ms * 1e-3) / 1e12
+        bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
+        bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4),
                 "traffic": _traffic_from_profiles(dom, workload),
+                "alg_flop_per_launch": flops, "alg_bytes_per_launch": alg_bytes,
+                "intensity_flop_per_byte": round(flops / alg_bytes, 1), "ridge_flop_per_byte": round(ridge, 1),
                 "kernel": dom, "avg_launch_ms": round(avg_ms, 4),
                 "launches": int(cnt[0] if dom == "fwd_sweep" else cnt[1]),
                 "other_sweep_ms_per_step": round((ms[1] if dom == "fwd_sweep" else ms[0]) / args.steps, 4)}
