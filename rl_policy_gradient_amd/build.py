@@ -18,11 +18,13 @@ BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["lmhead_fwd.hip", "lmhead_fwd_o.hip", "lmhead_mfma.hip", "lmhead_generic.hip", "loss_stage.hip",
            "plp_api.cpp"]
 
-# Per-source compiler options. The weight-gradient sweep gains about 1 % at
-# 512 to 16384 tokens without the scheduler's unclustered high-register-
-# pressure rescheduling stage (measured on MI355X).
+# Per-source compiler options. Both two-role sweeps are faster without the
+# scheduler's unclustered high-register-pressure rescheduling stage (measured
+# on MI355X: weight gradient about 1 % at 512 to 16384 tokens, forward 1-2 %
+# at 512 and 4096 tokens, with and without a bias; same results bit for bit).
 EXTRA = {
     "lmhead_mfma.hip": ["-mllvm", "-amdgpu-disable-unclustered-high-rp-reschedule"],
+    "lmhead_fwd_o.hip": ["-mllvm", "-amdgpu-disable-unclustered-high-rp-reschedule"],
 }
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -34,12 +34,14 @@ KERNEL_SOURCES = ("fwd_sweep.h", "lmhead_fwd.hip", "lmhead_fwd_o.hip", "lmhead_m
 
 
 def kernel_src_hash() -> str:
-    """Hash of the sources that define the sweeps' code and launch shapes; a
-    traffic summary taken on other sources is stale."""
+    """Hash of the sources and build options that define the sweeps' code and
+    launch shapes; a traffic summary taken on other ones is stale."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "rl_policy_gradient_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(ROOT, "rl_policy_gradient_amd", "build.py"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
