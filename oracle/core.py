@@ -13,7 +13,7 @@ Notation (rows are tokens, sequences are contiguous runs of T rows):
   R_i     = ratio tokens of sequence i              (defaults to M_i)
   n_i = max(1,|M_i|),  nt_i = max(1,|R_i|),  A_i = per-sequence advantage.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   R1  GMPO clip (Liger PR #1320, "The implementation", bullets 1 and 7): for
       A_i>0 the log-ratio is clipped from above only, c = min(lr, eps_high);
       for A_i<0 from below only, c = max(lr, -eps_low); this is PPO's
@@ -39,7 +39,9 @@ Readings taken where the pages are silent (each also listed in the design doc):
   R9  Quantile: torch.quantile's linear interpolation on the fp32 active
       entropies at probability 1 - q, mask = active & H >= thr. No active
       token gives an all-false mask and a NaN threshold. q = 1 turns the mask
-      off entirely.
+      off entirely. Past torch's 2^24-entry cap (PR #1558: a sort fallback)
+      the rank is still fp32(p) * fp32(n - 1) rounded to fp32, and both order
+      statistics are clamped to n - 1.
   R10 old_logp absent means on-policy (lr = 0); ratio_mask absent means R = M.
   R15 GRPO, BNPO and DAPO (named as loss types by Liger PR #1558, Testing,
       and PR #1320, Testing; their formulas are not printed): the token-level
@@ -183,6 +185,11 @@ def quantile_linear_f32(x32, prob: float) -> np.float32:
     a + w (b - a) for w < 1/2 and b + (w - 1)(b - a) otherwise. (This is the
     form torch's CPU kernel produces bit for bit; tests pin it against
     torch.quantile.)
+
+    Past 2^24 entries, where torch.quantile refuses the input and Liger PR
+    #1558 ("Details", the large-input bullet) falls back to a sort, the same
+    fp32 rank is kept (R9) and both order statistics are clamped to the last
+    one: fp32(n - 1) can round up to n there.
     """
     xs = np.sort(np.asarray(x32, np.float32))
     n = xs.shape[0]
@@ -190,8 +197,8 @@ def quantile_linear_f32(x32, prob: float) -> np.float32:
         return np.float32(np.nan)
     p32 = np.float32(prob)
     rank = np.float32(p32 * np.float32(n - 1))
-    lo = int(np.floor(rank))
-    hi = int(np.ceil(rank))
+    lo = min(int(np.floor(rank)), n - 1)
+    hi = min(int(np.ceil(rank)), n - 1)
     w = np.float32(rank - np.float32(lo))
     a, b = xs[lo], xs[hi]
     d = np.float32(b - a)

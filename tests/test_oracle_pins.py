@@ -511,3 +511,25 @@ def test_metrics_counts():
     assert m[7] == 4
     # mean over sequences of the sequence log-ratio: seqs 1 and 3 have 0.5, others 0
     assert m[1] == pytest.approx(0.25, abs=1e-15)
+
+
+def test_quantile_past_torch_cap():
+    """Past 2^24 entries (torch.quantile's cap; PR #1558 sorts instead):
+    n = 2^24 + 4, so fp32(n - 1) rounds up to n. q = 0 must give the maximum
+    exactly (the top tie group, not an index past the end); p = 1/2 gives the
+    rank fp32(0.5 * fp32(n - 1)) = 2^23 + 2, an integer, so the quantile is
+    that order statistic, checked by counting; and the kept fraction at
+    q = 0.2 is 0.2 up to the rank's fp32 rounding."""
+    n = (1 << 24) + 4
+    assert np.float32(n - 1) == np.float32(n)
+    r = _rng(31)
+    x = (11.75 + 0.01 * r.standard_normal(n)).astype(np.float32)
+    active = np.ones(n, bool)
+    m, thr = oracle.entropy_quantile_mask(x, active, 0.0)
+    assert thr == x.max() and m.sum() == (x == x.max()).sum()
+    k = (1 << 23) + 2
+    assert np.float32(np.float32(0.5) * np.float32(n - 1)) == np.float32(k)
+    v = oracle.quantile_linear_f32(x, 0.5)
+    assert (x < v).sum() <= k < (x <= v).sum()
+    m, thr = oracle.entropy_quantile_mask(x, active, 0.2)
+    assert abs(m.sum() - 0.2 * n) <= 8 + (x == thr).sum()
