@@ -5,6 +5,11 @@ MI355X, with the roofline of the dominant kernel and the CPU oracle beside it.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|4|5]
                   [--loss gmpo|gspo_token|grpo|bnpo|dapo] [--token-advantages]
 
+The default workload is the largest one-GPU shape: GMPO at B=128, T=32768
+(4.19M tokens), H=896, V=151936, with a bias, in outer chunks of 8 sequences.
+--config 2 is B=1 T=512, 3 is B=8 T=2048 GMPO + K3 KL, 4 is B=2 T=32768
+GSPO-token with the entropy mask.
+
 --loss runs the workload's inputs under another loss type (same clip
 parameters); --token-advantages gives every completion token its own
 advantage (N(0,1), zero off the completion) instead of one per sequence.
@@ -139,9 +144,9 @@ def _cpu_baseline(spec) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--loss", choices=["gmpo", "gspo_token", "grpo", "bnpo", "dapo"], default=None)
     ap.add_argument("--token-advantages", action="store_true")
@@ -149,8 +154,9 @@ def main() -> int:
                     help="K3 KL weighted by the token importance ratio (workloads with a KL term)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
-              "the data-parallel sharding is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py measures one GPU: there is no multi-GPU path (asked for --gpus {args.gpus}); "
+              "the path shards by whole sequences, each GPU running this call on its own share",
+              file=sys.stderr)
         return 2
 
     import torch
@@ -259,6 +265,11 @@ def main() -> int:
                 "kernel": dom, "avg_launch_ms": round(avg_ms, 4),
                 "launches": int(cnt[0] if dom == "fwd_sweep" else cnt[1]),
                 "other_sweep_ms_per_step": round((ms[1] if dom == "fwd_sweep" else ms[0]) / args.steps, 4)}
+    # the work the method itself does: the logits of every token (2HV) and
+    # the two gradient products (2HV each) of the tokens with dL/dlogp != 0;
+    # the 6NHV count charges the gradients of every token
+    method_flops = 2.0 * H * V * (N + 2.0 * n_active)
+    tflops_method = method_flops / (elapsed / args.steps) / 1e12
     line = {
         "metric": METRIC if not variant else METRIC.replace(
             "GMPO", spec.loss_type.upper() + (" (per-token advantages)" if tadv is not None else "")
@@ -276,6 +287,8 @@ def main() -> int:
         "data": "synthetic",
         "tflops_6nhv": round(tflops, 2),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tflops_method_work": round(tflops_method, 2),
+        "pct_bf16_peak_method_work": round(100.0 * tflops_method / PEAK_BF16_TFLOPS, 2),
         # what the path executes: the forward sweep's 4NHV plus the weight-gradient
         # sweep's 4HV per token with a gradient (its logits are recomputed)
         "executed_tflops": round(4.0 * H * V * (N + n_active) / (elapsed / args.steps) / 1e12, 2),
@@ -291,7 +304,10 @@ def main() -> int:
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and tadv is None:
-        line["cpu_baseline"] = _cpu_baseline(spec)
+        cb = _cpu_baseline(spec)
+        # the whole workload at the sample's rate (not run: extrapolated)
+        cb["extrapolated_full_workload_s"] = round(N / cb["value"], 1)
+        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
     return 0
 

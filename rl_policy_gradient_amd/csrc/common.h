@@ -147,10 +147,20 @@ hipError_t launch_compact_scatter(const float* g, const float* lse, const int64_
 hipError_t launch_gather_rows(int dtype, const void* X, const int* idx, const int* count_dev, int64_t cap,
                               int H, void* Xc, hipStream_t st);
 
-// Entropy quantile mask.
-size_t select_scratch_bytes();
-hipError_t launch_entropy_select(const float* ent, const uint8_t* active, int64_t N, float p32,
-                                 float* thr_dev, void* scratch, hipStream_t st);
+// Entropy quantile mask: the radix select's state and histogram (the
+// threshold first, so the later kernels read it as a float).
+struct SelectState {
+  float thr;                 // the threshold; NaN when no entry is active
+  float w;                   // interpolation weight rank - floor(rank)
+  unsigned pre[2];           // key prefixes of the two order statistics found so far
+  unsigned long long n;      // active entries
+  unsigned long long kk[2];  // ranks left within the current prefixes
+  int done;                  // no active entry: the remaining passes do nothing
+  int pad;
+  unsigned hist[2][2048];    // digit histogram of the current pass (one per order statistic)
+};
+hipError_t launch_entropy_select(const float* ent, const uint8_t* active, int64_t N, float p32, SelectState* state,
+                                 hipStream_t st);
 hipError_t launch_entropy_mask(const float* ent, const uint8_t* active, int64_t N, const float* thr_dev,
                                uint8_t* mask, hipStream_t st);
 hipError_t launch_store_thr(const float* thr_dev, float* thr_out, hipStream_t st);

@@ -15,7 +15,7 @@ namespace {
 // (sum 2^{z2-m2}, sum 2^{z2-m2} z2) against the reference m2 (z2 = z log2 e).
 // Grid: (row blocks) x Sv vocabulary splits, block id = rb * Sv + split.
 template <int KB, bool HAS_BIAS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf,
                      const __bf16* __restrict__ bias, int64_t N, int V, float inv_tau, int Sv,
                      int tiles_per_split, RowStats* __restrict__ stats) {

@@ -351,12 +351,13 @@ void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bia
 constexpr int kTailParts = 4;     // workgroups sharing one tail block of the weight-gradient sweep
 constexpr int kMaxTailWGs = 256;  // bound of the partial-sum scratch (workgroups)
 
-// Workgroups of `threads` threads of `kernel` the device holds at once
+// Workgroups of `threads` threads of `Kernel` the device holds at once
 // (compute units x workgroups per unit), computed once per device and
-// kernel (callers on several threads may compute it concurrently; they
-// store the same value).
-template <typename K>
-hipError_t resident_workgroups(K kernel, int threads, int* out) {
+// kernel: the cache is a static of this instantiation, one per kernel
+// (callers on several threads may compute it concurrently; they store the
+// same value).
+template <auto Kernel>
+hipError_t resident_workgroups(int threads, int* out) {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
@@ -372,7 +373,7 @@ hipError_t resident_workgroups(K kernel, int threads, int* out) {
   int cus = 0, per_cu = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, threads, 0);
   if (e != hipSuccess) return e;
   const int n = cus * (per_cu > 0 ? per_cu : 1);
   if (dev >= 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
@@ -431,8 +432,8 @@ hipError_t bwd_dispatch(const __bf16* Wf, const __bf16* b, const __bf16* hcf, co
   // fit the free slots (at most kTailParts, and kMaxTailWGs in all).
   const int nblk = (V + BQ - 1) / BQ;
   int resident = 0;
-  hipError_t e = b ? resident_workgroups(bwd_pp_kernel<KB, true>, 512, &resident)
-                   : resident_workgroups(bwd_pp_kernel<KB, false>, 512, &resident);
+  hipError_t e = b ? resident_workgroups<bwd_pp_kernel<KB, true>>(512, &resident)
+                   : resident_workgroups<bwd_pp_kernel<KB, false>>(512, &resident);
   if (e != hipSuccess) return e;
   const int rem = resident > 0 ? nblk % resident : 0;
   int parts = rem > 0 ? min(kTailParts, min(resident, kMaxTailWGs) / rem) : 1;

@@ -617,11 +617,16 @@ __global__ __launch_bounds__(NT) void gather_rows_kernel(const T* __restrict__ X
 
 // ---------------------------------------------------------------------------
 // Batch-global quantile of the active entropies (torch.quantile linear
-// interpolation in fp32), by MSB-first radix select on order-preserving
-// integer keys: one block, four 8-bit digit passes for each of the two order
-// statistics floor(rank) and ceil(rank).
+// interpolation in fp32), by MSB-first radix select over the whole grid on
+// order-preserving integer keys: three digit passes (11, 11 and 10 bits),
+// each a histogram kernel over all entries (workgroup histograms in LDS,
+// added into one global histogram with integer atomics, so the counts do
+// not depend on the order of the additions) and a one-workgroup scan that
+// picks the digit of each of the two order statistics floor(rank) and
+// ceil(rank). The scratch is a SelectState (thr first, so the threshold is
+// read through a float pointer by the later kernels).
 // ---------------------------------------------------------------------------
-constexpr int SEL_NT = 1024;
+constexpr int SEL_BINS = 2048;
 
 __device__ __forceinline__ unsigned f2key(float f) {
   const unsigned u = __float_as_uint(f);
@@ -630,82 +635,145 @@ __device__ __forceinline__ unsigned f2key(float f) {
 __device__ __forceinline__ float key2f(unsigned k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
+// Digit of pass p: bits [shift, shift + width) of the key.
+__device__ __forceinline__ int sel_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
+__device__ __forceinline__ int sel_width(int pass) { return pass == 2 ? 10 : 11; }
 
-__global__ __launch_bounds__(SEL_NT) void select_kernel(const float* __restrict__ ent, const uint8_t* __restrict__ active,
-                                                        int64_t N, float p32, float* __restrict__ thr_out) {
-  // one pair of histograms per wave (LDS atomics of a pass then collide only
-  // within a wave); bins are integer counts, so the result is order free
-  constexpr int SEL_W = SEL_NT / 64;
-  __shared__ unsigned hist[SEL_W][2][256];
-  __shared__ unsigned long long red[SEL_NT];
-  __shared__ unsigned pre[2];
-  __shared__ unsigned long long kk[2];
-  unsigned long long c = 0;
-#pragma unroll 8
-  for (int64_t t = threadIdx.x; t < N; t += SEL_NT) c += active[t] != 0 ? 1ull : 0ull;
-  red[threadIdx.x] = c;
-  __syncthreads();
-  for (int s = SEL_NT / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  const unsigned long long n = red[0];
-  if (n == 0) {
-    if (threadIdx.x == 0) *thr_out = __int_as_float(0x7fc00000);
-    return;
-  }
-  const float rank = __fmul_rn(p32, (float)(n - 1));
-  const float rlo = floorf(rank);
-  const float w = __fsub_rn(rank, rlo);
+__global__ __launch_bounds__(NT) void select_init_kernel(SelectState* __restrict__ s) {
+  unsigned* hist = &s->hist[0][0];
+  for (int k = threadIdx.x; k < 2 * SEL_BINS; k += NT) hist[k] = 0u;
   if (threadIdx.x == 0) {
-    kk[0] = (unsigned long long)rlo;
-    kk[1] = (unsigned long long)ceilf(rank);
-    pre[0] = pre[1] = 0u;
+    s->thr = __int_as_float(0x7fc00000);
+    s->w = 0.f;
+    s->pre[0] = s->pre[1] = 0u;
+    s->n = 0ull;
+    s->kk[0] = s->kk[1] = 0ull;
+    s->done = 0;
+  }
+}
+
+// Histogram of pass `pass` over the active entries whose key carries the
+// prefix found so far (one histogram while both order statistics share it).
+__global__ __launch_bounds__(NT) void select_hist_kernel(const float* __restrict__ ent,
+                                                         const uint8_t* __restrict__ active, int64_t N,
+                                                         SelectState* __restrict__ s, int pass) {
+  __shared__ unsigned lh[2][SEL_BINS];
+  if (s->done) return;  // uniform: no active entry
+  const int shift = sel_shift(pass);
+  const unsigned dmask = (1u << sel_width(pass)) - 1u;
+  const int top = shift + sel_width(pass);
+  const unsigned hmask = top >= 32 ? 0u : (0xffffffffu << top);
+  const unsigned p0 = s->pre[0], p1 = s->pre[1];
+  const bool same = p0 == p1;
+  for (int k = threadIdx.x; k < 2 * SEL_BINS; k += NT) (&lh[0][0])[k] = 0u;
+  __syncthreads();
+  for (int64_t t = (int64_t)blockIdx.x * NT + threadIdx.x; t < N; t += (int64_t)gridDim.x * NT) {
+    if (active[t] == 0) continue;
+    const unsigned key = f2key(ent[t]);
+    const unsigned d = (key >> shift) & dmask;
+    if ((key & hmask) == p0) atomicAdd(&lh[0][d], 1u);
+    if (!same && (key & hmask) == p1) atomicAdd(&lh[1][d], 1u);
   }
   __syncthreads();
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const unsigned hmask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
-    for (int k = threadIdx.x; k < SEL_W * 512; k += SEL_NT) (&hist[0][0][0])[k] = 0u;
-    __syncthreads();
-    const unsigned p0 = pre[0], p1 = pre[1];
-    const bool same = p0 == p1;  // both ranks still share their prefix: one histogram serves both
-    unsigned (*wh)[256] = hist[threadIdx.x >> 6];
-#pragma unroll 8
-    for (int64_t t = threadIdx.x; t < N; t += SEL_NT) {
-      if (active[t] == 0) continue;
-      const unsigned key = f2key(ent[t]);
-      const unsigned d = (key >> shift) & 255u;
-      if ((key & hmask) == p0) atomicAdd(&wh[0][d], 1u);
-      if (!same && (key & hmask) == p1) atomicAdd(&wh[1][d], 1u);
+  for (int k = threadIdx.x; k < (same ? 1 : 2) * SEL_BINS; k += NT) {
+    const unsigned v = (&lh[0][0])[k];
+    if (v != 0u) atomicAdd(&s->hist[0][0] + k, v);
+  }
+}
+
+// Digit of pass `pass` for both order statistics from the global histogram;
+// clears the histogram for the next pass. Pass 0 also counts the active
+// entries and fixes the ranks; the last pass writes the threshold.
+__global__ __launch_bounds__(NT) void select_scan_kernel(SelectState* __restrict__ s, int pass, float p32) {
+  // The rank, its fraction and the interpolation are each rounded to fp32 as
+  // torch.quantile rounds them: no multiply-add contraction here (it would
+  // take the fraction of the unrounded product).
+#pragma clang fp contract(off)
+  constexpr int PER = SEL_BINS / NT;
+  __shared__ unsigned long long red[4];
+  __shared__ unsigned long long tsum[NT];
+  // the state this kernel updates is kept in LDS and written back at the end
+  // (no global value is read back after a write within the kernel)
+  __shared__ unsigned long long sk[2];
+  __shared__ unsigned spre[2];
+  __shared__ float sw;
+  if (s->done) return;  // uniform
+  const int shift = sel_shift(pass);
+  const unsigned p0 = s->pre[0], p1 = s->pre[1];
+  const bool same = p0 == p1;
+  if (pass == 0) {
+    unsigned long long c = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) c += s->hist[0][threadIdx.x * PER + k];
+    const unsigned long long n = block_sum(c, red);
+    if (n == 0) {
+      if (threadIdx.x == 0) {
+        s->done = 1;
+        s->thr = __int_as_float(0x7fc00000);
+      }
+      return;
     }
-    __syncthreads();
-    // bin totals over the waves into wave 0's histograms
-    for (int k = threadIdx.x; k < 512; k += SEL_NT) {
-      unsigned tot = 0u;
-      for (int v = 0; v < SEL_W; ++v) tot += (&hist[v][0][0])[k];
-      (&hist[0][0][0])[k] = tot;
+    // rank = p (n - 1) in fp32 as torch.quantile forms it; past 2^24 entries
+    // fp32(n - 1) can round up to n, so both order statistics are clamped to
+    // the last one
+    const float rank = p32 * (float)(n - 1);
+    const float rlo = floorf(rank);
+    if (threadIdx.x == 0) {
+      s->n = n;
+      sw = rank - rlo;
+      sk[0] = min((unsigned long long)rlo, n - 1);
+      sk[1] = min((unsigned long long)ceilf(rank), n - 1);
     }
+  } else if (threadIdx.x == 0) {
+    sw = s->w;
+    sk[0] = s->kk[0];
+    sk[1] = s->kk[1];
+  }
+  if (threadIdx.x == 0) {
+    spre[0] = p0;
+    spre[1] = p1;
+  }
+  __syncthreads();
+  for (int r = 0; r < 2; ++r) {
+    const unsigned* hw = s->hist[same ? 0 : r];
+    unsigned long long loc = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) loc += hw[threadIdx.x * PER + k];
+    tsum[threadIdx.x] = loc;
     __syncthreads();
-    if (threadIdx.x < 2) {
-      const int which = threadIdx.x;
-      const unsigned* hw = hist[0][same ? 0 : which];
-      unsigned long long cum = 0, k = kk[which];
-      int b = 0;
-      for (; b < 255; ++b) {
+    for (int o = 1; o < NT; o <<= 1) {  // inclusive scan of the thread sums
+      const unsigned long long v = threadIdx.x >= o ? tsum[threadIdx.x - o] : 0ull;
+      __syncthreads();
+      tsum[threadIdx.x] += v;
+      __syncthreads();
+    }
+    const unsigned long long k = sk[r];
+    unsigned long long cum = tsum[threadIdx.x] - loc;  // bins before this thread's
+    __syncthreads();
+    if (k >= cum && k < cum + loc) {  // exactly one thread holds the rank
+      int b = threadIdx.x * PER;
+      for (int j = 0; j < PER - 1; ++j, ++b) {
         if (k < cum + hw[b]) break;
         cum += hw[b];
       }
-      kk[which] = k - cum;
-      pre[which] |= ((unsigned)b) << shift;
+      sk[r] = k - cum;
+      spre[r] |= (unsigned)b << shift;
     }
     __syncthreads();
   }
+  for (int k = threadIdx.x; k < 2 * SEL_BINS; k += NT) (&s->hist[0][0])[k] = 0u;
   if (threadIdx.x == 0) {
-    const float a = key2f(pre[0]);
-    const float b = key2f(pre[1]);
-    const float d = __fsub_rn(b, a);
-    *thr_out = w < 0.5f ? __fmaf_rn(w, d, a) : __fmaf_rn(__fsub_rn(w, 1.0f), d, b);
+    s->pre[0] = spre[0];
+    s->pre[1] = spre[1];
+    s->kk[0] = sk[0];
+    s->kk[1] = sk[1];
+    s->w = sw;
+    if (pass == 2) {
+      const float a = key2f(spre[0]);
+      const float b = key2f(spre[1]);
+      const float d = b - a;
+      s->thr = sw < 0.5f ? __builtin_fmaf(sw, d, a) : __builtin_fmaf(sw - 1.0f, d, b);
+    }
   }
 }
 
@@ -852,12 +920,16 @@ hipError_t launch_gather_rows(int dtype, const void* X, const int* idx, const in
   return hipGetLastError();
 }
 
-size_t select_scratch_bytes() { return 256; }
-
-hipError_t launch_entropy_select(const float* ent, const uint8_t* active, int64_t N, float p32, float* thr_dev,
-                                 void* scratch, hipStream_t st) {
-  (void)scratch;
-  hipLaunchKernelGGL(select_kernel, dim3(1), dim3(SEL_NT), 0, st, ent, active, N, p32, thr_dev);
+hipError_t launch_entropy_select(const float* ent, const uint8_t* active, int64_t N, float p32, SelectState* state,
+                                 hipStream_t st) {
+  // workgroups: about eight entries per thread, at most 1024 workgroups
+  int64_t g = (N + NT * 8 - 1) / (NT * 8);
+  g = g < 1 ? 1 : (g > 1024 ? 1024 : g);
+  hipLaunchKernelGGL(select_init_kernel, dim3(1), dim3(NT), 0, st, state);
+  for (int pass = 0; pass < 3; ++pass) {
+    hipLaunchKernelGGL(select_hist_kernel, dim3((unsigned)g), dim3(NT), 0, st, ent, active, N, state, pass);
+    hipLaunchKernelGGL(select_scan_kernel, dim3(1), dim3(NT), 0, st, state, pass, p32);
+  }
   return hipGetLastError();
 }
 

@@ -108,7 +108,7 @@ struct Bufs {
   SeqCoef* coef = nullptr;
   float* g = nullptr;
   LossAcc* acc = nullptr;
-  float* thr = nullptr;
+  SelectState* sel = nullptr;  // radix select state; its first field is the threshold
   unsigned long long* ntok = nullptr;  // the batch's completion tokens (BNPO / DAPO divisor)
   int* idx = nullptr;
   TokData* tok = nullptr;
@@ -158,7 +158,7 @@ size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
   b.coef = c.take<SeqCoef>(p.Bc);
   b.g = c.take<float>(p.Nc);
   b.acc = c.take<LossAcc>(1);
-  b.thr = c.take<float>(1);
+  b.sel = c.take<SelectState>(1);
   b.ntok = c.take<unsigned long long>(1);
   if (p.need_gw) {
     b.idx = c.take<int>(p.cap);
@@ -418,9 +418,9 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
         if (rc) return rc;
       }
     }
-    HIP_TRY(launch_entropy_select(b.ent, a->completion_mask, p.N, (float)(1.0 - a->top_entropy_quantile), b.thr,
-                                  nullptr, st));
-    HIP_TRY(launch_entropy_mask(b.ent, a->completion_mask, p.N, b.thr, b.emask, st));
+    HIP_TRY(launch_entropy_select(b.ent, a->completion_mask, p.N, (float)(1.0 - a->top_entropy_quantile), b.sel,
+                                  st));
+    HIP_TRY(launch_entropy_mask(b.ent, a->completion_mask, p.N, &b.sel->thr, b.emask, st));
   }
 
   for (int64_t c = 0; c < p.nchunks; ++c) {
@@ -439,7 +439,7 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
     const float* tadv = token_advantages(a) ? token_advantages(a) + r0 : nullptr;
     HIP_TRY(launch_loss_seq_partial(lpar, bc, b.lp + r0, old, ref, comp, ratio, em, adv, tadv, p.St, b.part, st));
     const bool last = c == p.nchunks - 1;
-    HIP_TRY(launch_loss_seq_final(lpar, bc, p.St, b.part, adv, b.coef, b.acc, c == 0, p.entropy ? b.thr : nullptr,
+    HIP_TRY(launch_loss_seq_final(lpar, bc, p.St, b.part, adv, b.coef, b.acc, c == 0, p.entropy ? &b.sel->thr : nullptr,
                                   last ? out->loss : nullptr, last ? out->metrics : nullptr, st));
     float* g = out->dlogp_out ? out->dlogp_out + r0 : b.g;
     int* cnt32 = p.need_gw ? (int*)b.cscratch : nullptr;
@@ -521,7 +521,7 @@ PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const 
 PLP_API int plp_entropy_quantile_mask_workspace_size(int64_t N, size_t* bytes) {
   if (!bytes) return fail(PLP_E_INVALID, "bytes is NULL");
   if (N < 0 || N >= kMaxRows) return fail(PLP_E_INVALID, "bad N=%lld", (long long)N);
-  *bytes = kAlign * 2;
+  *bytes = align_up(sizeof(SelectState)) + kAlign;
   return ok();
 }
 
@@ -535,15 +535,15 @@ PLP_API int plp_entropy_quantile_mask(const float* entropy, const uint8_t* activ
   if (N > 0 && (!entropy || !active || !mask_out)) return fail(PLP_E_INVALID, "entropy, active and mask_out are required");
   rc = check_ws(ws, ws_bytes, need);
   if (rc) return rc;
-  float* thr = (float*)ws;
+  SelectState* sel = (SelectState*)ws;
   if (q == 1.0) {
     if (N > 0) HIP_TRY(launch_copy_mask(active, N, mask_out, st));
     if (threshold_out) HIP_TRY(launch_set_nan(threshold_out, st));
     return ok();
   }
-  HIP_TRY(launch_entropy_select(entropy, active, N, (float)(1.0 - q), thr, nullptr, st));
-  if (N > 0) HIP_TRY(launch_entropy_mask(entropy, active, N, thr, mask_out, st));
-  if (threshold_out) HIP_TRY(launch_store_thr(thr, threshold_out, st));
+  HIP_TRY(launch_entropy_select(entropy, active, N, (float)(1.0 - q), sel, st));
+  if (N > 0) HIP_TRY(launch_entropy_mask(entropy, active, N, &sel->thr, mask_out, st));
+  if (threshold_out) HIP_TRY(launch_store_thr(&sel->thr, threshold_out, st));
   return ok();
 }
 
@@ -559,7 +559,7 @@ PLP_API int plp_policy_loss_workspace_size(const plp_args* a, size_t* bytes) {
   c.take<SeqCoef>(a->B);
   c.take<float>(N);
   c.take<LossAcc>(1);
-  c.take<float>(1);
+  c.take<SelectState>(1);
   c.take<unsigned long long>(1);
   *bytes = c.off + kAlign;
   return ok();
@@ -587,19 +587,19 @@ PLP_API int plp_policy_loss_from_logprobs(const plp_args* a, const float* logp, 
   SeqCoef* coef = c.take<SeqCoef>(a->B);
   float* gbuf = c.take<float>(N);
   LossAcc* acc = c.take<LossAcc>(1);
-  float* thr = c.take<float>(1);
+  SelectState* sel = c.take<SelectState>(1);
   unsigned long long* ntok = c.take<unsigned long long>(1);
   const LossParams lpar = loss_params(a, ntok);
   rc = count_tokens_if_needed(a, ntok, st);
   if (rc) return rc;
   if (q_on) {
-    HIP_TRY(launch_entropy_select(entropy, a->completion_mask, N, (float)(1.0 - a->top_entropy_quantile), thr, nullptr, st));
-    HIP_TRY(launch_entropy_mask(entropy, a->completion_mask, N, thr, emask, st));
+    HIP_TRY(launch_entropy_select(entropy, a->completion_mask, N, (float)(1.0 - a->top_entropy_quantile), sel, st));
+    HIP_TRY(launch_entropy_mask(entropy, a->completion_mask, N, &sel->thr, emask, st));
   }
   const uint8_t* em = q_on ? emask : nullptr;
   HIP_TRY(launch_loss_seq_partial(lpar, a->B, logp, a->old_logp, a->ref_logp, a->completion_mask, a->ratio_mask, em,
                                   a->advantages, token_advantages(a), St, part, st));
-  HIP_TRY(launch_loss_seq_final(lpar, a->B, St, part, a->advantages, coef, acc, true, q_on ? thr : nullptr, out->loss,
+  HIP_TRY(launch_loss_seq_final(lpar, a->B, St, part, a->advantages, coef, acc, true, q_on ? &sel->thr : nullptr, out->loss,
                                 out->metrics, st));
   float* g = out->dlogp_out ? out->dlogp_out : gbuf;
   HIP_TRY(launch_loss_tokens(PLP_DTYPE_F32, lpar, a->B, logp, a->old_logp, a->ref_logp, a->completion_mask,

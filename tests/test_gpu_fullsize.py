@@ -1,6 +1,7 @@
 """GPU parity at the workloads' full sizes (H=896, V=151936), through the C ABI.
 
-cfg 2 (B=1, T=512): against the whole live oracle run.
+cfg 2 (B=1, T=512): against the whole live oracle run; the no-grad
+selective_entropy entry point against the oracle's full-vocabulary forward.
 cfg 3 (B=8, T=2048, GMPO + K3 KL + bias) and cfg 4 (B=2, T=32768,
 GSPO-token + batch-global entropy mask q=0.2): every token's log-prob,
 entropy and dL/dlogp, the loss and metrics against the oracle fed with the
@@ -9,11 +10,20 @@ tests/golden/make_golden.py from oracle/ only); grad_h on 256 sampled tokens
 and grad_W / grad_b on 64 sampled vocabulary rows computed by the oracle
 one row at a time over all tokens.
 
-Where the fp32 entropies of the GPU and the oracle straddle the batch-global
-threshold (tokens within the entropy tolerance of it), both masks are valid
-readings of the same definition: those tokens are excluded from the
-per-token comparisons and their largest possible effect widens the loss
-tolerance; every other token's mask bit must agree exactly.
+The entropy mask is a decision taken on fp32 entropies about two tokens per
+fp32 ulp apart near the threshold at cfg 4, so it is checked in two steps:
+the GPU's mask and threshold equal, bit for bit, the oracle's quantile
+selection applied to the GPU's own entropy vector (whose values are checked
+against the oracle's within the entropy tolerance), and the loss, metrics and
+dL/dlogp are then compared with the oracle's loss stage fed that mask. The
+number of tokens where the oracle's selection on its own entropies differs
+is printed for information.
+
+cfg 5 (B=128, T=32768, 4.19M tokens, bias, outer chunks of 8 sequences): the
+oracle recomputes the whole loss stage (loss, metrics, every token's
+dL/dlogp) from the GPU's exported log-probs, the log-prob, entropy and grad_h
+rows of 8 sequences x 256 sampled tokens with the full vocabulary, and 64
+grad_W / grad_b rows summed over all 4.19M tokens.
 """
 import os
 import sys
@@ -75,6 +85,18 @@ def test_cfg2_full_against_live_oracle():
     _grad_ok(gpu["grad_hidden"], ref["grad_h"], "grad_h")
     _grad_ok(gpu["grad_weight"], ref["grad_W"], "grad_W")
 
+    # the no-grad streaming entropy entry point at the full vocabulary
+    import rl_policy_gradient_amd as plp
+    from tests.gpu_helpers import dev_tensor
+    ent, lp = plp.selective_entropy(dev_tensor(d["h_raw"], "bf16"), dev_tensor(d["W_raw"], "bf16"), None,
+                                    dev_tensor(d["targets"]))
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(ent.cpu().numpy(), d["fwd"]["entropy"], rtol=0, atol=LP_TOL)
+    np.testing.assert_allclose(lp.cpu().numpy(), d["fwd"]["logp"], rtol=0, atol=LP_TOL)
+    ent2, lp2 = plp.selective_entropy(dev_tensor(d["h_raw"], "bf16"), dev_tensor(d["W_raw"], "bf16"))
+    torch.cuda.synchronize()
+    assert lp2 is None and torch.equal(ent2, ent)
+
 
 # The other loss types at the B=1 T=512 size (same inputs as cfg 2 but for
 # the loss settings), against the whole live oracle run.
@@ -114,21 +136,24 @@ def test_full_size_sampled(cfg):
     np.testing.assert_allclose(gpu["logp"], fwd["logp"], rtol=0, atol=LP_TOL)
     np.testing.assert_allclose(gpu["entropy"], fwd["entropy"], rtol=0, atol=LP_TOL)
 
-    # entropy mask: exact outside the tolerance band around the threshold
-    band = np.zeros(N, bool)
+    # entropy mask: the oracle's selection on the GPU's entropy vector, bit
+    # for bit; the loss stage is then the oracle's with that mask
     if spec.top_entropy_quantile < 1.0:
-        thr, thr_gpu = float(ref["threshold"]), float(gpu["metrics"][4])
-        assert abs(thr_gpu - thr) <= LP_TOL
-        band = comp & (np.abs(fwd["entropy"].astype(np.float32) - thr) <= LP_TOL)
         em_gpu = gpu["entropy_mask"].astype(bool)
-        # the GPU mask follows its own entropies and threshold exactly
-        np.testing.assert_array_equal(em_gpu, comp & (gpu["entropy"] >= thr_gpu))
-        diff = em_gpu != ref["entropy_mask"]
-        assert not np.any(diff & ~band), np.nonzero(diff & ~band)[0][:10]
-        print(f"[info] cfg{cfg}: {band.sum()} tokens in the threshold band, {diff.sum()} mask bits differ there",
-              flush=True)
-        kept = ref["entropy_mask"].sum()
+        sel_mask, sel_thr = oracle.entropy_quantile_mask(gpu["entropy"], comp, spec.top_entropy_quantile)
+        np.testing.assert_array_equal(em_gpu, sel_mask)
+        thr_gpu = np.float32(gpu["metrics"][4])
+        assert thr_gpu.view(np.uint32) == np.float32(sel_thr).view(np.uint32), (thr_gpu, sel_thr)
+        diff = int((em_gpu != ref["entropy_mask"]).sum())
+        print(f"[info] cfg{cfg}: mask bits where the oracle's selection on its own entropies differs: {diff}; "
+              f"thresholds gpu {float(thr_gpu)!r} oracle {float(ref['threshold'])!r}", flush=True)
+        kept = em_gpu.sum()
         assert 0 < kept < comp.sum()
+        cfg_l = oracle.LossConfig.from_spec(spec)
+        part = oracle.policy_loss(cfg_l, fwd["logp"], d["old"], d["ref"], d["completion_mask"], None,
+                                  d["advantages"], entropy_mask=em_gpu, B_total=spec.B)
+        loss_ref, m_ref = oracle.finalize_metrics([part], sel_thr)
+        ref = dict(ref, loss=loss_ref, metrics=m_ref, g=part["g"], entropy_mask=em_gpu, parts=[part])
 
     # clip predicates: every active log-ratio sits further from a bound than
     # the GPU's log-prob differs from the oracle's, so no decision can differ
@@ -141,23 +166,20 @@ def test_full_size_sampled(cfg):
         assert min(m_hi, m_lo) > 2 * dlp
 
     # loss and metrics
-    w = 1.0 / (spec.B * np.maximum(1, comp.reshape(spec.B, spec.T).sum(1)))
-    pol = np.array([abs(p["seq_ratio"] * d["advantages"].astype(np.float64)).max() for p in ref["parts"]])
-    band_bound = float((band.reshape(spec.B, spec.T).sum(1) * w).sum() * max(1.0, pol.max()) * 1.01)
-    assert abs(gpu["loss"][0] - ref["loss"]) <= 1e-4 + band_bound, (gpu["loss"][0], ref["loss"], band_bound)
+    assert abs(gpu["loss"][0] - ref["loss"]) <= 1e-4, (gpu["loss"][0], ref["loss"])
     m, mo = gpu["metrics"], ref["metrics"]
     assert m[6] == mo[6] and m[7] == mo[7], (m, mo)
     assert np.float32(m[0]).view(np.uint32) == np.float32(mo[0]).view(np.uint32)
     np.testing.assert_allclose(m[[1, 2, 3]], mo[[1, 2, 3]], rtol=1e-4, atol=1e-6)
     if spec.top_entropy_quantile < 1.0:
-        assert abs(m[5] - mo[5]) * mo[6] <= band.sum() + 0.5
+        assert np.float32(m[5]).view(np.uint32) == np.float32(mo[5]).view(np.uint32), (m[5], mo[5])
 
-    # dL/dlogp of every token outside the band
-    ok = ~band
+    # dL/dlogp of every token
+    ok = np.ones(N, bool)
     g_ref = ref["g"]
-    np.testing.assert_allclose(gpu["dlogp"][ok], g_ref[ok], rtol=0, atol=1e-4 * np.abs(g_ref).max())
+    np.testing.assert_allclose(gpu["dlogp"], g_ref, rtol=0, atol=1e-4 * np.abs(g_ref).max())
 
-    # grad_h on sampled tokens with a gradient (outside the band)
+    # grad_h on sampled tokens with a gradient
     rng = np.random.default_rng(1000 + cfg)
     cand = np.nonzero((g_ref != 0) & ok)[0]
     rows = np.sort(rng.choice(cand, size=min(256, len(cand)), replace=False))
@@ -183,21 +205,23 @@ def test_cfg5_largest_single_gpu_shape():
     """B=128, T=32768 (4.19M tokens), bias, outer chunks of 8 sequences.
 
     old_logp = fp32(current + noise) with the current log-probs from the GPU's
-    own forward (an fp64 oracle pass over 4.19M tokens takes hours), so the
-    oracle checks only what does not depend on old_logp: log-prob and entropy
-    of 8 sequences x 256 completion tokens, and the direction of their grad_h
-    rows, W_y - sum_v p_v W_v. The rest are properties that hold at any size:
-    every output finite; grad_W and grad_b sum to zero over the vocabulary
-    (sum_v (onehot - p) = 0); dL/dlogp is one constant per sequence on its
-    unclipped ratio tokens and zero elsewhere (GMPO, q = 1, beta = 0); outer
-    chunks of 8 sequences agree with the whole batch in one chunk."""
+    own forward (an fp64 oracle pass over 4.19M tokens takes hours). Against
+    the oracle: the whole loss stage (loss, metrics, dL/dlogp of every token)
+    recomputed in fp64 from the GPU's exported log-probs; log-prob, entropy
+    and grad_h of 8 sequences x 256 completion tokens with the full
+    vocabulary; 64 grad_W / grad_b rows summed over all 4.19M tokens with
+    lse_t = z[t, y_t] (oracle) - logp_t (GPU). Every output finite; the
+    whole batch in one outer chunk gives the same loss and gradients."""
     import concurrent.futures as cf
+    import time
 
     import rl_policy_gradient_amd as plp
     from tests.gpu_helpers import dev_tensor
 
     spec = synth.CONFIGS[5]
     B, T, H, V, N = spec.B, spec.T, spec.H, spec.V, spec.N
+    tau = spec.temperature
+    t_start = time.time()
     _say("cfg5: generating inputs")
     dev = torch.device("cuda:0")
     h = torch.empty(N, H, dtype=torch.bfloat16, device=dev)
@@ -215,12 +239,13 @@ def test_cfg5_largest_single_gpu_shape():
     comp = synth.completion_mask(spec)
     adv = synth.advantages(spec)
     Wt, bt_, yt = dev_tensor(Wraw, "bf16"), dev_tensor(braw, "bf16"), dev_tensor(y)
-    _say("cfg5: current log-probs on the GPU")
+    _say(f"cfg5: current log-probs on the GPU ({time.time() - t_start:.0f} s)")
     _, lp_cur = plp.selective_entropy(h, Wt, bt_, yt)
     old = (lp_cur.double() + torch.from_numpy(synth.old_noise(spec)).to(dev)).float()
+    del lp_cur
     kw = dict(B=B, T=T, bias=bt_, old_logp=old, epsilon_low=spec.eps_low, epsilon_high=spec.eps_high,
               diagnostics=True)
-    _say("cfg5: fused, chunks of 8 sequences")
+    _say(f"cfg5: fused, chunks of 8 sequences ({time.time() - t_start:.0f} s)")
     out = plp.fused_lmhead_policy_loss_fwd_bwd(h, Wt, yt, dev_tensor(comp), dev_tensor(adv),
                                                chunk_sequences=spec.chunk_sequences, **kw)
     torch.cuda.synchronize()
@@ -230,49 +255,72 @@ def test_cfg5_largest_single_gpu_shape():
             continue
         assert bool(torch.isfinite(v.float()).all()), k
 
-    # sums over the vocabulary vanish: sum_v dz[t,v] = g_t (1 - sum_v p[t,v]) / tau = 0
-    gW = out["grad_weight"].float()
-    colsum = gW.sum(0).abs()
-    colabs = gW.abs().sum(0)
-    assert float((colsum / colabs.clamp(min=1e-30)).max()) < 2e-2
-    gb = out["grad_bias"].float()
-    assert float(gb.sum().abs()) < 2e-2 * float(gb.abs().sum())
+    # ---- the loss stage by the oracle from the GPU's log-probs ------------
+    _say(f"cfg5: oracle loss stage over 4.19M tokens ({time.time() - t_start:.0f} s)")
+    lp_gpu = out["logp"].cpu().numpy().astype(np.float64)
+    old_np = old.cpu().numpy()
+    cfg_l = oracle.LossConfig.from_spec(spec)
+    cs = spec.chunk_sequences
+    parts, g_ref = [], np.zeros(N)
+    for s0 in range(0, B, cs):
+        sl = slice(s0 * T, (s0 + cs) * T)
+        p = oracle.policy_loss(cfg_l, lp_gpu[sl], old_np[sl], None, comp[sl], None, adv[s0:s0 + cs], B_total=B)
+        g_ref[sl] = p["g"]
+        parts.append(p)
+    loss_ref, m_ref = oracle.finalize_metrics(parts, np.float32(np.nan))
+    m = out["metrics"].cpu().numpy()
+    assert abs(float(out["loss"][0]) - loss_ref) <= 1e-4, (float(out["loss"][0]), loss_ref)
+    assert m[6] == m_ref[6] and m[7] == m_ref[7], (m, m_ref)
+    assert np.float32(m[0]).view(np.uint32) == np.float32(m_ref[0]).view(np.uint32)
+    np.testing.assert_allclose(m[[1, 2, 3]], m_ref[[1, 2, 3]], rtol=1e-4, atol=1e-6)
+    g = out["dlogp"].cpu().numpy()
+    np.testing.assert_allclose(g, g_ref, rtol=0, atol=1e-4 * np.abs(g_ref).max())
+    assert np.array_equal(g != 0, g_ref != 0)
 
-    # dL/dlogp structure per sequence
-    g = out["dlogp"].cpu().numpy().reshape(B, T)
-    cm = comp.reshape(B, T) != 0
-    assert np.all(g[~cm] == 0)
-    for i in range(B):
-        nz = g[i][g[i] != 0]
-        if adv[i] == 0:
-            assert nz.size == 0
-        elif nz.size:
-            assert np.all(nz == nz[0]) and np.sign(nz[0]) == -np.sign(adv[i])
-
-    # oracle on sampled tokens
+    # ---- sampled tokens: log-prob, entropy and grad_h by value ------------
     rng = np.random.default_rng(5005)
+    cm = comp.reshape(B, T) != 0
     seqs = np.sort(rng.choice(B, 8, replace=False))
     rows = np.concatenate([i * T + np.sort(rng.choice(np.nonzero(cm[i])[0], 256, replace=False)) for i in seqs])
     hs, _ = synth.hidden(spec, rows)
-    _say("cfg5: oracle on 2048 sampled tokens")
-    f = oracle.forward_rows(hs, W32, b32, spec.temperature, y[rows])
-    np.testing.assert_allclose(out["logp"][torch.from_numpy(rows).to(dev)].cpu().numpy(), f["logp"], rtol=0,
-                               atol=LP_TOL)
-    np.testing.assert_allclose(out["entropy"][torch.from_numpy(rows).to(dev)].cpu().numpy(), f["entropy"],
-                               rtol=0, atol=LP_TOL)
-    vdir = oracle.grad_h_rows(hs, W32, b32, spec.temperature, y[rows], f["lse"], np.ones(len(rows)))
-    ghs = out["grad_hidden"][torch.from_numpy(rows).to(dev)].float().cpu().numpy()
-    gs = g.reshape(-1)[rows]
-    for k in np.nonzero(gs)[0]:
-        assert cosine(ghs[k], np.sign(gs[k]) * vdir[k]) >= 0.9999
+    _say(f"cfg5: oracle on 2048 sampled tokens ({time.time() - t_start:.0f} s)")
+    f = oracle.forward_rows(hs, W32, b32, tau, y[rows])
+    rows_t = torch.from_numpy(rows).to(dev)
+    np.testing.assert_allclose(out["logp"][rows_t].cpu().numpy(), f["logp"], rtol=0, atol=LP_TOL)
+    np.testing.assert_allclose(out["entropy"][rows_t].cpu().numpy(), f["entropy"], rtol=0, atol=LP_TOL)
+    gh_ref = oracle.grad_h_rows(hs, W32, b32, tau, y[rows], f["lse"], g_ref[rows])
+    _grad_ok(out["grad_hidden"][rows_t].float().cpu().numpy(), gh_ref, "grad_h rows")
 
-    # the whole batch in one chunk gives the same result
-    _say("cfg5: fused, one chunk")
-    del gW
+    # ---- 64 grad_W / grad_b rows summed over every token ------------------
+    _say(f"cfg5: oracle grad_W rows over 4.19M tokens ({time.time() - t_start:.0f} s)")
+    tg = np.unique(y[g_ref != 0])
+    vrows = np.unique(np.concatenate([rng.choice(tg, 32, replace=False), rng.choice(V, 32, replace=False)]))
+    gW_ref = np.zeros((len(vrows), H))
+    gb_ref = np.zeros(len(vrows))
+    step = 65536
+    for r0 in range(0, N, step):
+        r1 = min(N, r0 + step)
+        if not np.any(g_ref[r0:r1]):
+            continue
+        hc = h[r0:r1].float().cpu().numpy().astype(np.float64)
+        yc = y[r0:r1]
+        zy = (np.einsum("ij,ij->i", hc, W32[yc].astype(np.float64)) + b32[yc].astype(np.float64)) / tau
+        lse = zy - lp_gpu[r0:r1]
+        a_, b_ = oracle.grad_w_rows(hc, W32[vrows], b32[vrows], tau, yc, lse, g_ref[r0:r1], vrows)
+        gW_ref += a_
+        gb_ref += b_
+        if (r0 // step) % 16 == 15:
+            _say(f"cfg5: grad_W rows, {r1} tokens done ({time.time() - t_start:.0f} s)")
+    _grad_ok(out["grad_weight"][torch.from_numpy(vrows).to(dev)].float().cpu().numpy(), gW_ref, "grad_W rows")
+    _grad_ok(out["grad_bias"][torch.from_numpy(vrows).to(dev)].float().cpu().numpy(), gb_ref, "grad_b rows")
+
+    # ---- the whole batch in one outer chunk gives the same result ---------
+    _say(f"cfg5: fused, one chunk ({time.time() - t_start:.0f} s)")
     out1 = plp.fused_lmhead_policy_loss_fwd_bwd(h, Wt, yt, dev_tensor(comp), dev_tensor(adv), chunk_sequences=0,
                                                 **kw)
     torch.cuda.synchronize()
     assert abs(float(out1["loss"][0]) - float(out["loss"][0])) <= 1e-5
-    assert torch.equal(out1["dlogp"], out["dlogp"]) or float((out1["dlogp"] - out["dlogp"]).abs().max()) < 1e-9
+    assert float((out1["dlogp"] - out["dlogp"]).abs().max()) < 1e-9
     r = float((out1["grad_weight"].float() - out["grad_weight"].float()).norm() / out["grad_weight"].float().norm())
     assert r < 1e-2, r
+    _say(f"cfg5: done ({time.time() - t_start:.0f} s)")

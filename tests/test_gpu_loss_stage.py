@@ -33,6 +33,13 @@ def _say(msg):
     (1, 0.2, "normal"), (2, 0.5, "normal"), (1000, 0.2, "normal"), (4099, 0.8, "ties"),
     (65536, 0.2, "narrow"), (300001, 0.5, "normal"), (5000, 0.0, "ties"), (5000, 1.0, "normal"),
     (777, 0.37, "empty"), (3000, 0.2, "negative"),
+    # probabilities whose rank has a fraction that an fp32 multiply-add
+    # (instead of a rounded product) would change
+    (5003, 0.37, "normal"), (12345, 0.73, "negative"), (999, 0.91, "normal"),
+    # past torch.quantile's 2^24-entry cap (PR #1558 falls back to a sort):
+    # fp32(n - 1) rounds up to n, so the ranks are clamped
+    ((1 << 24) + 4, 0.0, "narrow_all"), ((1 << 24) + 4, 0.2, "narrow_all"),
+    ((1 << 24) + 20000, 0.2, "narrow_dense"),
 ])
 def test_entropy_quantile_mask(N, q, kind):
     import rl_policy_gradient_amd as plp
@@ -40,13 +47,21 @@ def test_entropy_quantile_mask(N, q, kind):
     r = np.random.default_rng(N + int(q * 100))
     if kind == "ties":
         H = (np.round(r.standard_normal(N) * 3) / 4 + 10).astype(np.float32)
-    elif kind == "narrow":
+    elif kind.startswith("narrow"):
         H = (11.75 + 0.01 * r.standard_normal(N)).astype(np.float32)
     elif kind == "negative":
         H = (r.standard_normal(N) * 1e-6).astype(np.float32)
     else:
         H = (r.standard_normal(N) * 2 + 8).astype(np.float32)
-    active = (r.uniform(size=N) < 0.85) if kind != "empty" else np.zeros(N, bool)
+    if kind == "empty":
+        active = np.zeros(N, bool)
+    elif kind == "narrow_all":
+        active = np.ones(N, bool)
+    elif kind == "narrow_dense":
+        active = r.uniform(size=N) < 0.9995
+        assert active.sum() > (1 << 24)
+    else:
+        active = r.uniform(size=N) < 0.85
     want_mask, want_thr = oracle.entropy_quantile_mask(H, active, q)
     mask, thr = plp.entropy_quantile_mask(dev_tensor(H), dev_tensor(active.astype(np.uint8)), q)
     torch.cuda.synchronize()
