@@ -29,7 +29,9 @@
  *   - All array pointers are DEVICE memory owned by the caller. The library
  *     allocates nothing, never frees or retains a pointer after it returns,
  *     and uses only the caller's workspace (size from the matching
- *     *_workspace_size query; the workspace must be 256-byte aligned).
+ *     *_workspace_size query; the workspace must be 256-byte aligned), except
+ *     plp_entropy_quantile_mask_noalloc, whose scratch is a static device
+ *     array of the library.
  *   - Calls only enqueue work on `stream`; outputs are valid once the stream
  *     has reached that point. Loss and metrics stay in device memory: no
  *     call synchronises with the host.
@@ -233,6 +235,22 @@ PLP_API int plp_entropy_quantile_mask_workspace_size(int64_t N, size_t* bytes);
 PLP_API int plp_entropy_quantile_mask(const float* entropy, const uint8_t* active, int64_t N, double q,
                                       uint8_t* mask_out, float* threshold_out, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream);
+
+/* The same mask without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Arguments, results and errors as for
+ * plp_entropy_quantile_mask. The select state (16.4 KB) lives in a static
+ * device array of 32 KB that the library holds on every device that runs the
+ * call until the process ends; its address is looked up once per device on
+ * the first call there. The call allocates nothing and enqueues on `stream`
+ * (on the stream's device). The scratch does not grow with N, so the largest
+ * input is the ABI's N < 2^31 (larger N: PLP_E_INVALID). Every call on one
+ * device shares that device's array and resets it first: calls that overlap
+ * on one device (concurrent streams, or threads) race and give wrong results.
+ * PLP_E_HIP when the stream's device or the array's address cannot be
+ * obtained. */
+PLP_API int plp_entropy_quantile_mask_noalloc(const float* entropy, const uint8_t* active, int64_t N, double q,
+                                              uint8_t* mask_out, float* threshold_out, hipStream_t stream);
 
 /* The loss stage alone, from given per-token log-probs (the GMPO / GSPO-token
  * / GRPO / BNPO / DAPO / K3 KL objective without the LM head). args: as for the fused

@@ -115,6 +115,7 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp, sz, _vp]
     L.plp_entropy_quantile_mask_workspace_size.argtypes = [ctypes.c_int64, P(sz)]
     L.plp_entropy_quantile_mask.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_double, _vp, _vp, _vp, sz, _vp]
+    L.plp_entropy_quantile_mask_noalloc.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_double, _vp, _vp, _vp]
     L.plp_policy_loss_workspace_size.argtypes = [P(PlpArgs), P(sz)]
     L.plp_policy_loss_from_logprobs.argtypes = [P(PlpArgs), _vp, _vp, P(PlpOutputs), _vp, sz, _vp]
     L.plp_profile_start.argtypes = [ctypes.c_int32]
@@ -123,6 +124,7 @@ def lib() -> ctypes.CDLL:
     L.plp_profile_stop.restype = ctypes.c_int
     for name in ("plp_workspace_size", "plp_fused_lmhead_policy_loss_fwd_bwd", "plp_selective_entropy_workspace_size",
                  "plp_selective_entropy", "plp_entropy_quantile_mask_workspace_size", "plp_entropy_quantile_mask",
+                 "plp_entropy_quantile_mask_noalloc",
                  "plp_policy_loss_workspace_size", "plp_policy_loss_from_logprobs"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L

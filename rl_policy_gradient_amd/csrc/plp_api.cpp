@@ -310,6 +310,63 @@ int forward_rows(const plp_args* a, const Plan& p, Bufs& b, int64_t r0, int64_t 
   return PLP_OK;
 }
 
+int check_quantile_args(const float* entropy, const uint8_t* active, int64_t N, double q, const uint8_t* mask_out) {
+  if (!(q >= 0.0 && q <= 1.0)) return fail(PLP_E_INVALID, "q must lie in [0, 1] (got %g)", q);
+  if (N > 0 && (!entropy || !active || !mask_out)) return fail(PLP_E_INVALID, "entropy, active and mask_out are required");
+  return PLP_OK;
+}
+
+// The batch-global mask with the select state in `sel` (whose contents the
+// first kernel resets).
+int quantile_mask(const float* entropy, const uint8_t* active, int64_t N, double q, uint8_t* mask_out,
+                  float* threshold_out, SelectState* sel, hipStream_t st) {
+  if (q == 1.0) {
+    if (N > 0) HIP_TRY(launch_copy_mask(active, N, mask_out, st));
+    if (threshold_out) HIP_TRY(launch_set_nan(threshold_out, st));
+    return ok();
+  }
+  HIP_TRY(launch_entropy_select(entropy, active, N, (float)(1.0 - q), sel, st));
+  if (N > 0) HIP_TRY(launch_entropy_mask(entropy, active, N, &sel->thr, mask_out, st));
+  if (threshold_out) HIP_TRY(launch_store_thr(&sel->thr, threshold_out, st));
+  return ok();
+}
+
+// Scratch of plp_entropy_quantile_mask_noalloc: the radix select's state in a
+// device array rather than a workspace. Every device that runs the call holds
+// its own copy until the process ends. On the host the array's name is only
+// a stand-in for the symbol: its device address is taken once per device
+// with hipGetSymbolAddress (with that device current) and only that address
+// is handed to kernels.
+constexpr size_t kStaticScratchBytes = 32768;
+static_assert(sizeof(SelectState) <= kStaticScratchBytes, "the select state fits the static scratch");
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PLP_E_UNSUPPORTED, "device %d: the static scratch is kept for devices 0-%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    HIP_TRY(hipGetDevice(&cur));
+    if (cur != dev) HIP_TRY(hipSetDevice(dev));
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) return fail(PLP_E_HIP, "hipSetDevice: %s", hipGetErrorString(e2));
+    }
+    if (e != hipSuccess) return fail(PLP_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    if (p == nullptr) return fail(PLP_E_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PLP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -531,20 +588,25 @@ PLP_API int plp_entropy_quantile_mask(const float* entropy, const uint8_t* activ
   size_t need = 0;
   int rc = plp_entropy_quantile_mask_workspace_size(N, &need);
   if (rc) return rc;
-  if (!(q >= 0.0 && q <= 1.0)) return fail(PLP_E_INVALID, "q must lie in [0, 1] (got %g)", q);
-  if (N > 0 && (!entropy || !active || !mask_out)) return fail(PLP_E_INVALID, "entropy, active and mask_out are required");
+  rc = check_quantile_args(entropy, active, N, q, mask_out);
+  if (rc) return rc;
   rc = check_ws(ws, ws_bytes, need);
   if (rc) return rc;
-  SelectState* sel = (SelectState*)ws;
-  if (q == 1.0) {
-    if (N > 0) HIP_TRY(launch_copy_mask(active, N, mask_out, st));
-    if (threshold_out) HIP_TRY(launch_set_nan(threshold_out, st));
-    return ok();
-  }
-  HIP_TRY(launch_entropy_select(entropy, active, N, (float)(1.0 - q), sel, st));
-  if (N > 0) HIP_TRY(launch_entropy_mask(entropy, active, N, &sel->thr, mask_out, st));
-  if (threshold_out) HIP_TRY(launch_store_thr(&sel->thr, threshold_out, st));
-  return ok();
+  return quantile_mask(entropy, active, N, q, mask_out, threshold_out, (SelectState*)ws, st);
+}
+
+PLP_API int plp_entropy_quantile_mask_noalloc(const float* entropy, const uint8_t* active, int64_t N, double q,
+                                              uint8_t* mask_out, float* threshold_out, hipStream_t st) {
+  if (N < 0 || N >= kMaxRows)
+    return fail(PLP_E_INVALID, "N=%lld outside [0, 2^31), the largest input of the static scratch", (long long)N);
+  int rc = check_quantile_args(entropy, active, N, q, mask_out);
+  if (rc) return rc;
+  int dev = 0;
+  HIP_TRY(hipStreamGetDevice(st, &dev));
+  void* sel = nullptr;
+  rc = static_scratch(dev, &sel);
+  if (rc) return rc;
+  return quantile_mask(entropy, active, N, q, mask_out, threshold_out, (SelectState*)sel, st);
 }
 
 PLP_API int plp_policy_loss_workspace_size(const plp_args* a, size_t* bytes) {

@@ -166,3 +166,14 @@ def test_other_entry_points_validate():
     a = _valid_args()
     assert L.plp_policy_loss_from_logprobs(ctypes.byref(a), None, None, None, None, 0, None) == abi.PLP_E_INVALID
     assert L.plp_abi_version() == 3
+
+
+def test_noalloc_quantile_rejects_bad_arguments_on_the_host():
+    """The no-allocation entry point checks its arguments before touching the
+    device: N outside [0, 2^31), q outside [0, 1], missing pointers."""
+    L = _lib()
+    assert L.plp_entropy_quantile_mask_noalloc(None, None, -1, 0.5, None, None, None) == abi.PLP_E_INVALID
+    assert L.plp_entropy_quantile_mask_noalloc(None, None, 1 << 31, 0.5, None, None, None) == abi.PLP_E_INVALID
+    assert b"2^31" in L.plp_last_error()
+    assert L.plp_entropy_quantile_mask_noalloc(None, None, 10, 1.5, None, None, None) == abi.PLP_E_INVALID
+    assert L.plp_entropy_quantile_mask_noalloc(None, None, 10, 0.5, None, None, None) == abi.PLP_E_INVALID
