@@ -77,6 +77,20 @@ struct LossParams {
   int kl_bc;           // KL term weighted by the token importance ratio
 };
 
+// Vocabulary splits of the forward sweep over `rows` token rows: the
+// smallest power of two (at most max_splits, every split keeping at least
+// one 32-row tile) for which row blocks x splits fill the 256 compute units,
+// trimmed to the splits that hold tiles. Evaluated on the host for a known
+// row count and in the kernels for a row count that lives on the device.
+__host__ __device__ inline int forward_splits(int64_t rows, int V, int max_splits) {
+  const int64_t nrb = (rows + 63) / 64;
+  const int n_tiles = (V + 31) / 32;
+  int sv = 1;
+  while ((int64_t)sv * nrb < 256 && sv < max_splits && sv * 2 <= n_tiles) sv *= 2;
+  const int tps = (n_tiles + sv - 1) / sv;
+  return (n_tiles + tps - 1) / tps;
+}
+
 // Token-level clipped losses (GRPO, BNPO, DAPO) share the per-token path.
 __host__ __device__ inline bool token_clip_loss(int loss_type) { return loss_type >= 2; }
 // Losses whose divisor is a token count rather than per-sample.
@@ -93,9 +107,21 @@ hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_de
                             __bf16* Xf, hipStream_t st);
 
 // Forward sweep on MFMA (bf16, H a multiple of 128, H <= 896); Wf is the
-// fragment-major copy of W.
+// fragment-major copy of W. With count_dev (the grad_h accumulator pass over
+// a compacted row list, with_o only) the sweep runs over the first
+// *count_dev rows of h (N is their capacity) with forward_splits(*count_dev,
+// V, Sv) splits, and stats / O use the row stride compact_stride(*count_dev).
 hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
-                           int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st);
+                           int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st,
+                           const int* count_dev = nullptr);
+// Row stride of the compacted pass's stats and O (whole 64-row blocks).
+__host__ __device__ inline int64_t compact_stride(int64_t rows) { return (rows + 63) / 64 * 64; }
+// grad_h of the compacted rows k < *count_dev from the compacted pass:
+// grad_h[idx[k]] = tok[k].gs (W_y - O/s) with y = tok[k].y (flagged rows
+// recomputed exactly from h row idx[k]); the other rows are left as they are.
+hipError_t launch_grad_h_compact(int dtype, const RowStats* stats, const float* O, int max_splits, int64_t cap, int H,
+                                 int V, const void* h, const void* W, const void* b, float inv_tau, const int* idx,
+                                 const TokData* tok, const int* count_dev, void* gh, hipStream_t st);
 
 // Weight-gradient sweep on MFMA over the compacted tokens (hcf and Wf are
 // fragment-major).

@@ -233,12 +233,26 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
 // P is double buffered (P(t+1) is written while P KV(t) still reads P(t)),
 // and so are the staged tiles. The statistics are bit-identical to the
 // statistics-only kernel's: every sum runs in the same order.
+//
+// With count_dev the rows are the first *count_dev rows of h (compacted
+// tokens), the splits forward_splits(*count_dev, V, Sv) and the row stride of
+// stats and O compact_stride(*count_dev); workgroups past the last block
+// exit at once.
 template <int KB, bool HAS_BIAS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, const __bf16* __restrict__ bias,
-                   int64_t N, int V, float inv_tau, int Sv, int tiles_per_split, RowStats* __restrict__ stats,
-                   float* __restrict__ O) {
+                   int64_t N_, int V, float inv_tau, int Sv_, int tiles_per_split_, RowStats* __restrict__ stats,
+                   float* __restrict__ O, const int* __restrict__ count_dev) {
   constexpr int H = 128 * KB;
+  int64_t N = N_, stride = N_;
+  int Sv = Sv_, tiles_per_split = tiles_per_split_;
+  if (count_dev) {
+    N = *count_dev;
+    Sv = forward_splits(N, V, Sv_);
+    tiles_per_split = ((V + BK - 1) / BK + Sv - 1) / Sv;
+    stride = compact_stride(N);
+    if ((int64_t)blockIdx.x >= stride / BQ * Sv) return;  // uniform: no rows for this workgroup
+  }
   constexpr int DS = Stage<KB>::DS;
   constexpr int TS = Stage<KB>::TS;
   constexpr int KS = DS / 16;
@@ -427,7 +441,7 @@ void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, 
       rs.sz = (szx + s_xd[(2 * (w ^ 2) + 1) * 64 + c]) * kLn2;
       rs.flag = (fl | __float_as_int(s_x[(w ^ 2) * 64 + c])) ? 1 : 0;
       rs.pad = 0;
-      stats[(int64_t)sv * N + my_row] = rs;
+      stats[(int64_t)sv * stride + my_row] = rs;
     }
   } else {
     // ======================= PV role =======================
@@ -475,7 +489,7 @@ void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, 
     }
     __syncthreads();  // R0
     __syncthreads();  // R1
-    float* Ob = O + (int64_t)sv * N * H;
+    float* Ob = O + (int64_t)sv * stride * H;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -492,15 +506,19 @@ void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, 
 
 template <bool HAS_BIAS>
 hipError_t fwd_pp_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
-                         int Sv, RowStats* stats, float* O, hipStream_t st) {
+                         int Sv, RowStats* stats, float* O, const int* count_dev, hipStream_t st) {
   const int n_tiles = (V + BK - 1) / BK;
   const int tps = (n_tiles + Sv - 1) / Sv;
   const int64_t nrb = (N + BQ - 1) / BQ;
-  const dim3 grid((unsigned)(nrb * Sv)), block(512);
+  // with a device row count, enough workgroups for any count up to N: row
+  // blocks x splits stays below 512 while the splits are above one
+  const int64_t wgs = count_dev ? (nrb > 512 ? nrb : 512) : nrb * Sv;
+  const dim3 grid((unsigned)wgs), block(512);
   switch (H / 128) {
-#define PLP_PP_CASE(K)                                                                                               \
-  case K:                                                                                                            \
-    hipLaunchKernelGGL((fwd_pp_kernel<K, HAS_BIAS>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats, O); \
+#define PLP_PP_CASE(K)                                                                                                \
+  case K:                                                                                                             \
+    hipLaunchKernelGGL((fwd_pp_kernel<K, HAS_BIAS>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats, O,  \
+                       count_dev);                                                                                    \
     break;
     PLP_PP_CASE(1)
     PLP_PP_CASE(2)
@@ -547,6 +565,6 @@ hipError_t fwd_stats_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, 
 // The variants with the grad_h accumulator (two-role form), from
 // lmhead_fwd_o.hip; b may be NULL.
 hipError_t launch_fwd_mfma_o(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
-                             int Sv, RowStats* stats, float* O, hipStream_t st);
+                             int Sv, RowStats* stats, float* O, const int* count_dev, hipStream_t st);
 
 }  // namespace plp

@@ -199,6 +199,73 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
   }
 }
 
+
+// grad_h of the compacted rows k < *count_dev after the accumulator pass over
+// them (stats and O with the row stride compact_stride(count) and
+// forward_splits(count, V, max_splits) splits): the split merge of the
+// accumulator as in combine_kernel, v = W_y - O/s, and
+// grad_h[idx[k]] = (g_k / tau) v with g_k / tau = tok[k].gs and y = tok[k].y.
+// A row any split flagged is recomputed exactly from h row idx[k].
+template <typename T>
+__global__ __launch_bounds__(NT) void grad_h_compact_kernel(const RowStats* __restrict__ stats,
+                                                            const float* __restrict__ O, int max_splits, int H, int V,
+                                                            const T* __restrict__ h, const T* __restrict__ W,
+                                                            const T* __restrict__ b, float inv_tau,
+                                                            const int* __restrict__ idx,
+                                                            const TokData* __restrict__ tok,
+                                                            const int* __restrict__ count_dev, T* __restrict__ gh) {
+  extern __shared__ float sm[];
+  const int64_t n = *count_dev;
+  const int64_t k = blockIdx.x;
+  if (k >= n) return;  // uniform
+  const int Sv = forward_splits(n, V, max_splits);
+  const int64_t stride = compact_stride(n);
+  __shared__ double s_c[64];
+  __shared__ double s_res[2];
+  __shared__ int s_flag;
+  const int64_t src = idx[k];
+  const TokData td = tok[k];
+  const int64_t yc = td.y < 0 ? 0 : (td.y >= V ? V - 1 : td.y);
+  if (threadIdx.x < 64) {
+    const int j = threadIdx.x;
+    const bool have = j < Sv;
+    RowStats rs;
+    if (have) rs = stats[(int64_t)j * stride + k];
+    int f = have ? rs.flag : 0;
+    float M = have ? rs.m : -INFINITY;
+    for (int o = 32; o > 0; o >>= 1) {
+      M = fmaxf(M, __shfl_xor(M, o, 64));
+      f |= __shfl_xor(f, o, 64);
+    }
+    const double c = (have && rs.s > 0.0) ? exp((double)rs.m - (double)M) : 0.0;
+    double cs = have ? c * rs.s : 0.0;
+    for (int o = 32; o > 0; o >>= 1) cs += __shfl_xor(cs, o, 64);
+    s_c[j] = c;
+    if (j == 0) {
+      s_flag = f;
+      s_res[0] = 1.0 / cs;
+    }
+  }
+  __syncthreads();
+  const float gs = td.gs;
+  T* out = gh + src * H;
+  if (s_flag) {
+    const RowResult r = row_exact<T>(h + src * H, W, b, td.y, H, V, inv_tau, true, sm);
+    const float* os = sm + H;
+    const double inv_s = 1.0 / r.s;
+    for (int d = threadIdx.x; d < H; d += NT)
+      out[d] = (T)(gs * (float)((double)ldf<T>(W, yc * H + d) - (double)os[d] * inv_s));
+    return;
+  }
+  const double inv_s = s_res[0];
+  const float* Orow = O + k * H;
+  const int64_t sstride = stride * H;
+  for (int d = threadIdx.x; d < H; d += NT) {
+    double o = 0.0;
+    for (int j = 0; j < Sv; ++j) o += s_c[j] * (double)Orow[j * sstride + d];
+    out[d] = (T)(gs * (float)((double)ldf<T>(W, yc * H + d) - o * inv_s));
+  }
+}
 // ---------------------------------------------------------------------------
 // Loss stage
 // ---------------------------------------------------------------------------
@@ -522,6 +589,13 @@ __global__ __launch_bounds__(NT) void token_kernel(LossParams p, int64_t Nc, con
   const int rows = (int)min((int64_t)TB, Nc - t0);
   const int HS = gridDim.y, Hs = H / HS, c0 = blockIdx.y * Hs;  // the launcher makes Hs a multiple of 4
   const int64_t base = t0 * H + c0;
+  if (v == nullptr) {  // uniform: grad_h of the rows with g != 0 comes later (compacted pass); zeros here
+    for (int e = threadIdx.x; e < rows * Hs; e += NT) {
+      const int r = e / Hs, col = e - r * Hs;
+      gh[base + (int64_t)r * H + col] = (T)0.f;
+    }
+    return;
+  }
   if ((Hs & 3) == 0) {
     for (int e = threadIdx.x * 4; e < rows * Hs; e += NT * 4) {
       const int r = e / Hs, col = e - r * Hs;
@@ -857,6 +931,22 @@ hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int 
       hipLaunchKernelGGL((combine_kernel<__bf16, false>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H,
                          V, hh, WW, bb, inv_tau, y, lp, ent, lse, vout);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_h_compact(int dtype, const RowStats* stats, const float* O, int max_splits, int64_t cap, int H,
+                                 int V, const void* h, const void* W, const void* b, float inv_tau, const int* idx,
+                                 const TokData* tok, const int* count_dev, void* gh, hipStream_t st) {
+  if (cap <= 0) return hipSuccess;
+  const size_t lds = row_exact_smem_bytes(H);
+  if (dtype == 0)
+    hipLaunchKernelGGL((grad_h_compact_kernel<float>), dim3((unsigned)cap), dim3(NT), lds, st, stats, O, max_splits,
+                       H, V, (const float*)h, (const float*)W, (const float*)b, inv_tau, idx, tok, count_dev,
+                       (float*)gh);
+  else
+    hipLaunchKernelGGL((grad_h_compact_kernel<__bf16>), dim3((unsigned)cap), dim3(NT), lds, st, stats, O, max_splits,
+                       H, V, (const __bf16*)h, (const __bf16*)W, (const __bf16*)b, inv_tau, idx, tok, count_dev,
+                       (__bf16*)gh);
   return hipGetLastError();
 }
 

@@ -95,6 +95,10 @@ struct Plan {
   int Sv = 1, St = 1;
   bool entropy = false;        // q < 1
   bool prepass = false;        // q < 1 with several chunks: stats-only pass first
+  // q < 1 on the matrix cores with grad_h: statistics-only pass over every
+  // row, then the grad_h accumulator pass over the compacted rows with g != 0
+  bool o_compact = false;
+  int64_t o2_rows = 0;         // row capacity of the compacted pass's stats / O (all splits)
 };
 
 struct Bufs {
@@ -118,6 +122,9 @@ struct Bufs {
   float* tail = nullptr;       // partial sums of the weight-gradient sweep's split tail blocks
   float* gW_acc = nullptr;
   float* gb_acc = nullptr;
+  RowStats* stats2 = nullptr;  // compacted accumulator pass (o_compact)
+  float* O2 = nullptr;
+  void* hcn = nullptr;         // its gathered hidden rows, natural layout
 };
 
 Plan make_plan(const plp_args* a, bool need_o, bool need_gw, bool need_gb) {
@@ -137,7 +144,10 @@ Plan make_plan(const plp_args* a, bool need_o, bool need_gw, bool need_gb) {
   p.St = (int)std::min<int64_t>(64, (p.T + 2047) / 2048);
   if (p.St < 1) p.St = 1;
   p.entropy = a->top_entropy_quantile < 1.0;
-  p.prepass = p.entropy && p.nchunks > 1;
+  p.o_compact = p.entropy && p.mfma && p.need_o;
+  p.prepass = p.entropy && (p.nchunks > 1 || p.o_compact);
+  // splits x row blocks < 512 while the splits are above one (forward_splits)
+  p.o2_rows = std::max<int64_t>(512 * kBQ, round_up(p.Nc, kBQ));
   return p;
 }
 
@@ -146,7 +156,11 @@ size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
   const int H = a->H, V = a->V;
   if (p.mfma) b.Wf = c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H);
   b.stats = c.take<RowStats>((size_t)p.Sv * p.Nc);
-  if (p.need_o) {
+  if (p.o_compact) {
+    b.stats2 = c.take<RowStats>((size_t)p.o2_rows);
+    b.O2 = c.take<float>((size_t)p.o2_rows * H);
+    b.hcn = c.take<char>((size_t)p.cap * H * esize(a->dtype));
+  } else if (p.need_o) {
     b.O = c.take<float>((size_t)p.Sv * p.Nc * H);
     b.v = p.Sv == 1 ? b.O : c.take<float>((size_t)p.Nc * H);
   }
@@ -160,11 +174,13 @@ size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
   b.acc = c.take<LossAcc>(1);
   b.sel = c.take<SelectState>(1);
   b.ntok = c.take<unsigned long long>(1);
-  if (p.need_gw) {
+  if (p.need_gw || p.o_compact) {
     b.idx = c.take<int>(p.cap);
     b.tok = c.take<TokData>(p.cap);
     b.count = c.take<int>(1);
     b.cscratch = c.take<char>(compact_scratch_bytes(p.Nc));
+  }
+  if (p.need_gw) {
     b.hc = c.take<char>((size_t)p.cap * H * esize(a->dtype));
     if (p.mfma) b.tail = c.take<float>(bwd_tail_scratch_floats(H));
     if (p.nchunks > 1) {
@@ -464,7 +480,7 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
 
   bool first_chunk_done = false;
   if (p.entropy) {
-    if (p.nchunks == 1) {
+    if (!p.prepass) {
       rc = forward_rows(a, p, b, 0, p.N, p.need_o, st);
       if (rc) return rc;
       first_chunk_done = true;
@@ -483,7 +499,11 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
   for (int64_t c = 0; c < p.nchunks; ++c) {
     const int64_t s0 = c * p.Bc, bc = std::min(p.Bc, p.B - s0);
     const int64_t r0 = s0 * p.T, n = bc * p.T;
-    if (!(c == 0 && first_chunk_done)) {
+    // the statistics of every row are in place after the q < 1 passes; the
+    // forward runs here for q = 1, and for q < 1 only to accumulate grad_h
+    // over whole chunks (the generic path with several chunks)
+    const bool fwd_here = !p.entropy || (p.need_o && !p.o_compact && !(c == 0 && first_chunk_done));
+    if (fwd_here) {
       rc = forward_rows(a, p, b, r0, n, p.need_o, st);
       if (rc) return rc;
     }
@@ -499,13 +519,26 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
     HIP_TRY(launch_loss_seq_final(lpar, bc, p.St, b.part, adv, b.coef, b.acc, c == 0, p.entropy ? &b.sel->thr : nullptr,
                                   last ? out->loss : nullptr, last ? out->metrics : nullptr, st));
     float* g = out->dlogp_out ? out->dlogp_out + r0 : b.g;
-    int* cnt32 = p.need_gw ? (int*)b.cscratch : nullptr;
+    int* cnt32 = (p.need_gw || p.o_compact) ? (int*)b.cscratch : nullptr;
+    char* gh = p.need_o ? (char*)out->grad_hidden + (size_t)r0 * H * es : nullptr;
+    // with the compacted accumulator pass the token kernel writes zero rows
+    // and the rows with g != 0 are written after that pass
     HIP_TRY(launch_loss_tokens(a->dtype, lpar, bc, b.lp + r0, old, ref, comp, ratio, em, tadv, b.coef, g, cnt32,
-                               p.need_o ? b.v : nullptr, H, inv_tau,
-                               p.need_o ? (char*)out->grad_hidden + (size_t)r0 * H * es : nullptr, st));
-    if (p.need_gw) {
+                               p.need_o && !p.o_compact ? b.v : nullptr, H, inv_tau, gh, st));
+    const char* hsrc = (const char*)a->hidden + (size_t)r0 * H * es;
+    if (p.need_gw || p.o_compact)
       HIP_TRY(launch_compact_scatter(g, b.lse + r0, a->targets + r0, n, inv_tau, cnt32, b.idx, b.tok, b.count, st));
-      const char* hsrc = (const char*)a->hidden + (size_t)r0 * H * es;
+    if (p.o_compact) {
+      HIP_TRY(launch_gather_rows(a->dtype, hsrc, b.idx, b.count, p.cap, H, b.hcn, st));
+      hipEvent_t* ev = prof_slot(0);
+      if (ev) HIP_TRY(hipEventRecord(ev[0], st));
+      HIP_TRY(launch_fwd_mfma((const __bf16*)b.hcn, b.Wf, (const __bf16*)a->bias, p.cap, H, V, inv_tau, kMaxSplits,
+                              true, b.stats2, b.O2, st, b.count));
+      if (ev) HIP_TRY(hipEventRecord(ev[1], st));
+      HIP_TRY(launch_grad_h_compact(a->dtype, b.stats2, b.O2, kMaxSplits, p.cap, H, V, hsrc, a->weight, a->bias,
+                                    inv_tau, b.idx, b.tok, b.count, gh, st));
+    }
+    if (p.need_gw) {
       if (p.mfma)
         HIP_TRY(launch_frag_copy((const __bf16*)hsrc, b.idx, b.count, n, p.cap / kBK, H, (__bf16*)b.hc, st));
       else

@@ -175,12 +175,14 @@ def test_fused_bnpo_chunk_invariance():
         assert rel_l2(o["grad_hidden"], outs[0]["grad_hidden"]) < 1e-2
 
 
-def test_fused_flagged_rows_recomputed():
+@pytest.mark.parametrize("q", [1.0, 0.5])
+def test_fused_flagged_rows_recomputed(q):
     """Logits far above the first vocabulary tile's max (bias -100 on the first
     tile, +60 further on) make the MFMA sweep flag the rows; the merge
-    recomputes them exactly."""
-    spec = synth.small("flagged", cfg_id=108, B=2, T=40, H=128, V=1000, bias=True)
-    _say("flagged rows")
+    recomputes them exactly. With q < 1 the grad_h accumulator runs as its own
+    pass over the rows with a gradient, whose merge recomputes them too."""
+    spec = synth.small("flagged", cfg_id=108, B=2, T=40, H=128, V=1000, bias=True, top_entropy_quantile=q)
+    _say(f"flagged rows q={q}")
     d = synth.make(spec)
     b = d["b"].copy()
     b[:32] = -100.0
