@@ -141,6 +141,36 @@ def _cpu_baseline(spec) -> dict:
                       f"fp64 forward+loss+backward in {dt:.2f} s"}
 
 
+def _cpu_baseline_full(cfg: int) -> dict:
+    """The fp64 oracle, as it stands, on a whole workload (forward, loss and
+    backward over every token, all host cores); the long-run companion of
+    the bounded sample timed beside each GPU measurement."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    spec = synth.CONFIGS[cfg]
+    d = synth.make(spec)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    fwd = oracle.forward_rows(d["h"], d["W"], d["b"], spec.temperature, d["targets"])
+    t1 = time.perf_counter()
+    old = synth.compose_logp(fwd["logp"], d["old_noise"])
+    ref = synth.compose_logp(fwd["logp"], d["ref_noise"])
+    out = oracle.run(oracle.LossConfig.from_spec(spec), d["h"], d["W"], d["b"], d["targets"], old, ref,
+                     d["completion_mask"], None, d["advantages"], fwd=fwd)
+    t2 = time.perf_counter()
+    assert np.isfinite(out["loss"])
+    return {"workload": spec.name, "tokens": spec.N, "cores": int(cores), "kind": "oracle",
+            "forward_s": round(t1 - t0, 2), "loss_and_backward_s": round(t2 - t1, 2),
+            "total_s": round(t2 - t0, 2), "tokens_per_s": round(spec.N / (t2 - t0), 3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,7 +182,16 @@ def main() -> int:
     ap.add_argument("--token-advantages", action="store_true")
     ap.add_argument("--kl-bias-correction", action="store_true",
                     help="K3 KL weighted by the token importance ratio (workloads with a KL term)")
+    ap.add_argument("--cpu-baseline-full", action="store_true",
+                    help="only time the CPU oracle on the whole workload (--config 2, 3 or 4; no GPU)")
     args = ap.parse_args()
+    if args.cpu_baseline_full:
+        if args.config == 5:
+            print("the whole 4.19M-token workload takes the oracle hours: its time is the sample rate "
+                  "extrapolated (cpu_baseline.extrapolated_full_workload_s)", file=sys.stderr)
+            return 2
+        print(json.dumps(_cpu_baseline_full(args.config)), flush=True)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: there is no multi-GPU path (asked for --gpus {args.gpus}); "
               "the path shards by whole sequences, each GPU running this call on its own share",
