@@ -141,6 +141,65 @@ def _cpu_baseline(spec) -> dict:
                       f"fp64 forward+loss+backward in {dt:.2f} s"}
 
 
+def _memory_sweep(dev) -> int:
+    """Peak device memory of one fused call (GMPO, bf16, H=896, grads of h
+    and W) beyond its inputs, over vocabulary sizes and token counts: the
+    caching allocator's peak during the call minus what was allocated before
+    it (workspace + outputs), beside the bytes a materialised [N, V] bf16
+    logit tensor would take. One JSON line per shape."""
+    import torch
+
+    import rl_policy_gradient_amd as plp
+
+    H = 896
+    for V in (32000, 65536, 151936):
+        for N in (512, 4096, 32768):
+            B, T = max(1, N // 4096), min(N, 4096)
+            g = torch.Generator(device=dev)
+            g.manual_seed(N + V)
+            h = torch.randn(N, H, generator=g, device=dev).to(torch.bfloat16)
+            W = (torch.randn(V, H, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+            y = torch.randint(0, V, (N,), generator=g, device=dev)
+            comp = torch.ones(N, dtype=torch.uint8, device=dev)
+            adv = torch.randn(B, generator=g, device=dev)
+            torch.cuda.synchronize()
+            before = torch.cuda.memory_allocated(dev)
+            torch.cuda.reset_peak_memory_stats(dev)
+            out = plp.fused_lmhead_policy_loss_fwd_bwd(h, W, y, comp, adv, B=B, T=T, epsilon_low=0.4,
+                                                       epsilon_high=0.4)
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated(dev) - before
+            ws = plp.workspace_size(B, T, H, V)
+            print(json.dumps({"V": V, "N": N, "H": H, "peak_bytes_beyond_inputs": int(peak), "workspace_bytes": int(ws),
+                              "outputs_bytes": int(N * H * 2 + V * H * 2 + 8 + 32),
+                              "materialised_bf16_logits_bytes": int(N * V * 2)}), flush=True)
+            del out, h, W, y, comp, adv
+            torch.cuda.empty_cache()
+    return 0
+
+
+def _flagged_rows(h, W, b, spec) -> int:
+    """Rows the forward sweep flags for the exact recompute: in some
+    vocabulary split a logit exceeds the max of the split's first 32-row tile
+    by more than 64 (the sweep's exponent reference slack). Computed here
+    from the logits with torch, split by split as the sweep walks them."""
+    import torch
+
+    z = (h.float() @ W.float().T + b.float()[None, :]) / spec.temperature
+    n_tiles = -(-spec.V // 32)
+    nrb = -(-spec.N // 64)
+    sv = 1
+    while sv * nrb < 256 and sv < 64 and sv * 2 <= n_tiles:
+        sv *= 2
+    tps = -(-n_tiles // sv)
+    flag = torch.zeros(spec.N, dtype=torch.bool, device=z.device)
+    for s0 in range(0, n_tiles, tps):
+        v0, v1 = 32 * s0, min(spec.V, 32 * (s0 + tps))
+        ref = z[:, v0:min(v1, v0 + 32)].max(dim=1).values
+        flag |= z[:, v0:v1].max(dim=1).values > ref + 64.0
+    return int(flag.sum().item())
+
+
 def _cpu_baseline_full(cfg: int) -> dict:
     """The fp64 oracle, as it stands, on a whole workload (forward, loss and
     backward over every token, all host cores); the long-run companion of
@@ -182,6 +241,11 @@ def main() -> int:
     ap.add_argument("--token-advantages", action="store_true")
     ap.add_argument("--kl-bias-correction", action="store_true",
                     help="K3 KL weighted by the token importance ratio (workloads with a KL term)")
+    ap.add_argument("--memory-sweep", action="store_true",
+                    help="peak device memory of one fused call over vocabulary sizes and token counts (one line each)")
+    ap.add_argument("--bias-std", type=float, default=None,
+                    help="--config 2 with a bias ~ N(0, S^2): logits far above a vocabulary split's first tile "
+                         "make the sweep flag rows for the exact recompute; reports how many")
     ap.add_argument("--cpu-baseline-full", action="store_true",
                     help="only time the CPU oracle on the whole workload (--config 2, 3 or 4; no GPU)")
     args = ap.parse_args()
@@ -206,7 +270,23 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.memory_sweep:
+        return _memory_sweep(dev)
     spec, inp = _workload(args.config, dev)
+    flagged = None
+    if args.bias_std is not None:
+        if args.config != 2:
+            print("--bias-std is for --config 2", file=sys.stderr)
+            return 2
+        g = torch.Generator(device=dev)
+        g.manual_seed(77)
+        b = (torch.randn(spec.V, generator=g, device=dev) * args.bias_std).to(torch.bfloat16)
+        inp["bias"] = b
+        spec = spec.replace(bias=True, name=f"{spec.name}_bias_std{args.bias_std:g}")
+        flagged = _flagged_rows(inp["hidden"], inp["weight"], b, spec)
+        _, lp = plp.selective_entropy(inp["hidden"], inp["weight"], b, inp["targets"])
+        inp["old_logp"] = (lp.double() + torch.randn(spec.N, generator=g, device=dev, dtype=torch.float64)
+                           * spec.old_noise_std).float().contiguous()
     N, H, V = spec.N, spec.H, spec.V
     variant = ""
     if args.loss and args.loss != spec.loss_type:
@@ -342,6 +422,8 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if flagged is not None:
+        line["config"]["flagged_rows"] = flagged
     if not args.no_cpu_baseline and tadv is None:
         cb = _cpu_baseline(spec)
         # the whole workload at the sample's rate (not run: extrapolated)

@@ -14,6 +14,12 @@
         HBM bytes per launch of one kernel: FETCH_SIZE and WRITE_SIZE (KiB per
         dispatch) averaged over its dispatches, each scaled by the factor the
         same counter shows on the plain copy.
+    python -m rl_policy_gradient_amd.profsum hbm TRACE_CSV --rows N --active NA --H H --V V --splits S
+            --chunks C [--entropy] --workload W [--fetch CSV --write CSV --copy-fetch CSV
+            --copy-write CSV] --out TXT --command "..."
+        the memory-bound kernels' algorithmic bytes per launch over their
+        average duration (GB/s and fraction of 8 TB/s), with the counters'
+        traffic beside them when the --pmc CSVs are given.
     python -m rl_policy_gradient_amd.profsum pmc PMC_CSV --match A,B --command "..."
         per-dispatch averages of every counter in a ``--pmc`` CSV for the
         kernels whose names contain A, B, ..., with the matrix-core and LDS
@@ -211,6 +217,114 @@ def cmd_traffic(args) -> int:
     return 0
 
 
+def small_kernel_bytes(wl: dict) -> dict:
+    """Algorithmic HBM bytes per launch of the memory-bound kernels of one
+    fused call (bf16 hidden states and weights, fp32 per-token arrays), for
+    a workload of `chunks` outer chunks of n rows, na of them with a
+    gradient, H, V, Sv vocabulary splits of the forward sweep, an optional
+    bias and q < 1 (statistics-only forward, then the grad_h accumulator
+    over the na rows). Each value reads and writes every byte the kernel
+    must move once; the bf16 element is 2 bytes, fp32 4."""
+    n, na, H, V, Sv = wl["n"], wl["na"], wl["H"], wl["V"], wl["Sv"]
+    q = wl["entropy"]
+    nblk = -(-V // 64)
+    rem = nblk % 256
+    parts = min(4, 256 // rem) if rem else 1
+    out = {
+        # split statistics, the accumulator splits and v (with grad_h in the
+        # forward), the row of h and the target row of W for the target logit;
+        # lp, entropy and lse out
+        "combine_kernel": Sv * n * 32 + Sv * n * H * 4 + n * H * 4 + 2 * n * H * 2 + 12 * n,
+        "combine_kernel (statistics only)": Sv * n * 32 + 2 * n * H * 2 + 12 * n,
+        # per-token inputs, g out; grad_h = g / tau v in bf16 (zeros when the
+        # accumulator pass runs over the compacted rows)
+        "token_kernel": 18 * n + (n * H * 2 if q else n * H * 4 + n * H * 2),
+        "compact_scatter_kernel": 16 * n + 20 * na,
+        # the fragment-major copy of W (once per call; rows padded to 64) and
+        # of the gathered rows with a gradient (once per chunk)
+        "frag_copy_kernel (W)": 2 * (-(-V // 64) * 64) * H * 2,
+        "frag_copy_kernel (gathered rows)": 2 * na * H * 2,
+        # parts fp32 partial sums of the shared tail blocks in, grad_W rows out
+        "tail_reduce_kernel": rem * 64 * H * 4 * parts + rem * 64 * H * 2 if parts > 1 else 0,
+        "select_hist_kernel": 5 * wl["N"],
+        "mask_kernel": 6 * wl["N"],
+        "grad_h_compact_kernel": na * (H * 4 + H * 2 + H * 2 + 32),
+        "gather_rows_kernel": 2 * na * H * 2,
+    }
+    return out
+
+
+def cmd_hbm(args) -> int:
+    wl = {"n": args.rows, "na": args.active, "H": args.H, "V": args.V, "Sv": args.splits, "entropy": args.entropy,
+          "chunks": args.chunks, "N": args.rows * args.chunks}
+    alg = small_kernel_bytes(wl)
+    d = kernel_durations(args.trace)
+    names = dict(zip(d.keys(), _demangle(list(d.keys()))))
+    traffic = {}
+    if args.fetch and args.write and args.copy_fetch and args.copy_write:
+        cf = counter_per_dispatch(args.copy_fetch, "FETCH_SIZE", "neg")
+        cw = counter_per_dispatch(args.copy_write, "WRITE_SIZE", "neg")
+        ff = args.copy_bytes / (1024.0 * max(cf))
+        wf = args.copy_bytes / (1024.0 * max(cw))
+        for k in {k.split(" ")[0] for k in alg}:
+            f = counter_per_dispatch(args.fetch, "FETCH_SIZE", k)
+            w = counter_per_dispatch(args.write, "WRITE_SIZE", k)
+            if f and w:
+                traffic[k] = statistics.mean(f) * 1024.0 * ff + statistics.mean(w) * 1024.0 * wf
+    lines = ["# HBM-bound kernels: algorithmic bytes per launch / median duration (kernel trace), against 8 TB/s",
+             f"# workload: {args.workload}; {args.chunks} chunk(s) of {args.rows} rows, {args.active} with a "
+             f"gradient per chunk, H={args.H} V={args.V}, {args.splits} vocabulary split(s)"
+             + ("; q < 1 (accumulator over the compacted rows)" if args.entropy else ""),
+             f"# command: {args.command}",
+             "# traffic: FETCH_SIZE + WRITE_SIZE per dispatch scaled by a plain copy's reading (when given)", "",
+             f"{'kernel':<40} {'calls':>6} {'med_us':>10} {'alg_MB':>10} {'GB/s':>9} {'frac':>6} {'traffic_MB':>11}"]
+    # Launches of one kernel name that move different amounts are told apart
+    # by the library kernel that follows them in time: the copy of W precedes
+    # a forward sweep and the gathered rows' copy the weight-gradient sweep;
+    # the merge after the statistics-only sweep has no accumulator (with
+    # q = 1 that sweep is the setup's log-prob pass, not part of a step).
+    seq = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                   r["Kernel_Name"]) for r in _rows(args.trace)), key=lambda x: x[0])
+    plp_seq = [x for x in seq if "plp" in x[2]]
+    split = {}
+    for i, (_, dur, name) in enumerate(plp_seq):
+        nxt = plp_seq[i + 1][2] if i + 1 < len(plp_seq) else ""
+        prv = plp_seq[i - 1][2] if i > 0 else ""
+        if "frag_copy_kernel" in name:
+            label = "frag_copy_kernel (gathered rows)" if "bwd_pp_kernel" in nxt else "frag_copy_kernel (W)"
+        elif "combine_kernel" in name:
+            if "fwd_mfma_kernel" in prv:
+                if not args.entropy:
+                    continue
+                label = "combine_kernel (statistics only)"
+            else:
+                label = "combine_kernel"
+        else:
+            continue
+        split.setdefault(label, []).append(dur)
+    rows = [(k, k, v) for k, v in split.items()]
+    for raw, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        if "frag_copy_kernel" in raw or "combine_kernel" in raw:
+            continue
+        key = next((k for k in alg if k in raw or k in names[raw]), None)
+        if key is not None:
+            rows.append((key, _short(names[raw], 40), v))
+    for key, label, v in rows:
+        if not v or alg.get(key, 0) == 0:
+            continue
+        us = statistics.median(v) / 1e3  # the median: setup calls of other sizes share some names
+        gbs = alg[key] / (us * 1e-6) / 1e9
+        tr = traffic.get(key) if " " not in key else None
+        lines.append(f"{label:<40} {len(v):>6} {us:>10.2f} {alg[key] / 1e6:>10.2f} {gbs:>9.1f} {gbs / 8000.0:>6.3f} "
+                     f"{(tr / 1e6) if tr else float('nan'):>11.2f}")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as fh:
+            fh.write(text)
+    sys.stdout.write(text)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -235,8 +349,18 @@ def main(argv=None) -> int:
     q.add_argument("--simds", type=int, default=4)
     q.add_argument("--out")
     q.add_argument("--command", default="")
+    b = sub.add_parser("hbm")
+    b.add_argument("trace")
+    for k in ("rows", "active", "H", "V", "splits", "chunks"):
+        b.add_argument("--" + k, type=int, required=True)
+    b.add_argument("--entropy", action="store_true")
+    b.add_argument("--workload", required=True)
+    for k in ("fetch", "write", "copy_fetch", "copy_write", "out"):
+        b.add_argument("--" + k.replace("_", "-"))
+    b.add_argument("--copy-bytes", type=float, default=float(1 << 30))
+    b.add_argument("--command", default="")
     args = ap.parse_args(argv)
-    return {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic, "pmc": cmd_pmc}[args.cmd](args)
+    return {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic, "pmc": cmd_pmc, "hbm": cmd_hbm}[args.cmd](args)
 
 
 if __name__ == "__main__":
