@@ -330,7 +330,8 @@ def main() -> int:
 
     L = _abi.lib()
     n_chunks = 1 if spec.chunk_sequences == 0 else -(-spec.B // spec.chunk_sequences)
-    _abi.check(L.plp_profile_start(4 * args.steps * n_chunks + 8))
+    # event pairs: a forward and up to a few weight-gradient launches per chunk
+    _abi.check(L.plp_profile_start(16 * args.steps * n_chunks + 64))
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -358,12 +359,24 @@ def main() -> int:
     # HBM bytes (forward: W and the chunk's hidden rows read once, bf16;
     # weight gradient: W read and grad_W written once, the active rows of h
     # read once, bias and grad_b when present)
-    n_c, na_c = N / n_chunks, n_active / n_chunks
+    # per step: the forward sweep(s) compute the logits of every row and the
+    # grad_h accumulator (of every row; with q < 1, a statistics-only sweep
+    # over every row and the accumulator pass over the rows with a gradient),
+    # reading W once per launch and each row once; the weight-gradient
+    # launches compute grad_W of the rows with a gradient, reading W and
+    # writing grad_W once per step and each such row once. Per launch: the
+    # step's amount over its launches.
+    q_lt_1 = spec.top_entropy_quantile < 1.0
+    fl_per_step = max(1.0, cnt[0] / args.steps)
+    wl_per_step = max(1.0, cnt[1] / args.steps)
+    fwd_flops = (2.0 * N + 4.0 * n_active) * H * V if q_lt_1 else 4.0 * H * V * N
+    fwd_rows = N + (n_active if q_lt_1 else 0)
+    fwd_bytes = fl_per_step * (2.0 * H * V + (2.0 * V if spec.bias else 0.0)) + 2.0 * H * fwd_rows
+    wg_flops = 2.0 * H * V * n_active
+    wg_bytes = 4.0 * H * V + 2.0 * H * n_active + (4.0 * V if spec.bias else 0.0)
     per_launch = {
-        "fwd_sweep": (4.0 * H * V * n_c, 2.0 * H * V + 2.0 * H * n_c + (2.0 * V if spec.bias else 0.0),
-                      ms[0] / max(1, cnt[0])),
-        "wgrad_sweep": (2.0 * H * V * na_c, 4.0 * H * V + 2.0 * H * na_c + (4.0 * V if spec.bias else 0.0),
-                        ms[1] / max(1, cnt[1])),
+        "fwd_sweep": (fwd_flops / fl_per_step, fwd_bytes / fl_per_step, ms[0] / max(1, cnt[0])),
+        "wgrad_sweep": (wg_flops / wl_per_step, wg_bytes / wl_per_step, ms[1] / max(1, cnt[1])),
     }
     dom = "fwd_sweep" if ms[0] >= ms[1] else "wgrad_sweep"
     flops, alg_bytes, avg_ms = per_launch[dom]
@@ -408,9 +421,9 @@ def main() -> int:
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tflops_method_work": round(tflops_method, 2),
         "pct_bf16_peak_method_work": round(100.0 * tflops_method / PEAK_BF16_TFLOPS, 2),
-        # what the path executes: the forward sweep's 4NHV plus the weight-gradient
+        # what the path executes: the forward sweeps plus the weight-gradient
         # sweep's 4HV per token with a gradient (its logits are recomputed)
-        "executed_tflops": round(4.0 * H * V * (N + n_active) / (elapsed / args.steps) / 1e12, 2),
+        "executed_tflops": round((fwd_flops + 2.0 * wg_flops) / (elapsed / args.steps) / 1e12, 2),
         "memory": {"inputs_bytes": int(mem_inputs), "workspace_bytes": int(ws.numel()),
                    "peak_bytes_beyond_inputs": int(peak_delta)},
         "config": {"workload": workload, "B": spec.B, "T": spec.T, "H": H, "V": V,

@@ -123,14 +123,16 @@ hipError_t launch_grad_h_compact(int dtype, const RowStats* stats, const float* 
                                  int V, const void* h, const void* W, const void* b, float inv_tau, const int* idx,
                                  const TokData* tok, const int* count_dev, void* gh, hipStream_t st);
 
-// Weight-gradient sweep on MFMA over the compacted tokens (hcf and Wf are
-// fragment-major).
+// Weight-gradient sweep on MFMA over the compacted tokens
+// [tok_begin, tok_begin + tok_len) of the *count_dev (hcf and Wf are
+// fragment-major; tok_begin a multiple of 32; hcf and tok point at token 0).
 // tail_scratch (bwd_tail_scratch_floats(H) floats, or NULL to keep every
 // vocabulary block in one workgroup) holds the fp32 partial sums of the
 // blocks whose token tiles are split over several workgroups.
 hipError_t launch_bwd_mfma(const __bf16* Wf, const __bf16* b, const __bf16* hcf, const TokData* tok,
-                           const int* count_dev, int H, int V, float inv_tau, int acc_mode, float* gW_acc,
-                           float* gb_acc, __bf16* gW_out, __bf16* gb_out, float* tail_scratch, hipStream_t st);
+                           const int* count_dev, int tok_begin, int tok_len, int H, int V, float inv_tau, int acc_mode,
+                           float* gW_acc, float* gb_acc, __bf16* gW_out, __bf16* gb_out, float* tail_scratch,
+                           hipStream_t st);
 size_t bwd_tail_scratch_floats(int H);
 
 // Generic (VALU) forward and weight-gradient sweeps for any H and fp32 or bf16.

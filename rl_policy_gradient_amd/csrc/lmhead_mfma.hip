@@ -69,7 +69,7 @@ void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bia
                    const int* __restrict__ count_dev, int V, float inv_tau, int acc_mode,
                    float* __restrict__ gW_acc, float* __restrict__ gb_acc, __bf16* __restrict__ gW_out,
                    __bf16* __restrict__ gb_out, int whole, int parts, float* __restrict__ part_w,
-                   float* __restrict__ part_b) {
+                   float* __restrict__ part_b, int tok_begin, int tok_len) {
   constexpr int H = 128 * KB;
   constexpr int DS = Stage<KB>::DS;
   constexpr int TS = Stage<KB>::TS;
@@ -87,7 +87,9 @@ void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bia
   const int w = wall & 3;  // H quarter
   const int hh = lane >> 5, c = lane & 31;
   const int nbq = w & 1, kh = w >> 1;
-  const int n_tok = *count_dev;
+  // this launch's share of the compacted tokens: [tok_begin, tok_begin + tok_len)
+  // of the *count_dev (tok and hcf already point at tok_begin)
+  const int n_tok = max(0, min(*count_dev - tok_begin, tok_len));
   const int n_tiles = (n_tok + BK - 1) / BK;
   // Workgroups below `whole` take a vocabulary block and all token tiles.
   // The blocks of the last, partial round are shared by `parts` workgroups
@@ -425,8 +427,10 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restric
 
 template <int KB>
 hipError_t bwd_dispatch(const __bf16* Wf, const __bf16* b, const __bf16* hcf, const TokData* tok, const int* count_dev,
-                        int V, float inv_tau, int acc_mode, float* gW_acc, float* gb_acc, __bf16* gW_out,
-                        __bf16* gb_out, float* tail_scratch, hipStream_t st) {
+                        int tok_begin, int tok_len, int V, float inv_tau, int acc_mode, float* gW_acc, float* gb_acc,
+                        __bf16* gW_out, __bf16* gb_out, float* tail_scratch, hipStream_t st) {
+  hcf += (size_t)tok_begin * (128 * KB);
+  tok += tok_begin;
   // Blocks of the last, partial round of workgroups are split over the token
   // tiles so that round ends sooner: `parts` workgroups per block, as many as
   // fit the free slots (at most kTailParts, and kMaxTailWGs in all).
@@ -445,10 +449,10 @@ hipError_t bwd_dispatch(const __bf16* Wf, const __bf16* b, const __bf16* hcf, co
   dim3 grid((unsigned)(whole + tail_wgs)), block(512);
   if (b)
     hipLaunchKernelGGL((bwd_pp_kernel<KB, true>), grid, block, 0, st, Wf, b, hcf, tok, count_dev, V, inv_tau,
-                       acc_mode, gW_acc, gb_acc, gW_out, gb_out, whole, parts, part_w, part_b);
+                       acc_mode, gW_acc, gb_acc, gW_out, gb_out, whole, parts, part_w, part_b, tok_begin, tok_len);
   else
     hipLaunchKernelGGL((bwd_pp_kernel<KB, false>), grid, block, 0, st, Wf, b, hcf, tok, count_dev, V, inv_tau,
-                       acc_mode, gW_acc, gb_acc, gW_out, gb_out, whole, parts, part_w, part_b);
+                       acc_mode, gW_acc, gb_acc, gW_out, gb_out, whole, parts, part_w, part_b, tok_begin, tok_len);
   e = hipGetLastError();
   if (e != hipSuccess || tail_wgs == 0) return e;
   hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)(rem * BQ)), dim3(256), 0, st, part_w, part_b, whole, parts,
@@ -471,22 +475,23 @@ hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_de
 }
 
 hipError_t launch_bwd_mfma(const __bf16* Wf, const __bf16* b, const __bf16* hcf, const TokData* tok,
-                           const int* count_dev, int H, int V, float inv_tau, int acc_mode, float* gW_acc,
-                           float* gb_acc, __bf16* gW_out, __bf16* gb_out, float* tail_scratch, hipStream_t st) {
+                           const int* count_dev, int tok_begin, int tok_len, int H, int V, float inv_tau, int acc_mode,
+                           float* gW_acc, float* gb_acc, __bf16* gW_out, __bf16* gb_out, float* tail_scratch,
+                           hipStream_t st) {
   switch (H / 128) {
-    case 1: return bwd_dispatch<1>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+    case 1: return bwd_dispatch<1>(Wf, b, hcf, tok, count_dev, tok_begin, tok_len, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
                                    tail_scratch, st);
-    case 2: return bwd_dispatch<2>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+    case 2: return bwd_dispatch<2>(Wf, b, hcf, tok, count_dev, tok_begin, tok_len, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
                                    tail_scratch, st);
-    case 3: return bwd_dispatch<3>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+    case 3: return bwd_dispatch<3>(Wf, b, hcf, tok, count_dev, tok_begin, tok_len, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
                                    tail_scratch, st);
-    case 4: return bwd_dispatch<4>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+    case 4: return bwd_dispatch<4>(Wf, b, hcf, tok, count_dev, tok_begin, tok_len, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
                                    tail_scratch, st);
-    case 5: return bwd_dispatch<5>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+    case 5: return bwd_dispatch<5>(Wf, b, hcf, tok, count_dev, tok_begin, tok_len, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
                                    tail_scratch, st);
-    case 6: return bwd_dispatch<6>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+    case 6: return bwd_dispatch<6>(Wf, b, hcf, tok, count_dev, tok_begin, tok_len, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
                                    tail_scratch, st);
-    case 7: return bwd_dispatch<7>(Wf, b, hcf, tok, count_dev, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
+    case 7: return bwd_dispatch<7>(Wf, b, hcf, tok, count_dev, tok_begin, tok_len, V, inv_tau, acc_mode, gW_acc, gb_acc, gW_out, gb_out,
                                    tail_scratch, st);
     default: return hipErrorInvalidValue;
   }

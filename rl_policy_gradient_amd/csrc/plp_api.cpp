@@ -99,6 +99,10 @@ struct Plan {
   // row, then the grad_h accumulator pass over the compacted rows with g != 0
   bool o_compact = false;
   int64_t o2_rows = 0;         // row capacity of the compacted pass's stats / O (all splits)
+  // weight-gradient launches: at most wg_sub compacted tokens each, so that
+  // the rows one launch streams (wg_sub x H bf16, 128 MB) stay in the 256 MB
+  // memory-side cache while every workgroup reads them; wg_launches in all
+  int64_t wg_sub = 0, wg_launches = 0;
 };
 
 struct Bufs {
@@ -148,6 +152,11 @@ Plan make_plan(const plp_args* a, bool need_o, bool need_gw, bool need_gb) {
   p.prepass = p.entropy && (p.nchunks > 1 || p.o_compact);
   // splits x row blocks < 512 while the splits are above one (forward_splits)
   p.o2_rows = std::max<int64_t>(512 * kBQ, round_up(p.Nc, kBQ));
+  p.wg_sub = p.mfma ? std::max<int64_t>(32 * kBK, ((int64_t)128 << 20) / (2 * a->H) / kBK * kBK) : p.cap;
+  for (int64_t c = 0; c < p.nchunks; ++c) {
+    const int64_t capc = round_up(std::min(p.Bc, p.B - c * p.Bc) * p.T, kBK);
+    p.wg_launches += (capc + p.wg_sub - 1) / p.wg_sub;
+  }
   return p;
 }
 
@@ -183,7 +192,7 @@ size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
   if (p.need_gw) {
     b.hc = c.take<char>((size_t)p.cap * H * esize(a->dtype));
     if (p.mfma) b.tail = c.take<float>(bwd_tail_scratch_floats(H));
-    if (p.nchunks > 1) {
+    if (p.wg_launches > 1) {
       b.gW_acc = c.take<float>((size_t)V * H);
       if (p.need_gb) b.gb_acc = c.take<float>(V);
     }
@@ -496,6 +505,7 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
     HIP_TRY(launch_entropy_mask(b.ent, a->completion_mask, p.N, &b.sel->thr, b.emask, st));
   }
 
+  int64_t wg_launch = 0;
   for (int64_t c = 0; c < p.nchunks; ++c) {
     const int64_t s0 = c * p.Bc, bc = std::min(p.Bc, p.B - s0);
     const int64_t r0 = s0 * p.T, n = bc * p.T;
@@ -543,16 +553,25 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
         HIP_TRY(launch_frag_copy((const __bf16*)hsrc, b.idx, b.count, n, p.cap / kBK, H, (__bf16*)b.hc, st));
       else
         HIP_TRY(launch_gather_rows(a->dtype, hsrc, b.idx, b.count, p.cap, H, b.hc, st));
-      const int mode = p.nchunks == 1 ? 0 : (c == 0 ? 1 : (c == p.nchunks - 1 ? 3 : 2));
-      if (p.mfma) {
-        hipEvent_t* ev = prof_slot(1);
-        if (ev) HIP_TRY(hipEventRecord(ev[0], st));
-        HIP_TRY(launch_bwd_mfma(b.Wf, (const __bf16*)a->bias, (const __bf16*)b.hc, b.tok, b.count, H, V, inv_tau, mode,
-                                b.gW_acc, b.gb_acc, (__bf16*)out->grad_weight, (__bf16*)out->grad_bias, b.tail, st));
-        if (ev) HIP_TRY(hipEventRecord(ev[1], st));
-      } else
-        HIP_TRY(launch_bwd_generic(a->dtype, a->weight, a->bias, b.hc, b.tok, b.count, H, V, inv_tau, mode, b.gW_acc,
-                                   b.gb_acc, out->grad_weight, out->grad_bias, st));
+      // accumulator modes over all weight-gradient launches of the call:
+      // 0 the only launch writes grad_W; 1 the first stores the fp32
+      // accumulator, 2 the middle ones add into it, 3 the last adds and
+      // writes grad_W
+      const int64_t capc = round_up(n, kBK);
+      for (int64_t k0 = 0; k0 < capc; k0 += p.wg_sub) {
+        const int mode = p.wg_launches == 1 ? 0 : (wg_launch == 0 ? 1 : (wg_launch == p.wg_launches - 1 ? 3 : 2));
+        ++wg_launch;
+        if (p.mfma) {
+          hipEvent_t* ev = prof_slot(1);
+          if (ev) HIP_TRY(hipEventRecord(ev[0], st));
+          HIP_TRY(launch_bwd_mfma(b.Wf, (const __bf16*)a->bias, (const __bf16*)b.hc, b.tok, b.count, (int)k0,
+                                  (int)std::min(p.wg_sub, capc - k0), H, V, inv_tau, mode, b.gW_acc, b.gb_acc,
+                                  (__bf16*)out->grad_weight, (__bf16*)out->grad_bias, b.tail, st));
+          if (ev) HIP_TRY(hipEventRecord(ev[1], st));
+        } else
+          HIP_TRY(launch_bwd_generic(a->dtype, a->weight, a->bias, b.hc, b.tok, b.count, H, V, inv_tau, mode,
+                                     b.gW_acc, b.gb_acc, out->grad_weight, out->grad_bias, st));
+      }
     }
   }
   if (out->logp_out) HIP_TRY(hipMemcpyAsync(out->logp_out, b.lp, p.N * sizeof(float), hipMemcpyDeviceToDevice, st));

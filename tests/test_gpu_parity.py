@@ -115,6 +115,14 @@ SMALL = {
     "generic_f32_grpo_token_adv": synth.small("generic_grpo_tadv", cfg_id=116, dtype="f32", B=3, T=30, H=48,
                                               V=300, loss_type=synth.GRPO, eps_low=0.1, eps_high=0.1,
                                               token_adv=True, chunk_sequences=2, beta=0.04, ref_noise_std=0.05),
+    # more compacted tokens than one weight-gradient launch takes (74880 at
+    # H=896): several launches accumulate grad_W in fp32, with and without
+    # outer chunks
+    "mfma_gmpo_wgrad_launches": synth.small("mfma_wg_split", cfg_id=120, B=3, T=32768, H=896, V=1000, w_std=0.02,
+                                            bias=True, prompt_lo=100, prompt_hi=4000),
+    "mfma_gmpo_wgrad_launches_chunked": synth.small("mfma_wg_split_ch", cfg_id=121, B=3, T=32768, H=896, V=1000,
+                                                    w_std=0.02, prompt_lo=100, prompt_hi=4000,
+                                                    chunk_sequences=2),
     # generic (vector ALU) path: fp32, and bf16 with H not a multiple of 128
     "generic_f32_cfg1": synth.CONFIGS[1],
     "generic_bf16_h96": synth.small("generic_h96", cfg_id=106, B=2, T=50, H=96, V=700, bias=True),
