@@ -21,6 +21,7 @@ __all__ = [
     "fused_lmhead_policy_loss_fwd_bwd",
     "selective_entropy",
     "entropy_quantile_mask",
+    "entropy_quantile_mask_noalloc",
     "policy_loss_from_logprobs",
     "workspace_size",
     "METRIC_NAMES",
@@ -241,6 +242,25 @@ def entropy_quantile_mask(entropy: torch.Tensor, active: torch.Tensor, q: float,
     thr = torch.empty(1, dtype=torch.float32, device=dev)
     _abi.check(L.plp_entropy_quantile_mask(_ptr(entropy), _ptr(active), N, float(q), _ptr(mask), _ptr(thr),
                                            ws.data_ptr(), ws.numel(), _stream(dev)))
+    return mask, thr
+
+
+def entropy_quantile_mask_noalloc(entropy: torch.Tensor, active: torch.Tensor, q: float, out=None):
+    """The batch-global high-entropy mask without a workspace
+    (plp_entropy_quantile_mask_noalloc: the select state lives in a static
+    device array of the library). Pass out=(mask u8 [N], threshold fp32 [1])
+    and a u8 `active` to call without any allocation. Returns (mask,
+    threshold)."""
+    N = entropy.numel()
+    dev = entropy.device
+    active = _mask_u8(active)
+    _check_vec(entropy, N, torch.float32, "entropy")
+    if out is None:
+        out = (torch.empty(N, dtype=torch.uint8, device=dev), torch.empty(1, dtype=torch.float32, device=dev))
+    mask, thr = out
+    _check_vec(mask, N, torch.uint8, "mask")
+    _abi.check(_abi.lib().plp_entropy_quantile_mask_noalloc(_ptr(entropy), _ptr(active), N, float(q), _ptr(mask),
+                                                            _ptr(thr), _stream(dev)))
     return mask, thr
 
 

@@ -12,16 +12,16 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Per (vocabulary split, row) result of the forward sweep: the reference m
-// all exponentials are taken against, sum exp(z-m), sum exp(z-m) z, and a
-// flag asking the merge to recompute the row exactly (a logit far above the
-// reference). zy is not read (the merge takes the target logit itself).
+// all exponentials are taken against, the largest logit zmax of the split,
+// sum exp(z-m), sum exp(z-m) z, and a flag: a logit above m + 64, whose
+// exponential the sweep clamped, so the row's statistics are to be taken
+// again against its true maximum.
 struct alignas(8) RowStats {
-  float m;
-  float zy;
+  double m;     // the reference, in natural units of the logits
   double s;
   double sz;
+  float zmax;
   int flag;
-  int pad;
 };
 
 // Per compacted token, what the weight-gradient sweep needs.
@@ -107,13 +107,19 @@ hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_de
                             __bf16* Xf, hipStream_t st);
 
 // Forward sweep on MFMA (bf16, H a multiple of 128, H <= 896); Wf is the
-// fragment-major copy of W. With count_dev (the grad_h accumulator pass over
-// a compacted row list, with_o only) the sweep runs over the first
-// *count_dev rows of h (N is their capacity) with forward_splits(*count_dev,
-// V, Sv) splits, and stats / O use the row stride compact_stride(*count_dev).
+// fragment-major copy of W. With count_dev (an accumulator pass over a
+// compacted row list, with_o only) the sweep runs over the first
+// min(*count_dev, N) rows of h, or with row_idx over rows row_idx[k] of h
+// (N is the list's capacity), with
+// forward_splits(that count, V, Sv) splits, and stats / O use the row stride
+// compact_stride(that count). With mref (natural-log units of the logits,
+// row k's at mref[k * mref_stride]) every row takes its exponentials against
+// that reference instead of its first tile's maximum; a reference at or
+// above the row's largest logit leaves nothing to flag.
 hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
                            int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st,
-                           const int* count_dev = nullptr);
+                           const int* count_dev = nullptr, const float* mref = nullptr, int mref_stride = 1,
+                           const int* row_idx = nullptr);
 // Row stride of the compacted pass's stats and O (whole 64-row blocks).
 __host__ __device__ inline int64_t compact_stride(int64_t rows) { return (rows + 63) / 64 * 64; }
 // grad_h of the compacted rows k < *count_dev from the compacted pass:
@@ -144,12 +150,32 @@ hipError_t launch_bwd_generic(int dtype, const void* W, const void* b, const voi
                               int acc_mode, float* gW_acc, float* gb_acc, void* gW_out, void* gb_out,
                               hipStream_t st);
 
+// The second forward pass over the rows the first one flagged: up to cap of
+// them, listed by launch_flag_scan (idx, their largest logit mref, *count,
+// and pos[row] = the row's place in the list or -1), taken again by the
+// accumulator sweep against mref into stats / O (compacted layout, at most
+// max_splits vocabulary splits).
+struct FlaggedPass {
+  int* idx;
+  float* mref;
+  int* pos;
+  int* count;
+  RowStats* stats;
+  float* O;
+  int cap;
+  int max_splits;
+};
+hipError_t launch_flag_scan(const RowStats* stats, int Sv, int64_t N, int cap2, int* idx, float* mref, int* pos,
+                            int* count, hipStream_t st);
+
 // Merge vocabulary splits: lp, H, lse per row and (when vout != NULL)
-// v = W_y - sum_v p W_v as fp32 [N,H] (grad_h = g / tau * v). Rows flagged by the sweep are
+// v = W_y - sum_v p W_v as fp32 [N,H] (grad_h = g / tau * v). Rows listed
+// by a second pass (fp) are merged from its results; rows still flagged are
 // recomputed here from h, W, b with an exact online max.
 hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int Sv, int64_t N, int H, int V,
                           const void* h, const void* W, const void* b, float inv_tau, const int64_t* y,
-                          float* lp, float* ent, float* lse, float* vout, hipStream_t st);
+                          float* lp, float* ent, float* lse, float* vout, hipStream_t st,
+                          const FlaggedPass* fp = nullptr);
 
 // Loss stage (per outer chunk): per-sequence partial sums, the per-sequence
 // merge (accumulators set on the first chunk; loss and metrics written on the

@@ -23,7 +23,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   constexpr int DS = Stage<KB>::DS;  // columns per wave
   constexpr int KS = DS / 16;        // 16-wide contraction steps per wave
   __shared__ f32x4 s_part[NW][2][4][64];
-  __shared__ float s_x[NW * 64];
+  __shared__ float s_x[2 * NW * 64];
   // the partials buffer is reused for the final cross-wave sums
   double* s_xd = reinterpret_cast<double*>(&s_part[0][0][0][0]);   // [NW][2][64]
 
@@ -59,11 +59,16 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   }
 
   const int64_t my_row = q0 + 32 * nbq + c;  // row whose epilogue this lane runs (with 3 other lanes)
-  // The epilogue works in base 2: z2 = z log2(e), p = 2^(z2 - m2).
+  // The epilogue works in base 2: z2 = z log2(e), p = 2^(z2 - m2). Base-2
+  // values go back to natural units of the logits with the inverse of the
+  // factor that made them (inv_tau / c2 in fp64), so the fp32 rounding of
+  // log2(e) in c2 does not shift the reference.
   const float c2 = inv_tau * kLog2e;
+  const double to_nat = (double)inv_tau / (double)c2;
   float m2 = -INFINITY;
   double s_acc = 0.0, sz_acc = 0.0;  // this lane's share of sum p, sum p z2
   bool flag = false;
+  float zmx = -INFINITY;             // the largest logit (base 2) this lane saw
 
   // Bias of tile rows kvq(kh, hh, 0..7), kept as packed bf16 (two groups of
   // four consecutive rows, one 8-byte load each when inside the vocabulary).
@@ -169,9 +174,12 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
     float z[8];
     logits(v0, sf, bv, z);
     float sp = 0.f, szp = 0.f;
+    // the tile's largest logit in this lane: the flag test and the row max
+    const float tm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+    flag |= tm > m2 + kRefSlack2;
+    zmx = fmaxf(zmx, tm);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      flag |= z[j] > m2 + kRefSlack2;
       const float pj = __builtin_amdgcn_exp2f(fminf(z[j] - m2, kRefSlack2));
       sp += pj;
       szp = fmaf(pj, z[j], szp);
@@ -195,21 +203,22 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   double szx = sz_acc + (double)__shfl_xor(sz_acc, 32, 64);
   int fl = flag ? 1 : 0;
   fl |= __shfl_xor(fl, 32, 64);
+  const float zm = fmaxf(zmx, other_half(zmx, hh));
   __syncthreads();
   if (hh == 0) {
     s_xd[(2 * w) * 64 + c] = sx;
     s_xd[(2 * w + 1) * 64 + c] = szx;
     s_x[w * 64 + c] = __int_as_float(fl);
+    s_x[NW * 64 + w * 64 + c] = zm;
   }
   __syncthreads();
   if (kh == 0 && hh == 0 && my_row < N) {
     RowStats rs;
-    rs.m = (float)((double)m2 * kLn2);
-    rs.zy = 0.f;
+    rs.m = (double)m2 * to_nat;
+    rs.zmax = (float)((double)fmaxf(zm, s_x[NW * 64 + (w ^ 2) * 64 + c]) * to_nat);
     rs.s = sx + s_xd[(2 * (w ^ 2)) * 64 + c];
-    rs.sz = (szx + s_xd[(2 * (w ^ 2) + 1) * 64 + c]) * kLn2;
+    rs.sz = (szx + s_xd[(2 * (w ^ 2) + 1) * 64 + c]) * to_nat;
     rs.flag = (fl | __float_as_int(s_x[(w ^ 2) * 64 + c])) ? 1 : 0;
-    rs.pad = 0;
     stats[(int64_t)sv * N + my_row] = rs;
   }
 }
@@ -234,20 +243,23 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
 // and so are the staged tiles. The statistics are bit-identical to the
 // statistics-only kernel's: every sum runs in the same order.
 //
-// With count_dev the rows are the first *count_dev rows of h (compacted
-// tokens), the splits forward_splits(*count_dev, V, Sv) and the row stride of
-// stats and O compact_stride(*count_dev); workgroups past the last block
-// exit at once.
+// With count_dev the rows are the first min(*count_dev, N) rows of a
+// compacted list (rows row_idx[k] of h when row_idx is given), the splits
+// forward_splits(that count, V, Sv) and the row stride of stats and O
+// compact_stride(that count); workgroups past the last block exit at once.
+// With mref the exponent reference of row k is mref[k * mref_stride]
+// (natural units) instead of the maximum of its first tile.
 template <int KB, bool HAS_BIAS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, const __bf16* __restrict__ bias,
                    int64_t N_, int V, float inv_tau, int Sv_, int tiles_per_split_, RowStats* __restrict__ stats,
-                   float* __restrict__ O, const int* __restrict__ count_dev) {
+                   float* __restrict__ O, const int* __restrict__ count_dev, const float* __restrict__ mref,
+                   int mref_stride, const int* __restrict__ row_idx) {
   constexpr int H = 128 * KB;
   int64_t N = N_, stride = N_;
   int Sv = Sv_, tiles_per_split = tiles_per_split_;
   if (count_dev) {
-    N = *count_dev;
+    N = min((int64_t)*count_dev, N_);
     Sv = forward_splits(N, V, Sv_);
     tiles_per_split = ((V + BK - 1) / BK + Sv - 1) / Sv;
     stride = compact_stride(N);
@@ -277,6 +289,7 @@ void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, 
   const int t_end = min(n_tiles, t_begin + tiles_per_split);
   const bool any = t_begin < t_end;
   const float c2 = inv_tau * kLog2e;
+  const double to_nat = (double)inv_tau / (double)c2;  // base 2 back to natural units (see above)
 
   if (srole) {
     // ======================= S role =======================
@@ -289,20 +302,32 @@ void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, 
     bf16x8 q[2][KS];
     bf16x8 a[KS];
     {
-      const auto rh = frag_rsrc(h + q0 * H, BQ * H * 2);
       const int row0 = (int)min((int64_t)c, N - 1 - q0), row1 = (int)min((int64_t)(32 + c), N - 1 - q0);
       const auto ra = frag_rsrc(frag_ptr<KB>(Wf, any ? t_begin : 0, w, 0, 0), any ? KS * 1024 : 0);
+      if (row_idx) {  // uniform: the resident rows are rows row_idx[q0 + r] of h
+        const __bf16* p0 = h + (int64_t)row_idx[q0 + row0] * H + d0 + 8 * hh;
+        const __bf16* p1 = h + (int64_t)row_idx[q0 + row1] * H + d0 + 8 * hh;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        q[0][ks] = ld_buf(rh, (row0 * H + d0 + 8 * hh) * 2, 32 * ks);
-        q[1][ks] = ld_buf(rh, (row1 * H + d0 + 8 * hh) * 2, 32 * ks);
-        a[ks] = ld_buf(ra, lane * 16, ks * 1024);
+        for (int ks = 0; ks < KS; ++ks) {
+          q[0][ks] = ld16(p0 + 16 * ks);
+          q[1][ks] = ld16(p1 + 16 * ks);
+          a[ks] = ld_buf(ra, lane * 16, ks * 1024);
+        }
+      } else {
+        const auto rh = frag_rsrc(h + q0 * H, BQ * H * 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          q[0][ks] = ld_buf(rh, (row0 * H + d0 + 8 * hh) * 2, 32 * ks);
+          q[1][ks] = ld_buf(rh, (row1 * H + d0 + 8 * hh) * 2, 32 * ks);
+          a[ks] = ld_buf(ra, lane * 16, ks * 1024);
+        }
       }
     }
     const int64_t my_row = q0 + 32 * nbq + c;
     float m2 = -INFINITY;
     double s_acc = 0.0, sz_acc = 0.0;
     bool flag = false;
+    float zmx = -INFINITY;  // the largest logit (base 2) this lane saw
     auto s_step = [&](f32x16 (&acc)[2], int buf, int t_next) {
       const auto r = frag_rsrc(frag_ptr<KB>(Wf, t_next, w, 0, 0), KS * 1024);
 #pragma unroll
@@ -374,9 +399,13 @@ void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, 
       logits(t * BK, sf, bv, z);
       float sp = 0.f, szp = 0.f;
       bf16x8 pa;
+      // the tile's largest logit in this lane: the flag test and the row max
+      const float tm =
+          fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+      flag |= tm > m2 + kRefSlack2;
+      zmx = fmaxf(zmx, tm);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        flag |= z[j] > m2 + kRefSlack2;
         const float pj = __builtin_amdgcn_exp2f(fminf(z[j] - m2, kRefSlack2));
         sp += pj;
         szp = fmaf(pj, z[j], szp);
@@ -404,7 +433,10 @@ void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, 
       if (hh == 0) s_x[w * 64 + c] = mx;
     }
     __syncthreads();  // P1
-    if (any) m2 = fmaxf(s_x[w * 64 + c], s_x[(w ^ 2) * 64 + c]);
+    if (any) {
+      m2 = mref ? (float)((double)mref[min(my_row, N - 1) * mref_stride] / to_nat)
+                : fmaxf(s_x[w * 64 + c], s_x[(w ^ 2) * 64 + c]);
+    }
     __syncthreads();  // P2
     if (any) epilogue(t_begin, sf);
     for (int t = t_begin; t < t_end; ++t) {
@@ -426,21 +458,22 @@ void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, 
     double szx = sz_acc + (double)__shfl_xor(sz_acc, 32, 64);
     int fl = flag ? 1 : 0;
     fl |= __shfl_xor(fl, 32, 64);
+    const float zm = fmaxf(zmx, other_half(zmx, hh));
     __syncthreads();  // R0
     if (hh == 0) {
       s_xd[(2 * w) * 64 + c] = sx;
       s_xd[(2 * w + 1) * 64 + c] = szx;
       s_x[w * 64 + c] = __int_as_float(fl);
+      s_x[NW * 64 + w * 64 + c] = zm;
     }
     __syncthreads();  // R1
     if (kh == 0 && hh == 0 && my_row < N) {
       RowStats rs;
-      rs.m = (float)((double)m2 * kLn2);
-      rs.zy = 0.f;
+      rs.m = (double)m2 * to_nat;
+      rs.zmax = (float)((double)fmaxf(zm, s_x[NW * 64 + (w ^ 2) * 64 + c]) * to_nat);
       rs.s = sx + s_xd[(2 * (w ^ 2)) * 64 + c];
-      rs.sz = (szx + s_xd[(2 * (w ^ 2) + 1) * 64 + c]) * kLn2;
+      rs.sz = (szx + s_xd[(2 * (w ^ 2) + 1) * 64 + c]) * to_nat;
       rs.flag = (fl | __float_as_int(s_x[(w ^ 2) * 64 + c])) ? 1 : 0;
-      rs.pad = 0;
       stats[(int64_t)sv * stride + my_row] = rs;
     }
   } else {
@@ -506,7 +539,8 @@ void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, 
 
 template <bool HAS_BIAS>
 hipError_t fwd_pp_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
-                         int Sv, RowStats* stats, float* O, const int* count_dev, hipStream_t st) {
+                         int Sv, RowStats* stats, float* O, const int* count_dev, const float* mref, int mref_stride,
+                         const int* row_idx, hipStream_t st) {
   const int n_tiles = (V + BK - 1) / BK;
   const int tps = (n_tiles + Sv - 1) / Sv;
   const int64_t nrb = (N + BQ - 1) / BQ;
@@ -518,7 +552,7 @@ hipError_t fwd_pp_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int
 #define PLP_PP_CASE(K)                                                                                                \
   case K:                                                                                                             \
     hipLaunchKernelGGL((fwd_pp_kernel<K, HAS_BIAS>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats, O,  \
-                       count_dev);                                                                                    \
+                       count_dev, mref, mref_stride, row_idx);                                                        \
     break;
     PLP_PP_CASE(1)
     PLP_PP_CASE(2)
@@ -565,6 +599,7 @@ hipError_t fwd_stats_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, 
 // The variants with the grad_h accumulator (two-role form), from
 // lmhead_fwd_o.hip; b may be NULL.
 hipError_t launch_fwd_mfma_o(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
-                             int Sv, RowStats* stats, float* O, const int* count_dev, hipStream_t st);
+                             int Sv, RowStats* stats, float* O, const int* count_dev, const float* mref,
+                             int mref_stride, const int* row_idx, hipStream_t st);
 
 }  // namespace plp

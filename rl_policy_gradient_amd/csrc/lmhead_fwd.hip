@@ -5,9 +5,11 @@
 namespace plp {
 
 hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
-                           int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st, const int* count_dev) {
-  if (with_o) return launch_fwd_mfma_o(h, Wf, b, N, H, V, inv_tau, Sv, stats, O, count_dev, st);
-  if (count_dev) return hipErrorInvalidValue;  // the compacted pass is the accumulator pass
+                           int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st, const int* count_dev,
+                           const float* mref, int mref_stride, const int* row_idx) {
+  if (with_o)
+    return launch_fwd_mfma_o(h, Wf, b, N, H, V, inv_tau, Sv, stats, O, count_dev, mref, mref_stride, row_idx, st);
+  if (count_dev || mref || row_idx) return hipErrorInvalidValue;  // the compacted passes are accumulator passes
   if (b) return fwd_stats_launch<true>(h, Wf, b, N, H, V, inv_tau, Sv, stats, st);
   return fwd_stats_launch<false>(h, Wf, b, N, H, V, inv_tau, Sv, stats, st);
 }

@@ -55,11 +55,10 @@ __global__ __launch_bounds__(NT) void fwd_generic_kernel(const T* __restrict__ h
   if (threadIdx.x == 0) {
     RowStats rs;
     rs.m = r.m;
-    rs.zy = r.zy;
+    rs.zmax = r.m;  // the exact online maximum
     rs.s = r.s;
     rs.sz = r.sz;
     rs.flag = 0;
-    rs.pad = 0;
     stats[row] = rs;
   }
   if constexpr (WITH_O) {

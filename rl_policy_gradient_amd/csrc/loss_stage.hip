@@ -51,13 +51,21 @@ __device__ V_ block_sum(V_ v, V_* red) {
 // than gathered inside the sweeps. A row any split flagged is recomputed
 // exactly (row_exact).
 // ---------------------------------------------------------------------------
+//
+// Rows the sweep flagged and a second pass took again against their largest
+// logit (pos[row] = k >= 0) are merged from that pass's statistics and
+// accumulator at position k (row stride compact_stride(n2) and
+// forward_splits(n2, V, max_splits2) splits, n2 = min(*count2, cap2)).
 template <typename T, bool EARLY>
 __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict__ stats, const float* __restrict__ O,
                                                      int Sv, int64_t N, int H, int V, const T* __restrict__ h,
                                                      const T* __restrict__ W, const T* __restrict__ b, float inv_tau,
                                                      const int64_t* __restrict__ y, float* __restrict__ lp,
                                                      float* __restrict__ ent, float* __restrict__ lse_out,
-                                                     float* __restrict__ vout) {
+                                                     float* __restrict__ vout, const int* __restrict__ pos,
+                                                     const RowStats* __restrict__ stats2,
+                                                     const float* __restrict__ O2, const int* __restrict__ count2,
+                                                     int cap2, int max_splits2) {
   extern __shared__ float sm[];
   const int64_t row = blockIdx.x;
   __shared__ double s_c[64];  // per-split weights e^{m_j - M}, up to 64 splits
@@ -68,45 +76,66 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
   // targets outside [0, V) are invalid input; clamp the index so they cannot
   // address memory outside W
   const int64_t yc = yv < 0 ? 0 : (yv >= V ? V - 1 : yv);
+  const RowStats* st_ = stats;
+  const float* O_ = O;
+  int Sv_ = Sv;
+  int64_t stride = N, srow = row;
   // EARLY (several splits, up to 32, one 4-column group per thread): each
   // thread's split accumulators are loaded first, so their latency overlaps
   // the split statistics and the target-logit dot product below. It costs
   // registers (two waves per SIMD), so a single split takes the plain form.
   const bool vec = (H & 3) == 0;
-  const bool early = EARLY && vout != nullptr && vec && Sv <= kEarlySplits && H / 4 <= NT;
+  bool early = EARLY && vout != nullptr && vec && Sv <= kEarlySplits && H / 4 <= NT;
   f32x4 opre[EARLY ? kEarlySplits : 1];
   if (early && (int)threadIdx.x < H / 4) {
 #pragma unroll
     for (int j = 0; j < (EARLY ? kEarlySplits : 1); ++j)
-      if (j < Sv) opre[j] = *reinterpret_cast<const f32x4*>(O + (int64_t)j * N * H + row * H + 4 * threadIdx.x);
+      if (j < Sv) opre[j] = *reinterpret_cast<const f32x4*>(O + ((int64_t)j * N + row) * H + 4 * threadIdx.x);
   }
-  if (threadIdx.x < 64) {
-    // one lane per split; butterfly reductions in a fixed order
-    const int j = threadIdx.x;
-    const bool have = j < Sv;
-    RowStats rs;
-    if (have) rs = stats[(int64_t)j * N + row];
-    int f = have ? rs.flag : 0;
-    float M = have ? rs.m : -INFINITY;
-    for (int o = 32; o > 0; o >>= 1) {
-      M = fmaxf(M, __shfl_xor(M, o, 64));
-      f |= __shfl_xor(f, o, 64);
+  // split statistics (one lane per split; butterfly reductions in a fixed order)
+  auto merge_stats = [&]() {
+    if (threadIdx.x < 64) {
+      const int j = threadIdx.x;
+      const bool have = j < Sv_;
+      RowStats rs;
+      if (have) rs = st_[(int64_t)j * stride + srow];
+      int f = have ? rs.flag : 0;
+      double M = have ? rs.m : -INFINITY;
+      for (int o = 32; o > 0; o >>= 1) {
+        M = fmax(M, __shfl_xor(M, o, 64));
+        f |= __shfl_xor(f, o, 64);
+      }
+      const double c = (have && rs.s > 0.0) ? exp(rs.m - M) : 0.0;
+      double cs = have ? c * rs.s : 0.0, csz = have ? c * rs.sz : 0.0;
+      for (int o = 32; o > 0; o >>= 1) {
+        cs += __shfl_xor(cs, o, 64);
+        csz += __shfl_xor(csz, o, 64);
+      }
+      s_c[j] = c;
+      if (j == 0) {
+        s_flag = f;
+        s_res[0] = M;
+        s_res[1] = cs;
+        s_res[2] = csz;
+      }
     }
-    const double c = (have && rs.s > 0.0) ? exp((double)rs.m - (double)M) : 0.0;
-    double cs = have ? c * rs.s : 0.0, csz = have ? c * rs.sz : 0.0;
-    for (int o = 32; o > 0; o >>= 1) {
-      cs += __shfl_xor(cs, o, 64);
-      csz += __shfl_xor(csz, o, 64);
-    }
-    s_c[j] = c;
-    if (j == 0) {
-      s_flag = f;
-      s_res[0] = (double)M;
-      s_res[1] = cs;
-      s_res[2] = csz;
+    __syncthreads();
+  };
+  merge_stats();
+  if (s_flag && pos != nullptr) {  // uniform: a flagged row the second pass may have taken
+    const int k = pos[row];
+    if (k >= 0) {
+      const int64_t n2 = min((int64_t)*count2, (int64_t)cap2);
+      st_ = stats2;
+      O_ = O2;
+      Sv_ = forward_splits(n2, V, max_splits2);
+      stride = compact_stride(n2);
+      srow = k;
+      early = false;
+      __syncthreads();  // every thread has read s_flag
+      merge_stats();
     }
   }
-  __syncthreads();
   if (s_flag) {
     const RowResult r = row_exact<T>(h + row * H, W, b, yv, H, V, inv_tau, vout != nullptr, sm);
     const double l = (double)r.m + log(r.s);
@@ -152,15 +181,15 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
   __syncthreads();
   if (vout) {
     const double inv_s = s_res[3];
-    const float* Orow = O + row * H;
-    const int64_t sstride = N * H;
+    const float* Orow = O_ + srow * H;
+    const int64_t sstride = stride * H;
     if (early) {
       const int d4 = threadIdx.x;
       if (d4 < H / 4) {
         double o[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
         for (int j = 0; j < (EARLY ? kEarlySplits : 1); ++j) {
-          if (j < Sv) {
+          if (j < Sv_) {
             const double c = s_c[j];
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] += c * (double)opre[j][k];
@@ -176,7 +205,7 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
       for (int d4 = threadIdx.x; d4 < H / 4; d4 += NT) {
         double o[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 8
-        for (int j = 0; j < Sv; ++j) {
+        for (int j = 0; j < Sv_; ++j) {
           const f32x4 x = *reinterpret_cast<const f32x4*>(Orow + j * sstride + 4 * d4);
           const double c = s_c[j];
 #pragma unroll
@@ -192,7 +221,7 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
       for (int d = threadIdx.x; d < H; d += NT) {
         double o = 0.0;
 #pragma unroll 8
-        for (int j = 0; j < Sv; ++j) o += s_c[j] * (double)Orow[j * sstride + d];
+        for (int j = 0; j < Sv_; ++j) o += s_c[j] * (double)Orow[j * sstride + d];
         vout[row * H + d] = (float)((double)ldf<T>(W, yc * H + d) - o * inv_s);
       }
     }
@@ -232,12 +261,12 @@ __global__ __launch_bounds__(NT) void grad_h_compact_kernel(const RowStats* __re
     RowStats rs;
     if (have) rs = stats[(int64_t)j * stride + k];
     int f = have ? rs.flag : 0;
-    float M = have ? rs.m : -INFINITY;
+    double M = have ? rs.m : -INFINITY;
     for (int o = 32; o > 0; o >>= 1) {
-      M = fmaxf(M, __shfl_xor(M, o, 64));
+      M = fmax(M, __shfl_xor(M, o, 64));
       f |= __shfl_xor(f, o, 64);
     }
-    const double c = (have && rs.s > 0.0) ? exp((double)rs.m - (double)M) : 0.0;
+    const double c = (have && rs.s > 0.0) ? exp(rs.m - M) : 0.0;
     double cs = have ? c * rs.s : 0.0;
     for (int o = 32; o > 0; o >>= 1) cs += __shfl_xor(cs, o, 64);
     s_c[j] = c;
@@ -266,6 +295,41 @@ __global__ __launch_bounds__(NT) void grad_h_compact_kernel(const RowStats* __re
     out[d] = (T)(gs * (float)((double)ldf<T>(W, yc * H + d) - o * inv_s));
   }
 }
+// Rows the forward sweep flagged (a logit above the split's reference by more
+// than the slack, in any split): numbered with an integer counter (their
+// order varies between calls, each row's results do not), up to cap2 of them
+// listed with their largest logit as the reference for the second pass;
+// pos[row] = its number, or -1 (not flagged, or past cap2: then the merge
+// recomputes the row on the vector ALU).
+__global__ void flag_init_kernel(int* __restrict__ count) {
+  if (threadIdx.x == 0) *count = 0;
+}
+
+__global__ __launch_bounds__(NT) void flag_scan_kernel(const RowStats* __restrict__ stats, int Sv, int64_t N,
+                                                       int cap2, int* __restrict__ idx, float* __restrict__ mref,
+                                                       int* __restrict__ pos, int* __restrict__ count) {
+  for (int64_t r = (int64_t)blockIdx.x * NT + threadIdx.x; r < N; r += (int64_t)gridDim.x * NT) {
+    int f = 0;
+    float zm = -INFINITY;
+    for (int j = 0; j < Sv; ++j) {
+      const RowStats rs = stats[(int64_t)j * N + r];
+      f |= rs.flag;
+      zm = fmaxf(zm, rs.zmax);
+    }
+    int k = -1;
+    if (f) {
+      k = atomicAdd(count, 1);
+      if (k < cap2) {
+        idx[k] = (int)r;
+        mref[k] = zm;
+      } else {
+        k = -1;
+      }
+    }
+    pos[r] = k;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Loss stage
 // ---------------------------------------------------------------------------
@@ -908,9 +972,23 @@ inline unsigned grid_for(int64_t n, int per_block) {
 
 }  // namespace
 
+hipError_t launch_flag_scan(const RowStats* stats, int Sv, int64_t N, int cap2, int* idx, float* mref, int* pos,
+                            int* count, hipStream_t st) {
+  hipLaunchKernelGGL(flag_init_kernel, dim3(1), dim3(64), 0, st, count);
+  if (N > 0)
+    hipLaunchKernelGGL(flag_scan_kernel, dim3(grid_for(N, NT)), dim3(NT), 0, st, stats, Sv, N, cap2, idx, mref, pos,
+                       count);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int Sv, int64_t N, int H, int V,
                           const void* h, const void* W, const void* b, float inv_tau, const int64_t* y, float* lp,
-                          float* ent, float* lse, float* vout, hipStream_t st) {
+                          float* ent, float* lse, float* vout, hipStream_t st, const FlaggedPass* fp) {
+  const int* pos = fp ? fp->pos : nullptr;
+  const RowStats* st2 = fp ? fp->stats : nullptr;
+  const float* O2 = fp ? fp->O : nullptr;
+  const int* cnt2 = fp ? fp->count : nullptr;
+  const int cap2 = fp ? fp->cap : 0, ms2 = fp ? fp->max_splits : 1;
   if (N <= 0) return hipSuccess;
   const size_t lds = row_exact_smem_bytes(H);
   const bool early = Sv > 1 && Sv <= kEarlySplits && vout != nullptr;
@@ -918,18 +996,18 @@ hipError_t launch_combine(int dtype, const RowStats* stats, const float* O, int 
     const float *hh = (const float*)h, *WW = (const float*)W, *bb = (const float*)b;
     if (early)
       hipLaunchKernelGGL((combine_kernel<float, true>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H, V,
-                         hh, WW, bb, inv_tau, y, lp, ent, lse, vout);
+                         hh, WW, bb, inv_tau, y, lp, ent, lse, vout, pos, st2, O2, cnt2, cap2, ms2);
     else
       hipLaunchKernelGGL((combine_kernel<float, false>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H, V,
-                         hh, WW, bb, inv_tau, y, lp, ent, lse, vout);
+                         hh, WW, bb, inv_tau, y, lp, ent, lse, vout, pos, st2, O2, cnt2, cap2, ms2);
   } else {
     const __bf16 *hh = (const __bf16*)h, *WW = (const __bf16*)W, *bb = (const __bf16*)b;
     if (early)
       hipLaunchKernelGGL((combine_kernel<__bf16, true>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H, V,
-                         hh, WW, bb, inv_tau, y, lp, ent, lse, vout);
+                         hh, WW, bb, inv_tau, y, lp, ent, lse, vout, pos, st2, O2, cnt2, cap2, ms2);
     else
       hipLaunchKernelGGL((combine_kernel<__bf16, false>), dim3((unsigned)N), dim3(NT), lds, st, stats, O, Sv, N, H,
-                         V, hh, WW, bb, inv_tau, y, lp, ent, lse, vout);
+                         V, hh, WW, bb, inv_tau, y, lp, ent, lse, vout, pos, st2, O2, cnt2, cap2, ms2);
   }
   return hipGetLastError();
 }
@@ -1000,7 +1078,8 @@ hipError_t launch_compact_scatter(const float* g, const float* lse, const int64_
 
 hipError_t launch_gather_rows(int dtype, const void* X, const int* idx, const int* count_dev, int64_t cap, int H,
                               void* Xc, hipStream_t st) {
-  const unsigned grid = grid_for(cap, 1);
+  // the rows are known only on the device: a bounded grid walks them
+  const unsigned grid = (unsigned)(cap < 4096 ? (cap > 0 ? cap : 1) : 4096);
   if (dtype == 0)
     hipLaunchKernelGGL((gather_rows_kernel<float>), dim3(grid), dim3(NT), 0, st, (const float*)X, idx, count_dev,
                        cap, H, (float*)Xc);

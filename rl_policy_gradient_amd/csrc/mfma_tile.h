@@ -63,7 +63,6 @@ constexpr int NW = 4;    // waves per workgroup
 // running sum far inside fp32 and bf16 range.
 constexpr float kRefSlack = 64.0f;
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr double kLn2 = 0.693147180559945309417;
 constexpr float kRefSlack2 = kRefSlack * kLog2e;  // the slack in base-2 units
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));

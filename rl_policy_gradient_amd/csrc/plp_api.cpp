@@ -37,6 +37,12 @@ int ok() {
 constexpr size_t kAlign = 256;
 constexpr int kBQ = 64, kBK = 32;
 constexpr int kMaxSplits = 64;
+// Rows of the second forward pass over flagged rows per call of the sweep
+// (more flagged rows than this are recomputed by the merge on the vector
+// ALU), and the row capacity of that pass's statistics and accumulator over
+// all its splits (splits x row blocks < 512 while the splits are above one).
+constexpr int64_t kFlagCap = 32768;
+constexpr int64_t kFlagRows = 512 * 64;
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
 // plp_args as of ABI version 1 (fields up to chunk_sequences); later fields
 // read as their defaults when struct_size ends before them.
@@ -126,9 +132,9 @@ struct Bufs {
   float* tail = nullptr;       // partial sums of the weight-gradient sweep's split tail blocks
   float* gW_acc = nullptr;
   float* gb_acc = nullptr;
-  RowStats* stats2 = nullptr;  // compacted accumulator pass (o_compact)
-  float* O2 = nullptr;
-  void* hcn = nullptr;         // its gathered hidden rows, natural layout
+  RowStats* stats2 = nullptr;  // compacted accumulator passes: the rows with g != 0 (o_compact) and the
+  float* O2 = nullptr;         // flagged rows of a forward sweep (one at a time)
+  FlaggedPass fp{};
 };
 
 Plan make_plan(const plp_args* a, bool need_o, bool need_gw, bool need_gb) {
@@ -165,11 +171,20 @@ size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
   const int H = a->H, V = a->V;
   if (p.mfma) b.Wf = c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H);
   b.stats = c.take<RowStats>((size_t)p.Sv * p.Nc);
-  if (p.o_compact) {
-    b.stats2 = c.take<RowStats>((size_t)p.o2_rows);
-    b.O2 = c.take<float>((size_t)p.o2_rows * H);
-    b.hcn = c.take<char>((size_t)p.cap * H * esize(a->dtype));
-  } else if (p.need_o) {
+  if (p.mfma) {
+    const int64_t rows2 = p.o_compact ? p.o2_rows : kFlagRows;
+    b.stats2 = c.take<RowStats>((size_t)rows2);
+    b.O2 = c.take<float>((size_t)rows2 * H);
+    b.fp.cap = (int)std::min(p.cap, kFlagCap);
+    b.fp.idx = c.take<int>((size_t)b.fp.cap);
+    b.fp.mref = c.take<float>((size_t)b.fp.cap);
+    b.fp.pos = c.take<int>((size_t)p.Nc);
+    b.fp.count = c.take<int>(1);
+    b.fp.stats = b.stats2;
+    b.fp.O = b.O2;
+    b.fp.max_splits = kMaxSplits;
+  }
+  if (p.need_o && !p.o_compact) {
     b.O = c.take<float>((size_t)p.Sv * p.Nc * H);
     b.v = p.Sv == 1 ? b.O : c.take<float>((size_t)p.Nc * H);
   }
@@ -314,6 +329,50 @@ LossParams loss_params(const plp_args* a, const unsigned long long* ntok_dev) {
   return p;
 }
 
+// The second forward pass: the rows the sweep flagged (up to fp.cap) listed
+// with their largest logit and swept again, read through the list, with that logit as
+// their exponent reference, which nothing can exceed; the merge takes their
+// statistics and accumulator from this pass. A call with no flagged row
+// costs the listing and the launches, whose workgroups find no row.
+hipError_t flagged_pass(int dtype, const void* h, const __bf16* Wf, const __bf16* bias, const RowStats* stats, int Sv,
+                        int64_t n, int H, int V, float inv_tau, const FlaggedPass& fp, hipStream_t st) {
+  (void)dtype;
+  hipError_t e = launch_flag_scan(stats, Sv, n, fp.cap, fp.idx, fp.mref, fp.pos, fp.count, st);
+  if (e != hipSuccess) return e;
+  return launch_fwd_mfma((const __bf16*)h, Wf, bias, fp.cap, H, V, inv_tau, fp.max_splits, true, fp.stats, fp.O, st,
+                         fp.count, fp.mref, 1, fp.idx);
+}
+
+// Workspace of plp_selective_entropy (sizes only when ws is NULL).
+struct SelBufs {
+  bool mfma = false;
+  int sv = 1;
+  RowStats* stats = nullptr;
+  float* scratch_lp = nullptr;
+  __bf16* Wf = nullptr;
+  FlaggedPass fp{};
+};
+
+size_t carve_selective(void* ws, int64_t N, int H, int V, int dtype, SelBufs& sb) {
+  Carver c(ws);
+  sb.mfma = mfma_eligible(dtype, H);
+  sb.sv = choose_splits(N, V, sb.mfma);
+  sb.stats = c.take<RowStats>((size_t)sb.sv * N);
+  sb.scratch_lp = c.take<float>(N);
+  if (sb.mfma) {
+    sb.Wf = c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H);
+    sb.fp.cap = (int)std::min(round_up(N, kBK), kFlagCap);
+    sb.fp.idx = c.take<int>((size_t)sb.fp.cap);
+    sb.fp.mref = c.take<float>((size_t)sb.fp.cap);
+    sb.fp.pos = c.take<int>((size_t)N);
+    sb.fp.count = c.take<int>(1);
+    sb.fp.stats = c.take<RowStats>((size_t)kFlagRows);
+    sb.fp.O = c.take<float>((size_t)kFlagRows * H);
+    sb.fp.max_splits = kMaxSplits;
+  }
+  return c.off + kAlign;
+}
+
 // Forward sweep + merge for rows [r0, r0 + n).
 int forward_rows(const plp_args* a, const Plan& p, Bufs& b, int64_t r0, int64_t n, bool with_o, hipStream_t st) {
   const size_t es = esize(a->dtype);
@@ -326,12 +385,14 @@ int forward_rows(const plp_args* a, const Plan& p, Bufs& b, int64_t r0, int64_t 
     HIP_TRY(launch_fwd_mfma((const __bf16*)h, b.Wf, (const __bf16*)a->bias, n, a->H, a->V, inv_tau, p.Sv, with_o,
                             b.stats, with_o ? b.O : nullptr, st));
     if (ev) HIP_TRY(hipEventRecord(ev[1], st));
+    HIP_TRY(flagged_pass(a->dtype, h, b.Wf, (const __bf16*)a->bias, b.stats, p.Sv, n, a->H, a->V, inv_tau, b.fp, st));
   } else {
     HIP_TRY(launch_fwd_generic(a->dtype, h, a->weight, a->bias, y, n, a->H, a->V, inv_tau, with_o, b.stats,
                                with_o ? b.O : nullptr, st));
   }
   HIP_TRY(launch_combine(a->dtype, b.stats, with_o ? b.O : nullptr, p.Sv, n, a->H, a->V, h, a->weight, a->bias,
-                         inv_tau, y, b.lp + r0, b.ent + r0, b.lse + r0, with_o ? b.v : nullptr, st));
+                         inv_tau, y, b.lp + r0, b.ent + r0, b.lse + r0, with_o ? b.v : nullptr, st,
+                         p.mfma ? &b.fp : nullptr));
   return PLP_OK;
 }
 
@@ -539,11 +600,13 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
     if (p.need_gw || p.o_compact)
       HIP_TRY(launch_compact_scatter(g, b.lse + r0, a->targets + r0, n, inv_tau, cnt32, b.idx, b.tok, b.count, st));
     if (p.o_compact) {
-      HIP_TRY(launch_gather_rows(a->dtype, hsrc, b.idx, b.count, p.cap, H, b.hcn, st));
       hipEvent_t* ev = prof_slot(0);
       if (ev) HIP_TRY(hipEventRecord(ev[0], st));
-      HIP_TRY(launch_fwd_mfma((const __bf16*)b.hcn, b.Wf, (const __bf16*)a->bias, p.cap, H, V, inv_tau, kMaxSplits,
-                              true, b.stats2, b.O2, st, b.count));
+      // each row's log-sum-exp (lse >= every logit of the row) as its
+      // exponent reference: nothing to flag in this pass
+      static_assert(offsetof(TokData, lse) == 0 && sizeof(TokData) == 4 * sizeof(float), "lse every 4 floats");
+      HIP_TRY(launch_fwd_mfma((const __bf16*)hsrc, b.Wf, (const __bf16*)a->bias, p.cap, H, V, inv_tau, kMaxSplits,
+                              true, b.stats2, b.O2, st, b.count, (const float*)b.tok, 4, b.idx));
       if (ev) HIP_TRY(hipEventRecord(ev[1], st));
       HIP_TRY(launch_grad_h_compact(a->dtype, b.stats2, b.O2, kMaxSplits, p.cap, H, V, hsrc, a->weight, a->bias,
                                     inv_tau, b.idx, b.tok, b.count, gh, st));
@@ -586,10 +649,8 @@ PLP_API int plp_selective_entropy_workspace_size(int64_t N, int32_t H, int32_t V
   if (!bytes) return fail(PLP_E_INVALID, "bytes is NULL");
   if (N < 1 || N >= kMaxRows || H < 1 || V < 1) return fail(PLP_E_INVALID, "bad sizes N=%lld H=%d V=%d", (long long)N, H, V);
   if (dtype != PLP_DTYPE_F32 && dtype != PLP_DTYPE_BF16) return fail(PLP_E_INVALID, "unknown dtype %d", dtype);
-  const bool mfma = mfma_eligible(dtype, H);
-  const int sv = choose_splits(N, V, mfma);
-  *bytes = align_up((size_t)sv * N * sizeof(RowStats)) + align_up((size_t)N * sizeof(float)) + kAlign;
-  if (mfma) *bytes += align_up((size_t)round_up(V, 2 * kBK) * H * sizeof(__bf16));
+  SelBufs sb;
+  *bytes = carve_selective(nullptr, N, H, V, dtype, sb);
   return ok();
 }
 
@@ -607,23 +668,21 @@ PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const 
   if (!mfma_eligible(dtype, H) && !generic_eligible(H)) return fail(PLP_E_UNSUPPORTED, "H=%d is not supported", H);
   rc = check_ws(ws, ws_bytes, need);
   if (rc) return rc;
-  const bool mfma = mfma_eligible(dtype, H);
-  const int sv = choose_splits(N, V, mfma);
-  Carver c(ws);
-  RowStats* stats = c.take<RowStats>((size_t)sv * N);
-  float* scratch_lp = c.take<float>(N);
-  __bf16* Wf = mfma ? c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H) : nullptr;
+  SelBufs sb;
+  carve_selective(ws, N, H, V, dtype, sb);
   const int64_t* y = targets;  // may be NULL: no target logit is taken
   const float inv_tau = 1.0f / temperature;
-  if (mfma) {
-    HIP_TRY(launch_frag_copy((const __bf16*)weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H, Wf, st));
-    HIP_TRY(launch_fwd_mfma((const __bf16*)hidden, Wf, (const __bf16*)bias, N, H, V, inv_tau, sv, false, stats, nullptr,
-                            st));
+  if (sb.mfma) {
+    HIP_TRY(launch_frag_copy((const __bf16*)weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H, sb.Wf, st));
+    HIP_TRY(launch_fwd_mfma((const __bf16*)hidden, sb.Wf, (const __bf16*)bias, N, H, V, inv_tau, sb.sv, false,
+                            sb.stats, nullptr, st));
+    HIP_TRY(flagged_pass(dtype, hidden, sb.Wf, (const __bf16*)bias, sb.stats, sb.sv, N, H, V, inv_tau, sb.fp, st));
   }
   else
-    HIP_TRY(launch_fwd_generic(dtype, hidden, weight, bias, y, N, H, V, inv_tau, false, stats, nullptr, st));
-  HIP_TRY(launch_combine(dtype, stats, nullptr, sv, N, H, V, hidden, weight, bias, inv_tau, y,
-                         logp_out ? logp_out : (y ? scratch_lp : nullptr), entropy_out, nullptr, nullptr, st));
+    HIP_TRY(launch_fwd_generic(dtype, hidden, weight, bias, y, N, H, V, inv_tau, false, sb.stats, nullptr, st));
+  HIP_TRY(launch_combine(dtype, sb.stats, nullptr, sb.sv, N, H, V, hidden, weight, bias, inv_tau, y,
+                         logp_out ? logp_out : (y ? sb.scratch_lp : nullptr), entropy_out, nullptr, nullptr, st,
+                         sb.mfma ? &sb.fp : nullptr));
   return ok();
 }
 

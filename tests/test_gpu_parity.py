@@ -183,14 +183,16 @@ def test_fused_bnpo_chunk_invariance():
         assert rel_l2(o["grad_hidden"], outs[0]["grad_hidden"]) < 1e-2
 
 
-@pytest.mark.parametrize("q", [1.0, 0.5])
-def test_fused_flagged_rows_recomputed(q):
+@pytest.mark.parametrize("q,B,T", [(1.0, 2, 40), (0.5, 2, 40), (1.0, 1, 33000)])
+def test_fused_flagged_rows_recomputed(q, B, T):
     """Logits far above the first vocabulary tile's max (bias -100 on the first
-    tile, +60 further on) make the MFMA sweep flag the rows; the merge
-    recomputes them exactly. With q < 1 the grad_h accumulator runs as its own
-    pass over the rows with a gradient, whose merge recomputes them too."""
-    spec = synth.small("flagged", cfg_id=108, B=2, T=40, H=128, V=1000, bias=True, top_entropy_quantile=q)
-    _say(f"flagged rows q={q}")
+    tile, +60 further on) make the MFMA sweep flag the rows; a second sweep
+    takes them again against their largest logit. With q < 1 the grad_h
+    accumulator runs as its own pass over the rows with a gradient, against
+    their log-sum-exp. With 33000 flagged rows, the 232 past the second
+    sweep's 32768 are recomputed by the merge on the vector ALU."""
+    spec = synth.small("flagged", cfg_id=108, B=B, T=T, H=128, V=1000, bias=True, top_entropy_quantile=q)
+    _say(f"flagged rows q={q} B={B} T={T}")
     d = synth.make(spec)
     b = d["b"].copy()
     b[:32] = -100.0
@@ -247,6 +249,26 @@ def test_selective_entropy(case):
     np.testing.assert_allclose(lp.cpu().numpy(), ref["logp"], rtol=0, atol=tol)
     assert none is None
     np.testing.assert_array_equal(ent.cpu().numpy(), ent2.cpu().numpy())
+
+
+def test_selective_entropy_flagged_rows():
+    """The no-grad entropy entry point with logits far above the first
+    tile's (bias -100 on it, +60 further on): every row flagged and taken
+    again by the second sweep."""
+    import rl_policy_gradient_amd as plp
+    spec = synth.small("se_flag", cfg_id=109, B=1, T=300, H=256, V=1500, bias=True, w_std=0.05)
+    _say("selective_entropy flagged rows")
+    d = synth.make(spec)
+    b = d["b"].copy()
+    b[:32] = -100.0
+    b[900:905] = 60.0
+    b_raw = synth.round_bf16_bits(b)
+    ref = oracle.forward_rows(d["h"], d["W"], synth.bf16_bits_to_f32(b_raw), 1.0, d["targets"])
+    ent, lp = plp.selective_entropy(dev_tensor(d["h_raw"], "bf16"), dev_tensor(d["W_raw"], "bf16"),
+                                    dev_tensor(b_raw, "bf16"), dev_tensor(d["targets"]))
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(ent.cpu().numpy(), ref["entropy"], rtol=0, atol=1e-4)
+    np.testing.assert_allclose(lp.cpu().numpy(), ref["logp"], rtol=0, atol=1e-4)
 
 
 

@@ -59,3 +59,20 @@ def test_noalloc_no_active_entry():
     _call_both(H, np.ones(N, bool), 0.3)
     m_ws, t_ws, m_na, t_na = _call_both(H, np.zeros(N, bool), 0.3)
     assert m_na.sum() == 0 and np.isnan(t_na) and np.isnan(t_ws)
+
+
+def test_noalloc_python_binding_into_given_outputs():
+    """The package's binding of the same name writes into the caller's
+    outputs and agrees with the workspace entry point."""
+    require_gpu()
+    import rl_policy_gradient_amd as plp
+    r = np.random.default_rng(5)
+    H = (r.standard_normal(7000) + 3).astype(np.float32)
+    active = (r.uniform(size=7000) < 0.7).astype(np.uint8)
+    e, a = dev_tensor(H), dev_tensor(active)
+    out = (torch.empty(7000, dtype=torch.uint8, device="cuda"), torch.empty(1, dtype=torch.float32, device="cuda"))
+    m, t = plp.entropy_quantile_mask_noalloc(e, a, 0.25, out=out)
+    m_ws, t_ws = plp.entropy_quantile_mask(e, a, 0.25)
+    torch.cuda.synchronize()
+    assert m is out[0] and t is out[1]
+    assert torch.equal(m, m_ws) and torch.equal(t, t_ws)
