@@ -10,6 +10,10 @@ The default workload is the largest one-GPU shape: GMPO at B=128, T=32768
 --config 2 is B=1 T=512, 3 is B=8 T=2048 GMPO + K3 KL, 4 is B=2 T=32768
 GSPO-token with the entropy mask.
 
+--prepared-weight makes the weight's matrix-core copy once before the timed
+steps (the case of several calls per weight update); the line's workload
+name carries "+prepared_weight".
+
 --loss runs the workload's inputs under another loss type (same clip
 parameters); --token-advantages gives every completion token its own
 advantage (N(0,1), zero off the completion) instead of one per sequence.
@@ -241,6 +245,10 @@ def main() -> int:
     ap.add_argument("--token-advantages", action="store_true")
     ap.add_argument("--kl-bias-correction", action="store_true",
                     help="K3 KL weighted by the token importance ratio (workloads with a KL term)")
+    ap.add_argument("--prepared-weight", action="store_true",
+                    help="make the weight's matrix-core copy once, before the timed steps (plp_prepare_weight), "
+                         "as for the calls between two weight updates, e.g. the micro-batches of a gradient "
+                         "accumulation; the steps then skip that copy")
     ap.add_argument("--memory-sweep", action="store_true",
                     help="peak device memory of one fused call over vocabulary sizes and token counts (one line each)")
     ap.add_argument("--bias-std", type=float, default=None,
@@ -317,11 +325,15 @@ def main() -> int:
     torch.cuda.reset_peak_memory_stats(dev)
     ws = torch.empty(plp.workspace_size(spec.B, spec.T, H, V, bias=spec.bias,
                                         top_entropy_quantile=spec.top_entropy_quantile,
-                                        chunk_sequences=spec.chunk_sequences, loss_type=spec.loss_type),
+                                        chunk_sequences=spec.chunk_sequences, loss_type=spec.loss_type,
+                                        weight_prepared=args.prepared_weight),
                      dtype=torch.uint8, device=dev)
+    wprep = plp.prepare_weight(inp["weight"]) if args.prepared_weight else None
+    if wprep is not None:
+        variant += "+prepared_weight"
     call_args = (inp["hidden"], inp["weight"], inp["targets"], inp["completion_mask"], inp["advantages"])
     call_kw = dict(bias=inp["bias"], old_logp=inp["old_logp"], ref_logp=inp["ref_logp"], workspace=ws,
-                   token_advantages=tadv, **kw)
+                   token_advantages=tadv, weight_prepared=wprep, **kw)
     out = plp.fused_lmhead_policy_loss_fwd_bwd(*call_args, **call_kw)
     out["dlogp"] = torch.empty(N, dtype=torch.float32, device=dev)
     for _ in range(args.warmup):
@@ -425,11 +437,13 @@ def main() -> int:
         # sweep's 4HV per token with a gradient (its logits are recomputed)
         "executed_tflops": round((fwd_flops + 2.0 * wg_flops) / (elapsed / args.steps) / 1e12, 2),
         "memory": {"inputs_bytes": int(mem_inputs), "workspace_bytes": int(ws.numel()),
+                   "prepared_weight_bytes": int(wprep.numel()) if wprep is not None else 0,
                    "peak_bytes_beyond_inputs": int(peak_delta)},
         "config": {"workload": workload, "B": spec.B, "T": spec.T, "H": H, "V": V,
                    "loss_type": spec.loss_type, "bias": spec.bias, "beta": spec.beta,
                    "top_entropy_quantile": spec.top_entropy_quantile, "chunk_sequences": spec.chunk_sequences,
                    "token_advantages": tadv is not None, "kl_bias_correction": spec.kl_bias_correction,
+                   "weight_prepared_outside_steps": wprep is not None,
                    "global_batch_tokens": N, "active_tokens_with_grad": n_active,
                    "event_ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4)},
         "roofline": roofline,

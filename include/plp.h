@@ -61,7 +61,7 @@ extern "C" {
 #endif
 
 #define PLP_API __attribute__((visibility("default")))
-#define PLP_ABI_VERSION 3
+#define PLP_ABI_VERSION 4
 
 /* Return codes. */
 #define PLP_OK 0
@@ -169,6 +169,19 @@ typedef struct plp_args {
                                    taken. The mean_kl metric reports the corrected term. Only
                                    read when beta != 0 or ref_logp is given. Default 0. */
   int32_t pad1;
+  /* ---- ABI version 4 ---- */
+  const void* weight_prepared;  /* the matrix-core copy of `weight` that plp_prepare_weight
+                                   made from its current values, or NULL (default): the call
+                                   then makes that copy itself, in its workspace. Given, the
+                                   call reads the weight's tiles from it and skips the copy,
+                                   and the workspace it needs shrinks by that copy's size; the
+                                   caller keeps it in step with `weight` (prepare again after
+                                   every change of the weight, e.g. once per optimizer step
+                                   for all the micro-batches of a gradient accumulation).
+                                   `weight` is still required: the target logit, the exact
+                                   recompute and nothing else read it. bf16 with H a multiple
+                                   of 128 up to 896 only (PLP_E_UNSUPPORTED otherwise);
+                                   16-byte aligned. */
 } plp_args;
 
 /* Outputs of the fused call. Every pointer except loss and metrics may be
@@ -194,8 +207,9 @@ PLP_API int plp_abi_version(void);
 PLP_API const char* plp_last_error(void);
 
 /* Workspace bytes needed by plp_fused_lmhead_policy_loss_fwd_bwd for these
- * arguments (only sizes, dtype, bias/NULL-ness, q and chunk_sequences are
- * read; pointers may be NULL). Host-only arithmetic: needs no GPU. */
+ * arguments (only sizes, dtype, the NULL-ness of bias and weight_prepared, q
+ * and chunk_sequences are read; pointers may be NULL). Host-only arithmetic:
+ * needs no GPU. */
 PLP_API int plp_workspace_size(const plp_args* args, size_t* bytes);
 
 /* The whole path: forward statistics, entropy mask (q < 1), loss, metrics and
@@ -211,6 +225,24 @@ PLP_API int plp_workspace_size(const plp_args* args, size_t* bytes);
 PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* args, const plp_outputs* out,
                                                  void* workspace, size_t workspace_bytes,
                                                  hipStream_t stream);
+
+/* The weight's copy in the layout the matrix-core sweeps stream (Liger PR
+ * #1320, "The implementation": the LM-head weight is read tile by tile in
+ * the forward and again in the backward; this is the layout of those tiles):
+ * 32-row tiles, each the four quarter-width column slices one after the
+ * other, each slice in 16-column steps of 64 lanes x 8 bf16 (lane l: row
+ * l % 32, columns 8 (l / 32) .. +7 of the step); rows past V up to a multiple
+ * of 64 are zero. Layout and size are private to this library version; the
+ * copy is only meant as plp_args.weight_prepared of calls on the same weight
+ * values. plp_prepared_weight_size gives its bytes (host arithmetic; no GPU);
+ * plp_prepare_weight writes it from weight [V,H] bf16 into `prepared`
+ * (caller-owned device memory of at least that size, 256-byte aligned),
+ * enqueued on `stream`. bf16 with H a multiple of 128 up to 896 only
+ * (otherwise PLP_E_UNSUPPORTED); NULL or misaligned pointers, a short
+ * buffer, V < 1: PLP_E_INVALID. */
+PLP_API int plp_prepared_weight_size(int32_t H, int32_t V, int32_t dtype, size_t* bytes);
+PLP_API int plp_prepare_weight(const void* weight, int32_t H, int32_t V, int32_t dtype, void* prepared,
+                               size_t prepared_bytes, hipStream_t stream);
 
 /* Streaming entropy and target log-prob over vocabulary tiles without
  * storing logits (PR #1558 "_selective_entropy_forward": running (m, sum

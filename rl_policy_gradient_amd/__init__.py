@@ -23,6 +23,8 @@ __all__ = [
     "entropy_quantile_mask",
     "entropy_quantile_mask_noalloc",
     "policy_loss_from_logprobs",
+    "prepare_weight",
+    "prepared_weight_size",
     "workspace_size",
     "METRIC_NAMES",
     "PlpError",
@@ -82,7 +84,7 @@ def _mask_u8(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
 def _fill_args(hidden, weight, bias, targets, old_logp, ref_logp, completion_mask, ratio_mask, advantages, B, T,
                loss_type, importance_sampling_level, reduction, epsilon_low, epsilon_high, beta, temperature,
                top_entropy_quantile, chunk_sequences, global_tokens=0, token_advantages=None,
-               kl_bias_correction=False) -> _abi.PlpArgs:
+               kl_bias_correction=False, weight_prepared=None) -> _abi.PlpArgs:
     a = _abi.new_args()
     a.B, a.T = int(B), int(T)
     if hidden is not None:
@@ -106,16 +108,18 @@ def _fill_args(hidden, weight, bias, targets, old_logp, ref_logp, completion_mas
     a.global_tokens = int(global_tokens)
     a.token_advantages = _ptr(token_advantages)
     a.kl_bias_correction = 1 if kl_bias_correction else 0
+    a.weight_prepared = _ptr(weight_prepared)
     return a
 
 
 def workspace_size(B, T, H, V, dtype=torch.bfloat16, bias=False, top_entropy_quantile=1.0, chunk_sequences=0,
-                   loss_type="gmpo") -> int:
+                   loss_type="gmpo", weight_prepared=False) -> int:
     """Bytes of workspace the fused call needs (host arithmetic, no GPU)."""
     a = _abi.new_args()
     a.B, a.T, a.H, a.V = B, T, H, V
     a.dtype = _abi.DTYPE_F32 if dtype == torch.float32 else _abi.DTYPE_BF16
     a.bias = 1 if bias else None
+    a.weight_prepared = 256 if weight_prepared else None
     a.loss_type = _LOSS[loss_type]
     a.is_level = _abi.IS_SEQUENCE if loss_type == "gspo_token" else _abi.IS_TOKEN
     a.top_entropy_quantile = top_entropy_quantile
@@ -137,6 +141,7 @@ def fused_lmhead_policy_loss_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor,
                                      chunk_sequences: int = 0, global_tokens: int = 0,
                                      token_advantages: Optional[torch.Tensor] = None,
                                      kl_bias_correction: bool = False,
+                                     weight_prepared: Optional[torch.Tensor] = None,
                                      grad_hidden: bool = True, grad_weight: bool = True,
                                      grad_bias: Optional[bool] = None, diagnostics: bool = False,
                                      workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
@@ -144,7 +149,9 @@ def fused_lmhead_policy_loss_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor,
     GRPO / BNPO / DAPO objective (plp_fused_lmhead_policy_loss_fwd_bwd);
     global_tokens is DAPO's divisor (0 = the batch's completion tokens);
     token_advantages fp32 [B*T] replaces advantages [B] (pass None for it);
-    kl_bias_correction weights each token's K3 term by its importance ratio.
+    kl_bias_correction weights each token's K3 term by its importance ratio;
+    weight_prepared is prepare_weight(weight) made from the weight's current
+    values (the call then skips that copy).
     hidden: [B, T, H] or
     [B*T, H] (then pass B and T); weight [V, H]; targets int64 [B*T];
     masks bool/u8 [B*T]; advantages fp32 [B]. Returns a dict of tensors."""
@@ -168,7 +175,8 @@ def fused_lmhead_policy_loss_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor,
         grad_bias = bias is not None
     a = _fill_args(hidden, weight, bias, targets, old_logp, ref_logp, completion_mask, ratio_mask, advantages, B, T,
                    loss_type, importance_sampling_level, reduction, epsilon_low, epsilon_high, beta, temperature,
-                   top_entropy_quantile, chunk_sequences, global_tokens, token_advantages, kl_bias_correction)
+                   top_entropy_quantile, chunk_sequences, global_tokens, token_advantages, kl_bias_correction,
+                   weight_prepared)
     L = _abi.lib()
     n = ctypes.c_size_t()
     _abi.check(L.plp_workspace_size(ctypes.byref(a), ctypes.byref(n)))
@@ -200,6 +208,28 @@ def fused_lmhead_policy_loss_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor,
     _abi.check(L.plp_fused_lmhead_policy_loss_fwd_bwd(ctypes.byref(a), ctypes.byref(o), ws.data_ptr(),
                                                       ws.numel() * ws.element_size(), _stream(dev)))
     return res
+
+
+def prepared_weight_size(H: int, V: int, dtype=torch.bfloat16) -> int:
+    """Bytes of the weight's matrix-core copy (plp_prepared_weight_size)."""
+    n = ctypes.c_size_t()
+    code = _abi.DTYPE_F32 if dtype == torch.float32 else _abi.DTYPE_BF16
+    _abi.check(_abi.lib().plp_prepared_weight_size(int(H), int(V), code, ctypes.byref(n)))
+    return n.value
+
+
+def prepare_weight(weight: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The matrix-core copy of weight [V, H] (plp_prepare_weight), for the
+    fused call's weight_prepared while the weight keeps these values."""
+    V, H = int(weight.shape[0]), int(weight.shape[1])
+    n = prepared_weight_size(H, V, weight.dtype)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=weight.device)
+    if out.numel() * out.element_size() < n:
+        raise ValueError(f"out holds {out.numel() * out.element_size()} bytes, {n} needed")
+    _abi.check(_abi.lib().plp_prepare_weight(_ptr(weight), H, V, _dtype_code(weight), _ptr(out),
+                                             out.numel() * out.element_size(), _stream(weight.device)))
+    return out
 
 
 def selective_entropy(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,

@@ -67,6 +67,7 @@ class PlpArgs(ctypes.Structure):
         ("token_advantages", _vp),
         ("kl_bias_correction", ctypes.c_int32),
         ("pad1", ctypes.c_int32),
+        ("weight_prepared", _vp),
     ]
 
 
@@ -118,13 +119,15 @@ def lib() -> ctypes.CDLL:
     L.plp_entropy_quantile_mask_noalloc.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_double, _vp, _vp, _vp]
     L.plp_policy_loss_workspace_size.argtypes = [P(PlpArgs), P(sz)]
     L.plp_policy_loss_from_logprobs.argtypes = [P(PlpArgs), _vp, _vp, P(PlpOutputs), _vp, sz, _vp]
+    L.plp_prepared_weight_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(sz)]
+    L.plp_prepare_weight.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, sz, _vp]
     L.plp_profile_start.argtypes = [ctypes.c_int32]
     L.plp_profile_stop.argtypes = [P(ctypes.c_double), P(ctypes.c_int32)]
     L.plp_profile_start.restype = ctypes.c_int
     L.plp_profile_stop.restype = ctypes.c_int
     for name in ("plp_workspace_size", "plp_fused_lmhead_policy_loss_fwd_bwd", "plp_selective_entropy_workspace_size",
                  "plp_selective_entropy", "plp_entropy_quantile_mask_workspace_size", "plp_entropy_quantile_mask",
-                 "plp_entropy_quantile_mask_noalloc",
+                 "plp_entropy_quantile_mask_noalloc", "plp_prepared_weight_size", "plp_prepare_weight",
                  "plp_policy_loss_workspace_size", "plp_policy_loss_from_logprobs"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L

@@ -115,11 +115,13 @@ hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_de
 // compact_stride(that count). With mref (natural-log units of the logits,
 // row k's at mref[k * mref_stride]) every row takes its exponentials against
 // that reference instead of its first tile's maximum; a reference at or
-// above the row's largest logit leaves nothing to flag.
+// above the row's largest logit leaves nothing to flag. clear_count (or
+// NULL; not count_dev) is set to zero by the sweep, for a launch_flag_scan
+// after it.
 hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
                            int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st,
                            const int* count_dev = nullptr, const float* mref = nullptr, int mref_stride = 1,
-                           const int* row_idx = nullptr);
+                           const int* row_idx = nullptr, int* clear_count = nullptr);
 // Row stride of the compacted pass's stats and O (whole 64-row blocks).
 __host__ __device__ inline int64_t compact_stride(int64_t rows) { return (rows + 63) / 64 * 64; }
 // grad_h of the compacted rows k < *count_dev from the compacted pass:
@@ -165,6 +167,8 @@ struct FlaggedPass {
   int cap;
   int max_splits;
 };
+// *count must be zero when the scan starts (the forward sweep before it
+// clears it, see clear_count).
 hipError_t launch_flag_scan(const RowStats* stats, int Sv, int64_t N, int cap2, int* idx, float* mref, int* pos,
                             int* count, hipStream_t st);
 

@@ -18,8 +18,9 @@ template <int KB, bool HAS_BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf,
                      const __bf16* __restrict__ bias, int64_t N, int V, float inv_tau, int Sv,
-                     int tiles_per_split, RowStats* __restrict__ stats) {
+                     int tiles_per_split, RowStats* __restrict__ stats, int* __restrict__ clear_count) {
   constexpr int H = 128 * KB;
+  if (clear_count && blockIdx.x == 0 && threadIdx.x == 0) *clear_count = 0;  // for the flag scan that follows
   constexpr int DS = Stage<KB>::DS;  // columns per wave
   constexpr int KS = DS / 16;        // 16-wide contraction steps per wave
   __shared__ f32x4 s_part[NW][2][4][64];
@@ -248,14 +249,16 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
 // forward_splits(that count, V, Sv) and the row stride of stats and O
 // compact_stride(that count); workgroups past the last block exit at once.
 // With mref the exponent reference of row k is mref[k * mref_stride]
-// (natural units) instead of the maximum of its first tile.
+// (natural units) instead of the maximum of its first tile. clear_count, when
+// given (never the count_dev of the same launch), is set to zero.
 template <int KB, bool HAS_BIAS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, const __bf16* __restrict__ bias,
                    int64_t N_, int V, float inv_tau, int Sv_, int tiles_per_split_, RowStats* __restrict__ stats,
                    float* __restrict__ O, const int* __restrict__ count_dev, const float* __restrict__ mref,
-                   int mref_stride, const int* __restrict__ row_idx) {
+                   int mref_stride, const int* __restrict__ row_idx, int* __restrict__ clear_count) {
   constexpr int H = 128 * KB;
+  if (clear_count && blockIdx.x == 0 && threadIdx.x == 0) *clear_count = 0;  // for the flag scan that follows
   int64_t N = N_, stride = N_;
   int Sv = Sv_, tiles_per_split = tiles_per_split_;
   if (count_dev) {
@@ -540,7 +543,8 @@ void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, 
 template <bool HAS_BIAS>
 hipError_t fwd_pp_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
                          int Sv, RowStats* stats, float* O, const int* count_dev, const float* mref, int mref_stride,
-                         const int* row_idx, hipStream_t st) {
+                         const int* row_idx, int* clear_count, hipStream_t st) {
+  if (clear_count && clear_count == count_dev) return hipErrorInvalidValue;
   const int n_tiles = (V + BK - 1) / BK;
   const int tps = (n_tiles + Sv - 1) / Sv;
   const int64_t nrb = (N + BQ - 1) / BQ;
@@ -552,7 +556,7 @@ hipError_t fwd_pp_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int
 #define PLP_PP_CASE(K)                                                                                                \
   case K:                                                                                                             \
     hipLaunchKernelGGL((fwd_pp_kernel<K, HAS_BIAS>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats, O,  \
-                       count_dev, mref, mref_stride, row_idx);                                                        \
+                       count_dev, mref, mref_stride, row_idx, clear_count);                                           \
     break;
     PLP_PP_CASE(1)
     PLP_PP_CASE(2)
@@ -570,7 +574,7 @@ hipError_t fwd_pp_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int
 
 template <bool HAS_BIAS>
 hipError_t fwd_stats_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V,
-                            float inv_tau, int Sv, RowStats* stats, hipStream_t st) {
+                            float inv_tau, int Sv, RowStats* stats, int* clear_count, hipStream_t st) {
   const int n_tiles = (V + BK - 1) / BK;
   const int tps = (n_tiles + Sv - 1) / Sv;
   const int64_t nrb = (N + BQ - 1) / BQ;
@@ -578,7 +582,8 @@ hipError_t fwd_stats_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, 
   switch (H / 128) {
 #define PLP_FWD_CASE(K)                                                                                              \
   case K:                                                                                                            \
-    hipLaunchKernelGGL((fwd_mfma_kernel<K, HAS_BIAS>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats); \
+    hipLaunchKernelGGL((fwd_mfma_kernel<K, HAS_BIAS>), grid, block, 0, st, h, Wf, b, N, V, inv_tau, Sv, tps, stats,   \
+                       clear_count);                                                                                 \
     break;
     PLP_FWD_CASE(1)
     PLP_FWD_CASE(2)
@@ -600,6 +605,6 @@ hipError_t fwd_stats_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, 
 // lmhead_fwd_o.hip; b may be NULL.
 hipError_t launch_fwd_mfma_o(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
                              int Sv, RowStats* stats, float* O, const int* count_dev, const float* mref,
-                             int mref_stride, const int* row_idx, hipStream_t st);
+                             int mref_stride, const int* row_idx, int* clear_count, hipStream_t st);
 
 }  // namespace plp

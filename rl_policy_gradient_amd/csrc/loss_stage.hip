@@ -301,20 +301,31 @@ __global__ __launch_bounds__(NT) void grad_h_compact_kernel(const RowStats* __re
 // listed with their largest logit as the reference for the second pass;
 // pos[row] = its number, or -1 (not flagged, or past cap2: then the merge
 // recomputes the row on the vector ALU).
-__global__ void flag_init_kernel(int* __restrict__ count) {
-  if (threadIdx.x == 0) *count = 0;
-}
-
+// The counter starts at zero: the forward sweep before the scan clears it.
 __global__ __launch_bounds__(NT) void flag_scan_kernel(const RowStats* __restrict__ stats, int Sv, int64_t N,
                                                        int cap2, int* __restrict__ idx, float* __restrict__ mref,
                                                        int* __restrict__ pos, int* __restrict__ count) {
+  static_assert(offsetof(RowStats, flag) == offsetof(RowStats, zmax) + 4, "zmax and flag adjacent");
   for (int64_t r = (int64_t)blockIdx.x * NT + threadIdx.x; r < N; r += (int64_t)gridDim.x * NT) {
     int f = 0;
     float zm = -INFINITY;
-    for (int j = 0; j < Sv; ++j) {
-      const RowStats rs = stats[(int64_t)j * N + r];
-      f |= rs.flag;
-      zm = fmaxf(zm, rs.zmax);
+    // (zmax, flag) of each split, eight loads in flight at a time
+    auto zf = [&](int j) { return *reinterpret_cast<const float2*>(&stats[(int64_t)j * N + r].zmax); };
+    int j = 0;
+    for (; j + 8 <= Sv; j += 8) {
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = zf(j + u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        zm = fmaxf(zm, v[u].x);
+        f |= __float_as_int(v[u].y);
+      }
+    }
+    for (; j < Sv; ++j) {
+      const float2 v = zf(j);
+      zm = fmaxf(zm, v.x);
+      f |= __float_as_int(v.y);
     }
     int k = -1;
     if (f) {
@@ -974,7 +985,6 @@ inline unsigned grid_for(int64_t n, int per_block) {
 
 hipError_t launch_flag_scan(const RowStats* stats, int Sv, int64_t N, int cap2, int* idx, float* mref, int* pos,
                             int* count, hipStream_t st) {
-  hipLaunchKernelGGL(flag_init_kernel, dim3(1), dim3(64), 0, st, count);
   if (N > 0)
     hipLaunchKernelGGL(flag_scan_kernel, dim3(grid_for(N, NT)), dim3(NT), 0, st, stats, Sv, N, cap2, idx, mref, pos,
                        count);

@@ -60,6 +60,10 @@ int kl_bias_correction(const plp_args* a) {
   return a->struct_size >= offsetof(plp_args, kl_bias_correction) + sizeof(int32_t) && a->kl_bias_correction ? 1 : 0;
 }
 
+const void* weight_prepared(const plp_args* a) {
+  return a->struct_size >= offsetof(plp_args, weight_prepared) + sizeof(void*) ? a->weight_prepared : nullptr;
+}
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -96,6 +100,7 @@ int choose_splits(int64_t rows, int V, bool mfma) {
 
 struct Plan {
   bool mfma = false;
+  bool wprep = false;          // the caller passed the weight's matrix-core copy
   bool need_o = false, need_gw = false, need_gb = false;
   int64_t B = 0, T = 0, N = 0, Bc = 0, Nc = 0, nchunks = 0, cap = 0;
   int Sv = 1, St = 1;
@@ -140,6 +145,7 @@ struct Bufs {
 Plan make_plan(const plp_args* a, bool need_o, bool need_gw, bool need_gb) {
   Plan p;
   p.mfma = mfma_eligible(a->dtype, a->H);
+  p.wprep = p.mfma && weight_prepared(a) != nullptr;
   p.need_o = need_o;
   p.need_gw = need_gw || need_gb;
   p.need_gb = need_gb;
@@ -169,7 +175,10 @@ Plan make_plan(const plp_args* a, bool need_o, bool need_gw, bool need_gb) {
 size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
   Carver c(ws);
   const int H = a->H, V = a->V;
-  if (p.mfma) b.Wf = c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H);
+  if (p.wprep)
+    b.Wf = (__bf16*)weight_prepared(a);  // read only
+  else if (p.mfma)
+    b.Wf = c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H);
   b.stats = c.take<RowStats>((size_t)p.Sv * p.Nc);
   if (p.mfma) {
     const int64_t rows2 = p.o_compact ? p.o2_rows : kFlagRows;
@@ -289,6 +298,17 @@ int check_loss_args(const plp_args* a, bool pointers = true) {
   return PLP_OK;
 }
 
+// weight_prepared: only where the matrix-core sweeps run, 16-byte aligned.
+int check_prepared(const plp_args* a) {
+  const void* wp = weight_prepared(a);
+  if (!wp) return PLP_OK;
+  if (!mfma_eligible(a->dtype, a->H))
+    return fail(PLP_E_UNSUPPORTED, "weight_prepared is for bf16 with H a multiple of 128 up to 896 (dtype %d, H=%d)",
+                a->dtype, a->H);
+  if ((uintptr_t)wp % 16 != 0) return fail(PLP_E_INVALID, "weight_prepared must be 16-byte aligned");
+  return PLP_OK;
+}
+
 int check_fused_args(const plp_args* a) {
   int rc = check_loss_args(a);
   if (rc) return rc;
@@ -300,7 +320,7 @@ int check_fused_args(const plp_args* a) {
   if (!mfma_eligible(a->dtype, a->H) && !generic_eligible(a->H))
     return fail(PLP_E_UNSUPPORTED, "H=%d is not supported (bf16 MFMA path: H multiple of 128 up to 896; "
                                    "generic path: H <= 4096)", a->H);
-  return PLP_OK;
+  return check_prepared(a);
 }
 
 // The batch's completion-token count, when the loss divides by it (BNPO, and
@@ -333,7 +353,8 @@ LossParams loss_params(const plp_args* a, const unsigned long long* ntok_dev) {
 // with their largest logit and swept again, read through the list, with that logit as
 // their exponent reference, which nothing can exceed; the merge takes their
 // statistics and accumulator from this pass. A call with no flagged row
-// costs the listing and the launches, whose workgroups find no row.
+// costs the listing and the launches, whose workgroups find no row. The
+// sweep before it has cleared fp.count (its clear_count).
 hipError_t flagged_pass(int dtype, const void* h, const __bf16* Wf, const __bf16* bias, const RowStats* stats, int Sv,
                         int64_t n, int H, int V, float inv_tau, const FlaggedPass& fp, hipStream_t st) {
   (void)dtype;
@@ -383,7 +404,7 @@ int forward_rows(const plp_args* a, const Plan& p, Bufs& b, int64_t r0, int64_t 
     hipEvent_t* ev = prof_slot(0);
     if (ev) HIP_TRY(hipEventRecord(ev[0], st));
     HIP_TRY(launch_fwd_mfma((const __bf16*)h, b.Wf, (const __bf16*)a->bias, n, a->H, a->V, inv_tau, p.Sv, with_o,
-                            b.stats, with_o ? b.O : nullptr, st));
+                            b.stats, with_o ? b.O : nullptr, st, nullptr, nullptr, 1, nullptr, b.fp.count));
     if (ev) HIP_TRY(hipEventRecord(ev[1], st));
     HIP_TRY(flagged_pass(a->dtype, h, b.Wf, (const __bf16*)a->bias, b.stats, p.Sv, n, a->H, a->V, inv_tau, b.fp, st));
   } else {
@@ -459,6 +480,31 @@ extern "C" {
 
 PLP_API int plp_abi_version(void) { return PLP_ABI_VERSION; }
 
+PLP_API int plp_prepared_weight_size(int32_t H, int32_t V, int32_t dtype, size_t* bytes) {
+  if (!bytes) return fail(PLP_E_INVALID, "bytes is NULL");
+  if (V < 1 || H < 1) return fail(PLP_E_INVALID, "H and V must be >= 1");
+  if (!mfma_eligible(dtype, H))
+    return fail(PLP_E_UNSUPPORTED, "the prepared weight is for bf16 with H a multiple of 128 up to 896 (dtype %d, H=%d)",
+                dtype, H);
+  *bytes = (size_t)round_up(V, 2 * kBK) * H * sizeof(__bf16);
+  return ok();
+}
+
+PLP_API int plp_prepare_weight(const void* weight, int32_t H, int32_t V, int32_t dtype, void* prepared,
+                               size_t prepared_bytes, hipStream_t st) {
+  size_t need = 0;
+  int rc = plp_prepared_weight_size(H, V, dtype, &need);
+  if (rc) return rc;
+  if (!weight || !prepared) return fail(PLP_E_INVALID, "weight and prepared are required");
+  if ((uintptr_t)weight % 16 != 0) return fail(PLP_E_INVALID, "weight must be 16-byte aligned");
+  if ((uintptr_t)prepared % kAlign != 0) return fail(PLP_E_INVALID, "prepared must be 256-byte aligned");
+  if (prepared_bytes < need)
+    return fail(PLP_E_INVALID, "prepared buffer too small: %zu bytes given, %zu needed", prepared_bytes, need);
+  HIP_TRY(launch_frag_copy((const __bf16*)weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H,
+                           (__bf16*)prepared, st));
+  return ok();
+}
+
 PLP_API int plp_profile_start(int32_t max_records) {
   if (max_records < 1) return fail(PLP_E_INVALID, "max_records must be >= 1");
   std::lock_guard<std::mutex> lk(g_prof.mu);
@@ -510,6 +556,9 @@ PLP_API int plp_workspace_size(const plp_args* a, size_t* bytes) {
   if (rc) return rc;
   if (a->H < 1 || a->V < 1) return fail(PLP_E_INVALID, "H and V must be >= 1");
   if (a->dtype != PLP_DTYPE_F32 && a->dtype != PLP_DTYPE_BF16) return fail(PLP_E_INVALID, "unknown dtype %d", a->dtype);
+  if (weight_prepared(a) && !mfma_eligible(a->dtype, a->H))
+    return fail(PLP_E_UNSUPPORTED, "weight_prepared is for bf16 with H a multiple of 128 up to 896 (dtype %d, H=%d)",
+                a->dtype, a->H);
   // Sized for every gradient output, the largest request.
   Plan p = make_plan(a, true, true, a->bias != nullptr);
   Bufs b;
@@ -545,7 +594,7 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
   rc = count_tokens_if_needed(a, b.ntok, st);
   if (rc) return rc;
 
-  if (p.mfma)
+  if (p.mfma && !p.wprep)
     HIP_TRY(launch_frag_copy((const __bf16*)a->weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H, b.Wf, st));
 
   bool first_chunk_done = false;
@@ -675,7 +724,7 @@ PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const 
   if (sb.mfma) {
     HIP_TRY(launch_frag_copy((const __bf16*)weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H, sb.Wf, st));
     HIP_TRY(launch_fwd_mfma((const __bf16*)hidden, sb.Wf, (const __bf16*)bias, N, H, V, inv_tau, sb.sv, false,
-                            sb.stats, nullptr, st));
+                            sb.stats, nullptr, st, nullptr, nullptr, 1, nullptr, sb.fp.count));
     HIP_TRY(flagged_pass(dtype, hidden, sb.Wf, (const __bf16*)bias, sb.stats, sb.sv, N, H, V, inv_tau, sb.fp, st));
   }
   else

@@ -49,9 +49,13 @@ def gpu_inputs(spec: synth.Spec, d: dict) -> dict:
     )
 
 
-def run_gpu(spec: synth.Spec, d: dict, **kw) -> dict:
+def run_gpu(spec: synth.Spec, d: dict, prepare_weight: bool = False, **kw) -> dict:
+    """The fused call on the seeded inputs; prepare_weight: pass the
+    weight's matrix-core copy made beforehand by plp.prepare_weight."""
     import rl_policy_gradient_amd as plp
     g = gpu_inputs(spec, d)
+    if prepare_weight:
+        kw["weight_prepared"] = plp.prepare_weight(g["weight"])
     args = dict(B=spec.B, T=spec.T, loss_type=spec.loss_type, epsilon_low=spec.eps_low,
                 epsilon_high=spec.eps_high, beta=spec.beta, temperature=spec.temperature,
                 top_entropy_quantile=spec.top_entropy_quantile, chunk_sequences=spec.chunk_sequences,

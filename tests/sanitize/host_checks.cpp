@@ -89,6 +89,18 @@ int main() {
               size_t bytes = 0;
               CHECK(plp_workspace_size(&a, &bytes) == PLP_OK);
               CHECK(bytes > 0 && bytes % 256 == 0);
+              // with the caller's matrix-core copy of the weight, less by its size
+              size_t wp = 0;
+              if (plp_prepared_weight_size(H, V, dt, &wp) == PLP_OK) {
+                a.weight_prepared = W;
+                size_t bytes2 = 0;
+                CHECK(plp_workspace_size(&a, &bytes2) == PLP_OK);
+                CHECK(bytes2 + wp == bytes);
+              } else {
+                a.weight_prepared = W;
+                size_t bytes2 = 0;
+                CHECK(plp_workspace_size(&a, &bytes2) == PLP_E_UNSUPPORTED);
+              }
             }
 
   // argument errors of the fused call
@@ -213,6 +225,12 @@ int main() {
     a.top_entropy_quantile = 1.0;
     CHECK(plp_policy_loss_from_logprobs(&a, (const float*)out_buf, nullptr, &o, nullptr, 0, nullptr) ==
           PLP_E_WORKSPACE);
+    CHECK(plp_prepared_weight_size(896, 151936, PLP_DTYPE_BF16, &bytes) == PLP_OK && bytes == (size_t)151936 * 896 * 2);
+    CHECK(plp_prepared_weight_size(896, 151936, PLP_DTYPE_F32, &bytes) == PLP_E_UNSUPPORTED);
+    CHECK(plp_prepared_weight_size(896, 151936, PLP_DTYPE_BF16, nullptr) == PLP_E_INVALID);
+    CHECK(plp_prepare_weight(W, 128, 1000, PLP_DTYPE_BF16, nullptr, 1 << 20, nullptr) == PLP_E_INVALID);
+    CHECK(plp_prepare_weight(W, 128, 1000, PLP_DTYPE_BF16, out_buf, 100, nullptr) == PLP_E_INVALID);
+    CHECK(plp_prepare_weight(W, 100, 1000, PLP_DTYPE_BF16, out_buf, 1 << 20, nullptr) == PLP_E_UNSUPPORTED);
     CHECK(plp_profile_start(0) == PLP_E_INVALID);
     CHECK(plp_profile_stop(nullptr, nullptr) == PLP_E_INVALID);
   }

@@ -109,6 +109,11 @@ def _call(a, o=None, ws=None, ws_bytes=0):
     (lambda a: setattr(a, "struct_size", 8), abi.PLP_E_INVALID, "struct_size"),
     (lambda a: setattr(a, "H", 5000), abi.PLP_E_UNSUPPORTED, "H=5000"),
     (lambda a: setattr(a, "dtype", 7), abi.PLP_E_INVALID, "dtype"),
+    (lambda a: setattr(a, "weight_prepared", 0x5008), abi.PLP_E_INVALID, "weight_prepared must be 16-byte"),
+    (lambda a: (setattr(a, "weight_prepared", 0x5000), setattr(a, "H", 200)), abi.PLP_E_UNSUPPORTED,
+     "weight_prepared is for bf16"),
+    (lambda a: (setattr(a, "weight_prepared", 0x5000), setattr(a, "dtype", abi.DTYPE_F32)), abi.PLP_E_UNSUPPORTED,
+     "weight_prepared is for bf16"),
 ])
 def test_validation_rejects_before_launch(mutate, code, msg):
     a = _valid_args()
@@ -165,7 +170,7 @@ def test_other_entry_points_validate():
     assert "q must lie" in L.plp_last_error().decode()
     a = _valid_args()
     assert L.plp_policy_loss_from_logprobs(ctypes.byref(a), None, None, None, None, 0, None) == abi.PLP_E_INVALID
-    assert L.plp_abi_version() == 3
+    assert L.plp_abi_version() == 4
 
 
 def test_noalloc_quantile_rejects_bad_arguments_on_the_host():
@@ -177,3 +182,43 @@ def test_noalloc_quantile_rejects_bad_arguments_on_the_host():
     assert b"2^31" in L.plp_last_error()
     assert L.plp_entropy_quantile_mask_noalloc(None, None, 10, 1.5, None, None, None) == abi.PLP_E_INVALID
     assert L.plp_entropy_quantile_mask_noalloc(None, None, 10, 0.5, None, None, None) == abi.PLP_E_INVALID
+
+
+def test_version_three_args_ignore_weight_prepared():
+    """A caller built against ABI version 3 (struct_size ending before
+    weight_prepared): the field is not read, so a misaligned value there does
+    not fail the call's checks."""
+    a = _valid_args()
+    a.struct_size = abi.PlpArgs.weight_prepared.offset
+    a.weight_prepared = 0x5008
+    rc, err = _call(a, ws=None, ws_bytes=0)
+    assert rc == abi.PLP_E_WORKSPACE, err
+
+
+def test_prepared_weight_size_and_checks():
+    """The weight's matrix-core copy: V rounded up to 64 rows of H bf16; the
+    fused call's workspace shrinks by exactly that much when the caller
+    passes it; shapes off the matrix-core path and bad buffers are rejected
+    on the host."""
+    import rl_policy_gradient_amd as plp
+    L = _lib()
+    n = ctypes.c_size_t()
+    assert L.plp_prepared_weight_size(896, 151936, abi.DTYPE_BF16, ctypes.byref(n)) == 0
+    assert n.value == 151936 * 896 * 2  # 151936 is a multiple of 64
+    assert L.plp_prepared_weight_size(128, 1000, abi.DTYPE_BF16, ctypes.byref(n)) == 0
+    assert n.value == 1024 * 128 * 2
+    assert plp.prepared_weight_size(128, 1000) == 1024 * 128 * 2
+    assert L.plp_prepared_weight_size(200, 1000, abi.DTYPE_BF16, ctypes.byref(n)) == abi.PLP_E_UNSUPPORTED
+    assert L.plp_prepared_weight_size(128, 1000, abi.DTYPE_F32, ctypes.byref(n)) == abi.PLP_E_UNSUPPORTED
+    assert L.plp_prepared_weight_size(128, 0, abi.DTYPE_BF16, ctypes.byref(n)) == abi.PLP_E_INVALID
+    need = 1024 * 128 * 2
+    assert L.plp_prepare_weight(None, 128, 1000, abi.DTYPE_BF16, 0x10000, need, None) == abi.PLP_E_INVALID
+    assert L.plp_prepare_weight(0x1000, 128, 1000, abi.DTYPE_BF16, 0x10080, need, None) == abi.PLP_E_INVALID
+    assert b"256-byte" in L.plp_last_error()
+    assert L.plp_prepare_weight(0x1000, 128, 1000, abi.DTYPE_BF16, 0x10000, need - 1, None) == abi.PLP_E_INVALID
+    assert b"too small" in L.plp_last_error()
+    for B, V, q, chunk in ((1, 151936, 1.0, 0), (8, 151936, 0.2, 2), (3, 1000, 1.0, 0)):
+        full = plp.workspace_size(B, 512, 896, V, top_entropy_quantile=q, chunk_sequences=chunk)
+        prep = plp.workspace_size(B, 512, 896, V, top_entropy_quantile=q, chunk_sequences=chunk,
+                                  weight_prepared=True)
+        assert full - prep == plp.prepared_weight_size(896, V)

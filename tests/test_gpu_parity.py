@@ -142,6 +142,24 @@ def test_fused_small(name):
     _check_fused(spec, d, gpu, ref)
 
 
+@pytest.mark.parametrize("name", ["mfma_gmpo_kl_bias_tau", "mfma_gspo_q", "mfma_gmpo_q_chunked", "mfma_gmpo_h896",
+                                  "mfma_gmpo_wgrad_launches_chunked"])
+def test_fused_prepared_weight(name):
+    """With the weight's matrix-core copy made beforehand (plp_prepare_weight)
+    the call reads the same tiles: every output bitwise equal to the call
+    that makes the copy itself, and the oracle's bar met."""
+    spec = SMALL[name]
+    _say(f"prepared weight {name} B={spec.B} T={spec.T} H={spec.H} V={spec.V}")
+    d = make_case(spec)
+    a = run_gpu(spec, d)
+    b = run_gpu(spec, d, prepare_weight=True)
+    assert set(a) == set(b)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    if spec.T <= 4096:
+        _check_fused(spec, d, b, run_oracle(spec, d))
+
+
 def test_fused_deterministic():
     spec = SMALL["mfma_gmpo_q_chunked"]
     _say("determinism")
