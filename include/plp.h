@@ -18,7 +18,7 @@
  *   - Streaming entropy and the high-entropy mask: Liger-Kernel PR #1558
  *     "support top_entropy_quantile", Details bullets (second accumulator
  *     sum exp(z-m)*z; H = log_z - sum_exp_z/sum_exp; threshold
- *     quantile(active entropies, 1-q) over the whole batch; the mask
+ *     at 1-q of the active tokens' entropies, one per batch; the mask
  *     multiplies the policy term before the KL penalty; q validated to [0,1],
  *     q = 1 is the feature off).
  *   - GSPO-token: Tinker "GSPO" page, the sequence-ratio, per-token-ratio and

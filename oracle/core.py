@@ -30,7 +30,8 @@ Readings taken where the pages are silent:
       over all B sequences of the batch (global B, so outer chunking does not
       change the result).
   R6  The entropy mask multiplies the per-token policy term of every loss
-      type, GMPO included (PR #1558, "ppo_loss_fn multiplies ...").
+      type, GMPO included (PR #1558, Details: the policy loss function
+      applies the mask after its loss-type branch, for every type).
   R7  KL is K3, exp(ref - lp) - (ref - lp) - 1, reduced like the policy term
       and not multiplied by the entropy mask.
   R8  The clip metric is token-level over the loss tokens M and does not
@@ -210,7 +211,8 @@ def quantile_linear_f32(x32, prob: float) -> np.float32:
 def entropy_quantile_mask(H32, active, q: float):
     """High-entropy token mask (PR #1558, Details bullet 2).
 
-    thr = quantile(active entropies, 1 - q) over the whole batch;
+    thr = quantile of the active tokens' entropies at 1 - q, one threshold
+    for the batch;
     mask = active & H >= thr. q = 1 keeps every active token (the feature off).
     Returns (mask bool [N], thr float32, NaN when undefined).
     """
@@ -449,8 +451,8 @@ def _dz(z, lse, g, y, tau):
 
 def backward(h, W, b, tau: float, targets, lse, g, chunk: int = 256):
     """grad_h = dz W, grad_W = dz^T h, grad_b = sum_t dz with
-    dz = g (onehot - softmax) / tau (PR #1320: input,
-    LM-head weight and bias gradients of the fused linear layer)."""
+    dz = g (onehot - softmax) / tau (PR #1320, The implementation: the
+    fused layer returns gradients for h, W and b)."""
     W64 = np.asarray(W, np.float64)
     b64 = None if b is None else np.asarray(b, np.float64)
     h = np.asarray(h)
@@ -514,7 +516,7 @@ def run(cfg: LossConfig, h, W, b, targets, old, ref, completion_mask, ratio_mask
 
     The outer loop walks chunks of whole sequences (PR #1320 tests outer chunk
     sizes 1, 2 and 5); the entropy threshold is taken over the whole batch
-    before any chunk's loss (PR #1558: chunk_size=1 and chunk_size=B agree).
+    before any chunk's loss (PR #1558: one-sequence chunks give the unchunked result).
     """
     B, T = cfg.B, cfg.T
     tau = cfg.temperature

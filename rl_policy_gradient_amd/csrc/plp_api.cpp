@@ -271,7 +271,7 @@ int check_loss_args(const plp_args* a, bool pointers = true) {
   if (a->is_level != PLP_IS_TOKEN && a->is_level != PLP_IS_SEQUENCE)
     return fail(PLP_E_INVALID, "unknown is_level %d", a->is_level);
   if (a->loss_type == PLP_LOSS_GMPO && a->is_level == PLP_IS_SEQUENCE)
-    return fail(PLP_E_UNSUPPORTED, "GMPO clips at token level before the sequence aggregation; "
+    return fail(PLP_E_UNSUPPORTED, "GMPO clips each token before it aggregates the sequence; "
                                    "sequence-level importance sampling is rejected");
   if (a->loss_type == PLP_LOSS_GSPO_TOKEN && a->is_level == PLP_IS_TOKEN)
     return fail(PLP_E_UNSUPPORTED, "GSPO_TOKEN uses the sequence-level ratio; set is_level = PLP_IS_SEQUENCE");

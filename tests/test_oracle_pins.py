@@ -107,8 +107,9 @@ def test_quantile_integral_rank_is_order_statistic():
 
 def test_mask_invariants():
     """q = 1 keeps exactly the active set; q in {0.2, 0.5, 0.8} drops some but
-    not all active tokens (PR #1558 asserts this so the test cannot pass
-    vacuously); no active token gives an empty mask; q = 0 keeps the top tie
+    not all active tokens (PR #1558, Testing, checks this too, so that a mask
+    that keeps everything cannot pass); no active token gives an empty mask;
+    q = 0 keeps the top tie
     group; q outside [0, 1] raises."""
     r = _rng(4)
     N = 4000
@@ -221,9 +222,9 @@ def test_gmpo_all_clipped_positive_advantage():
 
 
 def test_gmpo_exact_boundary_nextafter():
-    """PR #1320 'exact clipping boundaries and adjacent torch.nextafter
-    values': lr32 == fp32(eps) is not clipped (gradient flows); the next fp32
-    value outward is clipped (gradient zero); counts exact."""
+    """PR #1320, Testing (a log-ratio sitting exactly on a clip bound, and
+    its fp32 neighbours): lr32 == fp32(eps) is not clipped (gradient flows);
+    the next fp32 value outward is clipped (gradient zero); counts exact."""
     eh, el = 0.3, 0.2
     eh32, el32 = np.float32(eh), np.float32(el)
     old = np.float32(0.0)
@@ -256,7 +257,8 @@ def test_gmpo_exact_boundary_nextafter():
 
 def test_gmpo_zero_advantage_extreme_ratio_finite():
     """A = 0 with extreme log-ratios: loss and gradient finite and zero
-    (PR #1320 'extreme active log-ratio clips and finite gradients')."""
+    (PR #1320, Testing: very large log-ratios must clip and keep the
+    gradients finite)."""
     B, T = 2, 4
     comp = np.ones(B * T, np.uint8)
     lp = np.array([-1.0] * 8)
@@ -459,7 +461,7 @@ def test_gspo_token_gradient_equals_sequence_level_without_mask():
 @pytest.mark.parametrize("loss_type,q", [(GMPO, 1.0), (GMPO, 0.5), (GSPO_TOKEN, 0.5)])
 def test_chunk_invariance(loss_type, q):
     """Outer chunk sizes 1, 2, 5 and B agree (PR #1320 tests chunk sizes 1, 2,
-    5; PR #1558: the quantile is batch-global, so chunk_size 1 and B agree)."""
+    5; PR #1558: one quantile for the batch, so one-sequence chunks give the unchunked result)."""
     r = _rng(41)
     B, T, H, V = 6, 9, 6, 31
     h = r.standard_normal((B * T, H))
