@@ -354,9 +354,9 @@ def main() -> int:
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (ctypes.c_double * 2)()
-    cnt = (ctypes.c_int32 * 2)()
-    _abi.check(L.plp_profile_stop(ms, cnt))
+    ms = (ctypes.c_double * 3)()
+    cnt = (ctypes.c_int32 * 3)()
+    _abi.check(L.plp_profile_stop_n(ms, cnt, 3))
     elapsed = t1 - t0
     ms_step = 1e3 * elapsed / args.steps
     tokens_s = N * args.steps / elapsed
@@ -366,32 +366,39 @@ def main() -> int:
 
     # roofline of the dominant sweep
     n_active = int((out["dlogp"] != 0).sum().item())
-    # per launch: algorithmic FLOP (forward: logits + grad_h accumulator, 4HV
-    # per token; weight gradient: grad_W, 2HV per active token) and algorithmic
-    # HBM bytes (forward: W and the chunk's hidden rows read once, bf16;
-    # weight gradient: W read and grad_W written once, the active rows of h
-    # read once, bias and grad_b when present)
-    # per step: the forward sweep(s) compute the logits of every row and the
-    # grad_h accumulator (of every row; with q < 1, a statistics-only sweep
-    # over every row and the accumulator pass over the rows with a gradient),
-    # reading W once per launch and each row once; the weight-gradient
-    # launches compute grad_W of the rows with a gradient, reading W and
-    # writing grad_W once per step and each such row once. Per launch: the
-    # step's amount over its launches.
+    # per launch: algorithmic FLOP and HBM bytes of each sweep, the step's
+    # amount over its launches (the library times every launch of each kind
+    # with HIP events on the call's stream):
+    # - fwd_sweep, the forward sweep over every row of a chunk: the logits
+    #   (2HV per row) and, without the entropy mask, the grad_h accumulator
+    #   (another 2HV); it reads W once per launch and each row once;
+    # - fwd_compact_sweep (entropy mask on): the logits and the accumulator
+    #   again for the rows with a gradient only, 4HV each; W once per
+    #   launch, those rows once;
+    # - wgrad_sweep: 4HV per row with a gradient, the sweep's own step: it
+    #   forms the logits again, since the [N, V] probabilities are never
+    #   stored, and then the grad_W product (that product alone, 2HV, is
+    #   reported beside it); W read and grad_W written once per step, those
+    #   rows once, bias and grad_b when present.
     q_lt_1 = spec.top_entropy_quantile < 1.0
-    fl_per_step = max(1.0, cnt[0] / args.steps)
-    wl_per_step = max(1.0, cnt[1] / args.steps)
-    fwd_flops = (2.0 * N + 4.0 * n_active) * H * V if q_lt_1 else 4.0 * H * V * N
-    fwd_rows = N + (n_active if q_lt_1 else 0)
-    fwd_bytes = fl_per_step * (2.0 * H * V + (2.0 * V if spec.bias else 0.0)) + 2.0 * H * fwd_rows
-    wg_flops = 2.0 * H * V * n_active
-    wg_bytes = 4.0 * H * V + 2.0 * H * n_active + (4.0 * V if spec.bias else 0.0)
-    per_launch = {
-        "fwd_sweep": (fwd_flops / fl_per_step, fwd_bytes / fl_per_step, ms[0] / max(1, cnt[0])),
-        "wgrad_sweep": (wg_flops / wl_per_step, wg_bytes / wl_per_step, ms[1] / max(1, cnt[1])),
+    bias_b = 2.0 * V if spec.bias else 0.0
+    steps_f = float(args.steps)
+    kinds = {
+        "fwd_sweep": (0, (2.0 if q_lt_1 else 4.0) * H * V * N, 2.0 * H * N, 2.0 * H * V + bias_b),
+        "wgrad_sweep": (1, 4.0 * H * V * n_active, 2.0 * H * n_active + 4.0 * H * V + 2.0 * bias_b, 0.0),
+        "fwd_compact_sweep": (2, 4.0 * H * V * n_active, 2.0 * H * n_active, 2.0 * H * V + bias_b),
     }
-    dom = "fwd_sweep" if ms[0] >= ms[1] else "wgrad_sweep"
-    flops, alg_bytes, avg_ms = per_launch[dom]
+    per_launch = {}
+    for name, (k, fl_step, bytes_step, bytes_per_launch) in kinds.items():
+        if cnt[k] == 0:
+            continue
+        launches_step = cnt[k] / steps_f
+        per_launch[name] = (fl_step / launches_step, bytes_step / launches_step + bytes_per_launch,
+                            ms[k] / cnt[k], ms[k] / steps_f, int(cnt[k]))
+    fwd_flops = sum(kinds[n][1] for n in ("fwd_sweep", "fwd_compact_sweep") if n in per_launch)
+    wg_flops = kinds["wgrad_sweep"][1]
+    dom = max(per_launch, key=lambda n: per_launch[n][3])
+    flops, alg_bytes, avg_ms, _, n_launch = per_launch[dom]
     workload = spec.name + variant
     # the roof that binds is the one the algorithmic intensity falls under
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -407,8 +414,12 @@ def main() -> int:
                 "alg_flop_per_launch": flops, "alg_bytes_per_launch": alg_bytes,
                 "intensity_flop_per_byte": round(flops / alg_bytes, 1), "ridge_flop_per_byte": round(ridge, 1),
                 "kernel": dom, "avg_launch_ms": round(avg_ms, 4),
-                "launches": int(cnt[0] if dom == "fwd_sweep" else cnt[1]),
-                "other_sweep_ms_per_step": round((ms[1] if dom == "fwd_sweep" else ms[0]) / args.steps, 4)}
+                # the weight-gradient sweep's grad_W product alone (2HV per active
+                # token), without the logits it recomputes
+                "frac_grad_w_product_only": (round(0.5 * flops / (avg_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                                             if dom == "wgrad_sweep" else None),
+                "launches": n_launch,
+                "sweep_ms_per_step": {n: round(v[3], 4) for n, v in per_launch.items()}}
     # the work the method itself does: the logits of every token (2HV) and
     # the two gradient products (2HV each) of the tokens with dL/dlogp != 0;
     # the 6NHV count charges the gradients of every token
@@ -435,7 +446,7 @@ def main() -> int:
         "pct_bf16_peak_method_work": round(100.0 * tflops_method / PEAK_BF16_TFLOPS, 2),
         # what the path executes: the forward sweeps plus the weight-gradient
         # sweep's 4HV per token with a gradient (its logits are recomputed)
-        "executed_tflops": round((fwd_flops + 2.0 * wg_flops) / (elapsed / args.steps) / 1e12, 2),
+        "executed_tflops": round((fwd_flops + wg_flops) / (elapsed / args.steps) / 1e12, 2),
         "memory": {"inputs_bytes": int(mem_inputs), "workspace_bytes": int(ws.numel()),
                    "prepared_weight_bytes": int(wprep.numel()) if wprep is not None else 0,
                    "peak_bytes_beyond_inputs": int(peak_delta)},

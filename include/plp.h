@@ -300,13 +300,18 @@ PLP_API int plp_policy_loss_from_logprobs(const plp_args* args, const float* log
  * stream of each call, for benchmarks and roofline reports.
  * plp_profile_start(max_records): pre-creates 2*max_records events and turns
  * recording on (PLP_E_INVALID if max_records < 1; PLP_E_HIP if event creation
- * fails). While on, every forward sweep (kind 0) and weight-gradient sweep
- * (kind 1) launch is bracketed by an event pair, up to max_records pairs.
- * plp_profile_stop(ms[2], count[2]): waits for the recorded events, returns
- * per kind the summed milliseconds and the number of launches, destroys the
- * events and turns recording off. Process-global; not for concurrent use. */
+ * fails). While on, every forward sweep over all rows of a chunk (kind 0),
+ * weight-gradient sweep (kind 1) and, with the entropy mask, accumulator
+ * pass over the compacted rows with a gradient (kind 2) is bracketed by an
+ * event pair, up to max_records pairs. plp_profile_stop_n(ms[n], count[n],
+ * n >= 2): waits for the recorded events, returns per kind the summed
+ * milliseconds and the number of launches (with n = 2, kind 2 counts as kind
+ * 0), destroys the events and turns recording off; plp_profile_stop(ms[2],
+ * count[2]) is plp_profile_stop_n with n = 2. Process-global; not for
+ * concurrent use. */
 PLP_API int plp_profile_start(int32_t max_records);
 PLP_API int plp_profile_stop(double* ms_out, int32_t* count_out);
+PLP_API int plp_profile_stop_n(double* ms_out, int32_t* count_out, int32_t n_kinds);
 
 #ifdef __cplusplus
 }

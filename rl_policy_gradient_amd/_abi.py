@@ -123,6 +123,8 @@ def lib() -> ctypes.CDLL:
     L.plp_prepare_weight.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, sz, _vp]
     L.plp_profile_start.argtypes = [ctypes.c_int32]
     L.plp_profile_stop.argtypes = [P(ctypes.c_double), P(ctypes.c_int32)]
+    L.plp_profile_stop_n.argtypes = [P(ctypes.c_double), P(ctypes.c_int32), ctypes.c_int32]
+    L.plp_profile_stop_n.restype = ctypes.c_int
     L.plp_profile_start.restype = ctypes.c_int
     L.plp_profile_stop.restype = ctypes.c_int
     for name in ("plp_workspace_size", "plp_fused_lmhead_policy_loss_fwd_bwd", "plp_selective_entropy_workspace_size",

@@ -39,10 +39,8 @@ constexpr int kBQ = 64, kBK = 32;
 constexpr int kMaxSplits = 64;
 // Rows of the second forward pass over flagged rows per call of the sweep
 // (more flagged rows than this are recomputed by the merge on the vector
-// ALU), and the row capacity of that pass's statistics and accumulator over
-// all its splits (splits x row blocks < 512 while the splits are above one).
+// ALU); its statistics and accumulator hold compact_rows_needed rows.
 constexpr int64_t kFlagCap = 32768;
-constexpr int64_t kFlagRows = 512 * 64;
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
 // plp_args as of ABI version 1 (fields up to chunk_sequences); later fields
 // read as their defaults when struct_size ends before them.
@@ -65,6 +63,18 @@ const void* weight_prepared(const plp_args* a) {
 }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Rows of stats / O a compacted accumulator pass over at most `cap` listed
+// rows can use: the largest splits x row stride the sweep picks for any
+// count up to cap (both depend on the count through its 64-row blocks only).
+int64_t compact_rows_needed(int64_t cap, int V, int max_splits) {
+  int64_t best = 0;
+  for (int64_t nrb = 1; nrb <= (cap + 63) / 64; ++nrb) {
+    const int64_t rows = nrb * 64;
+    best = std::max<int64_t>(best, (int64_t)forward_splits(rows, V, max_splits) * compact_stride(rows));
+  }
+  return best;
+}
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Sequential carving of the caller's workspace.
@@ -163,7 +173,7 @@ Plan make_plan(const plp_args* a, bool need_o, bool need_gw, bool need_gb) {
   p.o_compact = p.entropy && p.mfma && p.need_o;
   p.prepass = p.entropy && (p.nchunks > 1 || p.o_compact);
   // splits x row blocks < 512 while the splits are above one (forward_splits)
-  p.o2_rows = std::max<int64_t>(512 * kBQ, round_up(p.Nc, kBQ));
+  p.o2_rows = p.mfma ? compact_rows_needed(p.o_compact ? p.cap : std::min(p.cap, kFlagCap), a->V, kMaxSplits) : 0;
   p.wg_sub = p.mfma ? std::max<int64_t>(32 * kBK, ((int64_t)128 << 20) / (2 * a->H) / kBK * kBK) : p.cap;
   for (int64_t c = 0; c < p.nchunks; ++c) {
     const int64_t capc = round_up(std::min(p.Bc, p.B - c * p.Bc) * p.T, kBK);
@@ -181,7 +191,7 @@ size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
     b.Wf = c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H);
   b.stats = c.take<RowStats>((size_t)p.Sv * p.Nc);
   if (p.mfma) {
-    const int64_t rows2 = p.o_compact ? p.o2_rows : kFlagRows;
+    const int64_t rows2 = p.o2_rows;
     b.stats2 = c.take<RowStats>((size_t)rows2);
     b.O2 = c.take<float>((size_t)rows2 * H);
     b.fp.cap = (int)std::min(p.cap, kFlagCap);
@@ -387,8 +397,9 @@ size_t carve_selective(void* ws, int64_t N, int H, int V, int dtype, SelBufs& sb
     sb.fp.mref = c.take<float>((size_t)sb.fp.cap);
     sb.fp.pos = c.take<int>((size_t)N);
     sb.fp.count = c.take<int>(1);
-    sb.fp.stats = c.take<RowStats>((size_t)kFlagRows);
-    sb.fp.O = c.take<float>((size_t)kFlagRows * H);
+    const int64_t rows2 = compact_rows_needed(sb.fp.cap, V, kMaxSplits);
+    sb.fp.stats = c.take<RowStats>((size_t)rows2);
+    sb.fp.O = c.take<float>((size_t)rows2 * H);
     sb.fp.max_splits = kMaxSplits;
   }
   return c.off + kAlign;
@@ -523,11 +534,16 @@ PLP_API int plp_profile_start(int32_t max_records) {
   return ok();
 }
 
-PLP_API int plp_profile_stop(double* ms_out, int32_t* count_out) {
+PLP_API int plp_profile_stop(double* ms_out, int32_t* count_out) { return plp_profile_stop_n(ms_out, count_out, 2); }
+
+PLP_API int plp_profile_stop_n(double* ms_out, int32_t* count_out, int32_t n_kinds) {
   if (!ms_out || !count_out) return fail(PLP_E_INVALID, "ms_out and count_out are required");
+  if (n_kinds < 2) return fail(PLP_E_INVALID, "n_kinds must be >= 2");
   std::lock_guard<std::mutex> lk(g_prof.mu);
-  ms_out[0] = ms_out[1] = 0.0;
-  count_out[0] = count_out[1] = 0;
+  for (int k = 0; k < n_kinds; ++k) {
+    ms_out[k] = 0.0;
+    count_out[k] = 0;
+  }
   int rc = PLP_OK;
   for (size_t i = 0; i < g_prof.used; ++i) {
     float ms = 0.f;
@@ -537,8 +553,10 @@ PLP_API int plp_profile_stop(double* ms_out, int32_t* count_out) {
       rc = fail(PLP_E_HIP, "event timing: %s", hipGetErrorString(r));
       break;
     }
-    ms_out[g_prof.kind[i]] += ms;
-    count_out[g_prof.kind[i]] += 1;
+    // with two kinds the compacted accumulator passes count as forward sweeps
+    const int k = g_prof.kind[i] < n_kinds ? g_prof.kind[i] : 0;
+    ms_out[k] += ms;
+    count_out[k] += 1;
   }
   for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
   g_prof.ev.clear();
@@ -649,7 +667,7 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
     if (p.need_gw || p.o_compact)
       HIP_TRY(launch_compact_scatter(g, b.lse + r0, a->targets + r0, n, inv_tau, cnt32, b.idx, b.tok, b.count, st));
     if (p.o_compact) {
-      hipEvent_t* ev = prof_slot(0);
+      hipEvent_t* ev = prof_slot(2);
       if (ev) HIP_TRY(hipEventRecord(ev[0], st));
       // each row's log-sum-exp (lse >= every logit of the row) as its
       // exponent reference: nothing to flag in this pass

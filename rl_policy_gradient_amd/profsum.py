@@ -94,24 +94,65 @@ def _rows(path):
         yield from csv.DictReader(fh)
 
 
-def kernel_durations(trace_csv: str) -> dict:
-    """{kernel name: [duration ns, ...]} from a rocprofv3 kernel-trace CSV."""
-    out = {}
-    for r in _rows(trace_csv):
-        d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-        out.setdefault(r["Kernel_Name"], []).append(d)
+def kernel_durations(trace_csv: str, split_passes: bool = False) -> dict:
+    """{kernel name: [duration ns, ...]} from a rocprofv3 kernel-trace CSV;
+    with split_passes the two-role forward sweep's second pass over flagged
+    rows and its pass over the compacted rows are keyed apart, as
+    (name, label) (pass_label)."""
+    seq = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), r["Kernel_Name"])
+                  for r in _rows(trace_csv)), key=lambda x: x[0])
+    out, prev = {}, ""
+    for _, d, n in seq:
+        key = n
+        if "plp" in n:
+            label = pass_label(n, prev) if split_passes else "main"
+            key = n if label == "main" else (n, label)
+            prev = n
+        out.setdefault(key, []).append(d)
     return out
 
 
-def counter_per_dispatch(pmc_csv: str, counter: str, match: str) -> list:
-    """Values of `counter` for every dispatch whose kernel name contains `match`."""
+def pass_label(name: str, prev: str) -> str:
+    """Which pass a launch of the two-role forward sweep is, from the library
+    kernel launched before it: after the flag scan it is the second pass over
+    the flagged rows, after the compaction the accumulator pass over the
+    compacted rows with a gradient; any other launch is labelled "main"."""
+    if "fwd_pp_kernel" in name:
+        if "flag_scan_kernel" in prev:
+            return "flagged"
+        if "compact_scatter_kernel" in prev:
+            return "compacted"
+    return "main"
+
+
+def _dispatch_labels(pmc_csv: str) -> dict:
+    """{dispatch id: pass label} over the library's dispatches of a --pmc CSV."""
+    names = {}
+    for r in _rows(pmc_csv):
+        names[int(r["Dispatch_Id"])] = r["Kernel_Name"]
+    labels, prev = {}, ""
+    for k in sorted(names):
+        n = names[k]
+        if "plp" not in n:
+            continue
+        labels[k] = pass_label(n, prev)
+        prev = n
+    return labels
+
+
+def counter_per_dispatch(pmc_csv: str, counter: str, match: str, which: str = "main") -> list:
+    """Values of `counter` for every dispatch whose kernel name contains
+    `match` and whose pass label (pass_label) is `which` ("any": all)."""
+    labels = _dispatch_labels(pmc_csv) if which != "any" else {}
     vals = {}
     for r in _rows(pmc_csv):
         if r["Counter_Name"] != counter or match not in r["Kernel_Name"]:
             continue
-        key = r["Dispatch_Id"]
+        key = int(r["Dispatch_Id"])
+        if which != "any" and labels.get(key, "main") != which:
+            continue
         vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
-    return [vals[k] for k in sorted(vals, key=int)]
+    return [vals[k] for k in sorted(vals)]
 
 
 def cmd_copy(args) -> int:
@@ -130,9 +171,12 @@ def cmd_copy(args) -> int:
 
 def cmd_pmc(args) -> int:
     per = {}  # match -> dispatch id -> counter -> value (summed over the CSV's rows)
+    labels = _dispatch_labels(args.csv)
     for r in _rows(args.csv):
         for m in args.match.split(","):
-            if m in r["Kernel_Name"]:
+            # a name:label entry takes that pass of the kernel only (pass_label)
+            kname, _, want = m.partition(":")
+            if kname in r["Kernel_Name"] and labels.get(int(r["Dispatch_Id"]), "main") == (want or "main"):
                 d = per.setdefault(m, {}).setdefault(r["Dispatch_Id"], {})
                 d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     lines = ["# rocprofv3 counter summary (per-dispatch averages)", f"# command: {args.command}",
@@ -162,13 +206,21 @@ def cmd_pmc(args) -> int:
     return 0
 
 
+_PASS_NAMES = {"flagged": "[second pass, flagged rows]", "compacted": "[compacted rows with a gradient]"}
+
+
 def cmd_stats(args) -> int:
-    d = kernel_durations(args.trace)
+    d = kernel_durations(args.trace, split_passes=True)
     total = sum(sum(v) for v in d.values())
-    lines = [f"# rocprofv3 kernel trace summary", f"# command: {args.command}", "",
+    lines = [f"# rocprofv3 kernel trace summary", f"# command: {args.command}",
+             "# the two-role forward sweep's launches after the flag scan (second pass over flagged rows) and",
+             "# after the compaction (rows with a gradient, entropy mask on) are listed on rows of their own", "",
              f"{'kernel':<92} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10} {'pct':>6}"]
     items = sorted(d.items(), key=lambda kv: -sum(kv[1]))
-    for name, (_, v) in zip(_demangle([k for k, _ in items]), items):
+    raw = [k if isinstance(k, str) else k[0] for k, _ in items]
+    for name, (key, v) in zip(_demangle(raw), items):
+        if not isinstance(key, str):
+            name = f"{_short(name, 60)} {_PASS_NAMES[key[1]]}"
         lines.append(f"{_short(name):<92} {len(v):>6} {statistics.mean(v) / 1e3:>10.2f} {min(v) / 1e3:>10.2f} "
                      f"{max(v) / 1e3:>10.2f} {sum(v) / 1e6:>10.3f} {100.0 * sum(v) / total:>6.2f}")
     text = "\n".join(lines) + "\n"
@@ -180,10 +232,10 @@ def cmd_stats(args) -> int:
 
 
 def cmd_traffic(args) -> int:
-    fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE", args.match)
-    write = counter_per_dispatch(args.write, "WRITE_SIZE", args.match)
-    cf = counter_per_dispatch(args.copy_fetch, "FETCH_SIZE", args.copy_match)
-    cw = counter_per_dispatch(args.copy_write, "WRITE_SIZE", args.copy_match)
+    fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE", args.match, args.which)
+    write = counter_per_dispatch(args.write, "WRITE_SIZE", args.match, args.which)
+    cf = counter_per_dispatch(args.copy_fetch, "FETCH_SIZE", args.copy_match, "any")
+    cw = counter_per_dispatch(args.copy_write, "WRITE_SIZE", args.copy_match, "any")
     if not (fetch and write and cf and cw):
         print("missing dispatches: fetch %d write %d copy %d/%d" % (len(fetch), len(write), len(cf), len(cw)))
         return 1
@@ -195,6 +247,7 @@ def cmd_traffic(args) -> int:
     d = {
         "kernel": args.kernel,
         "match": args.match,
+        "pass": args.which,
         "workload": args.workload,
         "dispatches": [len(fetch), len(write)],
         "fetch_kib_per_dispatch": statistics.mean(fetch),
@@ -279,21 +332,25 @@ def cmd_hbm(args) -> int:
              "# traffic: FETCH_SIZE + WRITE_SIZE per dispatch scaled by a plain copy's reading (when given)", "",
              f"{'kernel':<40} {'calls':>6} {'med_us':>10} {'alg_MB':>10} {'GB/s':>9} {'frac':>6} {'traffic_MB':>11}"]
     # Launches of one kernel name that move different amounts are told apart
-    # by the library kernel that follows them in time: the copy of W precedes
-    # a forward sweep and the gathered rows' copy the weight-gradient sweep;
-    # the merge after the statistics-only sweep has no accumulator (with
-    # q = 1 that sweep is the setup's log-prob pass, not part of a step).
+    # by the library kernels around them in time: the copy of W precedes a
+    # forward sweep and the gathered rows' copy the weight-gradient sweep;
+    # the merge after the statistics-only sweep (and its second pass over
+    # flagged rows) has no accumulator (with q = 1 that sweep is the setup's
+    # log-prob pass, not part of a step).
     seq = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
                    r["Kernel_Name"]) for r in _rows(args.trace)), key=lambda x: x[0])
     plp_seq = [x for x in seq if "plp" in x[2]]
     split = {}
+    sweep = ""  # the last forward sweep over all rows (not a second pass over flagged rows)
     for i, (_, dur, name) in enumerate(plp_seq):
         nxt = plp_seq[i + 1][2] if i + 1 < len(plp_seq) else ""
         prv = plp_seq[i - 1][2] if i > 0 else ""
+        if ("fwd_mfma_kernel" in name or "fwd_pp_kernel" in name) and pass_label(name, prv) == "main":
+            sweep = name
         if "frag_copy_kernel" in name:
             label = "frag_copy_kernel (gathered rows)" if "bwd_pp_kernel" in nxt else "frag_copy_kernel (W)"
         elif "combine_kernel" in name:
-            if "fwd_mfma_kernel" in prv:
+            if "fwd_mfma_kernel" in sweep:
                 if not args.entropy:
                     continue
                 label = "combine_kernel (statistics only)"
@@ -340,6 +397,8 @@ def main(argv=None) -> int:
         t.add_argument("--" + k.replace("_", "-"), required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--copy-match", default="neg")
+    t.add_argument("--which", default="main", choices=["main", "flagged", "compacted", "any"],
+                   help="pass of the two-role forward sweep to take (pass_label)")
     t.add_argument("--command", default="")
     q = sub.add_parser("pmc")
     q.add_argument("csv")
