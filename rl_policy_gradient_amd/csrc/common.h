@@ -77,18 +77,73 @@ struct LossParams {
   int kl_bc;           // KL term weighted by the token importance ratio
 };
 
-// Vocabulary splits of the forward sweep over `rows` token rows: the
-// smallest power of two (at most max_splits, every split keeping at least
-// one 32-row tile) for which row blocks x splits fill the 256 compute units,
-// trimmed to the splits that hold tiles. Evaluated on the host for a known
-// row count and in the kernels for a row count that lives on the device.
-__host__ __device__ inline int forward_splits(int64_t rows, int V, int max_splits) {
+// Vocabulary splits of the forward sweep over `rows` token rows (64-row
+// blocks x Sv contiguous vocabulary ranges, one workgroup each, one
+// workgroup per compute unit): the Sv in [1, max_splits] (max_splits <= 64;
+// every split holding at least one 32-row tile) with the shortest estimated
+// time for a 4096-tile vocabulary, counted in hundredths of one workgroup's
+// tile: ceil(blocks x Sv / 256) rounds of ceil(4096 / Sv) tiles, plus the
+// split accumulators' write and merge, about 0.07 tile per row block and
+// split (64 rows x H fp32 written and read again, against one tile's
+// 64 x 32 x H x 4 matrix FLOP at the measured rates). The reference
+// vocabulary keeps the choice, and so the workspace, a function of the row
+// count alone (V only bounds Sv by its tile count). forward_split_key orders
+// the candidates (time, then the smaller Sv); the host takes the least key in
+// a loop, a wave on the device in one lane per candidate, so both pick the
+// same Sv.
+__host__ __device__ inline unsigned long long forward_split_key(int64_t rows, int V, int max_splits, int sv) {
   const int64_t nrb = (rows + 63) / 64;
   const int n_tiles = (V + 31) / 32;
-  int sv = 1;
-  while ((int64_t)sv * nrb < 256 && sv < max_splits && sv * 2 <= n_tiles) sv *= 2;
+  if (sv < 1 || sv > max_splits || sv > n_tiles) return ~0ull;
   const int tps = (n_tiles + sv - 1) / sv;
-  return (n_tiles + tps - 1) / tps;
+  if ((n_tiles + tps - 1) / tps != sv) return ~0ull;  // a split would hold no tile
+  const unsigned long long t = (unsigned long long)((nrb * sv + 255) / 256) * (unsigned long long)((4096 + sv - 1) / sv) *
+                                   100ull +
+                               7ull * (unsigned long long)(nrb * sv);
+  return (t << 8) | (unsigned long long)sv;
+}
+inline int forward_splits(int64_t rows, int V, int max_splits) {
+  unsigned long long best = ~0ull;
+  for (int sv = 1; sv <= 64; ++sv) {
+    const unsigned long long k = forward_split_key(rows, V, max_splits, sv);
+    if (k < best) best = k;
+  }
+  return best == ~0ull ? 1 : (int)(best & 255ull);
+}
+// The same choice by one wave (all 64 lanes active, uniform arguments).
+__device__ inline int forward_splits_wave(int64_t rows, int V, int max_splits) {
+  unsigned long long k = forward_split_key(rows, V, max_splits, (int)(threadIdx.x & 63) + 1);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned long long o = __shfl_xor(k, off, 64);
+    k = o < k ? o : k;
+  }
+  // the same in every lane: made scalar, so that what derives from it stays
+  // in scalar registers
+  return __builtin_amdgcn_readfirstlane(k == ~0ull ? 1 : (int)(k & 255ull));
+}
+
+// Largest number of (row block, split) pairs the sweep uses for any row
+// count up to `rows` (the grid of a launch whose count lives on the device;
+// the rows of its statistics are 64 times this). Host only; remembers its
+// last few answers.
+int64_t forward_blocks_max(int64_t rows, int V, int max_splits);
+
+// Workgroup -> (row block, split) of the forward sweeps. Workgroup w runs on
+// XCD w % 8; each XCD takes a contiguous range of the split-major order of
+// the nrb x Sv blocks, so its compute units stream one vocabulary range of W
+// together and share its tiles in their L2. Returns false for a workgroup
+// with no block (grids are rounded up to a multiple of 8, or sized for the
+// largest count).
+__device__ inline bool forward_block(int64_t nrb, int Sv, int64_t& rb, int& sv) {
+  // 32-bit arithmetic: grids stay below 2^31 workgroups
+  const int nb = (int)nrb, total = nb * Sv, per = (total + 7) / 8;
+  const int j = (int)(blockIdx.x / 8);
+  const int g = (int)(blockIdx.x % 8) * per + j;
+  if (j >= per || g >= total) return false;
+  sv = g / nb;
+  rb = g - sv * nb;
+  return true;
 }
 
 // Token-level clipped losses (GRPO, BNPO, DAPO) share the per-token path.

@@ -13,7 +13,7 @@ namespace {
 
 // Forward sweep, statistics only: per token row, running
 // (sum 2^{z2-m2}, sum 2^{z2-m2} z2) against the reference m2 (z2 = z log2 e).
-// Grid: (row blocks) x Sv vocabulary splits, block id = rb * Sv + split.
+// Grid: (row blocks) x Sv vocabulary splits in the order of forward_block.
 template <int KB, bool HAS_BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf,
@@ -32,8 +32,10 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5, c = lane & 31;
   const int nbq = w & 1, kh = w >> 1;  // quarter this wave reduces: row block nbq, tile-row half kh
-  const int rb = blockIdx.x / Sv, sv = blockIdx.x - rb * Sv;
-  const int64_t q0 = (int64_t)rb * BQ;
+  int64_t rb;
+  int sv;
+  if (!forward_block((N + BQ - 1) / BQ, Sv, rb, sv)) return;  // uniform: no block for this workgroup
+  const int64_t q0 = rb * BQ;
   const int d0 = w * DS;
   const int n_tiles = (V + BK - 1) / BK;
   const int t_begin = sv * tiles_per_split;
@@ -247,7 +249,8 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
 // With count_dev the rows are the first min(*count_dev, N) rows of a
 // compacted list (rows row_idx[k] of h when row_idx is given), the splits
 // forward_splits(that count, V, Sv) and the row stride of stats and O
-// compact_stride(that count); workgroups past the last block exit at once.
+// compact_stride(that count); the grid is sized for the largest count
+// (forward_blocks_max) and workgroups with no block exit at once.
 // With mref the exponent reference of row k is mref[k * mref_stride]
 // (natural units) instead of the maximum of its first tile. clear_count, when
 // given (never the count_dev of the same launch), is set to zero.
@@ -263,11 +266,14 @@ void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, 
   int Sv = Sv_, tiles_per_split = tiles_per_split_;
   if (count_dev) {
     N = min((int64_t)*count_dev, N_);
-    Sv = forward_splits(N, V, Sv_);
+    if (N <= 0) return;  // uniform: an empty list (the usual second pass)
+    Sv = forward_splits_wave(N, V, Sv_);
     tiles_per_split = ((V + BK - 1) / BK + Sv - 1) / Sv;
     stride = compact_stride(N);
-    if ((int64_t)blockIdx.x >= stride / BQ * Sv) return;  // uniform: no rows for this workgroup
   }
+  int64_t rb;
+  int sv;
+  if (!forward_block((N + BQ - 1) / BQ, Sv, rb, sv)) return;  // uniform: no rows for this workgroup
   constexpr int DS = Stage<KB>::DS;
   constexpr int TS = Stage<KB>::TS;
   constexpr int KS = DS / 16;
@@ -284,8 +290,7 @@ void fwd_pp_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf, 
   const int w = wall & 3;  // H quarter
   const int hh = lane >> 5, c = lane & 31;
   const int nbq = w & 1, kh = w >> 1;
-  const int rb = blockIdx.x / Sv, sv = blockIdx.x - rb * Sv;
-  const int64_t q0 = (int64_t)rb * BQ;
+  const int64_t q0 = rb * BQ;
   const int d0 = w * DS;
   const int n_tiles = (V + BK - 1) / BK;
   const int t_begin = sv * tiles_per_split;
@@ -548,10 +553,10 @@ hipError_t fwd_pp_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int
   const int n_tiles = (V + BK - 1) / BK;
   const int tps = (n_tiles + Sv - 1) / Sv;
   const int64_t nrb = (N + BQ - 1) / BQ;
-  // with a device row count, enough workgroups for any count up to N: row
-  // blocks x splits stays below 512 while the splits are above one
-  const int64_t wgs = count_dev ? (nrb > 512 ? nrb : 512) : nrb * Sv;
-  const dim3 grid((unsigned)wgs), block(512);
+  // with a device row count, enough workgroups for any count up to N
+  int64_t blocks = count_dev ? forward_blocks_max(N, V, Sv) : nrb * Sv;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)((blocks + 7) / 8 * 8)), block(512);
   switch (H / 128) {
 #define PLP_PP_CASE(K)                                                                                                \
   case K:                                                                                                             \
@@ -578,7 +583,7 @@ hipError_t fwd_stats_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, 
   const int n_tiles = (V + BK - 1) / BK;
   const int tps = (n_tiles + Sv - 1) / Sv;
   const int64_t nrb = (N + BQ - 1) / BQ;
-  const dim3 grid((unsigned)(nrb * Sv)), block(256);
+  const dim3 grid((unsigned)((nrb * Sv + 7) / 8 * 8)), block(256);
   switch (H / 128) {
 #define PLP_FWD_CASE(K)                                                                                              \
   case K:                                                                                                            \

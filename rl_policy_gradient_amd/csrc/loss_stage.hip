@@ -128,7 +128,7 @@ __global__ __launch_bounds__(NT) void combine_kernel(const RowStats* __restrict_
       const int64_t n2 = min((int64_t)*count2, (int64_t)cap2);
       st_ = stats2;
       O_ = O2;
-      Sv_ = forward_splits(n2, V, max_splits2);
+      Sv_ = forward_splits_wave(n2, V, max_splits2);
       stride = compact_stride(n2);
       srow = k;
       early = false;
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(NT) void grad_h_compact_kernel(const RowStats* __re
   const int64_t n = *count_dev;
   const int64_t k = blockIdx.x;
   if (k >= n) return;  // uniform
-  const int Sv = forward_splits(n, V, max_splits);
+  const int Sv = forward_splits_wave(n, V, max_splits);
   const int64_t stride = compact_stride(n);
   __shared__ double s_c[64];
   __shared__ double s_res[2];

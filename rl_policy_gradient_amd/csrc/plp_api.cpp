@@ -15,6 +15,26 @@
 
 using namespace plp;
 
+int64_t plp::forward_blocks_max(int64_t rows, int V, int max_splits) {
+  // the answers of the last few (rows, V, max_splits), per thread: the loop
+  // runs up to rows / 64 x 64 key evaluations
+  struct Memo {
+    int64_t rows;
+    int V, max_splits;
+    int64_t blocks;
+  };
+  thread_local Memo memo[8] = {};
+  thread_local int next = 0;
+  for (const Memo& m : memo)
+    if (m.blocks > 0 && m.rows == rows && m.V == V && m.max_splits == max_splits) return m.blocks;
+  int64_t best = 0;
+  for (int64_t nrb = 1; nrb <= (rows + 63) / 64; ++nrb)
+    best = std::max<int64_t>(best, nrb * forward_splits(nrb * 64, V, max_splits));
+  memo[next] = Memo{rows, V, max_splits, best};
+  next = (next + 1) % 8;
+  return best;
+}
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -67,14 +87,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Rows of stats / O a compacted accumulator pass over at most `cap` listed
 // rows can use: the largest splits x row stride the sweep picks for any
 // count up to cap (both depend on the count through its 64-row blocks only).
-int64_t compact_rows_needed(int64_t cap, int V, int max_splits) {
-  int64_t best = 0;
-  for (int64_t nrb = 1; nrb <= (cap + 63) / 64; ++nrb) {
-    const int64_t rows = nrb * 64;
-    best = std::max<int64_t>(best, (int64_t)forward_splits(rows, V, max_splits) * compact_stride(rows));
-  }
-  return best;
-}
+int64_t compact_rows_needed(int64_t cap, int V, int max_splits) { return 64 * forward_blocks_max(cap, V, max_splits); }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Sequential carving of the caller's workspace.
@@ -95,18 +108,9 @@ bool mfma_eligible(int dtype, int H) { return dtype == PLP_DTYPE_BF16 && H % 128
 bool generic_eligible(int H) { return H >= 1 && H <= 4096; }
 size_t esize(int dtype) { return dtype == PLP_DTYPE_F32 ? 4 : 2; }
 
-// Vocabulary splits of the forward sweep: enough workgroups to fill the
-// 256 compute units when there are few row blocks; every split gets at least
-// one tile. Powers of two keep the row blocks of one split on one XCD.
-int choose_splits(int64_t rows, int V, bool mfma) {
-  if (!mfma) return 1;
-  const int64_t nrb = (rows + kBQ - 1) / kBQ;
-  const int n_tiles = (V + kBK - 1) / kBK;
-  int sv = 1;
-  while ((int64_t)sv * nrb < 256 && sv < kMaxSplits && sv * 2 <= n_tiles) sv *= 2;
-  const int tps = (n_tiles + sv - 1) / sv;
-  return (n_tiles + tps - 1) / tps;
-}
+// Vocabulary splits of the forward sweep over all rows of a chunk
+// (forward_splits); the generic path does not split.
+int choose_splits(int64_t rows, int V, bool mfma) { return mfma ? forward_splits(rows, V, kMaxSplits) : 1; }
 
 struct Plan {
   bool mfma = false;
