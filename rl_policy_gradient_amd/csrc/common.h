@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace plp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -102,9 +104,14 @@ __host__ __device__ inline unsigned long long forward_split_key(int64_t rows, in
                                7ull * (unsigned long long)(nrb * sv);
   return (t << 8) | (unsigned long long)sv;
 }
+// Largest Sv that can beat one split at nrb row blocks: one split costs at
+// most 1600 nrb + 408000 + 7 nrb, any Sv at least 1600 nrb + 7 nrb Sv, so only
+// nrb (Sv - 1) < 58286 can win; larger candidates need not be evaluated.
+inline int forward_splits_useful(int64_t nrb) { return nrb < 1 ? 64 : (int)std::min<int64_t>(64, 1 + 58285 / nrb); }
 inline int forward_splits(int64_t rows, int V, int max_splits) {
   unsigned long long best = ~0ull;
-  for (int sv = 1; sv <= 64; ++sv) {
+  const int top = forward_splits_useful((rows + 63) / 64);
+  for (int sv = 1; sv <= top; ++sv) {
     const unsigned long long k = forward_split_key(rows, V, max_splits, sv);
     if (k < best) best = k;
   }
