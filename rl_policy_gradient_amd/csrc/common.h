@@ -89,14 +89,19 @@ struct LossParams {
 // split (64 rows x H fp32 written and read again, against one tile's
 // 64 x 32 x H x 4 matrix FLOP at the measured rates). The reference
 // vocabulary keeps the choice, and so the workspace, a function of the row
-// count alone (V only bounds Sv by its tile count). forward_split_key orders
+// count alone (V only bounds Sv by its tile count). More than one split is
+// taken only while row blocks x splits stay within kMaxSplitBlocks (four
+// rounds), which bounds the split accumulators of a pass whose count lives on
+// the device at 1024 x 64 rows. forward_split_key orders
 // the candidates (time, then the smaller Sv); the host takes the least key in
 // a loop, a wave on the device in one lane per candidate, so both pick the
 // same Sv.
+constexpr int64_t kMaxSplitBlocks = 1024;
 __host__ __device__ inline unsigned long long forward_split_key(int64_t rows, int V, int max_splits, int sv) {
   const int64_t nrb = (rows + 63) / 64;
   const int n_tiles = (V + 31) / 32;
   if (sv < 1 || sv > max_splits || sv > n_tiles) return ~0ull;
+  if (sv > 1 && nrb * sv > kMaxSplitBlocks) return ~0ull;  // bounds the split accumulators
   const int tps = (n_tiles + sv - 1) / sv;
   if ((n_tiles + tps - 1) / tps != sv) return ~0ull;  // a split would hold no tile
   const unsigned long long t = (unsigned long long)((nrb * sv + 255) / 256) * (unsigned long long)((4096 + sv - 1) / sv) *

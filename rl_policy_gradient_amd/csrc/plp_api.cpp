@@ -27,11 +27,11 @@ int64_t plp::forward_blocks_max(int64_t rows, int V, int max_splits) {
   thread_local int next = 0;
   for (const Memo& m : memo)
     if (m.blocks > 0 && m.rows == rows && m.V == V && m.max_splits == max_splits) return m.blocks;
-  // past 58286 row blocks one split always wins (forward_splits_useful), so
-  // the count of blocks is the row blocks themselves
+  // several splits only while blocks x splits <= kMaxSplitBlocks, so past
+  // that many row blocks the count of blocks is the row blocks themselves
   const int64_t nrb_cap = (rows + 63) / 64;
   int64_t best = nrb_cap;
-  for (int64_t nrb = 1; nrb <= std::min<int64_t>(nrb_cap, 58286); ++nrb)
+  for (int64_t nrb = 1; nrb <= std::min<int64_t>(nrb_cap, kMaxSplitBlocks); ++nrb)
     best = std::max<int64_t>(best, nrb * forward_splits(nrb * 64, V, max_splits));
   memo[next] = Memo{rows, V, max_splits, best};
   next = (next + 1) % 8;
