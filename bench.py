@@ -50,7 +50,7 @@ def _workload(cfg: int, device):
     import synth
     from rl_policy_gradient_amd import selective_entropy
 
-    spec = synth.CONFIGS[cfg]
+    spec = synth.BY_ID[cfg]
     B, T, H, V, N = spec.B, spec.T, spec.H, spec.V, spec.N
     if cfg in (1, 2):
         d = synth.make(spec)
@@ -213,7 +213,7 @@ def _cpu_baseline_full(cfg: int) -> dict:
     import oracle
     import synth
 
-    spec = synth.CONFIGS[cfg]
+    spec = synth.BY_ID[cfg]
     d = synth.make(spec)
     try:
         from threadpoolctl import threadpool_info

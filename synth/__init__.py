@@ -82,20 +82,23 @@ class Spec:
         return dataclasses.replace(self, **kw)
 
 
-CONFIGS = {
-    1: Spec("tiny_gmpo_f32", 1, B=2, T=16, H=64, V=512, dtype="f32", w_std=0.05,
-            old_noise_std=0.2, prompt_fixed=4, adv_kind="pm1z"),
-    2: Spec("gmpo_bf16_b1_t512", 2, B=1, T=512, H=896, V=151936,
-            prompt_lo=32, prompt_hi=128),
-    3: Spec("gmpo_kl_bf16_b8_t2048", 3, B=8, T=2048, H=896, V=151936, bias=True,
-            eps_low=0.2, eps_high=0.3, beta=0.04, ref_noise_std=0.05,
-            prompt_lo=64, prompt_hi=512, zero_adv_fraction=0.25),
-    4: Spec("gspo_token_entropy_bf16_b2_t32768", 4, B=2, T=32768, H=896, V=151936,
-            loss_type=GSPO_TOKEN, eps_low=3e-4, eps_high=4e-4, old_noise_std=1e-4,
-            top_entropy_quantile=0.2, prompt_lo=256, prompt_hi=2048),
-    5: Spec("gmpo_bf16_b128_t32768_chunked", 5, B=128, T=32768, H=896, V=151936,
-            bias=True, chunk_sequences=8, prompt_lo=32, prompt_hi=128),
-}
+_SPECS = (
+    Spec("tiny_gmpo_f32", 1, B=2, T=16, H=64, V=512, dtype="f32", w_std=0.05,
+         old_noise_std=0.2, prompt_fixed=4, adv_kind="pm1z"),
+    Spec("gmpo_bf16_b1_t512", 2, B=1, T=512, H=896, V=151936,
+         prompt_lo=32, prompt_hi=128),
+    Spec("gmpo_kl_bf16_b8_t2048", 3, B=8, T=2048, H=896, V=151936, bias=True,
+         eps_low=0.2, eps_high=0.3, beta=0.04, ref_noise_std=0.05,
+         prompt_lo=64, prompt_hi=512, zero_adv_fraction=0.25),
+    Spec("gspo_token_entropy_bf16_b2_t32768", 4, B=2, T=32768, H=896, V=151936,
+         loss_type=GSPO_TOKEN, eps_low=3e-4, eps_high=4e-4, old_noise_std=1e-4,
+         top_entropy_quantile=0.2, prompt_lo=256, prompt_hi=2048),
+    Spec("gmpo_bf16_b128_t32768_chunked", 5, B=128, T=32768, H=896, V=151936,
+         bias=True, chunk_sequences=8, prompt_lo=32, prompt_hi=128),
+)
+# the workloads by name, and by the workload id that also seeds them
+WORKLOADS = {s.name: s for s in _SPECS}
+BY_ID = {s.cfg_id: s for s in _SPECS}
 
 
 def _rng(spec: Spec, stream: int) -> np.random.Generator:

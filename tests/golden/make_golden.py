@@ -1,13 +1,13 @@
 """Write the oracle's per-token forward statistics for the large workloads.
 
-Calls only the CPU oracle (and the seeded generators): for workload cfg it
+Calls only the CPU oracle (and the seeded generators): for each named workload it
 stores fp32 log-prob, log-sum-exp and entropy of every token, which the GPU
 tests use to form old/ref log-probs (fp32(current) + noise, the generators'
 recipe) and as expected values. Usage:
 
-    python tests/golden/make_golden.py 3 4
+    python tests/golden/make_golden.py gmpo_kl_bf16_b8_t2048 gspo_token_entropy_bf16_b2_t32768
 
-Output: tests/golden/fwd_cfg{N}.npz (arrays logp, lse, entropy; fp32).
+Output: tests/golden/fwd_<workload>.npz (arrays logp, lse, entropy; fp32).
 """
 import os
 import sys
@@ -23,9 +23,9 @@ import oracle  # noqa: E402
 import synth  # noqa: E402
 
 
-def main(cfgs):
-    for c in cfgs:
-        spec = synth.CONFIGS[c]
+def main(names):
+    for c in names:
+        spec = synth.WORKLOADS[c]
         t0 = time.time()
         h, _ = synth.hidden(spec)
         W, _ = synth.weight(spec)
@@ -42,11 +42,11 @@ def main(cfgs):
             r1 = min(N, r0 + step)
             f = oracle.forward_rows(h[r0:r1], W64, b64, spec.temperature, y[r0:r1])
             lp[r0:r1], lse[r0:r1], ent[r0:r1] = f["logp"], f["lse"], f["entropy"]
-            print(f"cfg{c}: {r1}/{N} rows, {time.time() - t0:.0f} s", flush=True)
-        out = os.path.join(HERE, f"fwd_cfg{c}.npz")
+            print(f"{c}: {r1}/{N} rows, {time.time() - t0:.0f} s", flush=True)
+        out = os.path.join(HERE, f"fwd_{c}.npz")
         np.savez_compressed(out, logp=lp, lse=lse, entropy=ent)
         print(f"wrote {out} in {time.time() - t0:.0f} s", flush=True)
 
 
 if __name__ == "__main__":
-    main([int(a) for a in sys.argv[1:]] or [3, 4])
+    main(sys.argv[1:] or ["gmpo_kl_bf16_b8_t2048", "gspo_token_entropy_bf16_b2_t32768"])

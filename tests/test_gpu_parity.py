@@ -142,7 +142,7 @@ SMALL = {
     "mfma_v1_degenerate_q": synth.small("mfma_v1", cfg_id=125, B=2, T=30, H=128, V=1, top_entropy_quantile=0.5),
     "generic_bf16_v1": synth.small("generic_v1", cfg_id=126, B=2, T=20, H=96, V=1, bias=True),
     # generic (vector ALU) path: fp32, and bf16 with H not a multiple of 128
-    "generic_f32_cfg1": synth.CONFIGS[1],
+    "generic_f32_tiny_b2_t16": synth.WORKLOADS["tiny_gmpo_f32"],
     "generic_bf16_h96": synth.small("generic_h96", cfg_id=106, B=2, T=50, H=96, V=700, bias=True),
     "generic_f32_gspo_chunked": synth.small("generic_gspo", cfg_id=107, dtype="f32", B=3, T=30, H=48, V=300,
                                             loss_type=synth.GSPO_TOKEN, eps_low=0.01, eps_high=0.01,

@@ -16,18 +16,18 @@ def test_bf16_rounding_matches_torch():
                                   torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy())
 
 
-def test_config_recipes():
-    s3 = synth.CONFIGS[3]
+def test_workload_recipes():
+    s3 = synth.WORKLOADS["gmpo_kl_bf16_b8_t2048"]
     a = synth.advantages(s3)
     assert (a == 0).sum() == 2
     P = synth.prompt_lengths(s3)
     assert P.min() >= 64 and P.max() <= 512
     m = synth.completion_mask(s3).reshape(s3.B, s3.T)
     assert all(m[i].sum() == s3.T - P[i] for i in range(s3.B))
-    s1 = synth.CONFIGS[1]
+    s1 = synth.WORKLOADS["tiny_gmpo_f32"]
     assert set(synth.advantages(s1).tolist()) <= {1.0, -1.0, 0.0}
     assert synth.completion_mask(s1).reshape(2, 16)[:, :4].sum() == 0
-    y = synth.targets(synth.CONFIGS[2])
+    y = synth.targets(synth.WORKLOADS["gmpo_bf16_b1_t512"])
     assert y.min() >= 0 and y.max() < 151936 and y.dtype == np.int64
 
 
