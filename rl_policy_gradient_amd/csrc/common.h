@@ -167,6 +167,12 @@ __host__ __device__ inline bool token_mean_loss(int loss_type) { return loss_typ
 // Launchers (each enqueues on `st`; return hipError_t of the launch)
 // ---------------------------------------------------------------------------
 
+// The bias as the forward sweeps read it: out[v] = fp32(b[v]) for v < V and
+// 0 up to the next multiple of 64 (bias_f32_len(V) floats), so that a lane
+// takes four rows with one 16-byte load and no bf16 unpacking.
+hipError_t launch_bias_f32(const __bf16* b, int V, float* out, hipStream_t st);
+inline int64_t bias_f32_len(int V) { return ((int64_t)V + 63) / 64 * 64; }
+
 // Fragment-major copy of bf16 rows for the MFMA sweeps (the layout is given
 // in mfma_tile.h): `tiles` 32-row tiles of X, or of X[idx[k]] when idx is
 // given; rows at or past `rows` (*count_dev when given) are zero.
@@ -185,7 +191,7 @@ hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_de
 // above the row's largest logit leaves nothing to flag. clear_count (or
 // NULL; not count_dev) is set to zero by the sweep, for a launch_flag_scan
 // after it.
-hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
+hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const float* b, int64_t N, int H, int V, float inv_tau,
                            int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st,
                            const int* count_dev = nullptr, const float* mref = nullptr, int mref_stride = 1,
                            const int* row_idx = nullptr, int* clear_count = nullptr);

@@ -4,7 +4,7 @@
 
 namespace plp {
 
-hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V, float inv_tau,
+hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const float* b, int64_t N, int H, int V, float inv_tau,
                            int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st, const int* count_dev,
                            const float* mref, int mref_stride, const int* row_idx, int* clear_count) {
   if (with_o)

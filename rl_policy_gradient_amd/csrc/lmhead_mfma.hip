@@ -462,6 +462,20 @@ hipError_t bwd_dispatch(const __bf16* Wf, const __bf16* b, const __bf16* hcf, co
 
 }  // namespace
 
+namespace {
+__global__ __launch_bounds__(256) void bias_f32_kernel(const __bf16* __restrict__ b, int V, int len,
+                                                       float* __restrict__ out) {
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  if (v < len) out[v] = v < V ? (float)b[v] : 0.f;
+}
+}  // namespace
+
+hipError_t launch_bias_f32(const __bf16* b, int V, float* out, hipStream_t st) {
+  const int len = (int)bias_f32_len(V);
+  hipLaunchKernelGGL(bias_f32_kernel, dim3((unsigned)((len + 255) / 256)), dim3(256), 0, st, b, V, len, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_dev, int64_t rows, int64_t tiles, int H,
                             __bf16* Xf, hipStream_t st) {
   if (tiles <= 0) return hipSuccess;

@@ -149,6 +149,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t frag_rsrc(const __bf16* base, 
 __device__ __forceinline__ bf16x8 ld_buf(__amdgpu_buffer_rsrc_t r, int lane_bytes, int const_bytes) {
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_bytes, const_bytes, 0));
 }
+// fp32 data through a buffer resource (byte range `bytes`), 16 bytes per lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t f32_rsrc(const float* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 ld_f4(__amdgpu_buffer_rsrc_t r, int lane_bytes) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_bytes, 0, 0));
+}
 // The same with the non-temporal hint: for data read once (the resident
 // rows of the weight-gradient sweep), so that it does not push the token
 // tiles every workgroup re-reads out of L2.

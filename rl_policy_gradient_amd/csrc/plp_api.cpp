@@ -135,6 +135,7 @@ struct Plan {
 
 struct Bufs {
   __bf16* Wf = nullptr;        // fragment-major copy of W (MFMA path)
+  float* bias2 = nullptr;      // the bias in fp32 for the forward sweeps (MFMA path with a bias)
   RowStats* stats = nullptr;
   float* O = nullptr;
   float* v = nullptr;
@@ -196,6 +197,7 @@ size_t carve(const plp_args* a, const Plan& p, void* ws, Bufs& b) {
     b.Wf = (__bf16*)weight_prepared(a);  // read only
   else if (p.mfma)
     b.Wf = c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H);
+  if (p.mfma && a->bias) b.bias2 = c.take<float>((size_t)bias_f32_len(V));
   b.stats = c.take<RowStats>((size_t)p.Sv * p.Nc);
   if (p.mfma) {
     const int64_t rows2 = p.o2_rows;
@@ -372,7 +374,7 @@ LossParams loss_params(const plp_args* a, const unsigned long long* ntok_dev) {
 // statistics and accumulator from this pass. A call with no flagged row
 // costs the listing and the launches, whose workgroups find no row. The
 // sweep before it has cleared fp.count (its clear_count).
-hipError_t flagged_pass(int dtype, const void* h, const __bf16* Wf, const __bf16* bias, const RowStats* stats, int Sv,
+hipError_t flagged_pass(int dtype, const void* h, const __bf16* Wf, const float* bias, const RowStats* stats, int Sv,
                         int64_t n, int H, int V, float inv_tau, const FlaggedPass& fp, hipStream_t st) {
   (void)dtype;
   hipError_t e = launch_flag_scan(stats, Sv, n, fp.cap, fp.idx, fp.mref, fp.pos, fp.count, st);
@@ -388,6 +390,7 @@ struct SelBufs {
   RowStats* stats = nullptr;
   float* scratch_lp = nullptr;
   __bf16* Wf = nullptr;
+  float* bias2 = nullptr;  // the bias in fp32 for the forward sweeps (when one is given)
   FlaggedPass fp{};
 };
 
@@ -399,6 +402,7 @@ size_t carve_selective(void* ws, int64_t N, int H, int V, int dtype, SelBufs& sb
   sb.scratch_lp = c.take<float>(N);
   if (sb.mfma) {
     sb.Wf = c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H);
+    sb.bias2 = c.take<float>((size_t)bias_f32_len(V));
     sb.fp.cap = (int)std::min(round_up(N, kBK), kFlagCap);
     sb.fp.idx = c.take<int>((size_t)sb.fp.cap);
     sb.fp.mref = c.take<float>((size_t)sb.fp.cap);
@@ -421,10 +425,10 @@ int forward_rows(const plp_args* a, const Plan& p, Bufs& b, int64_t r0, int64_t 
   if (p.mfma) {
     hipEvent_t* ev = prof_slot(0);
     if (ev) HIP_TRY(hipEventRecord(ev[0], st));
-    HIP_TRY(launch_fwd_mfma((const __bf16*)h, b.Wf, (const __bf16*)a->bias, n, a->H, a->V, inv_tau, p.Sv, with_o,
+    HIP_TRY(launch_fwd_mfma((const __bf16*)h, b.Wf, b.bias2, n, a->H, a->V, inv_tau, p.Sv, with_o,
                             b.stats, with_o ? b.O : nullptr, st, nullptr, nullptr, 1, nullptr, b.fp.count));
     if (ev) HIP_TRY(hipEventRecord(ev[1], st));
-    HIP_TRY(flagged_pass(a->dtype, h, b.Wf, (const __bf16*)a->bias, b.stats, p.Sv, n, a->H, a->V, inv_tau, b.fp, st));
+    HIP_TRY(flagged_pass(a->dtype, h, b.Wf, b.bias2, b.stats, p.Sv, n, a->H, a->V, inv_tau, b.fp, st));
   } else {
     HIP_TRY(launch_fwd_generic(a->dtype, h, a->weight, a->bias, y, n, a->H, a->V, inv_tau, with_o, b.stats,
                                with_o ? b.O : nullptr, st));
@@ -621,6 +625,7 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
 
   if (p.mfma && !p.wprep)
     HIP_TRY(launch_frag_copy((const __bf16*)a->weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H, b.Wf, st));
+  if (b.bias2) HIP_TRY(launch_bias_f32((const __bf16*)a->bias, V, b.bias2, st));
 
   bool first_chunk_done = false;
   if (p.entropy) {
@@ -679,7 +684,7 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
       // each row's log-sum-exp (lse >= every logit of the row) as its
       // exponent reference: nothing to flag in this pass
       static_assert(offsetof(TokData, lse) == 0 && sizeof(TokData) == 4 * sizeof(float), "lse every 4 floats");
-      HIP_TRY(launch_fwd_mfma((const __bf16*)hsrc, b.Wf, (const __bf16*)a->bias, p.cap, H, V, inv_tau, kMaxSplits,
+      HIP_TRY(launch_fwd_mfma((const __bf16*)hsrc, b.Wf, b.bias2, p.cap, H, V, inv_tau, kMaxSplits,
                               true, b.stats2, b.O2, st, b.count, (const float*)b.tok, 4, b.idx));
       if (ev) HIP_TRY(hipEventRecord(ev[1], st));
       HIP_TRY(launch_grad_h_compact(a->dtype, b.stats2, b.O2, kMaxSplits, p.cap, H, V, hsrc, a->weight, a->bias,
@@ -748,9 +753,11 @@ PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const 
   const float inv_tau = 1.0f / temperature;
   if (sb.mfma) {
     HIP_TRY(launch_frag_copy((const __bf16*)weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H, sb.Wf, st));
-    HIP_TRY(launch_fwd_mfma((const __bf16*)hidden, sb.Wf, (const __bf16*)bias, N, H, V, inv_tau, sb.sv, false,
+    if (bias) HIP_TRY(launch_bias_f32((const __bf16*)bias, V, sb.bias2, st));
+    const float* bias2 = bias ? sb.bias2 : nullptr;
+    HIP_TRY(launch_fwd_mfma((const __bf16*)hidden, sb.Wf, bias2, N, H, V, inv_tau, sb.sv, false,
                             sb.stats, nullptr, st, nullptr, nullptr, 1, nullptr, sb.fp.count));
-    HIP_TRY(flagged_pass(dtype, hidden, sb.Wf, (const __bf16*)bias, sb.stats, sb.sv, N, H, V, inv_tau, sb.fp, st));
+    HIP_TRY(flagged_pass(dtype, hidden, sb.Wf, bias2, sb.stats, sb.sv, N, H, V, inv_tau, sb.fp, st));
   }
   else
     HIP_TRY(launch_fwd_generic(dtype, hidden, weight, bias, y, N, H, V, inv_tau, false, sb.stats, nullptr, st));
