@@ -167,9 +167,9 @@ __host__ __device__ inline bool token_mean_loss(int loss_type) { return loss_typ
 // Launchers (each enqueues on `st`; return hipError_t of the launch)
 // ---------------------------------------------------------------------------
 
-// The bias as the forward sweeps read it: out[v] = fp32(b[v]) for v < V and
-// 0 up to the next multiple of 64 (bias_f32_len(V) floats), so that a lane
-// takes four rows with one 16-byte load and no bf16 unpacking.
+// The bias as the accumulator sweep reads it: out[v] = fp32(b[v]) for v < V
+// and 0 up to the next multiple of 64 (bias_f32_len(V) floats), so that a
+// lane takes four rows with one 16-byte load and no bf16 unpacking.
 hipError_t launch_bias_f32(const __bf16* b, int V, float* out, hipStream_t st);
 inline int64_t bias_f32_len(int V) { return ((int64_t)V + 63) / 64 * 64; }
 
@@ -180,7 +180,10 @@ hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_de
                             __bf16* Xf, hipStream_t st);
 
 // Forward sweep on MFMA (bf16, H a multiple of 128, H <= 896); Wf is the
-// fragment-major copy of W. With count_dev (an accumulator pass over a
+// fragment-major copy of W; the bias, when there is one, comes as its fp32
+// copy b32 (launch_bias_f32, read by the accumulator sweep) and as the
+// caller's bf16 b16 (read by the statistics-only sweep), both or neither.
+// With count_dev (an accumulator pass over a
 // compacted row list, with_o only) the sweep runs over the first
 // min(*count_dev, N) rows of h, or with row_idx over rows row_idx[k] of h
 // (N is the list's capacity), with
@@ -191,8 +194,8 @@ hipError_t launch_frag_copy(const __bf16* X, const int* idx, const int* count_de
 // above the row's largest logit leaves nothing to flag. clear_count (or
 // NULL; not count_dev) is set to zero by the sweep, for a launch_flag_scan
 // after it.
-hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const float* b, int64_t N, int H, int V, float inv_tau,
-                           int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st,
+hipError_t launch_fwd_mfma(const __bf16* h, const __bf16* Wf, const float* b32, const __bf16* b16, int64_t N, int H,
+                           int V, float inv_tau, int Sv, bool with_o, RowStats* stats, float* O, hipStream_t st,
                            const int* count_dev = nullptr, const float* mref = nullptr, int mref_stride = 1,
                            const int* row_idx = nullptr, int* clear_count = nullptr);
 // Row stride of the compacted pass's stats and O (whole 64-row blocks).

@@ -17,7 +17,7 @@ namespace {
 template <int KB, bool HAS_BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf,
-                     const float* __restrict__ bias2, int64_t N, int V, float inv_tau, int Sv,
+                     const __bf16* __restrict__ bias, int64_t N, int V, float inv_tau, int Sv,
                      int tiles_per_split, RowStats* __restrict__ stats, int* __restrict__ clear_count) {
   constexpr int H = 128 * KB;
   if (clear_count && blockIdx.x == 0 && threadIdx.x == 0) *clear_count = 0;  // for the flag scan that follows
@@ -73,18 +73,35 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   bool flag = false;
   float zmx = -INFINITY;             // the largest logit (base 2) this lane saw
 
-  // Bias of tile rows kvq(kh, hh, 0..7) from its fp32 copy (bias2, zero
-  // past V up to a multiple of 64): two groups of four consecutive rows, one
-  // 16-byte load each. (A copy scaled to base 2 would save the add but fix a
-  // rounding offset per vocabulary row that every token's log-sum-exp shares.)
-  const auto bias_r = f32_rsrc(bias2, HAS_BIAS ? ((V + 63) / 64) * 64 * 4 : 0);
-  auto load_bias = [&](int t, f32x4 (&bv)[2]) {
+  // Bias of tile rows kvq(kh, hh, 0..7), kept as packed bf16 (two groups of
+  // four consecutive rows, one 8-byte load each when inside the vocabulary).
+  const auto bias_r = frag_rsrc(bias, HAS_BIAS ? V * 2 : 0);
+  auto load_bias = [&](int t, uint2 (&bv)[2]) {
     if constexpr (HAS_BIAS) {
+      if ((t + 1) * BK <= V) {  // uniform: the whole tile lies inside the vocabulary
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) bv[hf] = ld_f4(bias_r, (t * BK + 16 * kh + 8 * hf + 4 * hh) * 4);
+        for (int hf = 0; hf < 2; ++hf) {
+          const int r0 = t * BK + 16 * kh + 8 * hf + 4 * hh;
+          bv[hf] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(bias_r, r0 * 2, 0, 0));
+        }
+      } else {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int r0 = t * BK + 16 * kh + 8 * hf + 4 * hh;
+          unsigned e[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_raw_buffer_load_b16(bias_r, min(r0 + j, V - 1) * 2, 0, 0);
+          bv[hf] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+        }
+      }
     } else {
-      bv[0] = bv[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bv[0] = bv[1] = make_uint2(0u, 0u);
     }
+  };
+  auto bias_at = [&](const uint2 (&bv)[2], int j) -> float {
+    const uint2 u = bv[j >> 2];
+    const unsigned wd = (j & 2) ? u.y : u.x;
+    return __uint_as_float((j & 1) ? (wd & 0xffff0000u) : (wd << 16));
   };
   // S^T of the tile held in `a` (tile rows past V are zero in the
   // fragment-major copy and masked in the epilogue); each k-slice of `a`,
@@ -116,19 +133,19 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
   };
   // Logits (base 2) of the eight tile rows this lane holds; rows past the
   // vocabulary get -1e30 (2^(-1e30 - m2) = 0 and 0 * z = 0).
-  auto logits = [&](int v0, const f32x4 (&sf)[2], const f32x4 (&bv)[2], float (&z)[8]) {
+  auto logits = [&](int v0, const f32x4 (&sf)[2], const uint2 (&bv)[2], float (&z)[8]) {
     const int lim = V - v0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float sv_ = sf[j >> 2][j & 3];
-      const float zz = HAS_BIAS ? (sv_ + bv[j >> 2][j & 3]) * c2 : sv_ * c2;
+      const float zz = HAS_BIAS ? (sv_ + bias_at(bv, j)) * c2 : sv_ * c2;
       z[j] = kvq(kh, hh, j) < lim ? zz : -1e30f;
     }
   };
 
   f32x16 acc[2];
   f32x4 sf[2];
-  f32x4 bv[2];
+  uint2 bv[2];
   if (any) {
     load_bias(t_begin, bv);
     s_step(a, acc, min(t_begin + 1, t_end - 1));
@@ -153,7 +170,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ h, const __bf16* __restrict__ Wf
     const int v0 = t * BK;
     const int tn = min(t + 1, t_end - 1);
     const int tnn = min(t + 2, t_end - 1);
-    f32x4 bvn[2];
+    uint2 bvn[2];
     load_bias(tn, bvn);
     // ---- epilogue of tile t (vector ALU; the scheduler interleaves it with
     //      the logit MFMAs of tile t+1 below) -------------------------------
@@ -540,7 +557,7 @@ hipError_t fwd_pp_launch(const __bf16* h, const __bf16* Wf, const float* b, int6
 }
 
 template <bool HAS_BIAS>
-hipError_t fwd_stats_launch(const __bf16* h, const __bf16* Wf, const float* b, int64_t N, int H, int V,
+hipError_t fwd_stats_launch(const __bf16* h, const __bf16* Wf, const __bf16* b, int64_t N, int H, int V,
                             float inv_tau, int Sv, RowStats* stats, int* clear_count, hipStream_t st) {
   const int n_tiles = (V + BK - 1) / BK;
   const int tps = (n_tiles + Sv - 1) / Sv;
