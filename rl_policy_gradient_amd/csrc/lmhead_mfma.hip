@@ -288,13 +288,16 @@ void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bia
       auto frag = [&](int db) {
         return ld_tr(tb + tr_base[0] + 16 * ks * TS + 32 * db, tb + tr_base[1] + 16 * ks * TS + 32 * db);
       };
-      bf16x8 b0 = frag(0);
+      // B fragments two column blocks ahead (one ahead in the forward
+      // sweep, where two cost 6 %: here they gain 2-3 %)
+      bf16x8 b0 = frag(0), b1 = frag(1 < DB ? 1 : DB - 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 b1 = frag(db + 1 < DB ? db + 1 : DB - 1);
+        const bf16x8 b2 = frag(db + 2 < DB ? db + 2 : DB - 1);
         o[0][db] = mfma32(p0, b0, o[0][db]);
         o[1][db] = mfma32(p1, b0, o[1][db]);
         b0 = b1;
+        b1 = b2;
       }
     };
     __syncthreads();  // P0
