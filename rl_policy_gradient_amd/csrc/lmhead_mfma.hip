@@ -132,7 +132,9 @@ void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bia
     auto stage_tok = [&](int t) {
       if (w == 0 && lane < BK) {
         const u32x4 pad = {0x7f800000u, 0u, 0xffffffffu, 0u};
-        *reinterpret_cast<u32x4*>(&s_tok[t & 1][lane]) = t * BK + lane < n_tok ? tk : pad;
+        u32x4 rec = t * BK + lane < n_tok ? tk : pad;
+        rec[0] = __float_as_uint(__uint_as_float(rec[0]) * kLog2e);  // lse in base 2 (+inf stays +inf)
+        *reinterpret_cast<u32x4*>(&s_tok[t & 1][lane]) = rec;
       }
     };
     if (any) load_tok(t_lo);
@@ -156,6 +158,7 @@ void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bia
     }
     const int my_v = q0 + 32 * nbq + c;
     const float bvl = HAS_BIAS ? (float)bias[min(my_v, V - 1)] : 0.f;
+    const float c2 = inv_tau * kLog2e;
     double gb_run = 0.0;
 
     auto s_step = [&](f32x16 (&acc)[2], int buf, int t_next) {
@@ -182,7 +185,9 @@ void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bia
                 (s_part[2][nbq][2 * kh + e][lane] + s_part[3][nbq][2 * kh + e][lane]);
     };
     // Epilogue of tile t: dz = g / tau ([v = y] - p) as bf16 P of this
-    // wave's quarter, and this lane's share of grad_b. Every token record is
+    // wave's quarter, and this lane's share of grad_b; p = 2^(z2 - lse2) in
+    // base 2 (the records' lse is scaled by log2 e once, when staged), and
+    // dz = [v = y] gs - gs p as one fma. Every token record is
     // read (padding included), so the reads are not guarded by branches;
     // rows past V give values that only reach their own grad_W / grad_b
     // rows, which are never stored.
@@ -198,11 +203,10 @@ void bwd_pp_kernel(const __bf16* __restrict__ Wf, const __bf16* __restrict__ bia
       float gsum = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float lse = rec[j][0], gs = rec[j][1];
+        const float lse2 = rec[j][0], gs = rec[j][1];
         const int y = __float_as_int(rec[j][2]);
-        const float z = (sf[j >> 2][j & 3] + bvl) * inv_tau;
-        const float pr = __expf(z - lse);
-        const float dz = gs * ((y == my_v ? 1.f : 0.f) - pr);
+        const float pr = __builtin_amdgcn_exp2f((sf[j >> 2][j & 3] + bvl) * c2 - lse2);
+        const float dz = __builtin_fmaf(-gs, pr, y == my_v ? gs : 0.f);
         gsum += dz;
         pa[j] = (__bf16)dz;
       }
