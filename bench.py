@@ -234,6 +234,48 @@ def _cpu_baseline_full(cfg: int) -> dict:
             "total_s": round(t2 - t0, 2), "tokens_per_s": round(spec.N / (t2 - t0), 3)}
 
 
+def _gemm_ceiling(dev) -> int:
+    """Plain library GEMMs (torch.mm, bf16 operands, fp32 accumulation) at the
+    contraction shapes of the sweeps, H=896 V=151936: the logits [N,H]x[H,V],
+    the grad_W product [V,N]x[N,H] and the grad_h product [N,V]x[V,H], each
+    timed with events over a few repetitions. They give the rate a vendor
+    GEMM reaches on this chip at these shapes, beside the sweeps' executed
+    rate; they are not part of the path. One JSON line per product."""
+    import torch
+
+    H, V = 896, 151936
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    for N in (16384, 65536):
+        h = torch.randn(N, H, generator=g, device=dev).to(torch.bfloat16)
+        wt = (torch.randn(H, V, generator=g, device=dev) * 0.02).to(torch.bfloat16)   # [H, V], contiguous
+        p = (torch.rand(N, V, generator=g, device=dev) * 1e-5).to(torch.bfloat16)      # [N, V]
+        pt = p.t().contiguous()                                                        # [V, N]
+        w = wt.t().contiguous()                                                        # [V, H]
+        cases = (("logits", lambda: torch.mm(h, wt), (N, H, V)),
+                 ("grad_w", lambda: torch.mm(pt, h), (V, N, H)),
+                 ("grad_h", lambda: torch.mm(p, w), (N, V, H)))
+        for name, fn, (m, k, n) in cases:
+            for _ in range(2):
+                out = fn()
+            torch.cuda.synchronize()
+            reps = 5
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                out = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            tf = 2.0 * m * k * n / (ms * 1e-3) / 1e12
+            print(json.dumps({"gemm": name, "M": m, "K": k, "N": n, "ms": round(ms, 4), "tflops": round(tf, 1),
+                              "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+            del out
+        del h, wt, p, pt, w
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +293,8 @@ def main() -> int:
                          "accumulation; the steps then skip that copy")
     ap.add_argument("--memory-sweep", action="store_true",
                     help="peak device memory of one fused call over vocabulary sizes and token counts (one line each)")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="time plain library bf16 GEMMs at the sweeps' contraction shapes (one line each)")
     ap.add_argument("--bias-std", type=float, default=None,
                     help="--config 2 with a bias ~ N(0, S^2): logits far above a vocabulary split's first tile "
                          "make the sweep flag rows for the exact recompute; reports how many")
@@ -280,6 +324,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.memory_sweep:
         return _memory_sweep(dev)
+    if args.gemm_ceiling:
+        return _gemm_ceiling(dev)
     spec, inp = _workload(args.config, dev)
     flagged = None
     if args.bias_std is not None:
