@@ -61,7 +61,7 @@ extern "C" {
 #endif
 
 #define PLP_API __attribute__((visibility("default")))
-#define PLP_ABI_VERSION 4
+#define PLP_ABI_VERSION 5
 
 /* Return codes. */
 #define PLP_OK 0
@@ -256,6 +256,25 @@ PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const 
                                   int64_t N, int32_t H, int32_t V, int32_t dtype, float temperature,
                                   const int64_t* targets, float* entropy_out, float* logp_out,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* plp_selective_entropy on a weight whose matrix-core copy the caller made
+ * with plp_prepare_weight (ABI version 5), for the no-grad passes between two
+ * weight updates (PR #1558, Details: the entropy pre-pass runs over the same
+ * LM-head weight as the loss that follows): the call reads weight_prepared
+ * instead of making that copy, so its workspace
+ * (plp_selective_entropy_prepared_workspace_size) has no copy of W. weight
+ * [V,H] is still read (target logits, flagged rows) and must hold the values
+ * weight_prepared was made from; the results are bit-identical to
+ * plp_selective_entropy's. bf16 with H a multiple of 128 up to 896 only
+ * (otherwise PLP_E_UNSUPPORTED); weight_prepared NULL or not 16-byte aligned:
+ * PLP_E_INVALID; other arguments and errors as for plp_selective_entropy. */
+PLP_API int plp_selective_entropy_prepared_workspace_size(int64_t N, int32_t H, int32_t V, int32_t dtype,
+                                                          size_t* bytes);
+PLP_API int plp_selective_entropy_prepared(const void* hidden, const void* weight, const void* weight_prepared,
+                                           const void* bias, int64_t N, int32_t H, int32_t V, int32_t dtype,
+                                           float temperature, const int64_t* targets, float* entropy_out,
+                                           float* logp_out, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
 
 /* Batch-global high-entropy mask (PR #1558, Details bullet 2):
  * thr = quantile(entropy[active], 1 - q) with torch.quantile's linear

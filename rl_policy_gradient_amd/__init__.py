@@ -234,10 +234,12 @@ def prepare_weight(weight: torch.Tensor, out: Optional[torch.Tensor] = None) -> 
 
 def selective_entropy(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
                       targets: Optional[torch.Tensor] = None, temperature: float = 1.0,
-                      workspace: Optional[torch.Tensor] = None):
+                      workspace: Optional[torch.Tensor] = None, weight_prepared: Optional[torch.Tensor] = None):
     """Per-row entropy (and target log-prob when targets are given) by a
     streaming online log-sum-exp over vocabulary tiles
-    (plp_selective_entropy). Returns (entropy, logp or None), fp32 [N]."""
+    (plp_selective_entropy; with weight_prepared, made by prepare_weight from
+    the weight's current values, plp_selective_entropy_prepared, which skips
+    that copy). Returns (entropy, logp or None), fp32 [N]."""
     h2 = hidden.reshape(-1, hidden.shape[-1])
     N, H = h2.shape
     V = weight.shape[0]
@@ -246,13 +248,22 @@ def selective_entropy(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional
         _check_vec(targets, N, torch.int64, "targets")
     L = _abi.lib()
     n = ctypes.c_size_t()
-    _abi.check(L.plp_selective_entropy_workspace_size(N, H, V, _dtype_code(h2), ctypes.byref(n)))
+    dt = _dtype_code(h2)
+    if weight_prepared is None:
+        _abi.check(L.plp_selective_entropy_workspace_size(N, H, V, dt, ctypes.byref(n)))
+    else:
+        _abi.check(L.plp_selective_entropy_prepared_workspace_size(N, H, V, dt, ctypes.byref(n)))
     ws = _workspace(n.value, dev, workspace)
     ent = torch.empty(N, dtype=torch.float32, device=dev)
     lp = torch.empty(N, dtype=torch.float32, device=dev) if targets is not None else None
-    _abi.check(L.plp_selective_entropy(_ptr(h2), _ptr(weight), _ptr(bias), N, H, V, _dtype_code(h2),
-                                       ctypes.c_float(temperature), _ptr(targets), _ptr(ent), _ptr(lp),
-                                       ws.data_ptr(), ws.numel(), _stream(dev)))
+    if weight_prepared is None:
+        _abi.check(L.plp_selective_entropy(_ptr(h2), _ptr(weight), _ptr(bias), N, H, V, dt,
+                                           ctypes.c_float(temperature), _ptr(targets), _ptr(ent), _ptr(lp),
+                                           ws.data_ptr(), ws.numel(), _stream(dev)))
+    else:
+        _abi.check(L.plp_selective_entropy_prepared(_ptr(h2), _ptr(weight), _ptr(weight_prepared), _ptr(bias), N,
+                                                    H, V, dt, ctypes.c_float(temperature), _ptr(targets),
+                                                    _ptr(ent), _ptr(lp), ws.data_ptr(), ws.numel(), _stream(dev)))
     return ent, lp
 
 

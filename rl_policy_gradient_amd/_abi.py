@@ -17,7 +17,7 @@ PLP_E_HIP = -4
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 LOSS_GMPO, LOSS_GSPO_TOKEN, LOSS_GRPO, LOSS_BNPO, LOSS_DAPO = 0, 1, 2, 3, 4
-ABI_VERSION = 3
+ABI_VERSION = 5
 IS_TOKEN, IS_SEQUENCE = 0, 1
 REDUCE_SEQ_MEAN, REDUCE_TOKEN_SUM = 0, 1
 
@@ -114,6 +114,10 @@ def lib() -> ctypes.CDLL:
                                                        ctypes.c_int32, P(sz)]
     L.plp_selective_entropy.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp, sz, _vp]
+    L.plp_selective_entropy_prepared_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                                ctypes.c_int32, P(sz)]
+    L.plp_selective_entropy_prepared.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp, sz, _vp]
     L.plp_entropy_quantile_mask_workspace_size.argtypes = [ctypes.c_int64, P(sz)]
     L.plp_entropy_quantile_mask.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_double, _vp, _vp, _vp, sz, _vp]
     L.plp_entropy_quantile_mask_noalloc.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_double, _vp, _vp, _vp]
@@ -128,10 +132,14 @@ def lib() -> ctypes.CDLL:
     L.plp_profile_start.restype = ctypes.c_int
     L.plp_profile_stop.restype = ctypes.c_int
     for name in ("plp_workspace_size", "plp_fused_lmhead_policy_loss_fwd_bwd", "plp_selective_entropy_workspace_size",
-                 "plp_selective_entropy", "plp_entropy_quantile_mask_workspace_size", "plp_entropy_quantile_mask",
+                 "plp_selective_entropy", "plp_selective_entropy_prepared_workspace_size",
+                 "plp_selective_entropy_prepared", "plp_entropy_quantile_mask_workspace_size", "plp_entropy_quantile_mask",
                  "plp_entropy_quantile_mask_noalloc", "plp_prepared_weight_size", "plp_prepare_weight",
                  "plp_policy_loss_workspace_size", "plp_policy_loss_from_logprobs"):
         getattr(L, name).restype = ctypes.c_int
+    if L.plp_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {L.plp_abi_version()}, this binding {ABI_VERSION}: "
+                          "rebuild it with `python -m rl_policy_gradient_amd.build`")
     _lib = L
     return L
 

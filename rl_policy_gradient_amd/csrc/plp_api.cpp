@@ -414,14 +414,15 @@ struct SelBufs {
   FlaggedPass fp{};
 };
 
-size_t carve_selective(void* ws, int64_t N, int H, int V, int dtype, SelBufs& sb) {
+// prepared: the weight's matrix-core copy comes from the caller (no Wf here).
+size_t carve_selective(void* ws, int64_t N, int H, int V, int dtype, bool prepared, SelBufs& sb) {
   Carver c(ws);
   sb.mfma = mfma_eligible(dtype, H);
   sb.sv = choose_splits(N, V, sb.mfma);
   sb.stats = c.take<RowStats>((size_t)sb.sv * N);
   sb.scratch_lp = c.take<float>(N);
   if (sb.mfma) {
-    sb.Wf = c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H);
+    if (!prepared) sb.Wf = c.take<__bf16>((size_t)round_up(V, 2 * kBK) * H);
     sb.bias2 = c.take<float>((size_t)bias_f32_len(V));
     sb.fp.cap = (int)std::min(round_up(N, kBK), kFlagCap);
     sb.fp.idx = c.take<int>((size_t)sb.fp.cap);
@@ -745,21 +746,30 @@ PLP_API int plp_fused_lmhead_policy_loss_fwd_bwd(const plp_args* a, const plp_ou
   return ok();
 }
 
-PLP_API int plp_selective_entropy_workspace_size(int64_t N, int32_t H, int32_t V, int32_t dtype, size_t* bytes) {
+namespace {
+
+int selective_workspace_size(int64_t N, int32_t H, int32_t V, int32_t dtype, bool prepared, size_t* bytes) {
   if (!bytes) return fail(PLP_E_INVALID, "bytes is NULL");
   if (N < 1 || N >= kMaxRows || H < 1 || V < 1) return fail(PLP_E_INVALID, "bad sizes N=%lld H=%d V=%d", (long long)N, H, V);
   if (dtype != PLP_DTYPE_F32 && dtype != PLP_DTYPE_BF16) return fail(PLP_E_INVALID, "unknown dtype %d", dtype);
+  if (prepared && !mfma_eligible(dtype, H))
+    return fail(PLP_E_UNSUPPORTED, "weight_prepared is for bf16 with H a multiple of 128 up to 896 (dtype %d, H=%d)",
+                dtype, H);
   SelBufs sb;
-  *bytes = carve_selective(nullptr, N, H, V, dtype, sb);
+  *bytes = carve_selective(nullptr, N, H, V, dtype, prepared, sb);
   return ok();
 }
 
-PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const void* bias, int64_t N, int32_t H,
-                                  int32_t V, int32_t dtype, float temperature, const int64_t* targets,
-                                  float* entropy_out, float* logp_out, void* ws, size_t ws_bytes, hipStream_t st) {
+// Both selective-entropy entry points; wprep is the caller's matrix-core copy
+// of the weight or NULL (then the call makes its own in the workspace).
+int selective_entropy(const void* hidden, const void* weight, const void* wprep, bool prepared, const void* bias,
+                      int64_t N, int32_t H, int32_t V, int32_t dtype, float temperature, const int64_t* targets,
+                      float* entropy_out, float* logp_out, void* ws, size_t ws_bytes, hipStream_t st) {
   size_t need = 0;
-  int rc = plp_selective_entropy_workspace_size(N, H, V, dtype, &need);
+  int rc = selective_workspace_size(N, H, V, dtype, prepared, &need);
   if (rc) return rc;
+  if (prepared && (!wprep || (uintptr_t)wprep % 16 != 0))
+    return fail(PLP_E_INVALID, "weight_prepared must be non-NULL and 16-byte aligned");
   if (!hidden || !weight || !entropy_out) return fail(PLP_E_INVALID, "hidden, weight and entropy_out are required");
   if (((uintptr_t)hidden | (uintptr_t)weight | (uintptr_t)bias) % 16 != 0)
     return fail(PLP_E_INVALID, "hidden, weight and bias must be 16-byte aligned");
@@ -769,11 +779,14 @@ PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const 
   rc = check_ws(ws, ws_bytes, need);
   if (rc) return rc;
   SelBufs sb;
-  carve_selective(ws, N, H, V, dtype, sb);
+  carve_selective(ws, N, H, V, dtype, prepared, sb);
   const int64_t* y = targets;  // may be NULL: no target logit is taken
   const float inv_tau = 1.0f / temperature;
   if (sb.mfma) {
-    HIP_TRY(launch_frag_copy((const __bf16*)weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H, sb.Wf, st));
+    if (prepared)
+      sb.Wf = (__bf16*)wprep;  // read only
+    else
+      HIP_TRY(launch_frag_copy((const __bf16*)weight, nullptr, nullptr, V, round_up(V, 2 * kBK) / kBK, H, sb.Wf, st));
     if (bias) HIP_TRY(launch_bias_f32((const __bf16*)bias, V, sb.bias2, st));
     const float* bias2 = bias ? sb.bias2 : nullptr;
     HIP_TRY(forward_sweep(hidden, sb.Wf, bias2, (const __bf16*)bias, N, H, V, inv_tau, sb.sv, false, sb.stats, nullptr,
@@ -786,6 +799,32 @@ PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const 
                          logp_out ? logp_out : (y ? sb.scratch_lp : nullptr), entropy_out, nullptr, nullptr, st,
                          sb.mfma ? &sb.fp : nullptr));
   return ok();
+}
+
+}  // namespace
+
+PLP_API int plp_selective_entropy_workspace_size(int64_t N, int32_t H, int32_t V, int32_t dtype, size_t* bytes) {
+  return selective_workspace_size(N, H, V, dtype, false, bytes);
+}
+
+PLP_API int plp_selective_entropy(const void* hidden, const void* weight, const void* bias, int64_t N, int32_t H,
+                                  int32_t V, int32_t dtype, float temperature, const int64_t* targets,
+                                  float* entropy_out, float* logp_out, void* ws, size_t ws_bytes, hipStream_t st) {
+  return selective_entropy(hidden, weight, nullptr, false, bias, N, H, V, dtype, temperature, targets, entropy_out,
+                           logp_out, ws, ws_bytes, st);
+}
+
+PLP_API int plp_selective_entropy_prepared_workspace_size(int64_t N, int32_t H, int32_t V, int32_t dtype,
+                                                          size_t* bytes) {
+  return selective_workspace_size(N, H, V, dtype, true, bytes);
+}
+
+PLP_API int plp_selective_entropy_prepared(const void* hidden, const void* weight, const void* weight_prepared,
+                                           const void* bias, int64_t N, int32_t H, int32_t V, int32_t dtype,
+                                           float temperature, const int64_t* targets, float* entropy_out,
+                                           float* logp_out, void* ws, size_t ws_bytes, hipStream_t st) {
+  return selective_entropy(hidden, weight, weight_prepared, true, bias, N, H, V, dtype, temperature, targets,
+                           entropy_out, logp_out, ws, ws_bytes, st);
 }
 
 PLP_API int plp_entropy_quantile_mask_workspace_size(int64_t N, size_t* bytes) {

@@ -202,6 +202,15 @@ int main() {
                                 nullptr, nullptr, 0, nullptr) == PLP_E_INVALID);
     CHECK(plp_selective_entropy(h, W, nullptr, 100, 256, 1000, PLP_DTYPE_BF16, 1.f, nullptr, (float*)out_buf,
                                 nullptr, nullptr, 0, nullptr) == PLP_E_WORKSPACE);
+    size_t prep_bytes = 0;
+    CHECK(plp_selective_entropy_prepared_workspace_size(100, 256, 1000, PLP_DTYPE_BF16, &prep_bytes) == PLP_OK &&
+          prep_bytes > 0 && prep_bytes < bytes);
+    CHECK(plp_selective_entropy_prepared_workspace_size(100, 200, 1000, PLP_DTYPE_BF16, &prep_bytes) ==
+          PLP_E_UNSUPPORTED);
+    CHECK(plp_selective_entropy_prepared(h, W, nullptr, nullptr, 100, 256, 1000, PLP_DTYPE_BF16, 1.f, nullptr,
+                                         (float*)out_buf, nullptr, nullptr, 0, nullptr) == PLP_E_INVALID);
+    CHECK(plp_selective_entropy_prepared(h, W, W, nullptr, 100, 256, 1000, PLP_DTYPE_BF16, 1.f, nullptr,
+                                         (float*)out_buf, nullptr, nullptr, 0, nullptr) == PLP_E_WORKSPACE);
     CHECK(plp_entropy_quantile_mask_workspace_size(-1, &bytes) == PLP_E_INVALID);
     CHECK(plp_entropy_quantile_mask_workspace_size(100, &bytes) == PLP_OK && bytes > 0);
     CHECK(plp_entropy_quantile_mask((const float*)out_buf, (const uint8_t*)m, 100, 2.0, (uint8_t*)out_buf, nullptr,

@@ -170,7 +170,7 @@ def test_other_entry_points_validate():
     assert "q must lie" in L.plp_last_error().decode()
     a = _valid_args()
     assert L.plp_policy_loss_from_logprobs(ctypes.byref(a), None, None, None, None, 0, None) == abi.PLP_E_INVALID
-    assert L.plp_abi_version() == 4
+    assert L.plp_abi_version() == 5 == abi.ABI_VERSION
 
 
 def test_noalloc_quantile_rejects_bad_arguments_on_the_host():
@@ -222,3 +222,36 @@ def test_prepared_weight_size_and_checks():
         prep = plp.workspace_size(B, 512, 896, V, top_entropy_quantile=q, chunk_sequences=chunk,
                                   weight_prepared=True)
         assert full - prep == plp.prepared_weight_size(896, V)
+
+
+def test_selective_entropy_prepared_size_and_checks():
+    """The selective-entropy call on a prepared weight: its workspace is the
+    plain call's less exactly the weight's copy; shapes off the matrix-core
+    path, a NULL or misaligned prepared copy and the plain call's own errors
+    are rejected on the host."""
+    import rl_policy_gradient_amd as plp
+    L = _lib()
+    n, m = ctypes.c_size_t(), ctypes.c_size_t()
+    for N, H, V in ((512, 896, 151936), (65536, 896, 151936), (37, 128, 1000), (1, 512, 40)):
+        assert L.plp_selective_entropy_workspace_size(N, H, V, abi.DTYPE_BF16, ctypes.byref(n)) == 0
+        assert L.plp_selective_entropy_prepared_workspace_size(N, H, V, abi.DTYPE_BF16, ctypes.byref(m)) == 0
+        assert n.value - m.value == plp.prepared_weight_size(H, V), (N, H, V)
+    assert L.plp_selective_entropy_prepared_workspace_size(64, 200, 100, abi.DTYPE_BF16,
+                                                           ctypes.byref(m)) == abi.PLP_E_UNSUPPORTED
+    assert L.plp_selective_entropy_prepared_workspace_size(64, 128, 100, abi.DTYPE_F32,
+                                                           ctypes.byref(m)) == abi.PLP_E_UNSUPPORTED
+    assert L.plp_selective_entropy_prepared_workspace_size(0, 128, 100, abi.DTYPE_BF16,
+                                                           ctypes.byref(m)) == abi.PLP_E_INVALID
+    assert L.plp_selective_entropy_prepared_workspace_size(64, 128, 100, abi.DTYPE_BF16, ctypes.byref(m)) == 0
+    ws = m.value
+
+    def call(wprep, h=0x1000, w=0x2000, ent=0x3000, ws_ptr=0x100000, ws_bytes=ws):
+        return L.plp_selective_entropy_prepared(h, w, wprep, None, 64, 128, 100, abi.DTYPE_BF16, ctypes.c_float(1.0),
+                                                None, ent, None, ws_ptr, ws_bytes, None)
+
+    assert call(None) == abi.PLP_E_INVALID
+    assert b"weight_prepared" in L.plp_last_error()
+    assert call(0x4008) == abi.PLP_E_INVALID
+    assert b"16-byte" in L.plp_last_error()
+    assert call(0x4000, ent=None) == abi.PLP_E_INVALID
+    assert call(0x4000, ws_bytes=ws - 1) == abi.PLP_E_WORKSPACE

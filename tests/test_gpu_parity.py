@@ -290,6 +290,48 @@ def test_selective_entropy(case):
     np.testing.assert_array_equal(ent.cpu().numpy(), ent2.cpu().numpy())
 
 
+@pytest.mark.parametrize("case", [
+    dict(N=200, H=256, V=1000, bias=False, tau=1.0, flag=False),
+    dict(N=131, H=896, V=4099, bias=True, tau=1.3, flag=False),
+    dict(N=90, H=640, V=40, bias=True, tau=1.0, flag=False),
+    dict(N=300, H=256, V=1500, bias=True, tau=1.0, flag=True),
+])
+def test_selective_entropy_prepared_weight(case):
+    """plp_selective_entropy_prepared on the weight's matrix-core copy made
+    beforehand (plp_prepare_weight): entropy and log-prob bitwise equal to the
+    plain call's (which makes the same copy itself), twice in a row on the same
+    copy, and the oracle's bar met; with flag, logits far above the first
+    tile's (as in the flagged-row test) send every row through the second
+    sweep, which reads the prepared copy too."""
+    import rl_policy_gradient_amd as plp
+    spec = synth.small("se_prep", cfg_id=111, B=1, T=case["N"], H=case["H"], V=case["V"], bias=case["bias"],
+                       w_std=0.05, prompt_fixed=0)
+    _say(f"selective_entropy prepared weight {case}")
+    d = synth.make(spec)
+    b_raw = d["b_raw"]
+    if case["flag"]:
+        b = d["b"].copy()
+        b[:32] = -100.0
+        b[900:905] = 60.0
+        b_raw = synth.round_bf16_bits(b)
+    b_f = synth.bf16_bits_to_f32(b_raw) if b_raw is not None else None
+    ref = oracle.forward_rows(d["h"], d["W"], b_f, case["tau"], d["targets"])
+    h = dev_tensor(d["h_raw"], "bf16")
+    W = dev_tensor(d["W_raw"], "bf16")
+    bt = dev_tensor(b_raw, "bf16") if b_raw is not None else None
+    y = dev_tensor(d["targets"])
+    wp = plp.prepare_weight(W)
+    ent, lp = plp.selective_entropy(h, W, bt, y, temperature=case["tau"])
+    outs = [plp.selective_entropy(h, W, bt, y, temperature=case["tau"], weight_prepared=wp) for _ in range(2)]
+    torch.cuda.synchronize()
+    for ent_p, lp_p in outs:
+        np.testing.assert_array_equal(ent_p.cpu().numpy(), ent.cpu().numpy())
+        np.testing.assert_array_equal(lp_p.cpu().numpy(), lp.cpu().numpy())
+    tol = 1e-4 if case["flag"] else 2e-5
+    np.testing.assert_allclose(outs[0][0].cpu().numpy(), ref["entropy"], rtol=0, atol=tol)
+    np.testing.assert_allclose(outs[0][1].cpu().numpy(), ref["logp"], rtol=0, atol=tol)
+
+
 def test_selective_entropy_flagged_rows():
     """The no-grad entropy entry point with logits far above the first
     tile's (bias -100 on it, +60 further on): every row flagged and taken
