@@ -21,23 +21,30 @@ pytestmark = pytest.mark.gpu
 LOSSES = (synth.GMPO, synth.GSPO_TOKEN, synth.GRPO, synth.BNPO, synth.DAPO)
 
 
-def _draw(k: int, rng: np.random.Generator) -> synth.Spec:
-    generic = rng.random() < 0.25
+def _draw(k: int, rng: np.random.Generator, large: bool = False) -> synth.Spec:
+    generic = not large and rng.random() < 0.25
     if generic:
         dtype = "f32" if rng.random() < 0.6 else "bf16"
         H = int(rng.choice([32, 48, 64, 96] if dtype == "f32" else [96, 200]))
     else:
         dtype = "bf16"
-        H = 128 * int(rng.integers(1, 8))
-    B = int(rng.integers(1, 5))
-    T = int(rng.choice([1, 7, 33, 64, 100, 129, 257]))
-    V = int(rng.choice([1, 2, 31, 33, 500, 1000, 1531, 2500]))
+        H = 128 * int(rng.integers(4 if large else 1, 8))
+    if large:  # LM-head vocabularies, a few hundred to a few thousand tokens
+        B = int(rng.integers(1, 4))
+        T = int(rng.choice([300, 700, 1025]))
+        V = int(rng.choice([32000, 65536, 151936]))
+    else:
+        B = int(rng.integers(1, 5))
+        T = int(rng.choice([1, 7, 33, 64, 100, 129, 257]))
+        V = int(rng.choice([1, 2, 31, 33, 500, 1000, 1531, 2500]))
     loss = LOSSES[int(rng.integers(0, len(LOSSES)))]
+    if large:  # few cases: every loss type in turn
+        loss = LOSSES[k % len(LOSSES)]
     kw = dict(cfg_id=300 + k, B=B, T=T, H=H, V=V, dtype=dtype, loss_type=loss,
-              bias=bool(rng.random() < 0.5), w_std=0.05 if H <= 256 else 0.03,
+              bias=bool(rng.random() < 0.5), w_std=0.02 if large else (0.05 if H <= 256 else 0.03),
               temperature=float(rng.choice([1.0, 1.0, 0.7, 1.3])),
               top_entropy_quantile=float(rng.choice([1.0, 1.0, 0.5, 0.2])),
-              prompt_lo=0, prompt_hi=min(10, max(0, T - 1)),
+              prompt_lo=0, prompt_hi=min(100 if large else 10, max(0, T - 1)),
               zero_adv_fraction=float(rng.choice([0.0, 0.0, 0.25])))
     if loss == synth.GSPO_TOKEN:
         kw.update(eps_low=3e-3, eps_high=4e-3, old_noise_std=1e-2)
@@ -56,9 +63,9 @@ def _draw(k: int, rng: np.random.Generator) -> synth.Spec:
     return synth.small(f"random{k}", **kw)
 
 
-def _cases(n: int = 96):
+def _cases(n: int = 96, n_large: int = 6):
     rng = np.random.default_rng(20261202)
-    return [_draw(k, rng) for k in range(n)]
+    return [_draw(k, rng) for k in range(n)] + [_draw(n + k, rng, large=True) for k in range(n_large)]
 
 
 CASES = _cases()
